@@ -1,0 +1,389 @@
+"""DensityKV per-head token banks in float64 (oracle; test infrastructure only).
+
+Page: "DensityKV: Density-Guided KV Cache Compression for Long Video
+Generation" (paper summary).  Sections used:
+
+* Method, "Soft-Riesz Density" and appendix B.1: a regularised inverse-power
+  interaction of the squared post-RoPE key distance, with bandwidth sigma,
+  decay p and softening eps; the density of a state is the sum of its
+  interactions with the other states of the same (layer, head) bank.
+* Method, "Online Density-Constrained Bank Update" and appendix B.1 "Online
+  Bank Update": candidates ordered by mean-normalised insertion disturbance
+  (lower first); the largest prefix length k that every head of the layer can
+  admit; each bank state's density may grow to at most tau times its frozen
+  insertion baseline; evictions take the states that cross that bound, then
+  the densest, until capacity is released; co-admitted states set their
+  baselines together; values stay paired with their keys.
+* Appendix D: defaults M = 9,360, tau = 2.0, sigma = 8; appendix E: eps = 1,
+  p = 2, the candidate order, baseline, eviction and prefix ablations.
+
+Readings where the page is silent (each is listed in the design notes):
+
+* phi(d2) = (eps + d2 / sigma^2) ** (-p / 2)   (Riesz 1/r^p on the softened distance)
+* the self term is excluded from a state's density; the density counts bank
+  states only (not sink, window or rejected candidates)
+* disturbance D(c) = sum over bank states of phi(c, b); delta = D / mean D over
+  the head's candidates (0 when the bank is empty or the mean is 0); order is
+  ascending (delta, token id), per head
+* for prefix length k: projected density rho'(k) = rho + sum over the first k
+  candidates of phi; a state crosses when rho'(k) > tau * rho0 (strict; never
+  when tau is infinite); eviction count e(k) = max(0, n + k - M); k is
+  feasible when every density head has |crossed| <= e(k) and k <= min(N, M);
+  k = 0 (admit nothing, evict nothing) is always feasible
+* eviction set = crossed states plus the highest projected densities among the
+  rest (ties: lower token id first) until e(k*) states are chosen
+* admitted states get rho0 = their density in the new bank; survivors keep rho0
+
+Parity pins (tests/test_oracle_density.py): closed-form densities on collinear
+keys, permutation and rotation invariance, the A.1 logit-gap bound, FIFO
+reduction at p = 0 and tau = inf, full admission when capacity exceeds the
+history, top-e-by-density eviction at tau = inf, the duplicate-key invariant,
+a hand-computed admission example under tests/golden/, and agreement of the
+blocked prefix-sum tier with a from-scratch brute-force tier.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Params:
+    M: int
+    tau: float = 2.0
+    sigma: float = 8.0
+    eps: float = 1.0
+    p: float = 2.0
+
+
+# ---------------------------------------------------------------------------
+# interaction and density
+# ---------------------------------------------------------------------------
+
+def phi(d2: np.ndarray, prm: Params) -> np.ndarray:
+    """Soft-Riesz interaction of squared distances: (eps + d2/sigma^2)^(-p/2)."""
+    base = prm.eps + np.asarray(d2, dtype=np.float64) / (prm.sigma * prm.sigma)
+    if prm.p == 0.0:
+        return np.ones_like(base)
+    return base ** (-prm.p / 2.0)
+
+
+def sqdist_direct(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """sum_i (a_i - b_i)^2 for every row pair, from the differences themselves."""
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    out = np.empty((A.shape[0], B.shape[0]), dtype=np.float64)
+    step = max(1, int(4_000_000 // max(1, B.shape[0] * max(1, A.shape[1]))))
+    for i in range(0, A.shape[0], step):
+        diff = A[i:i + step, None, :] - B[None, :, :]
+        out[i:i + step] = np.einsum("mnd,mnd->mn", diff, diff)
+    return out
+
+
+def sqdist_gram(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """Same quantity through ||a||^2 + ||b||^2 - 2 a.b in float64 (large shapes)."""
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    na = np.einsum("md,md->m", A, A)
+    nb = np.einsum("nd,nd->n", B, B)
+    return np.maximum(na[:, None] + nb[None, :] - 2.0 * (A @ B.T), 0.0)
+
+
+def sqdist(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    if A.shape[0] * B.shape[0] * max(1, A.shape[1]) <= 2_000_000:
+        return sqdist_direct(A, B)
+    return sqdist_gram(A, B)
+
+
+def phi_matrix(A: np.ndarray, B: np.ndarray, prm: Params) -> np.ndarray:
+    return phi(sqdist(A, B), prm)
+
+
+def _row_block(ncols: int) -> int:
+    return max(1, int(16_000_000 // max(1, ncols)))
+
+
+def phi_rowsum(A: np.ndarray, B: np.ndarray, prm: Params) -> np.ndarray:
+    """For each row a of A: sum over rows b of B of phi(a, b)."""
+    out = np.zeros(A.shape[0], dtype=np.float64)
+    if B.shape[0] == 0:
+        return out
+    step = _row_block(B.shape[0])
+    for i in range(0, A.shape[0], step):
+        out[i:i + step] = phi_matrix(A[i:i + step], B, prm).sum(axis=1)
+    return out
+
+
+def density(K: np.ndarray, prm: Params) -> np.ndarray:
+    """rho_x = sum over y != x in the same set of phi(||x - y||^2)."""
+    n = K.shape[0]
+    out = np.zeros(n, dtype=np.float64)
+    if n == 0:
+        return out
+    step = _row_block(n)
+    for i in range(0, n, step):
+        blk = phi_matrix(K[i:i + step], K, prm)
+        rows = np.arange(blk.shape[0])
+        blk[rows, i + rows] = 0.0
+        out[i:i + step] = blk.sum(axis=1)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# bank state
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class HeadBank:
+    """One (layer, head) bank: exact K/V rows, token ids and frozen baselines."""
+    tok: np.ndarray      # int64 [n]
+    K: np.ndarray        # float64 [n, d]
+    V: np.ndarray        # float64 [n, d]
+    rho0: np.ndarray     # float64 [n]
+
+    @staticmethod
+    def empty(d: int) -> "HeadBank":
+        return HeadBank(np.zeros(0, np.int64), np.zeros((0, d)), np.zeros((0, d)), np.zeros(0))
+
+    @property
+    def n(self) -> int:
+        return int(self.tok.shape[0])
+
+    def sorted_by_tok(self) -> "HeadBank":
+        o = np.argsort(self.tok, kind="stable")
+        return HeadBank(self.tok[o], self.K[o], self.V[o], self.rho0[o])
+
+
+# ---------------------------------------------------------------------------
+# stages (one head)
+# ---------------------------------------------------------------------------
+
+def disturbance(bankK: np.ndarray, candK: np.ndarray, prm: Params):
+    """Insertion disturbance D(c) and its mean-normalised form delta(c)."""
+    D = phi_rowsum(np.asarray(candK, np.float64), np.asarray(bankK, np.float64), prm)
+    mean = D.mean() if D.size else 0.0
+    delta = D / mean if (bankK.shape[0] > 0 and mean > 0.0) else np.zeros_like(D)
+    return D, delta
+
+
+def candidate_order(delta: np.ndarray, tok: np.ndarray) -> np.ndarray:
+    """Permutation sorting candidates by ascending (delta, token id)."""
+    return np.lexsort((np.asarray(tok, np.int64), np.asarray(delta, np.float64))).astype(np.int64)
+
+
+def crossing_times(bankK, rho, rho0, candK_sorted, prm: Params, at: Sequence[np.ndarray] = ()):
+    """First prefix length k at which each bank state crosses tau * rho0.
+
+    Returns (t, vals) where t[b] in [0, kmax] is the smallest k with
+    rho'_b(k) = rho_b + sum_{j<k} phi(b, c_j) > tau * rho0_b, or kmax + 1 when
+    the state never crosses within kmax = len(candK_sorted).  The running sum
+    follows the candidate order.  For each per-row array of prefix lengths in
+    ``at`` the projected densities rho'_b(at[b]) are returned in ``vals``.
+    """
+    n, kmax = bankK.shape[0], candK_sorted.shape[0]
+    t = np.full(n, kmax + 1, dtype=np.int64)
+    vals = [np.empty(n, dtype=np.float64) for _ in at]
+    step = _row_block(kmax + 1)
+    finite = math.isfinite(prm.tau)
+    for i in range(0, n, step):
+        m = min(step, n - i)
+        blk = np.empty((m, kmax + 1), dtype=np.float64)
+        blk[:, 0] = 0.0
+        if kmax:
+            np.cumsum(phi_matrix(bankK[i:i + m], candK_sorted, prm), axis=1, out=blk[:, 1:])
+        blk += rho[i:i + m, None]
+        if finite:
+            crossed = blk > (prm.tau * rho0[i:i + m])[:, None]
+            anyc = crossed.any(axis=1)
+            tt = t[i:i + m]
+            tt[anyc] = np.argmax(crossed[anyc], axis=1)
+        for a, o in zip(at, vals):
+            o[i:i + m] = blk[np.arange(m), np.asarray(a)[i:i + m]]
+    return t, vals
+
+
+def projected_density(bankK, rho, candK_sorted, k: int, prm: Params) -> np.ndarray:
+    """rho'_b(k) = rho_b + sum over the first k ordered candidates of phi(b, c)."""
+    return rho + phi_rowsum(bankK, np.asarray(candK_sorted, np.float64)[:k], prm)
+
+
+def feasible_prefix(ts: Sequence[np.ndarray], ns: Sequence[int], M: int, kmax: int):
+    """Largest k in [0, kmax] feasible for every density head.
+
+    |V_h(k)| = #{b : t_b <= k}; e_h(k) = max(0, n_h + k - M); feasible iff
+    |V_h(k)| <= e_h(k) for all h.  k = 0 is always feasible.
+    Returns (kstar, feasible[k] boolean array).
+    """
+    ks = np.arange(kmax + 1)
+    feas = np.ones(kmax + 1, dtype=bool)
+    for t, n in zip(ts, ns):
+        hist = np.bincount(np.minimum(t, kmax + 1), minlength=kmax + 2)[: kmax + 1]
+        Vk = np.cumsum(hist)
+        ek = np.maximum(0, n + ks - M)
+        feas &= Vk <= ek
+    feas[0] = True
+    return int(np.nonzero(feas)[0].max()), feas
+
+
+def eviction_set(proj_k: np.ndarray, crossed: np.ndarray, tok: np.ndarray, e: int) -> np.ndarray:
+    """Boolean mask: crossed states, then the highest projected densities.
+
+    Among non-crossed states ties in projected density go to the lower token
+    id first.  The total count is e (the crossed set never exceeds e at a
+    feasible k).
+    """
+    n = proj_k.shape[0]
+    ev = np.array(crossed, dtype=bool, copy=True)
+    r = e - int(ev.sum())
+    if r < 0:
+        raise ValueError("crossed set exceeds the eviction count")
+    if r > 0:
+        rest = np.nonzero(~ev)[0]
+        o = np.lexsort((tok[rest], -proj_k[rest]))
+        ev[rest[o[:r]]] = True
+    assert int(ev.sum()) == e and n >= e
+    return ev
+
+
+# ---------------------------------------------------------------------------
+# one layer update (all heads)
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class UpdateInfo:
+    kstar: int
+    kmax: int
+    D: List[Optional[np.ndarray]]
+    delta: List[Optional[np.ndarray]]
+    order: List[Optional[np.ndarray]]
+    t: List[Optional[np.ndarray]]
+    rho: List[Optional[np.ndarray]]          # density before the update
+    proj: List[Optional[np.ndarray]]         # projected density at k*
+    crossed: List[Optional[np.ndarray]]      # mask over old bank rows at k*
+    evicted: List[Optional[np.ndarray]]      # mask over old bank rows
+    e: List[int]
+    feasible: Optional[np.ndarray]
+
+
+def update_layer(banks: List[Optional[HeadBank]], candK: np.ndarray, candV: np.ndarray,
+                 cand_tok: np.ndarray, prm: Params, heads: Optional[Sequence[int]] = None,
+                 order: Optional[Sequence[np.ndarray]] = None, kstar: Optional[int] = None):
+    """Apply one admission/eviction update to the density heads of a layer.
+
+    ``banks[h]`` is None for heads that do not keep a density bank; ``heads``
+    restricts the update to those heads (default: every head with a bank).
+    ``order`` may supply a per-head candidate permutation (stage replay) and
+    ``kstar`` a prefix length to apply instead of the computed one.
+    Returns (new_banks, UpdateInfo).  Candidate rows are [H][N][d].
+    """
+    H = len(banks)
+    heads = [h for h in range(H) if banks[h] is not None] if heads is None else list(heads)
+    N = int(cand_tok.shape[0])
+    kmax = min(N, prm.M)
+    tok = np.asarray(cand_tok, np.int64)
+    info = UpdateInfo(0, kmax, [None] * H, [None] * H, [None] * H, [None] * H, [None] * H,
+                      [None] * H, [None] * H, [None] * H, [0] * H, None)
+    for h in heads:
+        b = banks[h]
+        D, delta = disturbance(b.K, candK[h], prm)
+        pi = candidate_order(delta, tok) if order is None else np.asarray(order[h], np.int64)
+        rho = density(b.K, prm)
+        t, _ = crossing_times(b.K, rho, b.rho0, np.asarray(candK[h], np.float64)[pi[:kmax]], prm)
+        info.D[h], info.delta[h], info.order[h], info.t[h], info.rho[h] = D, delta, pi, t, rho
+    ks, feas = feasible_prefix([info.t[h] for h in heads], [banks[h].n for h in heads], prm.M, kmax)
+    info.feasible = feas
+    info.kstar = ks if kstar is None else int(kstar)
+    k = info.kstar
+    new = list(banks)
+    for h in heads:
+        b = banks[h]
+        e = max(0, b.n + k - prm.M)
+        proj_k = projected_density(b.K, info.rho[h], np.asarray(candK[h], np.float64)[info.order[h]], k, prm)
+        crossed = (info.t[h] <= k) if k > 0 else np.zeros(b.n, bool)
+        ev = eviction_set(proj_k, crossed, b.tok, e) if k > 0 else np.zeros(b.n, bool)
+        info.proj[h], info.crossed[h], info.evicted[h], info.e[h] = proj_k, crossed, ev, e
+        adm = info.order[h][:k]
+        keep = ~ev
+        K2 = np.concatenate([b.K[keep], np.asarray(candK[h], np.float64)[adm]])
+        V2 = np.concatenate([b.V[keep], np.asarray(candV[h], np.float64)[adm]])
+        tok2 = np.concatenate([b.tok[keep], tok[adm]])
+        rho_new = density(K2, prm)
+        rho0 = np.concatenate([b.rho0[keep], rho_new[keep.sum():]])
+        new[h] = HeadBank(tok2, K2, V2, rho0)
+    return new, info
+
+
+def update_layer_brute(banks: List[Optional[HeadBank]], candK, candV, cand_tok, prm: Params,
+                       heads: Optional[Sequence[int]] = None):
+    """Same update recomputing every prefix length from scratch (tiny inputs).
+
+    For each k the projected density of every bank state is summed directly
+    over the first k ordered candidates, with distances from explicit
+    differences; no running sums, no Gram form.
+    """
+    H = len(banks)
+    heads = [h for h in range(H) if banks[h] is not None] if heads is None else list(heads)
+    N = int(cand_tok.shape[0])
+    kmax = min(N, prm.M)
+    tok = np.asarray(cand_tok, np.int64)
+    orders, rhos = {}, {}
+    for h in heads:
+        b = banks[h]
+        Dmat = phi(sqdist_direct(np.asarray(candK[h], np.float64), b.K), prm)
+        D = Dmat.sum(axis=1)
+        mean = D.mean() if D.size else 0.0
+        delta = D / mean if (b.n > 0 and mean > 0) else np.zeros(N)
+        orders[h] = np.array(sorted(range(N), key=lambda c: (delta[c], tok[c])), dtype=np.int64)
+        Bm = phi(sqdist_direct(b.K, b.K), prm)
+        np.fill_diagonal(Bm, 0.0)
+        rhos[h] = Bm.sum(axis=1)
+
+    def crossed_at(h, k):
+        b = banks[h]
+        if k == 0 or not math.isfinite(prm.tau):
+            return np.zeros(b.n, bool), rhos[h].copy()
+        adm = np.asarray(candK[h], np.float64)[orders[h][:k]]
+        pr = rhos[h] + phi(sqdist_direct(b.K, adm), prm).sum(axis=1)
+        return pr > prm.tau * b.rho0, pr
+
+    kstar = 0
+    for k in range(kmax + 1):
+        ok = True
+        for h in heads:
+            c, _ = crossed_at(h, k)
+            if int(c.sum()) > max(0, banks[h].n + k - prm.M):
+                ok = False
+                break
+        if ok:
+            kstar = k
+    new = list(banks)
+    for h in heads:
+        b = banks[h]
+        c, pr = crossed_at(h, kstar)
+        if kstar > 0:
+            adm_full = np.asarray(candK[h], np.float64)[orders[h][:kstar]]
+            pr = rhos[h] + phi(sqdist_direct(b.K, adm_full), prm).sum(axis=1)
+        e = max(0, b.n + kstar - prm.M)
+        ev = c.copy()
+        rest = sorted([i for i in range(b.n) if not ev[i]], key=lambda i: (-pr[i], b.tok[i]))
+        for i in rest[: e - int(ev.sum())]:
+            ev[i] = True
+        adm = orders[h][:kstar]
+        keep = ~ev
+        K2 = np.concatenate([b.K[keep], np.asarray(candK[h], np.float64)[adm]])
+        V2 = np.concatenate([b.V[keep], np.asarray(candV[h], np.float64)[adm]])
+        tok2 = np.concatenate([b.tok[keep], tok[adm]])
+        Bm = phi(sqdist_direct(K2, K2), prm)
+        np.fill_diagonal(Bm, 0.0)
+        rnew = Bm.sum(axis=1)
+        rho0 = np.concatenate([b.rho0[keep], rnew[keep.sum():]])
+        new[h] = HeadBank(tok2, K2, V2, rho0)
+    return new, kstar, orders
+
+
+def bank_payload_bytes(L: int, H: int, M: int, dk: int, dv: int, elem_bytes: int = 2) -> int:
+    """Bytes of the exact K/V payload of L layers x H heads x M states."""
+    return L * H * M * (dk + dv) * elem_bytes

@@ -1,0 +1,82 @@
+"""Forcing-KV static / dynamic head retention in float64.
+
+Test infrastructure only (see the package header).
+
+Page: "Forcing-KV: Hybrid KV Cache Compression for Efficient Autoregressive
+Video Diffusion Models" (paper notes).
+
+* Section 3.3 (static structural pruning): a static head's chunk queries
+  attend over the sink frame, the transition frame -- the frame just before
+  the chunk, token range [(iC-1)F, iCF) -- and the current chunk
+  [iCF, (i+1)CF).
+* Section 3.4 (dynamic similarity pruning): every latent frame is cut into
+  contiguous segments; segment j of frame t scores the cosine similarity of
+  the keys of frame t and frame t+1 on that segment; BottomK keeps the
+  floor(r * n) lowest scores (least redundant).
+* Section 3.5 sketch: the adjacent-frame chain ends with the first frame of
+  the new chunk; a segment's score is the mean of token-wise cosines; token
+  features concatenate all dynamic heads, so the kept indices are shared by
+  the dynamic heads; the selection is one global BottomK over all (frame,
+  segment) items; kept items are gathered in token order.
+
+Readings: cos(a, b) = a.b / max(|a| |b|, 1e-8); r is the kept fraction and
+the kept count is floor(r * items) computed in double precision; ties in the
+BottomK go to the lower item index.
+
+Parity pins (tests/test_oracle_forcing.py): r = 1 keeps everything (full
+attention), r = 0 keeps nothing, identical adjacent frames score exactly 1,
+the cosine agrees with torch's cosine_similarity in float64, and the static
+token ranges reproduce the section 3.3 formula.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+COS_EPS = 1e-8
+
+
+def segment_scores(hist: np.ndarray, nxt: np.ndarray, F: int, seg_len: int) -> np.ndarray:
+    """Scores s[t * nseg + j] for history frames t and segments j.
+
+    hist: [H_dyn][T*F][d] history keys of the dynamic heads (time order);
+    nxt:  [H_dyn][F][d] keys of the first frame of the new chunk.
+    Token features concatenate the dynamic heads.
+    """
+    hist = np.asarray(hist, np.float64)
+    nxt = np.asarray(nxt, np.float64)
+    Hd, TF, d = hist.shape
+    T = TF // F
+    nseg = F // seg_len
+    chain = np.concatenate([hist, nxt], axis=1)               # [Hd][(T+1)F][d]
+    feats = chain.transpose(1, 0, 2).reshape((T + 1), F, Hd * d)
+    a, b = feats[:-1], feats[1:]                               # [T][F][Hd*d]
+    dot = np.einsum("tfx,tfx->tf", a, b)
+    na = np.sqrt(np.einsum("tfx,tfx->tf", a, a))
+    nb = np.sqrt(np.einsum("tfx,tfx->tf", b, b))
+    cos = dot / np.maximum(na * nb, COS_EPS)
+    return cos.reshape(T, nseg, seg_len).mean(axis=2).reshape(-1)
+
+
+def keep_count(r: float, items: int) -> int:
+    return int(math.floor(float(r) * items))
+
+
+def bottomk(scores: np.ndarray, r: float) -> np.ndarray:
+    """Indices of the floor(r * n) lowest scores (ties: lower index), ascending."""
+    k = keep_count(r, scores.shape[0])
+    order = np.lexsort((np.arange(scores.shape[0]), np.asarray(scores, np.float64)))
+    return np.sort(order[:k])
+
+
+def kept_token_rows(kept: np.ndarray, F: int, seg_len: int) -> np.ndarray:
+    """History row indices covered by the kept (frame, segment) items, in token order."""
+    nseg = F // seg_len
+    rows = [np.arange(seg_len) + (i // nseg) * F + (i % nseg) * seg_len for i in np.asarray(kept)]
+    return np.concatenate(rows) if rows else np.zeros(0, dtype=np.int64)
+
+
+def static_rows(T: int, F: int) -> np.ndarray:
+    """History rows a static head keeps: the transition frame [(T-1)F, TF)."""
+    return np.arange((T - 1) * F, T * F) if T > 0 else np.zeros(0, dtype=np.int64)
