@@ -1,0 +1,214 @@
+"""Benchmark: one layer-chunk of the head-wise compressed KV cache on one GPU.
+
+A step is the whole hot path for one layer and one chunk at 480P
+(Wan2.1-1.3B-like layer: 12 heads, head_dim 128, bf16, 1,560 tokens per
+latent frame):
+
+  kvbank_score   Soft-Riesz disturbance of 23,400 candidate keys against the
+                 9,360-state bank of every head, mean-normalised, ordered
+  kvbank_update  crossing scan, shared prefix, eviction, density fix-ups,
+                 gather into the bank, segment tables
+  chunk_attention  4,680 chunk queries over sink + bank + 6-frame window +
+                 chunk (up to 24,960 keys per head)
+
+The bank is restored from a device snapshot at the start of every step (the
+same update is replayed), and that copy is inside the timed region.
+Inputs are synthetic (seeded kvsynth generator), resident in HBM before
+timing starts.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ms/chunk/layer + attention TFLOP/s (% of bf16 peak) at 480P and 1080P, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def setup(name: str, seed: int = 0):
+    import numpy as np
+    import torch
+    import kv_cache_compression_head_amd as kb
+    from kv_cache_compression_head_amd.pipeline import LayerCache
+    from kvsynth import WORKLOADS, LayerGen, frame_tokens
+
+    wl = WORKLOADS[name]
+    gen = LayerGen(wl, seed, 0)
+    kdt = torch.bfloat16
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(kdt).contiguous()
+    devi = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to("cuda")
+    (b0, b1), (c0, c1) = wl.bank_updates
+    w0, w1 = wl.window
+    q0, q1 = wl.chunk
+    t = time.time()
+    inp = {}
+    inp["bankK"], inp["bankV"], inp["bankT"] = dev(gen.keys_all(range(b0, b1))), dev(gen.values_all(range(b0, b1))), devi(frame_tokens(wl, b0, b1))
+    inp["candK"], inp["candV"], inp["candT"] = dev(gen.keys_all(range(c0, c1))), dev(gen.values_all(range(c0, c1))), devi(frame_tokens(wl, c0, c1))
+    rw = [f - w0 for f in range(w0, w1)]
+    rc = [f - w0 for f in range(q0, q1)]
+    lay = kb.KVLayout(sink_k=dev(gen.keys_all([0])), sink_v=dev(gen.values_all([0])),
+                      win_k=dev(gen.keys_all(range(w0, w1), rw)), win_v=dev(gen.values_all(range(w0, w1))),
+                      win_start=0, win_len=(w1 - w0) * wl.F,
+                      chunk_k=dev(gen.keys_all(range(q0, q1), rc)), chunk_v=dev(gen.values_all(range(q0, q1))))
+    Q = dev(gen.queries_all(range(q0, q1), rc))
+    log(f"inputs generated in {time.time() - t:.1f}s")
+    desc = kb.LayerDesc(H=wl.H, d=wl.d, M=wl.M, dtype=kb.KVB_BF16, frame_tokens=wl.F, labels=[0] * wl.H,
+                        tau=wl.tau, sigma=wl.sigma, eps=wl.eps, p=wl.p)
+    lc = LayerCache(desc, seg_cap=8, max_N=max(inp["candK"].shape[1], inp["bankK"].shape[1]))
+    # cold bank: frames b0..b1 admitted together into the empty bank
+    lc.step(inp["bankK"], inp["bankV"], inp["bankT"], lay)
+    torch.cuda.synchronize()
+    assert int(lc.bank.count.min().cpu()) == wl.M, "cold bank not full"
+    snap = lc.bank.clone()
+    O = torch.empty(wl.H, wl.Lq, wl.d, dtype=kdt, device="cuda")
+    return wl, lc, snap, inp, lay, Q, O
+
+
+def one_step(lc, snap, inp, lay, Q, O, ev=None):
+    if ev is not None:
+        ev[0].record()
+    lc.bank.copy_(snap)
+    if ev is not None:
+        ev[1].record()
+    D, s, o = lc.score(inp["candK"], inp["candT"], lay)
+    if ev is not None:
+        ev[2].record()
+    lc.update(inp["candK"], inp["candV"], inp["candT"], D, o, lay)
+    if ev is not None:
+        ev[3].record()
+    lc.attention(Q, O)
+    if ev is not None:
+        ev[4].record()
+
+
+def cpu_baseline(name: str, seed: int = 0, heads=(0,)):
+    """The fp64 oracle on a bounded sample: the same layer-chunk for a subset
+    of heads (prefix computed over that subset), extrapolated to all heads."""
+    import numpy as np
+    from kvsynth import WORKLOADS, LayerGen, frame_tokens
+    from oracle import density as od
+    from oracle.attention import attention
+
+    wl = WORKLOADS[name]
+    gen = LayerGen(wl, seed, 0)
+    prm = od.Params(M=wl.M, tau=wl.tau, sigma=wl.sigma, eps=wl.eps, p=wl.p)
+    (b0, b1), (c0, c1) = wl.bank_updates
+    w0, w1 = wl.window
+    q0, q1 = wl.chunk
+    rw = [f - w0 for f in range(w0, w1)]
+    rc = [f - w0 for f in range(q0, q1)]
+    data = {}
+    for h in heads:
+        data[h] = dict(bK=gen.keys(h, range(b0, b1)).astype(np.float64), bV=gen.values(h, range(b0, b1)).astype(np.float64),
+                       cK=gen.keys(h, range(c0, c1)).astype(np.float64), cV=gen.values(h, range(c0, c1)).astype(np.float64),
+                       sK=gen.keys(h, [0]).astype(np.float64), sV=gen.values(h, [0]).astype(np.float64),
+                       wK=gen.keys(h, range(w0, w1), rw).astype(np.float64), wV=gen.values(h, range(w0, w1)).astype(np.float64),
+                       qK=gen.keys(h, range(q0, q1), rc).astype(np.float64), qV=gen.values(h, range(q0, q1)).astype(np.float64),
+                       Q=gen.queries(h, range(q0, q1), rc).astype(np.float64))
+    btok, ctok = frame_tokens(wl, b0, b1), frame_tokens(wl, c0, c1)
+    # cold bank (not timed): co-admitted, baselines = in-bank density
+    banks = [None] * wl.H
+    for h in heads:
+        banks[h] = od.HeadBank(btok.astype(np.int64), data[h]["bK"], data[h]["bV"], od.density(data[h]["bK"], prm))
+    cK = np.zeros((wl.H, 0, wl.d))
+    t = time.perf_counter()
+    cK = {h: data[h]["cK"] for h in heads}
+    cV = {h: data[h]["cV"] for h in heads}
+    new, info = od.update_layer(banks, cK, cV, ctok, prm, heads=list(heads))
+    for h in heads:
+        K = np.concatenate([data[h]["sK"], new[h].K, data[h]["wK"], data[h]["qK"]])
+        V = np.concatenate([data[h]["sV"], new[h].V, data[h]["wV"], data[h]["qV"]])
+        attention(data[h]["Q"], K, V)
+    dt = time.perf_counter() - t
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    return dt, threads, info.kstar
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="480p", choices=["480p", "1080p"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no "
+              "multi-GPU component to run)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import kv_cache_compression_head_amd as kb
+    kb.load_library()
+    wl, lc, snap, inp, lay, Q, O = setup(args.config)
+    log("setup done")
+    for _ in range(args.warmup):
+        one_step(lc, snap, inp, lay, Q, O)
+    torch.cuda.synchronize()
+    # timed region: exactly K steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(lc, snap, inp, lay, Q, O, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1000.0 / args.steps
+    stage = {"restore": [], "score": [], "update": [], "attention": []}
+    for e in evs:
+        stage["restore"].append(e[0].elapsed_time(e[1]))
+        stage["score"].append(e[1].elapsed_time(e[2]))
+        stage["update"].append(e[2].elapsed_time(e[3]))
+        stage["attention"].append(e[3].elapsed_time(e[4]))
+    avg = {k: sum(v) / len(v) for k, v in stage.items()}
+    kstar = int(lc.out.k_star.cpu()[0])
+    counts = lc.bank.count.cpu().tolist()
+    lkv = [wl.F + c + (wl.window[1] - wl.window[0]) * wl.F + wl.Lq for c in counts]
+    attn_flop = sum(4.0 * wl.Lq * l * wl.d for l in lkv)
+    attn_tflops = attn_flop / (avg["attention"] * 1e-3) / 1e12
+    # algorithmic bytes of the attention launch: Q + O + each head's K and V once
+    attn_bytes = sum(2 * wl.Lq * wl.d * 2 + 2 * l * wl.d * 2 for l in lkv)
+    roof = {"kernel": "attn_bf16_kernel (chunk_attention)", "bound": "mfma", "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None, "algorithmic_flop_per_launch": attn_flop, "algorithmic_bytes_per_launch": attn_bytes}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, 1 of 12 heads)")
+        dt, threads, ks_cpu = cpu_baseline(args.config)
+        cpu = {"value": round(dt * wl.H * 1000.0, 1), "unit": "ms/chunk/layer", "cores": threads, "kind": "oracle",
+               "sample": f"fp64 oracle, 1 of {wl.H} heads of the same layer-chunk (score + update + attention, "
+                         f"prefix over that head alone, k*={ks_cpu}), measured {dt:.2f} s, scaled x{wl.H}",
+               "host_cpus": len(os.sched_getaffinity(0))}
+    res = {
+        "metric": METRIC, "value": round(ms_step, 4), "unit": "ms/chunk/layer", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.config}: one layer-chunk, H={wl.H}, d={wl.d}, F={wl.F}, M={wl.M}, "
+                               f"N={inp['candK'].shape[1]}, Lq={wl.Lq}, window={wl.window[1] - wl.window[0]} frames, "
+                               f"tau={wl.tau}, sigma={wl.sigma}, p={wl.p}"},
+        "stages_ms": {k: round(v, 4) for k, v in avg.items()},
+        "attention_tflops": round(attn_tflops, 2), "attention_frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "k_star": kstar, "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,206 @@
+/*
+ * kvbank -- head-wise compressed KV cache for chunk-by-chunk autoregressive
+ * video diffusion, one attention layer at a time, on AMD Instinct MI355X
+ * (gfx950).  Plain C ABI: device pointers, sizes and a HIP stream; no
+ * framework types.
+ *
+ * The operations follow two methods described on public pages:
+ *
+ *  - "DensityKV: Density-Guided KV Cache Compression for Long Video
+ *    Generation" (paper summary): per-(layer, head) banks of exact K/V pairs,
+ *    Soft-Riesz density of post-RoPE keys, candidates ordered by
+ *    mean-normalised insertion disturbance, the largest prefix length that
+ *    every head of the layer can admit under an insertion-relative density
+ *    growth bound tau, eviction of crossed states then the densest
+ *    (Method; appendix B.1; defaults in appendices D-E).
+ *  - "Forcing-KV: Hybrid KV Cache Compression for Efficient Autoregressive
+ *    Video Diffusion Models" (paper notes): static heads keep the sink frame,
+ *    the transition frame and the current chunk (section 3.3); dynamic heads
+ *    keep the least similar frame segments (section 3.4).
+ *
+ * Readings fixed where the pages are silent:
+ *   phi(d2) = (eps + d2 / sigma^2)^(-p/2) with d2 the squared distance of
+ *   post-RoPE keys; a state's density excludes itself and counts bank states
+ *   only; delta(c) = D(c) / mean D with D(c) = sum over the bank of phi(c, b);
+ *   candidates ordered by ascending (delta, token id) per head; a state
+ *   crosses at prefix length k when rho_b + sum_{j<k} phi(b, c_j) > tau *
+ *   rho0_b (strict); e(k) = max(0, n + k - M); k is feasible when every
+ *   density head has |crossed| <= e(k), k <= min(N, M); k = 0 always
+ *   feasible; eviction = crossed states, then the largest projected
+ *   densities (ties: lower token id first); admitted states get rho0 = rho =
+ *   their density in the new bank.  Forcing-KV: cos(a, b) = a.b /
+ *   max(|a||b|, 1e-8) on keys concatenated over the dynamic heads; kept count
+ *   floor(r * items) in double precision; ties to the lower item index.
+ *
+ * Ownership and execution: the caller allocates every buffer (bank,
+ * candidates, outputs, workspace); the library never allocates or frees
+ * device memory and keeps no state besides a thread-local error string.
+ * Every call is asynchronous on the given stream and never synchronises;
+ * buffers must stay alive until the stream has executed the work.  Host-side
+ * checks run before any launch; a negative status means nothing was queued.
+ * Device-side conditions never trap: they set bits in kvb_update_out.status.
+ *
+ * Layouts: all K/V/Q buffers are head-major [H][rows][d], contiguous, dtype
+ * KVB_BF16 (uint16 bit patterns) or KVB_F32, 16-byte aligned.
+ */
+#ifndef KVBANK_H
+#define KVBANK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* kvb_stream_t;   /* same type as hipStream_t */
+
+/* status codes (return values) */
+#define KVB_OK          0
+#define KVB_EINVAL     (-1)   /* null or misaligned (16 B) pointer */
+#define KVB_ESHAPE     (-2)   /* bad H, d, M, N, F, segment capacity ... */
+#define KVB_EDTYPE     (-3)   /* unsupported dtype */
+#define KVB_EPARAM     (-4)   /* tau < 1 or NaN, sigma <= 0, eps <= 0 with p > 0, p < 0 or NaN, r not in [0,1],
+                                 seg_len not dividing F, bad head label */
+#define KVB_EWORKSPACE (-5)   /* workspace too small */
+#define KVB_EHIP       (-6)   /* HIP runtime error at launch (message in kvb_last_error) */
+
+/* device status bits (kvb_update_out.status) */
+#define KVB_DEV_SEGOVF  4u    /* segment table capacity exceeded (truncated) */
+#define KVB_DEV_EVICT   8u    /* eviction count inconsistent with the crossed set */
+
+/* element types */
+#define KVB_BF16 0
+#define KVB_F32  1
+
+/* head labels */
+#define KVB_HEAD_DENSITY 0    /* DensityKV bank */
+#define KVB_HEAD_STATIC  1    /* Forcing-KV static head */
+#define KVB_HEAD_DYNAMIC 2    /* Forcing-KV dynamic head */
+
+#define KVB_MAX_HEADS 64
+#define KVB_MAX_SEGMENTS 256  /* per head, attention side */
+
+typedef struct kvb_params {
+  float tau;          /* density growth bound, >= 1 (may be +inf) */
+  float sigma;        /* Soft-Riesz bandwidth, > 0 */
+  float eps;          /* softening, > 0 unless p == 0 */
+  float p;            /* decay exponent, >= 0 */
+  int32_t seg_len;    /* Forcing-KV segment length in tokens (divides F); used by dynamic heads */
+  int32_t reserved;
+  double retention;   /* Forcing-KV kept fraction r in [0, 1] */
+} kvb_params;
+
+typedef struct kvb_layer_desc {
+  int32_t H;             /* heads, 1 .. KVB_MAX_HEADS */
+  int32_t d;             /* head dim: 64 or 128 */
+  int32_t M;             /* bank capacity per head (>= 0; > 0 when a density head exists) */
+  int32_t dtype;         /* KVB_BF16 or KVB_F32 */
+  int32_t frame_tokens;  /* F: tokens per latent frame */
+  int32_t reserved;
+  const uint8_t* label;  /* HOST pointer, H head labels */
+  kvb_params params;
+} kvb_layer_desc;
+
+typedef struct kvb_bank {   /* device pointers, updated in place */
+  void* K;          /* [H][M][d] */
+  void* V;          /* [H][M][d] */
+  int32_t* tok;     /* [H][M] token ids */
+  float* rho0;      /* [H][M] frozen insertion baselines */
+  float* rho;       /* [H][M] current densities (maintained incrementally) */
+  int32_t* count;   /* [H] occupancy n_h; slots [0, n_h) are live */
+} kvb_bank;
+
+typedef struct kvb_kv_layout {   /* device pointers of the non-bank KV of the layer */
+  const void* sink_k; const void* sink_v; int32_t sink_len;    /* [H][sink_len][d] sink frame(s) */
+  int32_t win_cap;                                            /* rows per head of the window ring */
+  const void* win_k; const void* win_v;                       /* [H][win_cap][d] local window ring */
+  int32_t win_start; int32_t win_len;                         /* live rows: win_len rows from win_start (mod cap) */
+  const void* chunk_k; const void* chunk_v; int32_t chunk_len; /* [H][chunk_len][d] current chunk */
+  int32_t reserved;
+} kvb_kv_layout;
+
+typedef struct kvb_segment {   /* one contiguous run of retained rows of one head */
+  const void* k;   /* device pointer to the first K row */
+  const void* v;   /* device pointer to the first V row */
+  int32_t len;     /* rows */
+  int32_t reserved;
+} kvb_segment;
+
+typedef struct kvb_update_out {   /* device pointers written by kvbank_update */
+  int32_t* k_star;        /* [1] shared admitted prefix length */
+  int32_t* n_mandatory;   /* [H] states that crossed tau * rho0 at k* */
+  int32_t* n_evicted;     /* [H] */
+  uint32_t* status;       /* [1] OR of KVB_DEV_* bits (caller zeroes it) */
+  kvb_segment* segs;      /* [H][seg_cap] segment table read by chunk_attention */
+  int32_t* nseg;          /* [H] */
+  int32_t seg_cap;        /* >= 5 for density heads, 3 for static, 2 + kept items for dynamic; <= 256 */
+  int32_t reserved;
+  int32_t* t_cross;       /* optional [H][M]: per bank slot, the smallest prefix length at which the
+                             state crosses tau * rho0 (min(N, M) + 1 if never), for density heads */
+  float* rho_proj;        /* optional [H][M]: projected density rho'(k*) per bank slot (rows that
+                             crossed at k* keep their current density) */
+} kvb_update_out;
+
+typedef struct kvb_attn_desc {
+  int32_t H, d, Lq, dtype;
+  float scale;            /* softmax scale; <= 0 selects 1/sqrt(d) */
+  int32_t seg_cap;        /* row stride (entries) of the segment table, <= KVB_MAX_SEGMENTS */
+  int32_t out_f32;        /* 1: O is fp32; 0: O has the input dtype */
+  int32_t reserved;
+} kvb_attn_desc;
+
+/* Workspace bytes needed by kvbank_score and kvbank_update for N
+ * candidates per head.  Host only; no device work. */
+int kvbank_workspace_size(const kvb_layer_desc* L, int32_t N, size_t* bytes);
+
+/* Scoring (DensityKV Method, "Online Density-Constrained Bank Update";
+ * Forcing-KV section 3.4).
+ *   cand_k   [H][N][d]  post-RoPE candidate keys (density heads: the frames that
+ *                        just left the local window; Forcing-KV heads: the history
+ *                        frames in time order, N a multiple of F)
+ *   cand_tok [N]         token ids, shared by the heads, unique
+ *   lay                  needed by dynamic heads (the chunk's first frame pairs with
+ *                        the last history frame); may be NULL without dynamic heads
+ * Outputs (device, [H][N], row stride N):
+ *   density heads: out_D = D(c), out_score = delta(c), out_order = candidate
+ *                  indices sorted by ascending (delta, token id)
+ *   dynamic heads: out_score[0:items] = segment scores (items = N / seg_len, item
+ *                  i covers history rows [i*seg_len, (i+1)*seg_len)), out_order
+ *                  = item indices sorted ascending by (score, index)
+ *   static heads:  untouched
+ * N = 0 is a no-op. */
+int kvbank_score(const kvb_layer_desc* L, const kvb_bank* bank, const void* cand_k, const int32_t* cand_tok,
+                 int32_t N, const kvb_kv_layout* lay, float* out_D, float* out_score, int32_t* out_order, void* ws,
+                 size_t ws_bytes, kvb_stream_t stream);
+
+/* Admission / eviction and segment table (DensityKV appendix B.1 "Online
+ * Bank Update"; Forcing-KV sections 3.3-3.4).
+ *   density heads: shared prefix k*, eviction set, exact K/V/token moves into
+ *     the bank (freed slots first, then appended; live slots stay dense),
+ *     density fix-ups; D and order are kvbank_score's outputs.
+ *   static heads:  segments [sink, last F candidate rows, chunk]
+ *   dynamic heads: keep floor(r * items) lowest-scoring items; segments [sink,
+ *     kept runs in token order, chunk]
+ *   density heads' segments: [sink, bank[0:n_h], window (<= 2 ring runs), chunk]
+ * Writes out->k_star, n_mandatory, n_evicted, segs, nseg; ORs out->status. */
+int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, const void* cand_v,
+                  const int32_t* cand_tok, int32_t N, const float* D, const int32_t* order,
+                  const kvb_kv_layout* lay, kvb_update_out* out, void* ws, size_t ws_bytes, kvb_stream_t stream);
+
+/* Native attention of the chunk's queries over each head's segment table
+ * (DensityKV card page Figure 2; Forcing-KV section 3.3):
+ *   O_h = softmax(Q_h K_h^T * scale) V_h,  Q, O [H][Lq][d].
+ * No workspace is used (ws may be NULL). */
+int chunk_attention(const kvb_attn_desc* A, const void* Q, const kvb_segment* segs, const int32_t* nseg, void* O,
+                    void* ws, size_t ws_bytes, kvb_stream_t stream);
+
+/* Message of the last non-OK status on this thread ("" if none). */
+const char* kvb_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVBANK_H */

@@ -1,0 +1,414 @@
+// C-ABI of the kvbank library: argument checks, workspace layout and the
+// launch sequence of one layer's scoring, bank update and chunk attention.
+// Every check runs on the host before the first launch.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kvb_launch.hpp"
+#include "../../include/kvbank.h"
+
+using namespace kvb;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return KVB_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define REQ_PTR(p, a, name)                                                         \
+  do {                                                                              \
+    if (!(p)) return fail(KVB_EINVAL, "%s is NULL", name);                          \
+    if (!aligned((p), (a))) return fail(KVB_EINVAL, "%s is not %d-byte aligned", name, (int)(a)); \
+  } while (0)
+
+#define HIPCHK(expr)                                                                \
+  do {                                                                              \
+    hipError_t e_ = (expr);                                                         \
+    if (e_ != hipSuccess) return fail(KVB_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+struct Heads {
+  uint64_t dens = 0, stat = 0, dyn = 0;
+  int ndyn = 0;
+  int dyn_list[64];
+};
+
+int check_layer(const kvb_layer_desc* L, int32_t N, Heads* hd) {
+  if (!L) return fail(KVB_EINVAL, "layer descriptor is NULL");
+  if (L->H < 1 || L->H > KVB_MAX_HEADS) return fail(KVB_ESHAPE, "H=%d outside [1, %d]", L->H, KVB_MAX_HEADS);
+  if (L->d != 64 && L->d != 128) return fail(KVB_ESHAPE, "d=%d (supported: 64, 128)", L->d);
+  if (L->dtype != KVB_BF16 && L->dtype != KVB_F32) return fail(KVB_EDTYPE, "dtype=%d", L->dtype);
+  if (L->frame_tokens <= 0) return fail(KVB_ESHAPE, "frame_tokens=%d", L->frame_tokens);
+  if (L->M < 0) return fail(KVB_ESHAPE, "M=%d", L->M);
+  if (N < 0) return fail(KVB_ESHAPE, "N=%d", N);
+  if ((int64_t)N + (int64_t)L->M >= (int64_t)1 << 30) return fail(KVB_ESHAPE, "N + M too large");
+  if (!L->label) return fail(KVB_EINVAL, "label is NULL");
+  for (int h = 0; h < L->H; ++h) {
+    const uint8_t lab = L->label[h];
+    if (lab == KVB_HEAD_DENSITY) hd->dens |= 1ull << h;
+    else if (lab == KVB_HEAD_STATIC) hd->stat |= 1ull << h;
+    else if (lab == KVB_HEAD_DYNAMIC) {
+      hd->dyn |= 1ull << h;
+      hd->dyn_list[hd->ndyn++] = h;
+    } else return fail(KVB_EPARAM, "label[%d]=%d (0 density, 1 static, 2 dynamic)", h, (int)lab);
+  }
+  const kvb_params& P = L->params;
+  if (hd->dens) {
+    if (L->M <= 0) return fail(KVB_ESHAPE, "density heads need M > 0");
+    if (!(P.tau >= 1.0f)) return fail(KVB_EPARAM, "tau=%g must be >= 1", (double)P.tau);
+    if (!(P.sigma > 0.0f) || !isfinite(P.sigma)) return fail(KVB_EPARAM, "sigma=%g must be > 0", (double)P.sigma);
+    if (!(P.p >= 0.0f) || !isfinite(P.p)) return fail(KVB_EPARAM, "p=%g must be >= 0", (double)P.p);
+    if (P.p > 0.0f && (!(P.eps > 0.0f) || !isfinite(P.eps)))
+      return fail(KVB_EPARAM, "eps=%g must be > 0 when p > 0", (double)P.eps);
+  }
+  if (hd->dyn) {
+    if (P.seg_len <= 0 || L->frame_tokens % P.seg_len != 0)
+      return fail(KVB_EPARAM, "seg_len=%d must divide frame_tokens=%d", P.seg_len, L->frame_tokens);
+    if (!(P.retention >= 0.0 && P.retention <= 1.0)) return fail(KVB_EPARAM, "retention=%g not in [0,1]", P.retention);
+  }
+  if ((hd->dyn || hd->stat) && N % L->frame_tokens != 0)
+    return fail(KVB_ESHAPE, "Forcing-KV heads need N (%d) to be a multiple of frame_tokens (%d)", N, L->frame_tokens);
+  return KVB_OK;
+}
+
+int phi_mode_of(float p) {
+  if (p == 2.0f) return PHI_P2;
+  if (p == 0.0f) return PHI_P0;
+  if (p == 1.0f) return PHI_P1;
+  if (p == 4.0f) return PHI_P4;
+  return PHI_GEN;
+}
+
+PhiConst phi_const(const kvb_params& P) {
+  PhiConst c;
+  c.inv_s2 = 1.0f / (P.sigma * P.sigma);
+  c.c2 = -2.0f * c.inv_s2;
+  c.eps = P.p > 0.0f ? P.eps : 0.0f;
+  c.neg_half_p = -0.5f * P.p;
+  return c;
+}
+
+constexpr int SCAN_SUB = 32;      // candidates per scan subtile
+constexpr int MAX_SPLITS = 8;
+
+struct Layout {
+  size_t normB, normC, k0, k1, v0, v1, t, cp, hist, rhoP, evict, surv, evl, nsurv, nev, accS, accAE, accAA,
+      cos, split, total;
+  int kmax, cps, ncp;
+};
+
+size_t bump(size_t* off, size_t bytes) {
+  const size_t at = *off;
+  *off += (bytes + 255) & ~(size_t)255;
+  return at;
+}
+
+Layout layout_of(const kvb_layer_desc* L, int32_t N) {
+  Layout o{};
+  const int64_t H = L->H, M = L->M;
+  o.kmax = (int)(N < L->M ? N : L->M);
+  const int64_t nsub = (o.kmax + SCAN_SUB - 1) / SCAN_SUB;
+  o.cps = 8;
+  while ((nsub + o.cps - 1) / o.cps > 256) o.cps *= 2;
+  o.ncp = (int)((nsub + o.cps - 1) / o.cps) + 1;
+  size_t off = 0;
+  o.normB = bump(&off, H * M * 4);
+  o.normC = bump(&off, H * N * 4);
+  o.k0 = bump(&off, H * N * 8);
+  o.k1 = bump(&off, H * N * 8);
+  o.v0 = bump(&off, H * N * 4);
+  o.v1 = bump(&off, H * N * 4);
+  o.t = bump(&off, H * M * 4);
+  o.cp = bump(&off, H * (int64_t)o.ncp * M * 4);
+  o.hist = bump(&off, H * (int64_t)(o.kmax + 2) * 4);
+  o.rhoP = bump(&off, H * M * 4);
+  o.evict = bump(&off, H * M);
+  o.surv = bump(&off, H * M * 4);
+  o.evl = bump(&off, H * M * 4);
+  o.nsurv = bump(&off, H * 4);
+  o.nev = bump(&off, H * 4);
+  o.accS = bump(&off, H * M * 4);
+  o.accAE = bump(&off, H * (int64_t)o.kmax * 4);
+  o.accAA = bump(&off, H * (int64_t)o.kmax * 4);
+  o.cos = bump(&off, (int64_t)N * 4);
+  o.split = bump(&off, H * (int64_t)MAX_SPLITS * N * 4);
+  o.total = off;
+  return o;
+}
+
+template <typename T> T* at(void* ws, size_t off) { return reinterpret_cast<T*>((char*)ws + off); }
+
+int check_bank(const kvb_bank* B, const kvb_layer_desc* L) {
+  if (!B) return fail(KVB_EINVAL, "bank is NULL");
+  REQ_PTR(B->K, 16, "bank.K");
+  REQ_PTR(B->V, 16, "bank.V");
+  REQ_PTR(B->tok, 4, "bank.tok");
+  REQ_PTR(B->rho0, 4, "bank.rho0");
+  REQ_PTR(B->rho, 4, "bank.rho");
+  REQ_PTR(B->count, 4, "bank.count");
+  (void)L;
+  return KVB_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return KVB_OK;
+  if (ws_bytes < need) return fail(KVB_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  REQ_PTR(ws, 16, "ws");
+  return KVB_OK;
+}
+
+int choose_splits(int H, int rows, int ncols) {
+  const int wgs = H * ((rows + 63) / 64);
+  const int tiles = (ncols + 63) / 64;
+  int s = 1;
+  while (s < MAX_SPLITS && wgs * s < 1024 && s * 2 <= tiles) s *= 2;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvb_last_error(void) { return g_err; }
+
+int kvbank_workspace_size(const kvb_layer_desc* L, int32_t N, size_t* bytes) {
+  Heads hd;
+  int rc = check_layer(L, N, &hd);
+  if (rc) return rc;
+  if (!bytes) return fail(KVB_EINVAL, "bytes is NULL");
+  *bytes = layout_of(L, N).total;
+  return ok();
+}
+
+int kvbank_score(const kvb_layer_desc* L, const kvb_bank* bank, const void* cand_k, const int32_t* cand_tok,
+                 int32_t N, const kvb_kv_layout* lay, float* out_D, float* out_score, int32_t* out_order, void* ws,
+                 size_t ws_bytes, kvb_stream_t stream) {
+  Heads hd;
+  int rc = check_layer(L, N, &hd);
+  if (rc) return rc;
+  if (N == 0 || !(hd.dens || hd.dyn)) return ok();
+  const Layout lo = layout_of(L, N);
+  if ((rc = check_ws(ws, ws_bytes, lo.total))) return rc;
+  REQ_PTR(cand_k, 16, "cand_k");
+  REQ_PTR(out_score, 4, "out_score");
+  REQ_PTR(out_order, 4, "out_order");
+  if (hd.dens) {
+    if ((rc = check_bank(bank, L))) return rc;
+    REQ_PTR(cand_tok, 4, "cand_tok");
+    REQ_PTR(out_D, 4, "out_D");
+  }
+  if (hd.dyn) {
+    if (!lay) return fail(KVB_EINVAL, "layout is NULL (needed by dynamic heads)");
+    REQ_PTR(lay->chunk_k, 16, "layout.chunk_k");
+    if (lay->chunk_len < L->frame_tokens) return fail(KVB_ESHAPE, "chunk_len < frame_tokens");
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const int H = L->H, M = L->M, d = L->d, et = L->dtype;
+  const PhiConst pc = phi_const(L->params);
+  if (hd.dens) {
+    float* nB = at<float>(ws, lo.normB);
+    float* nC = at<float>(ws, lo.normC);
+    HIPCHK(launch_norms(bank->K, et, H, M, d, pc.inv_s2, nB, st));
+    HIPCHK(launch_norms(cand_k, et, H, N, d, pc.inv_s2, nC, st));
+    GramLaunch g{};
+    g.k = KeysDesc{bank->K, cand_k, nB, nC, M, N, d, H, et};
+    g.rows = VList{nullptr, nullptr, 0, 0, 0, M, N, 0};
+    g.cols = VList{nullptr, bank->count, 0, 1, 0, 0, M, 0};
+    g.pc = pc;
+    g.phi_mode = phi_mode_of(L->params.p);
+    g.active = hd.dens;
+    g.splits = choose_splits(H, N, M);
+    if (g.splits > 1) {
+      g.out = at<float>(ws, lo.split);
+      g.out_hstride = (int64_t)MAX_SPLITS * N;
+      g.split_stride = N;
+    } else {
+      g.out = out_D;
+      g.out_hstride = N;
+      g.split_stride = 0;
+    }
+    HIPCHK(launch_gram(g, st));
+    if (g.splits > 1)
+      HIPCHK(launch_sum_splits(g.out, (int64_t)MAX_SPLITS * N, N, g.splits, out_D, N, H, N, st));
+    HIPCHK(launch_delta(out_D, bank->count, hd.dens, H, N, out_score, st));
+    HIPCHK(launch_sort(out_score, N, cand_tok, 0, hd.dens, H, N, at<uint64_t>(ws, lo.k0), at<uint64_t>(ws, lo.k1),
+                       at<int32_t>(ws, lo.v0), at<int32_t>(ws, lo.v1), out_order, N, st));
+  }
+  if (hd.dyn) {
+    const int F = L->frame_tokens, T = N / F, seg = L->params.seg_len;
+    CosLaunch c{};
+    c.hist = cand_k; c.nxt = lay->chunk_k; c.et = et; c.H = H; c.d = d; c.F = F; c.T = T; c.seg_len = seg;
+    c.nxt_rows = lay->chunk_len; c.ndyn = hd.ndyn;
+    for (int i = 0; i < hd.ndyn; ++i) c.dyn_heads[i] = hd.dyn_list[i];
+    c.cosbuf = at<float>(ws, lo.cos); c.scores = out_score; c.score_hstride = N;
+    HIPCHK(launch_segment_cosine(c, st));
+    const int items = T * (F / seg);
+    HIPCHK(launch_sort(out_score, N, nullptr, 0, hd.dyn, H, items, at<uint64_t>(ws, lo.k0), at<uint64_t>(ws, lo.k1),
+                       at<int32_t>(ws, lo.v0), at<int32_t>(ws, lo.v1), out_order, N, st));
+  }
+  return ok();
+}
+
+int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, const void* cand_v,
+                  const int32_t* cand_tok, int32_t N, const float* D, const int32_t* order,
+                  const kvb_kv_layout* lay, kvb_update_out* out, void* ws, size_t ws_bytes, kvb_stream_t stream) {
+  Heads hd;
+  int rc = check_layer(L, N, &hd);
+  if (rc) return rc;
+  const Layout lo = layout_of(L, N);
+  if ((rc = check_ws(ws, ws_bytes, lo.total))) return rc;
+  if (!lay) return fail(KVB_EINVAL, "layout is NULL");
+  if (!out) return fail(KVB_EINVAL, "update output is NULL");
+  REQ_PTR(out->k_star, 4, "out.k_star");
+  REQ_PTR(out->n_mandatory, 4, "out.n_mandatory");
+  REQ_PTR(out->n_evicted, 4, "out.n_evicted");
+  REQ_PTR(out->status, 4, "out.status");
+  REQ_PTR(out->segs, 8, "out.segs");
+  REQ_PTR(out->nseg, 4, "out.nseg");
+  if (out->t_cross && !aligned(out->t_cross, 4)) return fail(KVB_EINVAL, "out.t_cross is not 4-byte aligned");
+  if (out->rho_proj && !aligned(out->rho_proj, 4)) return fail(KVB_EINVAL, "out.rho_proj is not 4-byte aligned");
+  if (out->seg_cap > KVB_MAX_SEGMENTS) return fail(KVB_ESHAPE, "seg_cap=%d > %d", out->seg_cap, KVB_MAX_SEGMENTS);
+  const int H = L->H, M = L->M, d = L->d, et = L->dtype, F = L->frame_tokens;
+  const int has_sink = lay->sink_len > 0, has_chunk = lay->chunk_len > 0;
+  if (lay->sink_len < 0 || lay->chunk_len < 0 || lay->win_len < 0 || lay->win_cap < 0)
+    return fail(KVB_ESHAPE, "negative layout length");
+  if (has_sink) { REQ_PTR(lay->sink_k, 16, "layout.sink_k"); REQ_PTR(lay->sink_v, 16, "layout.sink_v"); }
+  if (has_chunk) { REQ_PTR(lay->chunk_k, 16, "layout.chunk_k"); REQ_PTR(lay->chunk_v, 16, "layout.chunk_v"); }
+  if (lay->win_len > 0) {
+    REQ_PTR(lay->win_k, 16, "layout.win_k");
+    REQ_PTR(lay->win_v, 16, "layout.win_v");
+    if (lay->win_len > lay->win_cap || lay->win_start < 0 || lay->win_start >= lay->win_cap)
+      return fail(KVB_ESHAPE, "window ring: start=%d len=%d cap=%d", lay->win_start, lay->win_len, lay->win_cap);
+  }
+  int items = 0, keep = 0;
+  if (hd.dyn) {
+    items = (N / F) * (F / L->params.seg_len);
+    keep = (int)floor(L->params.retention * (double)items);
+  }
+  {
+    int need = 0;
+    if (hd.dens) need = 4 + (lay->win_len > 0 ? 1 : 0);
+    if (hd.stat) need = need > 3 ? need : 3;
+    if (hd.dyn) need = need > 2 + keep ? need : 2 + keep;
+    if (out->seg_cap < need) return fail(KVB_ESHAPE, "seg_cap=%d < %d needed", out->seg_cap, need);
+  }
+  if (hd.dens) {
+    if ((rc = check_bank(bank, L))) return rc;
+    if (N > 0) {
+      REQ_PTR(cand_k, 16, "cand_k");
+      REQ_PTR(cand_v, 16, "cand_v");
+      REQ_PTR(cand_tok, 4, "cand_tok");
+      REQ_PTR(D, 4, "D");
+      REQ_PTR(order, 4, "order");
+    }
+  }
+  if (hd.dyn && N > 0) REQ_PTR(order, 4, "order");
+  if ((hd.stat || hd.dyn) && N > 0) { REQ_PTR(cand_k, 16, "cand_k"); REQ_PTR(cand_v, 16, "cand_v"); }
+
+  hipStream_t st = (hipStream_t)stream;
+  const PhiConst pc = phi_const(L->params);
+  const int pm = phi_mode_of(L->params.p);
+  HIPCHK(launch_fill_i32(out->n_mandatory, H, 0, st));
+  HIPCHK(launch_fill_i32(out->n_evicted, H, 0, st));
+  HIPCHK(launch_fill_i32(out->k_star, 1, 0, st));
+  if (hd.dens && N > 0) {
+    const int kmax = lo.kmax;
+    float* nB = at<float>(ws, lo.normB);
+    float* nC = at<float>(ws, lo.normC);
+    HIPCHK(launch_norms(bank->K, et, H, M, d, pc.inv_s2, nB, st));
+    HIPCHK(launch_norms(cand_k, et, H, N, d, pc.inv_s2, nC, st));
+    const KeysDesc kd{bank->K, cand_k, nB, nC, M, N, d, H, et};
+    ScanLaunch s{};
+    s.k = kd; s.rho = bank->rho; s.rho0 = bank->rho0; s.count = bank->count; s.order = order;
+    s.active = hd.dens; s.kmax = kmax; s.tau = L->params.tau; s.cps = lo.cps; s.ncp = lo.ncp;
+    s.cp = at<float>(ws, lo.cp); s.kstar = out->k_star;
+    s.t_out = out->t_cross ? out->t_cross : at<int32_t>(ws, lo.t);
+    s.rhoP = out->rho_proj ? out->rho_proj : at<float>(ws, lo.rhoP);
+    s.pc = pc; s.phi_mode = pm;
+    HIPCHK(launch_scan(s, false, st));
+    SelectLaunch sel{};
+    sel.H = H; sel.M = M; sel.kmax = kmax; sel.active = hd.dens; sel.count = bank->count;
+    sel.t = s.t_out; sel.hist = at<int32_t>(ws, lo.hist); sel.kstar = out->k_star; sel.rhoP = s.rhoP;
+    sel.bank_tok = bank->tok; sel.evict = at<uint8_t>(ws, lo.evict); sel.surv = at<int32_t>(ws, lo.surv);
+    sel.evl = at<int32_t>(ws, lo.evl); sel.n_surv = at<int32_t>(ws, lo.nsurv); sel.n_ev = out->n_evicted;
+    sel.n_mand = out->n_mandatory; sel.status = out->status;
+    HIPCHK(launch_kstar(sel, st));
+    HIPCHK(launch_scan(s, true, st));
+    HIPCHK(launch_evict(sel, st));
+    // density fix-ups: survivors x evicted, admitted x evicted, admitted x admitted
+    GramLaunch g{};
+    g.k = kd; g.pc = pc; g.phi_mode = pm; g.splits = 1; g.split_stride = 0; g.active = hd.dens;
+    const VList evl{sel.evl, sel.n_ev, M, 1, 0, 0, M, 0};
+    const VList srv{sel.surv, sel.n_surv, M, 1, 0, 0, M, 0};
+    const VList adm{order, out->k_star, N, 0, M, 0, kmax, 0};
+    g.rows = srv; g.cols = evl; g.out = at<float>(ws, lo.accS); g.out_hstride = M; g.self_excl = 0;
+    HIPCHK(launch_gram(g, st));
+    g.rows = adm; g.cols = evl; g.out = at<float>(ws, lo.accAE); g.out_hstride = kmax;
+    HIPCHK(launch_gram(g, st));
+    g.rows = adm; g.cols = adm; g.out = at<float>(ws, lo.accAA); g.out_hstride = kmax; g.self_excl = 1;
+    HIPCHK(launch_gram(g, st));
+    ApplyLaunch ap{};
+    ap.H = H; ap.M = M; ap.N = N; ap.d = d; ap.et = et; ap.kmax = kmax; ap.active = hd.dens;
+    ap.bankK = bank->K; ap.bankV = bank->V; ap.bank_tok = bank->tok; ap.rho0 = bank->rho0; ap.rho = bank->rho;
+    ap.count = bank->count; ap.candK = cand_k; ap.candV = cand_v; ap.cand_tok = cand_tok; ap.order = order;
+    ap.D = D; ap.kstar = out->k_star; ap.surv = sel.surv; ap.n_surv = sel.n_surv; ap.evl = sel.evl;
+    ap.n_ev = sel.n_ev; ap.rhoP = s.rhoP; ap.acc_surv = at<float>(ws, lo.accS);
+    ap.acc_adm_ev = at<float>(ws, lo.accAE); ap.acc_adm_adm = at<float>(ws, lo.accAA);
+    HIPCHK(launch_apply(ap, st));
+  }
+  SegLaunch sg{};
+  sg.H = H; sg.d = d; sg.et = et; sg.M = M; sg.N = N; sg.F = F;
+  for (int h = 0; h < H; ++h) sg.label[h] = L->label[h];
+  sg.sink_k = lay->sink_k; sg.sink_v = lay->sink_v; sg.sink_len = lay->sink_len;
+  sg.win_k = lay->win_k; sg.win_v = lay->win_v; sg.win_cap = lay->win_cap; sg.win_start = lay->win_start;
+  sg.win_len = lay->win_len;
+  sg.chunk_k = lay->chunk_k; sg.chunk_v = lay->chunk_v; sg.chunk_len = lay->chunk_len;
+  sg.bankK = hd.dens ? bank->K : nullptr; sg.bankV = hd.dens ? bank->V : nullptr;
+  sg.count = hd.dens ? bank->count : nullptr;
+  sg.candK = cand_k; sg.candV = cand_v;
+  sg.dyn_order = order; sg.dyn_order_hstride = N;
+  sg.seg_len = hd.dyn ? L->params.seg_len : 1; sg.items = items; sg.keep = keep;
+  sg.segs = reinterpret_cast<SegEntry*>(out->segs); sg.nseg = out->nseg; sg.seg_cap = out->seg_cap;
+  sg.status = out->status;
+  HIPCHK(launch_segments(sg, st));
+  return ok();
+}
+
+int chunk_attention(const kvb_attn_desc* A, const void* Q, const kvb_segment* segs, const int32_t* nseg, void* O,
+                    void* ws, size_t ws_bytes, kvb_stream_t stream) {
+  (void)ws; (void)ws_bytes;
+  if (!A) return fail(KVB_EINVAL, "attention descriptor is NULL");
+  if (A->H < 1 || A->H > KVB_MAX_HEADS) return fail(KVB_ESHAPE, "H=%d", A->H);
+  if (A->d != 64 && A->d != 128) return fail(KVB_ESHAPE, "d=%d (supported: 64, 128)", A->d);
+  if (A->dtype != KVB_BF16 && A->dtype != KVB_F32) return fail(KVB_EDTYPE, "dtype=%d", A->dtype);
+  if (A->Lq < 0) return fail(KVB_ESHAPE, "Lq=%d", A->Lq);
+  if (A->seg_cap < 1 || A->seg_cap > KVB_MAX_SEGMENTS) return fail(KVB_ESHAPE, "seg_cap=%d", A->seg_cap);
+  if (A->Lq == 0) return ok();
+  REQ_PTR(Q, 16, "Q");
+  REQ_PTR(O, 16, "O");
+  REQ_PTR(segs, 8, "segs");
+  REQ_PTR(nseg, 4, "nseg");
+  AttnLaunch a{};
+  a.H = A->H; a.d = A->d; a.Lq = A->Lq; a.et = A->dtype; a.out_f32 = A->dtype == KVB_F32 ? 1 : (A->out_f32 ? 1 : 0);
+  a.scale = A->scale > 0.0f ? A->scale : 1.0f / sqrtf((float)A->d);
+  a.Q = Q; a.O = O; a.segs = reinterpret_cast<const SegEntry*>(segs); a.nseg = nseg; a.seg_cap = A->seg_cap;
+  HIPCHK(launch_attention(a, (hipStream_t)stream));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+// Internal launch interface between the C-ABI layer and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "kvb_common.hpp"
+
+namespace kvb {
+
+enum ElemType { ET_BF16 = 0, ET_F32 = 1 };
+
+struct KeysDesc {            // one layer's keys in two buffers (see KeySpace)
+  const void* bankK;
+  const void* candK;
+  const float* bankN;
+  const float* candN;
+  int32_t M, N, d, H;
+  int32_t et;
+};
+
+// |k|^2 * scale for rows [H][rows][d]
+hipError_t launch_norms(const void* keys, int et, int H, int rows, int d, float scale, float* out,
+                        hipStream_t s);
+
+// out[h*out_hstride + split*split_stride + i] = sum_{j in cols} phi(row_i, col_j)
+struct GramLaunch {
+  KeysDesc k;
+  VList rows, cols;
+  float* out;
+  int64_t out_hstride;
+  int64_t split_stride;
+  int32_t splits;
+  int32_t self_excl;
+  PhiConst pc;
+  int32_t phi_mode;
+  uint64_t active;        // bit h: head computed
+};
+hipError_t launch_gram(const GramLaunch& g, hipStream_t s);
+
+// sum split partials in order: dst[h*dst_hstride+i] = sum_s src[h*src_hstride + s*split_stride + i]
+hipError_t launch_sum_splits(const float* src, int64_t src_hstride, int64_t split_stride, int splits,
+                             float* dst, int64_t dst_hstride, int H, int n, hipStream_t s);
+
+struct ScanLaunch {
+  KeysDesc k;
+  const float* rho;       // [H][M] current density
+  const float* rho0;      // [H][M]
+  const int32_t* count;   // [H]
+  const int32_t* order;   // [H][N] candidate permutation
+  uint64_t active;        // bit h: density head
+  int32_t kmax;
+  float tau;              // may be +inf
+  int32_t cps;            // subtiles per checkpoint
+  int32_t ncp;            // checkpoints per row
+  float* cp;              // [H][ncp][M]
+  int32_t* t_out;         // [H][M] (scan)
+  const int32_t* kstar;   // device scalar (sum)
+  float* rhoP;            // [H][M] (sum)
+  PhiConst pc;
+  int32_t phi_mode;
+};
+hipError_t launch_scan(const ScanLaunch& a, bool sum_mode, hipStream_t s);
+
+// ---- selection / bookkeeping ----------------------------------------------
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
+// keys for sorting: key = float_key(score[h][i]) << 32 | tie[i]; value = i
+hipError_t launch_sort(const float* score, int64_t score_hstride, const int32_t* tie, int64_t tie_hstride,
+                       uint64_t head_on, int H, int n, uint64_t* kbuf0, uint64_t* kbuf1,
+                       int32_t* vbuf0, int32_t* vbuf1, int32_t* out_order, int64_t out_hstride,
+                       hipStream_t s);
+
+// per head: mean of D over n, delta = D / mean (0 if bank empty or mean 0)
+hipError_t launch_delta(const float* D, const int32_t* count, uint64_t head_on, int H, int n,
+                        float* delta, hipStream_t s);
+
+struct SelectLaunch {
+  int32_t H, M, kmax;
+  uint64_t active;           // bit h: density head
+  const int32_t* count;      // [H] bank occupancy
+  const int32_t* t;          // [H][M] crossing times
+  int32_t* hist;             // [H][kmax+2] scratch, becomes |V_h(k)|
+  int32_t* kstar;            // device scalar
+  const float* rhoP;         // [H][M]
+  const int32_t* bank_tok;   // [H][M]
+  uint8_t* evict;            // [H][M]
+  int32_t* surv;             // [H][M] survivor slots (ascending)
+  int32_t* evl;              // [H][M] evicted slots (ascending)
+  int32_t* n_surv;           // [H]
+  int32_t* n_ev;             // [H]
+  int32_t* n_mand;           // [H]
+  uint32_t* status;          // device status word
+};
+hipError_t launch_kstar(const SelectLaunch& a, hipStream_t s);
+hipError_t launch_evict(const SelectLaunch& a, hipStream_t s);
+
+struct ApplyLaunch {
+  int32_t H, M, N, d, et, kmax;
+  uint64_t active;
+  void* bankK; void* bankV;
+  int32_t* bank_tok; float* rho0; float* rho; int32_t* count;
+  const void* candK; const void* candV; const int32_t* cand_tok;
+  const int32_t* order;       // [H][N]
+  const float* D;             // [H][N]
+  const int32_t* kstar;
+  const int32_t* surv; const int32_t* n_surv;
+  const int32_t* evl; const int32_t* n_ev;
+  const float* rhoP;          // [H][M]
+  const float* acc_surv;      // [H][M] sum over evicted for survivors (by survivor position)
+  const float* acc_adm_ev;    // [H][kmax] sum over evicted for admitted
+  const float* acc_adm_adm;   // [H][kmax] sum over other admitted for admitted
+};
+hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s);
+
+// ---- segment tables ---------------------------------------------------------
+struct SegEntry { const void* k; const void* v; int32_t len; int32_t pad; };
+
+struct SegLaunch {
+  int32_t H, d, et, M, N, F;
+  uint8_t label[64];
+  const void* sink_k; const void* sink_v; int32_t sink_len;
+  const void* win_k; const void* win_v; int32_t win_cap, win_start, win_len;
+  const void* chunk_k; const void* chunk_v; int32_t chunk_len;
+  const void* bankK; const void* bankV; const int32_t* count;
+  const void* candK; const void* candV;
+  const int32_t* dyn_order; int64_t dyn_order_hstride;  // item order (dynamic heads)
+  int32_t seg_len, items, keep;
+  SegEntry* segs; int32_t* nseg; int32_t seg_cap;
+  uint32_t* status;
+};
+hipError_t launch_segments(const SegLaunch& a, hipStream_t s);
+
+// ---- Forcing-KV segment similarity ------------------------------------------
+struct CosLaunch {
+  const void* hist;    // [H][T*F][d]
+  const void* nxt;     // [H][>=F][d] (first F rows used)
+  int32_t et, H, d, F, T, seg_len;
+  int32_t nxt_rows;    // rows per head in nxt
+  int32_t ndyn; int32_t dyn_heads[64];
+  float* cosbuf;       // [T][F]
+  float* scores;       // [H][N] (written for dynamic heads)
+  int64_t score_hstride;
+};
+hipError_t launch_segment_cosine(const CosLaunch& a, hipStream_t s);
+
+// ---- attention ----------------------------------------------------------------
+struct AttnLaunch {
+  int32_t H, d, Lq, et, out_f32;
+  float scale;
+  const void* Q; void* O;
+  const SegEntry* segs; const int32_t* nseg; int32_t seg_cap;
+};
+hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
+
+}  // namespace kvb

@@ -1,0 +1,485 @@
+// Ordering, prefix feasibility, eviction selection, compaction/gather and
+// segment tables for the per-head token banks.
+//
+// DensityKV paper-summary page, Method ("Online Density-Constrained Bank
+// Update") and appendix B.1 ("Online Bank Update"): candidates are taken in
+// ascending mean-normalised disturbance; one prefix length is shared by the
+// heads of a layer and must be admissible for every head; the states that
+// cross their growth bound are evicted first, then the densest, until the
+// capacity is released; admitted states keep their exact values and set
+// their baselines together.  Forcing-KV notes page, sections 3.3-3.5: static
+// heads keep [sink, transition frame, chunk]; dynamic heads keep the BottomK
+// segments in token order.
+#include "kvb_common.hpp"
+#include "kvb_launch.hpp"
+
+namespace kvb {
+
+enum : uint32_t { DEV_NONFINITE = 1u, DEV_COUNT = 2u, DEV_SEGOVF = 4u, DEV_EVICT = 8u };
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// mean-normalised disturbance: delta = D / mean_c D (0 if bank empty or mean 0)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void delta_kernel(const float* __restrict__ D, const int32_t* __restrict__ count,
+                                                    uint64_t on, int n, float* __restrict__ delta) {
+  const int h = blockIdx.x;
+  if (!head_on(on, h)) return;
+  __shared__ float red[256];
+  float s = 0.0f;
+  for (int i = threadIdx.x; i < n; i += 256) s += D[(int64_t)h * n + i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o >= 1; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  const float mean = red[0] / (float)n;
+  const bool zero = count[h] <= 0 || !(mean > 0.0f);
+  for (int i = threadIdx.x; i < n; i += 256) delta[(int64_t)h * n + i] = zero ? 0.0f : D[(int64_t)h * n + i] / mean;
+}
+
+hipError_t launch_delta(const float* D, const int32_t* count, uint64_t on, int H, int n, float* delta,
+                        hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(delta_kernel, dim3(H), dim3(256), 0, st, D, count, on, n, delta);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// sort: key = float_key(score) << 32 | tie (tie = token id or item index),
+// ascending; value = index.  Blocks of 2048 are sorted in LDS (bitonic), then
+// sorted runs are merged pairwise by rank (binary search in the other run).
+// ---------------------------------------------------------------------------
+constexpr int SORT_BS = 2048;
+
+KVB_DEV uint64_t sort_key(const float* score, const int32_t* tie, int64_t tie_hstride, int h, int i,
+                          int64_t score_hstride) {
+  const uint32_t hi = float_key(score[(int64_t)h * score_hstride + i]);
+  const uint32_t lo = tie ? (uint32_t)tie[(int64_t)h * tie_hstride + i] : (uint32_t)i;
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__global__ __launch_bounds__(256) void block_sort_kernel(const float* __restrict__ score, int64_t score_hstride,
+                                                         const int32_t* __restrict__ tie, int64_t tie_hstride,
+                                                         uint64_t on, int n,
+                                                         uint64_t* __restrict__ kout, int32_t* __restrict__ vout,
+                                                         int32_t* __restrict__ final_out, int64_t final_hstride) {
+  const int h = blockIdx.y;
+  if (!head_on(on, h)) return;
+  __shared__ uint64_t sk[SORT_BS];
+  __shared__ int32_t sv[SORT_BS];
+  const int base = blockIdx.x * SORT_BS;
+  for (int i = threadIdx.x; i < SORT_BS; i += 256) {
+    const int g = base + i;
+    if (g < n) {
+      sk[i] = sort_key(score, tie, tie_hstride, h, g, score_hstride);
+      sv[i] = g;
+    } else {
+      sk[i] = ~0ull;
+      sv[i] = -1;
+    }
+  }
+  __syncthreads();
+  for (int k = 2; k <= SORT_BS; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int p = threadIdx.x; p < SORT_BS / 2; p += 256) {
+        const int i = (p / j) * 2 * j + (p % j);
+        const int l = i + j;
+        const bool up = ((i & k) == 0);
+        const uint64_t a = sk[i], b = sk[l];
+        if ((a > b) == up) {
+          sk[i] = b; sk[l] = a;
+          const int32_t t = sv[i]; sv[i] = sv[l]; sv[l] = t;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < SORT_BS; i += 256) {
+    const int g = base + i;
+    if (g < n) {
+      if (final_out) final_out[(int64_t)h * final_hstride + g] = sv[i];
+      else {
+        kout[(int64_t)h * n + g] = sk[i];
+        vout[(int64_t)h * n + g] = sv[i];
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void merge_kernel(const uint64_t* __restrict__ kin, const int32_t* __restrict__ vin,
+                                                    uint64_t on, int n, int L,
+                                                    uint64_t* __restrict__ kout, int32_t* __restrict__ vout,
+                                                    int32_t* __restrict__ final_out, int64_t final_hstride) {
+  const int h = blockIdx.y;
+  if (!head_on(on, h)) return;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int64_t hb = (int64_t)h * n;
+  const int pair0 = (i / (2 * L)) * (2 * L);
+  const int a0 = pair0, a1 = min(n, pair0 + L);
+  const int b0 = a1, b1 = min(n, pair0 + 2 * L);
+  const uint64_t key = kin[hb + i];
+  int lo, hi, pos;
+  if (i < a1) {   // element of run A: count B elements < key
+    lo = b0; hi = b1;
+    while (lo < hi) { const int m = (lo + hi) >> 1; if (kin[hb + m] < key) lo = m + 1; else hi = m; }
+    pos = pair0 + (i - a0) + (lo - b0);
+  } else {        // element of run B: count A elements < key
+    lo = a0; hi = a1;
+    while (lo < hi) { const int m = (lo + hi) >> 1; if (kin[hb + m] < key) lo = m + 1; else hi = m; }
+    pos = pair0 + (i - b0) + (lo - a0);
+  }
+  if (final_out) final_out[(int64_t)h * final_hstride + pos] = vin[hb + i];
+  else {
+    kout[hb + pos] = key;
+    vout[hb + pos] = vin[hb + i];
+  }
+}
+
+hipError_t launch_sort(const float* score, int64_t score_hstride, const int32_t* tie, int64_t tie_hstride,
+                       uint64_t on, int H, int n, uint64_t* k0, uint64_t* k1, int32_t* v0, int32_t* v1,
+                       int32_t* out, int64_t out_hstride, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int nb = (n + SORT_BS - 1) / SORT_BS;
+  const bool single = nb == 1;
+  hipLaunchKernelGGL(block_sort_kernel, dim3(nb, H), dim3(256), 0, st, score, score_hstride, tie, tie_hstride, on,
+                     n, k0, v0, single ? out : nullptr, out_hstride);
+  if (single) return hipGetLastError();
+  uint64_t* ka = k0; uint64_t* kb = k1;
+  int32_t* va = v0; int32_t* vb = v1;
+  for (int L = SORT_BS; L < n; L <<= 1) {
+    const bool last = 2 * L >= n;
+    hipLaunchKernelGGL(merge_kernel, dim3((n + 255) / 256, H), dim3(256), 0, st, ka, va, on, n, L, kb, vb,
+                       last ? out : nullptr, out_hstride);
+    uint64_t* tk = ka; ka = kb; kb = tk;
+    int32_t* tv = va; va = vb; vb = tv;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// shared prefix length k*
+// ---------------------------------------------------------------------------
+__global__ void hist_kernel(const int32_t* __restrict__ t, const int32_t* __restrict__ count,
+                            uint64_t active, int M, int kmax, int32_t* __restrict__ hist) {
+  const int h = blockIdx.y;
+  if (!head_on(active, h)) return;
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= count[h]) return;
+  int v = t[(int64_t)h * M + b];
+  v = v < 0 ? 0 : (v > kmax + 1 ? kmax + 1 : v);
+  atomicAdd(&hist[(int64_t)h * (kmax + 2) + v], 1);
+}
+
+__global__ __launch_bounds__(1024) void cumsum_kernel(int32_t* __restrict__ hist, uint64_t active,
+                                                      int len) {
+  const int h = blockIdx.x;
+  if (!head_on(active, h)) return;
+  __shared__ int32_t s[1024];
+  int32_t carry = 0;
+  int32_t* p = hist + (int64_t)h * len;
+  for (int base = 0; base < len; base += 1024) {
+    const int i = base + threadIdx.x;
+    int32_t v = i < len ? p[i] : 0;
+    s[threadIdx.x] = v;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      const int32_t add = (int)threadIdx.x >= o ? s[threadIdx.x - o] : 0;
+      __syncthreads();
+      s[threadIdx.x] += add;
+      __syncthreads();
+    }
+    if (i < len) p[i] = s[threadIdx.x] + carry;
+    carry += s[1023];
+    __syncthreads();
+  }
+}
+
+__global__ void feasible_kernel(const int32_t* __restrict__ cum, const int32_t* __restrict__ count,
+                                uint64_t active, int H, int M, int kmax,
+                                int32_t* __restrict__ kstar) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k > kmax) return;
+  bool ok = true;
+  if (k > 0) {
+    for (int h = 0; h < H; ++h) {
+      if (!head_on(active, h)) continue;
+      const int e = max(0, count[h] + k - M);
+      if (cum[(int64_t)h * (kmax + 2) + k] > e) { ok = false; break; }
+    }
+  }
+  if (ok) atomicMax(kstar, k);
+}
+
+hipError_t launch_kstar(const SelectLaunch& a, hipStream_t st) {
+  hipError_t e;
+  if ((e = launch_fill_i32(a.hist, (int64_t)a.H * (a.kmax + 2), 0, st)) != hipSuccess) return e;
+  if ((e = launch_fill_i32(a.kstar, 1, 0, st)) != hipSuccess) return e;
+  if (a.M > 0)
+    hipLaunchKernelGGL(hist_kernel, dim3((a.M + 255) / 256, a.H), dim3(256), 0, st, a.t, a.count, a.active, a.M,
+                       a.kmax, a.hist);
+  hipLaunchKernelGGL(cumsum_kernel, dim3(a.H), dim3(1024), 0, st, a.hist, a.active, a.kmax + 2);
+  hipLaunchKernelGGL(feasible_kernel, dim3((a.kmax + 1 + 255) / 256), dim3(256), 0, st, a.hist, a.count, a.active,
+                     a.H, a.M, a.kmax, a.kstar);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// eviction: crossed states plus the r = e - |V| largest keys
+// (projected density desc, token asc) among the rest, by an MSB-first radix
+// select over 64-bit keys; then ballot/prefix-sum compaction of the evicted
+// and surviving slots, both in ascending slot order.
+// ---------------------------------------------------------------------------
+KVB_DEV uint64_t evict_key(float rp, int32_t tok) {
+  return ((uint64_t)float_key(rp) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)tok);
+}
+
+__global__ __launch_bounds__(1024) void evict_kernel(SelectLaunch a) {
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int M = a.M;
+  const int64_t hb = (int64_t)h * M;
+  if (!head_on(a.active, h)) return;
+  const int n = a.count[h];
+  const int ks = *a.kstar;
+  const int e = ks > 0 ? max(0, n + ks - M) : 0;
+  __shared__ int hist[256];
+  __shared__ int s_nm;
+  __shared__ uint64_t s_prefix, s_mask;
+  __shared__ int s_rem;
+  __shared__ int wsum[16];
+  __shared__ int s_base_e, s_base_s;
+  if (tid == 0) { s_nm = 0; s_prefix = 0; s_mask = 0; s_base_e = 0; s_base_s = 0; }
+  __syncthreads();
+  int nm_local = 0;
+  for (int b = tid; b < n; b += 1024) nm_local += (ks > 0 && a.t[hb + b] <= ks) ? 1 : 0;
+  atomicAdd(&s_nm, nm_local);
+  __syncthreads();
+  const int nm = s_nm;
+  int r = e - nm;
+  if (r < 0) {
+    if (tid == 0) atomicOr(a.status, DEV_EVICT);
+    r = 0;
+  }
+  if (tid == 0) s_rem = r;
+  __syncthreads();
+  // radix select of the r-th largest key among non-crossed states
+  if (r > 0) {
+    for (int pass = 0; pass < 8; ++pass) {
+      const int shift = 56 - 8 * pass;
+      for (int i = tid; i < 256; i += 1024) hist[i] = 0;
+      __syncthreads();
+      const uint64_t pre = s_prefix, msk = s_mask;
+      for (int b = tid; b < n; b += 1024) {
+        if (ks > 0 && a.t[hb + b] <= ks) continue;
+        const uint64_t key = evict_key(a.rhoP[hb + b], a.bank_tok[hb + b]);
+        if ((key & msk) == pre) atomicAdd(&hist[(key >> shift) & 0xFF], 1);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int rem = s_rem;
+        int dsel = 0;
+        for (int dgt = 255; dgt >= 0; --dgt) {
+          const int c = hist[dgt];
+          if (c >= rem) { dsel = dgt; break; }
+          rem -= c;
+        }
+        s_rem = rem;
+        s_prefix = pre | ((uint64_t)dsel << shift);
+        s_mask = msk | (0xFFull << shift);
+      }
+      __syncthreads();
+    }
+  }
+  const uint64_t thr = s_prefix;
+  // compaction in ascending slot order
+  for (int base = 0; base < n; base += 1024) {
+    const int b = base + tid;
+    bool ev = false, live = b < n;
+    if (live) {
+      const bool mand = ks > 0 && a.t[hb + b] <= ks;
+      ev = mand || (r > 0 && evict_key(a.rhoP[hb + b], a.bank_tok[hb + b]) >= thr);
+      a.evict[hb + b] = ev ? 1 : 0;
+    }
+    const uint64_t be = __ballot(live && ev);
+    const uint64_t bs = __ballot(live && !ev);
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int pe = __popcll(be & lt), ps = __popcll(bs & lt);
+    if (lane == 0) wsum[w] = (__popcll(be) << 16) | __popcll(bs);
+    __syncthreads();
+    int oe = 0, os = 0;
+    for (int j = 0; j < w; ++j) { oe += wsum[j] >> 16; os += wsum[j] & 0xFFFF; }
+    const int be0 = s_base_e, bs0 = s_base_s;
+    if (live && ev) a.evl[hb + be0 + oe + pe] = b;
+    if (live && !ev) a.surv[hb + bs0 + os + ps] = b;
+    __syncthreads();
+    if (tid == 0) {
+      int te = 0, ts = 0;
+      for (int j = 0; j < 16; ++j) { te += wsum[j] >> 16; ts += wsum[j] & 0xFFFF; }
+      s_base_e += te; s_base_s += ts;
+    }
+    __syncthreads();
+  }
+  for (int b = n + tid; b < M; b += 1024) a.evict[hb + b] = 0;
+  if (tid == 0) {
+    a.n_ev[h] = s_base_e;
+    a.n_surv[h] = s_base_s;
+    a.n_mand[h] = nm;
+    if (s_base_e != e) atomicOr(a.status, DEV_EVICT);
+  }
+}
+
+hipError_t launch_evict(const SelectLaunch& a, hipStream_t st) {
+  hipLaunchKernelGGL(evict_kernel, dim3(a.H), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// apply: survivors' density update, gather of admitted K/V rows into freed
+// slots (then appended after the old occupancy), baselines of admitted rows
+// ---------------------------------------------------------------------------
+__global__ void apply_surv_kernel(ApplyLaunch a) {
+  const int h = blockIdx.y;
+  if (!head_on(a.active, h)) return;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.n_surv[h]) return;
+  const int64_t hb = (int64_t)h * a.M;
+  const int slot = a.surv[hb + i];
+  a.rho[hb + slot] = a.rhoP[hb + slot] - a.acc_surv[hb + i];
+}
+
+// 8 rows per 256-thread block; each row moves K and V (16-byte chunks)
+template <int CPR>
+__global__ __launch_bounds__(256) void apply_adm_kernel(ApplyLaunch a) {
+  const int h = blockIdx.y;
+  if (!head_on(a.active, h)) return;
+  const int ks = *a.kstar;
+  constexpr int RPB = 256 / (2 * CPR);
+  const int j = blockIdx.x * RPB + threadIdx.x / (2 * CPR);
+  if (j >= ks) return;
+  const int part = (threadIdx.x % (2 * CPR)) / CPR;   // 0 = K, 1 = V
+  const int c = threadIdx.x % CPR;
+  const int64_t hb = (int64_t)h * a.M;
+  const int ne = a.n_ev[h];
+  const int nold = a.n_surv[h] + ne;
+  const int slot = j < ne ? a.evl[hb + j] : nold + (j - ne);
+  const int cand = a.order[(int64_t)h * a.N + j];
+  if ((unsigned)slot >= (unsigned)a.M || (unsigned)cand >= (unsigned)a.N) return;
+  const int esz = a.et == ET_BF16 ? 2 : 4;
+  const int64_t rowb = (int64_t)a.d * esz;
+  const char* src = (const char*)(part ? a.candV : a.candK) + ((int64_t)h * a.N + cand) * rowb;
+  char* dst = (char*)(part ? a.bankV : a.bankK) + (hb + slot) * rowb;
+  *reinterpret_cast<u32x4_t*>(dst + c * 16) = *reinterpret_cast<const u32x4_t*>(src + c * 16);
+  if (threadIdx.x % (2 * CPR) == 0) {
+    const int64_t hk = (int64_t)h * a.kmax + j;
+    const float r = (a.D[(int64_t)h * a.N + cand] - a.acc_adm_ev[hk]) + a.acc_adm_adm[hk];
+    a.rho[hb + slot] = r;
+    a.rho0[hb + slot] = r;
+    a.bank_tok[hb + slot] = a.cand_tok[cand];
+  }
+}
+
+__global__ void commit_count_kernel(ApplyLaunch a) {
+  const int h = threadIdx.x;
+  if (h >= a.H || !head_on(a.active, h)) return;
+  a.count[h] = a.n_surv[h] + *a.kstar;
+}
+
+hipError_t launch_apply(const ApplyLaunch& a, hipStream_t st) {
+  if (a.M > 0)
+    hipLaunchKernelGGL(apply_surv_kernel, dim3((a.M + 255) / 256, a.H), dim3(256), 0, st, a);
+  const int cpr = a.d * (a.et == ET_BF16 ? 2 : 4) / 16;
+  if (a.kmax > 0) {
+    if (cpr == 16)
+      hipLaunchKernelGGL((apply_adm_kernel<16>), dim3((a.kmax + 7) / 8, a.H), dim3(256), 0, st, a);
+    else if (cpr == 8)
+      hipLaunchKernelGGL((apply_adm_kernel<8>), dim3((a.kmax + 15) / 16, a.H), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((apply_adm_kernel<32>), dim3((a.kmax + 3) / 4, a.H), dim3(256), 0, st, a);
+  }
+  hipLaunchKernelGGL(commit_count_kernel, dim3(1), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// segment tables consumed by chunk attention
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void segments_kernel(SegLaunch a) {
+  const int h = blockIdx.x;
+  const int esz = a.et == ET_BF16 ? 2 : 4;
+  const int64_t rowb = (int64_t)a.d * esz;
+  SegEntry* out = a.segs + (int64_t)h * a.seg_cap;
+  extern __shared__ uint32_t bits[];
+  __shared__ int s_n;
+  const uint8_t lab = a.label[h];
+  if (threadIdx.x == 0) s_n = 0;
+  __syncthreads();
+  auto push = [&](const void* kb, const void* vb, int64_t head_rows, int64_t row0, int len) {
+    if (len <= 0) return;
+    const int i = s_n;
+    if (i >= a.seg_cap) { atomicOr(a.status, DEV_SEGOVF); return; }
+    out[i].k = (const char*)kb + ((int64_t)h * head_rows + row0) * rowb;
+    out[i].v = (const char*)vb + ((int64_t)h * head_rows + row0) * rowb;
+    out[i].len = len;
+    out[i].pad = 0;
+    s_n = i + 1;
+  };
+  if (lab == 2) {
+    const int words = (a.items + 31) / 32;
+    for (int i = threadIdx.x; i < words; i += 64) bits[i] = 0u;
+    __syncthreads();
+    for (int j = threadIdx.x; j < a.keep; j += 64) {
+      const int it = a.dyn_order[(int64_t)h * a.dyn_order_hstride + j];
+      if ((unsigned)it < (unsigned)a.items) atomicOr(&bits[it >> 5], 1u << (it & 31));
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    push(a.sink_k, a.sink_v, a.sink_len, 0, a.sink_len);
+    if (lab == 0) {
+      push(a.bankK, a.bankV, a.M, 0, a.count[h]);
+      if (a.win_len > 0) {
+        const int first = min(a.win_len, a.win_cap - a.win_start);
+        push(a.win_k, a.win_v, a.win_cap, a.win_start, first);
+        push(a.win_k, a.win_v, a.win_cap, 0, a.win_len - first);
+      }
+    } else if (lab == 1) {
+      if (a.N >= a.F) push(a.candK, a.candV, a.N, a.N - a.F, a.F);
+    } else {
+      int it = 0;
+      while (it < a.items) {
+        if (bits[it >> 5] & (1u << (it & 31))) {
+          int end = it + 1;
+          while (end < a.items && (bits[end >> 5] & (1u << (end & 31)))) ++end;
+          push(a.candK, a.candV, a.N, (int64_t)it * a.seg_len, (end - it) * a.seg_len);
+          it = end;
+        } else {
+          ++it;
+        }
+      }
+    }
+    push(a.chunk_k, a.chunk_v, a.chunk_len, 0, a.chunk_len);
+    a.nseg[h] = s_n;
+  }
+}
+
+hipError_t launch_segments(const SegLaunch& a, hipStream_t st) {
+  const size_t shm = (size_t)((a.items + 31) / 32 + 1) * 4;
+  hipLaunchKernelGGL(segments_kernel, dim3(a.H), dim3(64), shm, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvb

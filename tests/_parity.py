@@ -1,0 +1,171 @@
+"""Stage-replay parity checks of the HIP bank update against the fp64 oracle.
+
+Each stage of the GPU update is compared with the oracle's stage computed on
+the GPU's validated decision of the previous stage, so one floating-point
+near-tie cannot cascade into later stages.  A discrete mismatch is accepted
+only where the oracle's deciding gap is below ``GAP`` (relative):
+
+* order inversions: |delta_i - delta_j| / delta_j
+* crossing flips:  |rho'(k) - tau rho0| / (tau rho0)
+* eviction swaps:  |rho'_a - rho'_b| / rho'_b
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List
+
+import numpy as np
+
+from oracle import density as od
+
+GAP = 1e-4
+
+
+@dataclass
+class GpuBank:
+    tok: np.ndarray      # [H][M] int
+    K: np.ndarray        # [H][M][d] float64
+    V: np.ndarray
+    rho0: np.ndarray     # [H][M]
+    rho: np.ndarray
+    count: np.ndarray    # [H]
+
+    @staticmethod
+    def read(bank) -> "GpuBank":
+        return GpuBank(bank.tok.cpu().numpy().astype(np.int64), bank.K.float().cpu().numpy().astype(np.float64),
+                       bank.V.float().cpu().numpy().astype(np.float64), bank.rho0.cpu().numpy().astype(np.float64),
+                       bank.rho.cpu().numpy().astype(np.float64), bank.count.cpu().numpy().astype(np.int64))
+
+    def head(self, h) -> od.HeadBank:
+        n = int(self.count[h])
+        return od.HeadBank(self.tok[h, :n].copy(), self.K[h, :n].copy(), self.V[h, :n].copy(), self.rho0[h, :n].copy())
+
+
+def check_order(order: np.ndarray, delta: np.ndarray, tok: np.ndarray, gap: float = GAP) -> int:
+    """GPU permutation vs oracle delta: every inversion must be a near-tie;
+    exactly equal deltas must be ordered by token id.  Returns the number of
+    adjacent near-tie inversions."""
+    n = delta.shape[0]
+    assert np.array_equal(np.sort(order), np.arange(n)), "order is not a permutation"
+    d = delta[order]
+    t = tok[order]
+    runmax = np.maximum.accumulate(d)
+    scale = np.maximum(np.abs(runmax), 1e-30)
+    bad = (runmax - d) > gap * scale
+    assert not bad.any(), f"order inversion beyond the gap at positions {np.nonzero(bad)[0][:10]}"
+    eq = d[1:] == d[:-1]
+    assert np.all(t[1:][eq] > t[:-1][eq]), "equal scores not ordered by token id"
+    return int(np.sum(d[1:] < d[:-1]))
+
+
+def check_crossings(t_gpu, bankK, rho, rho0, candK_sorted, prm, gap=GAP) -> int:
+    """GPU crossing prefix lengths vs the oracle's on the same order.  Rows that
+    differ must be near-ties at the disputed prefix lengths."""
+    t_or, _ = od.crossing_times(bankK, rho, rho0, candK_sorted, prm)
+    diff = np.nonzero(t_gpu != t_or)[0]
+    if diff.size == 0:
+        return 0
+    kmax = candK_sorted.shape[0]
+    # oracle crosses earlier -> check at the last k the GPU did not cross;
+    # GPU crosses earlier -> check at the first k the GPU did cross
+    k_check = np.clip(np.where(t_or[diff] < t_gpu[diff], t_gpu[diff] - 1, t_gpu[diff]), 0, kmax)
+    _, (vals,) = od.crossing_times(bankK[diff], rho[diff], rho0[diff], candK_sorted, prm, at=[k_check])
+    thr = prm.tau * rho0[diff]
+    rel = np.abs(vals - thr) / np.maximum(thr, 1e-30)
+    assert np.all(rel < gap), f"crossing mismatch beyond the gap: rows {diff[rel >= gap][:10]} rel {rel[rel >= gap][:5]}"
+    return int(diff.size)
+
+
+def check_evictions(ev_gpu: np.ndarray, mand: np.ndarray, proj: np.ndarray, gap=GAP):
+    """GPU eviction completion must be a densest top-r of the oracle's
+    projected densities, up to near-ties."""
+    assert np.all(ev_gpu[mand]), "a crossed state was not evicted"
+    rest = ~mand
+    evd = ev_gpu & rest
+    kept = (~ev_gpu) & rest
+    if evd.any() and kept.any():
+        lo = proj[evd].min()
+        hi = proj[kept].max()
+        assert lo >= hi - gap * max(abs(hi), 1e-30), f"eviction completion not densest: min evicted {lo} < max kept {hi}"
+
+
+@dataclass
+class Report:
+    kstar: int
+    order_near_ties: int = 0
+    crossing_near_ties: int = 0
+    admitted: List[int] = field(default_factory=list)
+    evicted: List[int] = field(default_factory=list)
+
+
+def replay_update(before: GpuBank, after: GpuBank, candK, candV, cand_tok, D_gpu, delta_gpu, order_gpu,
+                  t_gpu, rhoP_gpu, kstar_gpu, n_mand_gpu, n_ev_gpu, prm: od.Params, heads: List[int],
+                  rtol_D=2e-5, rtol_rho=1e-4) -> Report:
+    """Stage-replay check of one layer update over the listed density heads."""
+    N = cand_tok.shape[0]
+    kmax = min(N, prm.M)
+    tok = cand_tok.astype(np.int64)
+    k = int(kstar_gpu)
+    rep = Report(kstar=k)
+    tl, ns, cache = [], [], {}
+    for h in heads:
+        b = before.head(h)
+        rho_def = od.density(b.K, prm)
+        # stored density (maintained incrementally on the GPU) vs its definition
+        np.testing.assert_allclose(before.rho[h, :b.n], rho_def, rtol=rtol_rho, atol=1e-6)
+        # stage 1: disturbance and order
+        D, delta = od.disturbance(b.K, candK[h], prm)
+        np.testing.assert_allclose(D_gpu[h], D, rtol=rtol_D, atol=1e-6)
+        np.testing.assert_allclose(delta_gpu[h], delta, rtol=rtol_D, atol=1e-6)
+        rep.order_near_ties += check_order(order_gpu[h], delta, tok)
+        # stage 2: crossing prefix lengths on the GPU's order
+        pi = order_gpu[h].astype(np.int64)
+        cs = np.asarray(candK[h], np.float64)[pi[:kmax]]
+        tg = t_gpu[h, :b.n].astype(np.int64)
+        rep.crossing_near_ties += check_crossings(tg, b.K, rho_def, b.rho0, cs, prm)
+        tl.append(tg)
+        ns.append(b.n)
+        cache[h] = (b, rho_def, cs, pi, tg)
+    # stage 3: shared prefix from the GPU's crossing times (integer logic, exact)
+    ks_ref, _ = od.feasible_prefix(tl, ns, prm.M, kmax)
+    assert ks_ref == k, f"k* {k} != oracle prefix {ks_ref} on the GPU crossing times"
+    for h in heads:
+        b, rho_def, cs, pi, tg = cache[h]
+        e = max(0, b.n + k - prm.M) if k > 0 else 0
+        assert int(n_ev_gpu[h]) == e, f"head {h}: evicted {int(n_ev_gpu[h])} != e {e}"
+        mand = (tg <= k) if k > 0 else np.zeros(b.n, bool)
+        assert int(n_mand_gpu[h]) == int(mand.sum()), f"head {h}: n_mandatory"
+        # stage 4: projected densities and eviction set
+        proj = od.projected_density(b.K, rho_def, cs, k, prm)
+        live = ~mand
+        np.testing.assert_allclose(rhoP_gpu[h, :b.n][live], proj[live], rtol=rtol_rho, atol=1e-6)
+        new_n = int(after.count[h])
+        assert new_n == b.n - e + k, f"head {h}: count {new_n} != {b.n - e + k}"
+        new_toks = set(after.tok[h, :new_n].tolist())
+        adm_toks = tok[pi[:k]]
+        assert set(adm_toks.tolist()) <= new_toks, f"head {h}: admitted tokens missing"
+        ev_gpu = np.array([t not in new_toks for t in b.tok.tolist()], dtype=bool)
+        assert int(ev_gpu.sum()) == e
+        check_evictions(ev_gpu, mand, proj)
+        rep.admitted.append(k)
+        rep.evicted.append(e)
+        # stage 5: new bank -- exact pairing, frozen baselines, densities
+        hb = after.head(h)
+        oldpos = {int(t): i for i, t in enumerate(b.tok.tolist())}
+        cpos = {int(t): i for i, t in enumerate(tok.tolist())}
+        is_new = np.zeros(hb.n, bool)
+        for i, t in enumerate(hb.tok.tolist()):
+            if t in oldpos:
+                j = oldpos[t]
+                assert np.array_equal(hb.K[i], b.K[j]) and np.array_equal(hb.V[i], b.V[j]), "survivor row moved"
+                assert hb.rho0[i] == b.rho0[j], "survivor baseline changed"
+            else:
+                is_new[i] = True
+                j = cpos[t]
+                assert np.array_equal(hb.K[i], np.asarray(candK[h][j], np.float64)), "admitted K not exact"
+                assert np.array_equal(hb.V[i], np.asarray(candV[h][j], np.float64)), "admitted V not paired"
+        rho_new = od.density(hb.K, prm)
+        np.testing.assert_allclose(after.rho[h, :hb.n], rho_new, rtol=rtol_rho, atol=1e-6)
+        np.testing.assert_allclose(hb.rho0[is_new], rho_new[is_new], rtol=rtol_rho, atol=1e-6)
+    return rep

@@ -1,0 +1,146 @@
+"""Shared drivers for the GPU parity tests (HIP path through the C ABI,
+checked against the fp64 oracle)."""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from kvsynth import LayerGen, Workload, frame_tokens
+from oracle import density as od
+from oracle.attention import attention as oracle_attention
+
+from _parity import GpuBank, replay_update
+
+
+def banner(msg: str):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+def gpu_available() -> bool:
+    import torch
+    return torch.cuda.is_available()
+
+
+def kv_dtype(wl: Workload):
+    import torch
+    return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+
+def layer_for(wl: Workload, prm: od.Params, labels=None, seg_cap=8, diagnostics=True, seg_len=0, retention=0.0):
+    import kv_cache_compression_head_amd as kb
+    from kv_cache_compression_head_amd.pipeline import LayerCache
+    desc = kb.LayerDesc(H=wl.H, d=wl.d, M=prm.M, dtype=kb.KVB_BF16 if wl.dtype == "bf16" else kb.KVB_F32,
+                        frame_tokens=wl.F, labels=list(labels) if labels is not None else [0] * wl.H,
+                        tau=prm.tau, sigma=prm.sigma, eps=prm.eps, p=prm.p, seg_len=seg_len, retention=retention)
+    return LayerCache(desc, seg_cap=seg_cap, diagnostics=diagnostics)
+
+
+def dev(x, dtype):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(dtype).contiguous()
+
+
+def dev_i32(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to("cuda")
+
+
+def run_update(lc, gen: LayerGen, wl: Workload, prm: od.Params, frames: Tuple[int, int], heads: List[int],
+               lay=None, replay=True, candK=None, candV=None, ctok=None):
+    """Score + update with the given candidate frames; stage-replay check."""
+    import torch
+    import kv_cache_compression_head_amd as kb
+    t0, t1 = frames
+    if candK is None:
+        candK = gen.keys_all(range(t0, t1))
+        candV = gen.values_all(range(t0, t1))
+        ctok = frame_tokens(wl, t0, t1)
+    kdt = kv_dtype(wl)
+    before = GpuBank.read(lc.bank) if replay else None
+    cK, cV, ct = dev(candK, kdt), dev(candV, kdt), dev_i32(ctok)
+    lay = lay if lay is not None else kb.KVLayout()
+    D, s, o = lc.score(cK, ct, lay)
+    lc.update(cK, cV, ct, D, o, lay)
+    torch.cuda.synchronize()
+    st = int(lc.out.status.cpu()[0])
+    assert st == 0, f"device status {st:#x}"
+    if not replay:
+        return None
+    after = GpuBank.read(lc.bank)
+    return replay_update(before, after, candK.astype(np.float64), candV.astype(np.float64), np.asarray(ctok),
+                         D.cpu().numpy(), s.cpu().numpy(), o.cpu().numpy(), lc.out.t_cross.cpu().numpy(),
+                         lc.out.rho_proj.cpu().numpy(), int(lc.out.k_star.cpu()[0]),
+                         lc.out.n_mandatory.cpu().numpy(), lc.out.n_evicted.cpu().numpy(), prm, heads)
+
+
+@dataclasses.dataclass
+class AttnInputs:
+    Q: np.ndarray
+    sinkK: np.ndarray
+    sinkV: np.ndarray
+    winK: np.ndarray
+    winV: np.ndarray
+    chunkK: np.ndarray
+    chunkV: np.ndarray
+
+
+def attn_inputs(gen: LayerGen, wl: Workload, sink=True) -> AttnInputs:
+    w0, w1 = wl.window
+    c0, c1 = wl.chunk
+    base = w0 if w1 > w0 else c0
+    wf, cf = list(range(w0, w1)), list(range(c0, c1))
+    rt_w = [f - base for f in wf]
+    rt_c = [f - base for f in cf]
+    H = wl.H
+    z = np.zeros((H, 0, wl.d), np.float32)
+    return AttnInputs(
+        Q=gen.queries_all(cf, rt_c),
+        sinkK=gen.keys_all([0]) if sink else z, sinkV=gen.values_all([0]) if sink else z,
+        winK=gen.keys_all(wf, rt_w) if wf else z, winV=gen.values_all(wf) if wf else z,
+        chunkK=gen.keys_all(cf, rt_c), chunkV=gen.values_all(cf))
+
+
+def layout_for(ai: AttnInputs, kdt, win_start=0):
+    """Device layout; the window ring is rotated by win_start to exercise wrap-around."""
+    import kv_cache_compression_head_amd as kb
+    H, W = ai.winK.shape[0], ai.winK.shape[1]
+    lay = kb.KVLayout()
+    t = {}
+    if ai.sinkK.shape[1]:
+        t["sk"], t["sv"] = dev(ai.sinkK, kdt), dev(ai.sinkV, kdt)
+        lay.sink_k, lay.sink_v = t["sk"], t["sv"]
+    if W:
+        ring_k = np.roll(ai.winK, win_start, axis=1)
+        ring_v = np.roll(ai.winV, win_start, axis=1)
+        t["wk"], t["wv"] = dev(ring_k, kdt), dev(ring_v, kdt)
+        lay.win_k, lay.win_v, lay.win_start, lay.win_len = t["wk"], t["wv"], win_start % W, W
+    t["ck"], t["cv"] = dev(ai.chunkK, kdt), dev(ai.chunkV, kdt)
+    lay.chunk_k, lay.chunk_v = t["ck"], t["cv"]
+    lay._keep = t
+    return lay
+
+
+def check_attention(O_gpu: np.ndarray, ai: AttnInputs, bank: Optional[GpuBank], heads: Sequence[int],
+                    max_abs: float, mean_abs: float, rows: Optional[np.ndarray] = None):
+    errs = []
+    for h in heads:
+        parts_k = [ai.sinkK[h], ai.winK[h], ai.chunkK[h]]
+        parts_v = [ai.sinkV[h], ai.winV[h], ai.chunkV[h]]
+        if bank is not None:
+            n = int(bank.count[h])
+            parts_k.insert(1, bank.K[h, :n])
+            parts_v.insert(1, bank.V[h, :n])
+        K = np.concatenate([np.asarray(p, np.float64) for p in parts_k])
+        V = np.concatenate([np.asarray(p, np.float64) for p in parts_v])
+        Q = np.asarray(ai.Q[h], np.float64)
+        r = np.arange(Q.shape[0]) if rows is None else rows
+        ref = oracle_attention(Q[r], K, V)
+        err = np.abs(O_gpu[h][r].astype(np.float64) - ref)
+        errs.append(err)
+    e = np.concatenate([x.reshape(-1) for x in errs])
+    assert e.max() <= max_abs, f"attention max-abs {e.max():.3e} > {max_abs}"
+    assert e.mean() <= mean_abs, f"attention mean-abs {e.mean():.3e} > {mean_abs}"
+    return float(e.max()), float(e.mean())

@@ -1,0 +1,95 @@
+"""GPU parity of chunk_attention on ragged segment tables (fp64 oracle)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from kvsynth import round_bf16
+from oracle.attention import attention as oracle_attention
+
+import gpu_common as gc
+
+pytestmark = pytest.mark.gpu
+
+
+def _seg_table(H, seg_cap, per_head):
+    import torch
+    import kv_cache_compression_head_amd as kb
+    arr = (kb.kvb_segment * (H * seg_cap))()
+    ns = []
+    for h, segs in enumerate(per_head):
+        for i, (kp, vp, ln) in enumerate(segs):
+            arr[h * seg_cap + i] = kb.kvb_segment(kp, vp, ln, 0)
+        ns.append(len(segs))
+    raw = np.frombuffer(bytes(arr), dtype=np.uint8).copy()
+    return torch.from_numpy(raw).to("cuda"), torch.tensor(ns, dtype=torch.int32, device="cuda")
+
+
+@pytest.mark.parametrize("d,Lq,lens,dtype", [
+    (128, 300, [[70, 1, 64, 129], [5], [64 * 5]], "bf16"),
+    (64, 129, [[33, 31], [1, 2, 3, 4, 5, 200], [640]], "bf16"),
+    (128, 4680, [[1560, 9360, 3120, 1560, 4680]], "bf16"),
+    (64, 48, [[16, 64, 48], [16, 60, 48]], "f32"),
+])
+def test_attention_ragged(d, Lq, lens, dtype):
+    import torch
+    import kv_cache_compression_head_amd as kb
+    gc.banner(f"attention d={d} Lq={Lq} lens={lens} {dtype}")
+    rng = np.random.default_rng(d + Lq)
+    H = len(lens)
+    kdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    rnd = (lambda x: round_bf16(x)) if dtype == "bf16" else (lambda x: x.astype(np.float32))
+    Q = rnd(rng.normal(size=(H, Lq, d)).astype(np.float32) * 1.5)
+    seg_cap = max(len(l) for l in lens) + 1
+    keep = []
+    per_head = []
+    Ks, Vs = [], []
+    for h, ls in enumerate(lens):
+        segs = []
+        kk, vv = [], []
+        for ln in ls:
+            k = rnd(rng.normal(size=(ln, d)).astype(np.float32) * 1.5)
+            v = rnd(rng.normal(size=(ln, d)).astype(np.float32))
+            tk, tv = gc.dev(k, kdt), gc.dev(v, kdt)
+            keep += [tk, tv]
+            segs.append((tk.data_ptr(), tv.data_ptr(), ln))
+            kk.append(k)
+            vv.append(v)
+        per_head.append(segs)
+        Ks.append(np.concatenate(kk))
+        Vs.append(np.concatenate(vv))
+    segs_t, nseg_t = _seg_table(H, seg_cap, per_head)
+    Qd = gc.dev(Q, kdt)
+    O = torch.empty(H, Lq, d, dtype=torch.float32, device="cuda")
+    kb.chunk_attention(H, d, Lq, kb.KVB_BF16 if dtype == "bf16" else kb.KVB_F32, Qd, segs_t, nseg_t, seg_cap, O,
+                       out_f32=True)
+    torch.cuda.synchronize()
+    On = O.cpu().numpy()
+    tol = (2e-2, 2e-3) if dtype == "bf16" else (1e-4, 1e-5)
+    errs = []
+    for h in range(H):
+        ref = oracle_attention(Q[h].astype(np.float64), Ks[h].astype(np.float64), Vs[h].astype(np.float64))
+        errs.append(np.abs(On[h] - ref).reshape(-1))
+    e = np.concatenate(errs)
+    assert e.max() <= tol[0] and e.mean() <= tol[1], (e.max(), e.mean())
+
+
+def test_attention_bf16_output_dtype():
+    import torch
+    import kv_cache_compression_head_amd as kb
+    rng = np.random.default_rng(7)
+    H, Lq, d, L = 2, 200, 128, 333
+    Q = round_bf16(rng.normal(size=(H, Lq, d)).astype(np.float32))
+    K = round_bf16(rng.normal(size=(H, L, d)).astype(np.float32))
+    V = round_bf16(rng.normal(size=(H, L, d)).astype(np.float32))
+    tk, tv = gc.dev(K, torch.bfloat16), gc.dev(V, torch.bfloat16)
+    per_head = [[(tk[h].data_ptr(), tv[h].data_ptr(), L)] for h in range(H)]
+    segs_t, nseg_t = _seg_table(H, 2, per_head)
+    O = torch.empty(H, Lq, d, dtype=torch.bfloat16, device="cuda")
+    kb.chunk_attention(H, d, Lq, kb.KVB_BF16, gc.dev(Q, torch.bfloat16), segs_t, nseg_t, 2, O)
+    torch.cuda.synchronize()
+    On = O.float().cpu().numpy()
+    for h in range(H):
+        ref = oracle_attention(Q[h].astype(np.float64), K[h].astype(np.float64), V[h].astype(np.float64))
+        e = np.abs(On[h] - ref)
+        assert e.max() <= 2e-2 and e.mean() <= 2e-3

@@ -1,0 +1,127 @@
+"""GPU parity of the DensityKV path (scoring, admission/eviction, attention)
+through the C ABI against the fp64 oracle, with stage replay."""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+
+from kvsynth import WORKLOADS, LayerGen, Workload, frame_tokens
+from oracle import density as od
+
+import gpu_common as gc
+from _parity import GpuBank
+
+pytestmark = pytest.mark.gpu
+
+
+def _prm(wl, **kw):
+    base = dict(M=wl.M, tau=wl.tau, sigma=wl.sigma, eps=wl.eps, p=wl.p)
+    base.update(kw)
+    return od.Params(**base)
+
+
+def _stream(wl, prm, seed=0, attn=True, max_abs=1e-4, mean_abs=1e-5, win_start=0):
+    import torch
+    gc.banner(f"density stream {wl.name} dtype={wl.dtype} M={prm.M} tau={prm.tau} p={prm.p} seed={seed}")
+    gen = LayerGen(wl, seed, 0)
+    lc = gc.layer_for(wl, prm)
+    heads = list(range(wl.H))
+    reps = []
+    for fr in wl.bank_updates:
+        r = gc.run_update(lc, gen, wl, prm, fr, heads)
+        gc.banner(f"  update {fr}: k*={r.kstar} evicted/head={r.evicted[:4]} order near-ties={r.order_near_ties} "
+                  f"crossing near-ties={r.crossing_near_ties}")
+        reps.append(r)
+    if attn:
+        ai = gc.attn_inputs(gen, wl)
+        kdt = gc.kv_dtype(wl)
+        lay = gc.layout_for(ai, kdt, win_start=win_start)
+        lc.update(None, None, None, None, None, lay)      # N = 0: segment table only
+        Q = gc.dev(ai.Q, kdt)
+        O = lc.attention(Q, out_f32=True)
+        torch.cuda.synchronize()
+        bank = GpuBank.read(lc.bank)
+        mx, mn = gc.check_attention(O.cpu().numpy(), ai, bank, heads, max_abs, mean_abs)
+        gc.banner(f"  attention max-abs {mx:.2e} mean-abs {mn:.2e}")
+    return reps, lc
+
+
+def test_tiny_f32_default():
+    wl = WORKLOADS["tiny"]
+    reps, _ = _stream(wl, _prm(wl))
+    assert [r.kstar for r in reps][0] == 48
+
+
+def test_tiny_bf16():
+    wl = dataclasses.replace(WORKLOADS["tiny"], dtype="bf16", name="tiny-bf16")
+    _stream(wl, _prm(wl), max_abs=2e-2, mean_abs=2e-3)
+
+
+def test_tiny_fifo_p0_tau_inf():
+    wl = WORKLOADS["tiny"]
+    prm = _prm(wl, tau=math.inf, p=0.0)
+    _, lc = _stream(wl, prm, attn=False)
+    bank = GpuBank.read(lc.bank)
+    last = wl.bank_updates[-1][1] * wl.F
+    for h in range(wl.H):
+        assert sorted(bank.tok[h, :bank.count[h]].tolist()) == list(range(last - 64, last))
+
+
+def test_tiny_full_admission():
+    wl = WORKLOADS["tiny"]
+    prm = _prm(wl, M=144, tau=math.inf)
+    reps, lc = _stream(wl, prm)
+    assert all(r.kstar == 48 for r in reps)
+
+
+@pytest.mark.parametrize("p,tau", [(1.0, 1.3), (4.0, 1.3), (3.0, 1.2), (2.0, 1.05)])
+def test_tiny_phi_modes(p, tau):
+    wl = WORKLOADS["tiny"]
+    _stream(wl, _prm(wl, p=p, tau=tau), attn=False)
+
+
+def test_duplicate_rejected_on_gpu():
+    """Far-apart bank keys plus a candidate duplicating one: the duplicate is
+    ordered last and is the only candidate rejected."""
+    import torch
+    import kv_cache_compression_head_amd as kb
+    d, n = 64, 60
+    wl = dataclasses.replace(WORKLOADS["tiny"], H=1, M=100)
+    prm = od.Params(M=100, tau=2.0)
+    lc = gc.layer_for(wl, prm)
+    K = (np.eye(d)[:n] * 200.0).astype(np.float32)[None]
+    V = np.random.default_rng(0).normal(size=(1, n, d)).astype(np.float32)
+    gc.run_update(lc, None, wl, prm, (0, 0), [0], candK=K, candV=V, ctok=np.arange(n, dtype=np.int32))
+    cK = np.concatenate([np.eye(d)[n:n + 3] * 200.0, K[0, 5:6]]).astype(np.float32)[None]
+    cV = np.ones((1, 4, d), np.float32)
+    rep = gc.run_update(lc, None, wl, prm, (0, 0), [0], candK=cK, candV=cV,
+                        ctok=np.array([100, 101, 102, 103], np.int32))
+    assert rep.kstar == 3
+    bank = GpuBank.read(lc.bank)
+    toks = set(bank.tok[0, :bank.count[0]].tolist())
+    assert 103 not in toks and {100, 101, 102, 5} <= toks
+
+
+MID = Workload(name="mid", H=4, d=128, width=52, height=30, dtype="bf16", M=3120, tau=2.0,
+               bank_updates=((1, 3), (3, 7)), window=(7, 9), chunk=(9, 12))
+
+
+def test_mid_bf16_default():
+    _stream(MID, _prm(MID), max_abs=2e-2, mean_abs=2e-3, win_start=1000)
+
+
+def test_mid_bf16_tight_tau():
+    _stream(MID, _prm(MID, tau=1.02), attn=False, seed=1)
+
+
+def test_empty_update_and_zero_candidates():
+    import torch
+    import kv_cache_compression_head_amd as kb
+    wl = WORKLOADS["tiny"]
+    prm = _prm(wl)
+    lc = gc.layer_for(wl, prm)
+    lc.update(None, None, None, None, None, kb.KVLayout())
+    torch.cuda.synchronize()
+    assert int(lc.bank.count.sum().cpu()) == 0
+    assert lc.out.nseg.cpu().tolist() == [0, 0]

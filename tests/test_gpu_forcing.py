@@ -1,0 +1,114 @@
+"""GPU parity of the Forcing-KV path (segment similarity, BottomK, static /
+dynamic segment tables, ragged chunk attention) against the fp64 oracle."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from kvsynth import WORKLOADS, LayerGen, frame_tokens, head_labels
+from oracle import forcing as of
+from oracle.attention import attention as oracle_attention
+
+import gpu_common as gc
+from _parity import check_order
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(wl, seed=0, rows=None):
+    import torch
+    import kv_cache_compression_head_amd as kb
+    gc.banner(f"forcing {wl.name} seg_len={wl.seg_len} r={wl.retention} seed={seed}")
+    gen = LayerGen(wl, seed, 0)
+    labels = head_labels(wl, seed)
+    F, H, d = wl.F, wl.H, wl.d
+    h0, h1 = wl.history
+    c0, c1 = wl.chunk
+    hist_f = list(range(h0, h1))
+    ch_f = list(range(c0, c1))
+    histK = gen.keys_all(hist_f, hist_f)
+    histV = gen.values_all(hist_f)
+    sinkK, sinkV = gen.keys_all([0], [0]), gen.values_all([0])
+    chK, chV = gen.keys_all(ch_f, ch_f), gen.values_all(ch_f)
+    Q = gen.queries_all(ch_f, ch_f)
+    T = len(hist_f)
+    items = T * (F // wl.seg_len)
+    keep = of.keep_count(wl.retention, items)
+    seg_cap = min(256, 2 + keep + 1)
+    from kvsynth import Workload
+    prm_M = 0
+    import kv_cache_compression_head_amd.pipeline as pl
+    desc = kb.LayerDesc(H=H, d=d, M=prm_M, dtype=kb.KVB_BF16, frame_tokens=F, labels=labels.tolist(),
+                        seg_len=wl.seg_len, retention=wl.retention)
+    lc = pl.LayerCache(desc, seg_cap=seg_cap)
+    kdt = torch.bfloat16
+    N = T * F
+    hk, hv = gc.dev(histK, kdt), gc.dev(histV, kdt)
+    tok = gc.dev_i32(frame_tokens(wl, h0, h1))
+    lay = kb.KVLayout(sink_k=gc.dev(sinkK, kdt), sink_v=gc.dev(sinkV, kdt),
+                      chunk_k=gc.dev(chK, kdt), chunk_v=gc.dev(chV, kdt))
+    D, s, o = lc.score(hk, tok, lay)
+    lc.update(hk, hv, tok, D, o, lay)
+    O = lc.attention(gc.dev(Q, kdt), out_f32=True)
+    torch.cuda.synchronize()
+    assert int(lc.out.status.cpu()[0]) == 0
+    dyn = [h for h in range(H) if labels[h] == 2]
+    stat = [h for h in range(H) if labels[h] == 1]
+    # segment scores (shared by the dynamic heads)
+    ref = of.segment_scores(histK[dyn], chK[dyn][:, :F], F, wl.seg_len)
+    s_np, o_np = s.cpu().numpy(), o.cpu().numpy()
+    for h in dyn:
+        np.testing.assert_allclose(s_np[h, :items], ref, rtol=2e-5, atol=2e-6)
+        check_order(o_np[h, :items], ref, np.arange(items))
+    kept = np.sort(o_np[dyn[0], :keep])
+    # segment tables
+    segs = lc.segments()
+    esz = 2
+    base_k = hk.data_ptr()
+    for h in range(H):
+        sg = segs[h]
+        assert sg[0][2] == F and sg[-1][2] == wl.Lq
+        mid = sg[1:-1]
+        if labels[h] == 1:
+            assert len(mid) == 1 and mid[0][2] == F
+            assert mid[0][0] == base_k + (h * N + (T - 1) * F) * d * esz
+        else:
+            got_rows = []
+            for (kp, vp, ln) in mid:
+                r0 = (kp - base_k) // (d * esz) - h * N
+                got_rows.extend(range(r0, r0 + ln))
+            assert got_rows == of.kept_token_rows(kept, F, wl.seg_len).tolist()
+    # attention rows (sampled at large sizes)
+    O_np = O.cpu().numpy()
+    rr = np.arange(wl.Lq) if rows is None else rows
+    errs = []
+    for h in range(H):
+        if labels[h] == 1:
+            sel = of.static_rows(T, F)
+        else:
+            sel = of.kept_token_rows(kept, F, wl.seg_len)
+        K = np.concatenate([sinkK[h], histK[h][sel], chK[h]]).astype(np.float64)
+        V = np.concatenate([sinkV[h], histV[h][sel], chV[h]]).astype(np.float64)
+        refo = oracle_attention(Q[h][rr].astype(np.float64), K, V)
+        errs.append(np.abs(O_np[h][rr] - refo))
+    e = np.concatenate([x.reshape(-1) for x in errs])
+    assert e.max() <= 2e-2 and e.mean() <= 2e-3, (e.max(), e.mean())
+    gc.banner(f"forcing {wl.name}: kept items {kept.tolist()[:12]} attention max-abs {e.max():.2e} mean-abs {e.mean():.2e}")
+    return kept
+
+
+def test_forcing_480p_full():
+    wl = WORKLOADS["fkv480p"]
+    kept = _run(wl, rows=np.random.default_rng(0).choice(wl.Lq, 512, replace=False))
+    assert kept.shape[0] == 8
+
+
+def test_forcing_six_segments_per_frame():
+    wl = dataclasses.replace(WORKLOADS["fkv480p"], seg_len=260, retention=0.33, name="fkv-n6")
+    _run(wl, rows=np.arange(0, 4680, 37))
+
+
+def test_forcing_small_shapes():
+    wl = dataclasses.replace(WORKLOADS["fkv480p"], width=8, height=4, H=4, n_static=2, seg_len=8, retention=0.5,
+                             history=(1, 6), chunk=(6, 9), name="fkv-small")
+    _run(wl)
