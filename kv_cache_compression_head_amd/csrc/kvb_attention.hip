@@ -7,9 +7,13 @@
 // is the concatenation of the head's segments (order irrelevant).
 //
 // bf16 path: flash-style online softmax.  Work-group = 4 waves x 32 queries;
-// KV tiles of 64 keys staged in LDS (K row-major, V transposed).  Scores are
-// computed transposed (S^T = K Q^T, 16x16x32 MFMA) so that every lane holds
-// keys of a single query; P^T feeds O^T = V^T P^T directly as the B operand.
+// KV tiles of 64 keys staged in LDS (K row-major, V transposed), double
+// buffered: the next tile's global loads are in flight while the current
+// tile is multiplied.  Scores are computed transposed (S^T = K Q^T, 16x16x32
+// MFMA) so every lane holds keys of a single query; P^T feeds
+// O^T = V^T P^T directly as the B operand.  The running maximum is only
+// moved when a tile raises it by more than 2^8 (exact: numerator and
+// denominator share the stale maximum).
 #include "kvb_common.hpp"
 #include "kvb_launch.hpp"
 
@@ -17,22 +21,35 @@ namespace kvb {
 
 constexpr int ATT_TK = 64;          // keys per tile
 constexpr int ATT_QW = 32;          // queries per wave
+constexpr int ATT_QB = 128;         // queries per work-group
 constexpr int ATT_MAXSEG = 256;     // segments cached in LDS
+constexpr float ATT_RESCALE_LOG2 = 8.0f;
 
-struct SegCache {
-  const SegEntry* segs;
-  int n;
-};
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// locate virtual key j: segment index via the LDS prefix table
-KVB_DEV int seg_find(const int* pre, int n, int j) {
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    const int m = (lo + hi + 1) >> 1;
-    if (pre[m] <= j) lo = m; else hi = m - 1;
-  }
-  return lo;
+KVB_DEV uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
 }
+
+// per-slot cursor over the segment prefix table (rows only move forward);
+// the current segment's bounds and base pointer stay in registers
+struct SegCursor {
+  int s, lo, hi;
+  const uint16_t* base;
+  KVB_DEV void init(const int* pre, const void* const* bases) {
+    s = 0; lo = pre[0]; hi = pre[1]; base = (const uint16_t*)bases[0];
+  }
+  KVB_DEV const uint16_t* row(const int* pre, const void* const* bases, int nseg, int j, int D) {
+    if (j >= hi) {
+      while (s + 1 < nseg && pre[s + 1] <= j) ++s;
+      lo = pre[s]; hi = pre[s + 1]; base = (const uint16_t*)bases[s];
+    }
+    return base + (int64_t)(j - lo) * D;
+  }
+};
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __restrict__ Q, void* __restrict__ O,
@@ -41,12 +58,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
                                                            float scale_log2, int out_f32, int nqt) {
   using Op = Ops<uint16_t>;
   constexpr int LDK = D + 8;              // K row stride (elements)
-  constexpr int LDV = ATT_TK + 8;         // V^T row stride (elements)
+  constexpr int LDV = ATT_TK + 4;         // V^T row stride (elements): 34 dwords, conflict-free b64 reads
   constexpr int NKS = D / 32;             // k-steps for S^T
   constexpr int NDB = D / 16;             // d blocks for O^T
   constexpr int CPR = D / 8;              // 16-byte chunks per row
-  __shared__ __attribute__((aligned(16))) uint16_t sK[ATT_TK * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * LDV];
+  constexpr int KPASS = ATT_TK * CPR / 256;   // K chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][ATT_TK * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * LDV];
   __shared__ int s_pre[ATT_MAXSEG + 1];
   __shared__ const void* s_k[ATT_MAXSEG];
   __shared__ const void* s_v[ATT_MAXSEG];
@@ -75,7 +93,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
   const int Lkv = s_pre[nseg];
 
   // query fragments (B operand of S^T = K Q^T)
-  const int q0 = qt * 128 + w * ATT_QW;
+  const int q0 = qt * ATT_QB + w * ATT_QW;
   s16x8_t qf[2][NKS];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -96,52 +114,68 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
   float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
   float l_run[2] = {0.f, 0.f};
 
-  const int ntile = (Lkv + ATT_TK - 1) / ATT_TK;
-  for (int tile = 0; tile < ntile; ++tile) {
-    const int kbase = tile * ATT_TK;
-    // ---- stage K (row-major) and V (transposed) ----
-    {
-      // K: rows r = tid / CPR + (256 / CPR) * i
+  // staging registers and cursors
+  const bool vthr = tid < 16 * CPR;
+  const int kg = tid / CPR, dc = tid % CPR;          // V: keys 4kg..4kg+3, d 8dc..8dc+7
+  u32x4_t rk[KPASS], rv[4];
+  SegCursor ck[KPASS], cv[4];
+  if (nseg > 0) {
 #pragma unroll
-      for (int i = 0; i < ATT_TK * CPR / 256; ++i) {
-        const int r = tid / CPR + (256 / CPR) * i;
-        const int c = tid % CPR;
-        const int j = kbase + r;
-        u32x4_t val = {0u, 0u, 0u, 0u};
-        if (j < Lkv) {
-          const int s = seg_find(s_pre, nseg, j);
-          const uint16_t* p = (const uint16_t*)s_k[s] + (int64_t)(j - s_pre[s]) * D + c * 8;
-          val = *reinterpret_cast<const u32x4_t*>(p);
-        }
-        *reinterpret_cast<u32x4_t*>(sK + r * LDK + c * 8) = val;
-      }
-      // V: thread covers keys 4kg..4kg+3 and d 8dc..8dc+7
-      if (tid < 16 * CPR) {
-        const int kg = tid / CPR, dc = tid % CPR;
-        uint16_t vv[4][8];
+    for (int i = 0; i < KPASS; ++i) ck[i].init(s_pre, s_k);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = kbase + 4 * kg + i;
-          u32x4_t val = {0u, 0u, 0u, 0u};
-          if (j < Lkv) {
-            const int s = seg_find(s_pre, nseg, j);
-            const uint16_t* p = (const uint16_t*)s_v[s] + (int64_t)(j - s_pre[s]) * D + dc * 8;
-            val = *reinterpret_cast<const u32x4_t*>(p);
-          }
-          const uint16_t* e = reinterpret_cast<const uint16_t*>(&val);
+    for (int i = 0; i < 4; ++i) cv[i].init(s_pre, s_v);
+  }
+
+  auto fetch = [&](int kbase) {
 #pragma unroll
-          for (int x = 0; x < 8; ++x) vv[i][x] = e[x];
-        }
+    for (int i = 0; i < KPASS; ++i) {
+      const int r = tid / CPR + (256 / CPR) * i;
+      const int j = kbase + r;
+      if (j < Lkv) rk[i] = gload16(ck[i].row(s_pre, s_k, nseg, j, D) + (tid % CPR) * 8);
+      else rk[i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    if (vthr) {
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const uint32_t lo = (uint32_t)vv[0][x] | ((uint32_t)vv[1][x] << 16);
-          const uint32_t hi = (uint32_t)vv[2][x] | ((uint32_t)vv[3][x] << 16);
-          uint2 pk; pk.x = lo; pk.y = hi;
-          *reinterpret_cast<uint2*>(sV + (8 * dc + x) * LDV + 4 * kg) = pk;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int j = kbase + 4 * kg + i;
+        if (j < Lkv) rv[i] = gload16(cv[i].row(s_pre, s_v, nseg, j, D) + dc * 8);
+        else rv[i] = u32x4_t{0u, 0u, 0u, 0u};
       }
     }
-    __syncthreads();
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KPASS; ++i) {
+      const int r = tid / CPR + (256 / CPR) * i;
+      *reinterpret_cast<u32x4_t*>(&sK[buf][r * LDK + (tid % CPR) * 8]) = rk[i];
+    }
+    if (vthr) {
+      // transpose 4 keys x 8 d into 8 rows of V^T (4 keys each)
+      const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&rv[0]);
+      const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&rv[1]);
+      const uint16_t* e2 = reinterpret_cast<const uint16_t*>(&rv[2]);
+      const uint16_t* e3 = reinterpret_cast<const uint16_t*>(&rv[3]);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        uint2 pk;
+        pk.x = (uint32_t)e0[x] | ((uint32_t)e1[x] << 16);
+        pk.y = (uint32_t)e2[x] | ((uint32_t)e3[x] << 16);
+        *reinterpret_cast<uint2*>(&sV[buf][(8 * dc + x) * LDV + 4 * kg]) = pk;
+      }
+    }
+  };
+
+  const int ntile = (Lkv + ATT_TK - 1) / ATT_TK;
+  if (ntile > 0) {
+    fetch(0);
+    stage(0);
+  }
+  __syncthreads();
+  for (int tile = 0; tile < ntile; ++tile) {
+    const int cur = tile & 1;
+    const int kbase = tile * ATT_TK;
+    const bool more = tile + 1 < ntile;
+    if (more) fetch(kbase + ATT_TK);
 
     // ---- S^T = K Q^T ----
     f32x4_t s[4][2];
@@ -149,7 +183,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
     for (int kb = 0; kb < 4; ++kb) {
       s[kb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       s[kb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kp = sK + (16 * kb + (lane & 15)) * LDK;
+      const uint16_t* kp = sK[cur] + (16 * kb + (lane & 15)) * LDK;
 #pragma unroll
       for (int k = 0; k < NKS; ++k) {
         const s16x8_t a = Op::load(kp + Op::off16(k, lane));
@@ -158,63 +192,74 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
       }
     }
     // ---- online softmax (log2 domain), lane owns query 16qb + (lane & 15) ----
-    const bool partial = kbase + ATT_TK > Lkv;
-    s16x4_t pk[2][4];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx = -__builtin_inff();
+    if (kbase + ATT_TK > Lkv) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = s[kb][qb][i] * scale_log2;
-          if (partial && kbase + 16 * kb + 4 * g + i >= Lkv) v = -__builtin_inff();
-          s[kb][qb][i] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int i = 0; i < 4; ++i)
+          if (kbase + 16 * kb + 4 * g + i >= Lkv) { s[kb][0][i] = -__builtin_inff(); s[kb][1][i] = -__builtin_inff(); }
+    }
+    float mt[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = s[0][qb][0];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m_run[qb], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew);
-      m_run[qb] = mnew;
+      mt[qb] = mx * scale_log2;
+    }
+    const bool grow = (mt[0] > m_run[0] + ATT_RESCALE_LOG2) || (mt[1] > m_run[1] + ATT_RESCALE_LOG2);
+    if (__any(grow)) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float mnew = fmaxf(m_run[qb], mt[qb]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew);
+        m_run[qb] = mnew;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db][qb] *= alpha;
+      }
+    }
+    uint32_t pk[2][4][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float nm = -m_run[qb];
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(s[kb][qb][i] - mnew);
+          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i], scale_log2, nm));
           ls += p[i];
         }
-        s16x4_t v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = (short)f32_to_bf16(p[i]);
-        pk[qb][kb] = v;
+        pk[qb][kb][0] = pack_bf16x2(p[0], p[1]);
+        pk[qb][kb][1] = pack_bf16x2(p[2], p[3]);
       }
-      l_run[qb] = l_run[qb] * alpha + ls;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db][qb] *= alpha;
+      l_run[qb] += ls;
     }
     // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int hk = 0; hk < 2; ++hk) {
-      s16x8_t b0, b1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        b0[i] = pk[0][2 * hk][i]; b0[4 + i] = pk[0][2 * hk + 1][i];
-        b1[i] = pk[1][2 * hk][i]; b1[4 + i] = pk[1][2 * hk + 1][i];
-      }
+      u32x4_t b0 = {pk[0][2 * hk][0], pk[0][2 * hk][1], pk[0][2 * hk + 1][0], pk[0][2 * hk + 1][1]};
+      u32x4_t b1 = {pk[1][2 * hk][0], pk[1][2 * hk][1], pk[1][2 * hk + 1][0], pk[1][2 * hk + 1][1]};
+      const s16x8_t bb0 = __builtin_bit_cast(s16x8_t, b0);
+      const s16x8_t bb1 = __builtin_bit_cast(s16x8_t, b1);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const uint16_t* vp = sV + (16 * db + (lane & 15)) * LDV + 32 * hk + 4 * g;
+        const uint16_t* vp = sV[cur] + (16 * db + (lane & 15)) * LDV + 32 * hk + 4 * g;
         const uint2 lo = *reinterpret_cast<const uint2*>(vp);
         const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
-        u32x4_t raw = {lo.x, lo.y, hi.x, hi.y};
+        const u32x4_t raw = {lo.x, lo.y, hi.x, hi.y};
         const s16x8_t a = __builtin_bit_cast(s16x8_t, raw);
-        o[db][0] = Op::mma16(a, b0, o[db][0]);
-        o[db][1] = Op::mma16(a, b1, o[db][1]);
+        o[db][0] = Op::mma16(a, bb0, o[db][0]);
+        o[db][1] = Op::mma16(a, bb1, o[db][1]);
       }
     }
+    if (more) stage(cur ^ 1);
     __syncthreads();
   }
 
@@ -236,8 +281,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
           *reinterpret_cast<float4*>((float*)O + off) = v;
         } else {
           uint2 pkv;
-          pkv.x = (uint32_t)f32_to_bf16(o[db][qb][0] * inv) | ((uint32_t)f32_to_bf16(o[db][qb][1] * inv) << 16);
-          pkv.y = (uint32_t)f32_to_bf16(o[db][qb][2] * inv) | ((uint32_t)f32_to_bf16(o[db][qb][3] * inv) << 16);
+          pkv.x = pack_bf16x2(o[db][qb][0] * inv, o[db][qb][1] * inv);
+          pkv.y = pack_bf16x2(o[db][qb][2] * inv, o[db][qb][3] * inv);
           *reinterpret_cast<uint2*>((uint16_t*)O + off) = pkv;
         }
       }
@@ -245,7 +290,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
   }
 }
 
-// fp32 reference-precision path (small shapes): one thread per (head, query)
+// fp32 path (small shapes): one thread per (head, query), online softmax
 template <int D>
 __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ Q, float* __restrict__ O,
                                                       const SegEntry* __restrict__ segs,
@@ -290,7 +335,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t st) {
   if (a.Lq <= 0 || a.H <= 0) return hipSuccess;
   if (a.et == ET_BF16) {
-    const int nqt = (a.Lq + 127) / 128;
+    const int nqt = (a.Lq + ATT_QB - 1) / ATT_QB;
     const float sl2 = a.scale * 1.4426950408889634f;
     const dim3 grid((unsigned)(nqt * a.H));
     if (a.d == 128)

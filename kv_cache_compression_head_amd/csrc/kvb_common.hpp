@@ -148,6 +148,13 @@ template <typename E> struct KeySpace {
   }
 };
 
+// 16-byte load through the global address space (generic pointers that are
+// known to point to device memory; keeps the load off the LDS counter)
+KVB_DEV u32x4_t gload16(const void* p) {
+  typedef __attribute__((address_space(1))) const u32x4_t gvec;
+  return *(gvec*)(p);
+}
+
 // order-preserving map of a float to an unsigned key (ascending floats ->
 // ascending keys; -0 and +0 differ, NaN not expected)
 KVB_DEV uint32_t float_key(float f) {

@@ -179,8 +179,10 @@ __global__ void hist_kernel(const int32_t* __restrict__ t, const int32_t* __rest
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= count[h]) return;
   int v = t[(int64_t)h * M + b];
-  v = v < 0 ? 0 : (v > kmax + 1 ? kmax + 1 : v);
-  atomicAdd(&hist[(int64_t)h * (kmax + 2) + v], 1);
+  v = v < 0 ? 0 : v;
+  // states that never cross within kmax do not enter any |V_h(k)|; skipping
+  // them avoids serialising most atomics on one bin
+  if (v <= kmax) atomicAdd(&hist[(int64_t)h * (kmax + 2) + v], 1);
 }
 
 __global__ __launch_bounds__(1024) void cumsum_kernel(int32_t* __restrict__ hist, uint64_t active,
