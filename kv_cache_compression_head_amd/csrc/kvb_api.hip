@@ -107,8 +107,8 @@ constexpr int SCAN_SUB = 32;      // candidates per scan subtile
 constexpr int MAX_SPLITS = 8;
 
 struct Layout {
-  size_t normB, normC, k0, k1, v0, v1, t, cp, hist, rhoP, evict, surv, evl, nsurv, nev, accS, accAE, accAA,
-      cos, split, total;
+  size_t normB, normC, augB, augC, k0, k1, v0, v1, t, cp, hist, rhoP, evict, surv, evl, fixl, nsurv, nfix,
+      fmode, accS, accAE, accAA, cos, split, total;
   int kmax, cps, ncp;
 };
 
@@ -129,6 +129,8 @@ Layout layout_of(const kvb_layer_desc* L, int32_t N) {
   size_t off = 0;
   o.normB = bump(&off, H * M * 4);
   o.normC = bump(&off, H * N * 4);
+  o.augB = bump(&off, H * M * 16);
+  o.augC = bump(&off, H * N * 16);
   o.k0 = bump(&off, H * N * 8);
   o.k1 = bump(&off, H * N * 8);
   o.v0 = bump(&off, H * N * 4);
@@ -140,13 +142,15 @@ Layout layout_of(const kvb_layer_desc* L, int32_t N) {
   o.evict = bump(&off, H * M);
   o.surv = bump(&off, H * M * 4);
   o.evl = bump(&off, H * M * 4);
+  o.fixl = bump(&off, H * M * 4);
   o.nsurv = bump(&off, H * 4);
-  o.nev = bump(&off, H * 4);
+  o.nfix = bump(&off, H * 4);
+  o.fmode = bump(&off, H * 4);
   o.accS = bump(&off, H * M * 4);
   o.accAE = bump(&off, H * (int64_t)o.kmax * 4);
   o.accAA = bump(&off, H * (int64_t)o.kmax * 4);
   o.cos = bump(&off, (int64_t)N * 4);
-  o.split = bump(&off, H * (int64_t)MAX_SPLITS * N * 4);
+  o.split = bump(&off, H * (int64_t)MAX_SPLITS * (N > L->M ? N : L->M) * 4);
   o.total = off;
   return o;
 }
@@ -173,11 +177,31 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
 }
 
 int choose_splits(int H, int rows, int ncols) {
-  const int wgs = H * ((rows + 63) / 64);
+  const int wgs = H * ((rows + 255) / 256);
   const int tiles = (ncols + 63) / 64;
   int s = 1;
   while (s < MAX_SPLITS && wgs * s < 1024 && s * 2 <= tiles) s *= 2;
   return s;
+}
+
+// one gram launch over rows_ub rows and at most cols_ub columns, with the
+// column range split over work-groups when the row tiles alone cannot fill
+// the device; split partials are summed in a fixed order
+hipError_t run_gram(GramLaunch g, int H, int rows_ub, int cols_ub, float* dst, int64_t dst_hstride, float* split,
+                    int64_t split_n, hipStream_t st) {
+  g.splits = choose_splits(H, rows_ub, cols_ub);
+  if (g.splits > 1) {
+    g.out = split;
+    g.out_hstride = (int64_t)MAX_SPLITS * split_n;
+    g.split_stride = split_n;
+  } else {
+    g.out = dst;
+    g.out_hstride = dst_hstride;
+    g.split_stride = 0;
+  }
+  hipError_t e = launch_gram(g, st);
+  if (e != hipSuccess || g.splits == 1) return e;
+  return launch_sum_splits(split, (int64_t)MAX_SPLITS * split_n, split_n, g.splits, dst, dst_hstride, H, rows_ub, st);
 }
 
 }  // namespace
@@ -223,10 +247,12 @@ int kvbank_score(const kvb_layer_desc* L, const kvb_bank* bank, const void* cand
   if (hd.dens) {
     float* nB = at<float>(ws, lo.normB);
     float* nC = at<float>(ws, lo.normC);
-    HIPCHK(launch_norms(bank->K, et, H, M, d, pc.inv_s2, nB, st));
-    HIPCHK(launch_norms(cand_k, et, H, N, d, pc.inv_s2, nC, st));
+    void* aB = at<void>(ws, lo.augB);
+    void* aC = at<void>(ws, lo.augC);
+    HIPCHK(launch_norms(bank->K, et, H, M, d, pc.inv_s2, nB, aB, st));
+    HIPCHK(launch_norms(cand_k, et, H, N, d, pc.inv_s2, nC, aC, st));
     GramLaunch g{};
-    g.k = KeysDesc{bank->K, cand_k, nB, nC, M, N, d, H, et};
+    g.k = KeysDesc{bank->K, cand_k, nB, nC, aB, aC, M, N, d, H, et};
     g.rows = VList{nullptr, nullptr, 0, 0, 0, M, N, 0};
     g.cols = VList{nullptr, bank->count, 0, 1, 0, 0, M, 0};
     g.pc = pc;
@@ -330,9 +356,11 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
     const int kmax = lo.kmax;
     float* nB = at<float>(ws, lo.normB);
     float* nC = at<float>(ws, lo.normC);
-    HIPCHK(launch_norms(bank->K, et, H, M, d, pc.inv_s2, nB, st));
-    HIPCHK(launch_norms(cand_k, et, H, N, d, pc.inv_s2, nC, st));
-    const KeysDesc kd{bank->K, cand_k, nB, nC, M, N, d, H, et};
+    void* aB = at<void>(ws, lo.augB);
+    void* aC = at<void>(ws, lo.augC);
+    HIPCHK(launch_norms(bank->K, et, H, M, d, pc.inv_s2, nB, aB, st));
+    HIPCHK(launch_norms(cand_k, et, H, N, d, pc.inv_s2, nC, aC, st));
+    const KeysDesc kd{bank->K, cand_k, nB, nC, aB, aC, M, N, d, H, et};
     ScanLaunch s{};
     s.k = kd; s.rho = bank->rho; s.rho0 = bank->rho0; s.count = bank->count; s.order = order;
     s.active = hd.dens; s.kmax = kmax; s.tau = L->params.tau; s.cps = lo.cps; s.ncp = lo.ncp;
@@ -347,6 +375,7 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
     sel.bank_tok = bank->tok; sel.evict = at<uint8_t>(ws, lo.evict); sel.surv = at<int32_t>(ws, lo.surv);
     sel.evl = at<int32_t>(ws, lo.evl); sel.n_surv = at<int32_t>(ws, lo.nsurv); sel.n_ev = out->n_evicted;
     sel.n_mand = out->n_mandatory; sel.status = out->status;
+    sel.fixl = at<int32_t>(ws, lo.fixl); sel.n_fix = at<int32_t>(ws, lo.nfix); sel.fmode = at<int32_t>(ws, lo.fmode);
     HIPCHK(launch_kstar(sel, st));
     HIPCHK(launch_scan(s, true, st));
     HIPCHK(launch_evict(sel, st));
@@ -354,21 +383,24 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
     GramLaunch g{};
     g.k = kd; g.pc = pc; g.phi_mode = pm; g.splits = 1; g.split_stride = 0; g.active = hd.dens;
     const VList evl{sel.evl, sel.n_ev, M, 1, 0, 0, M, 0};
+    const VList fxl{sel.fixl, sel.n_fix, M, 1, 0, 0, M, 0};
     const VList srv{sel.surv, sel.n_surv, M, 1, 0, 0, M, 0};
     const VList adm{order, out->k_star, N, 0, M, 0, kmax, 0};
-    g.rows = srv; g.cols = evl; g.out = at<float>(ws, lo.accS); g.out_hstride = M; g.self_excl = 0;
-    HIPCHK(launch_gram(g, st));
-    g.rows = adm; g.cols = evl; g.out = at<float>(ws, lo.accAE); g.out_hstride = kmax;
-    HIPCHK(launch_gram(g, st));
-    g.rows = adm; g.cols = adm; g.out = at<float>(ws, lo.accAA); g.out_hstride = kmax; g.self_excl = 1;
-    HIPCHK(launch_gram(g, st));
+    float* split = at<float>(ws, lo.split);
+    const int64_t sstride = (N > M ? N : M);
+    g.rows = srv; g.cols = evl; g.self_excl = 0;
+    HIPCHK(run_gram(g, H, M, kmax, at<float>(ws, lo.accS), M, split, sstride, st));
+    g.rows = adm; g.cols = fxl;
+    HIPCHK(run_gram(g, H, kmax, M, at<float>(ws, lo.accAE), kmax, split, sstride, st));
+    g.rows = adm; g.cols = adm; g.self_excl = 1;
+    HIPCHK(run_gram(g, H, kmax, kmax, at<float>(ws, lo.accAA), kmax, split, sstride, st));
     ApplyLaunch ap{};
     ap.H = H; ap.M = M; ap.N = N; ap.d = d; ap.et = et; ap.kmax = kmax; ap.active = hd.dens;
     ap.bankK = bank->K; ap.bankV = bank->V; ap.bank_tok = bank->tok; ap.rho0 = bank->rho0; ap.rho = bank->rho;
     ap.count = bank->count; ap.candK = cand_k; ap.candV = cand_v; ap.cand_tok = cand_tok; ap.order = order;
     ap.D = D; ap.kstar = out->k_star; ap.surv = sel.surv; ap.n_surv = sel.n_surv; ap.evl = sel.evl;
     ap.n_ev = sel.n_ev; ap.rhoP = s.rhoP; ap.acc_surv = at<float>(ws, lo.accS);
-    ap.acc_adm_ev = at<float>(ws, lo.accAE); ap.acc_adm_adm = at<float>(ws, lo.accAA);
+    ap.acc_adm_ev = at<float>(ws, lo.accAE); ap.acc_adm_adm = at<float>(ws, lo.accAA); ap.fmode = sel.fmode;
     HIPCHK(launch_apply(ap, st));
   }
   SegLaunch sg{};

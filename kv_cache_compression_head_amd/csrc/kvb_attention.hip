@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
   __shared__ const void* s_k[ATT_MAXSEG];
   __shared__ const void* s_v[ATT_MAXSEG];
 
-  const int bid = blockIdx.x;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);   // head-major items, one XCD per range
   const int h = bid / nqt;
   const int qt = bid % nqt;
   const int lane = lane_id(), w = wave_id();

@@ -130,12 +130,17 @@ KVB_DEV int vlist_at(const VList& L, int h, int i) {
 }
 
 // Keys of one layer in two buffers: bank [H][M][d] and candidates [H][N][d],
-// with their scaled squared norms (|k|^2 / sigma^2) in [H][M] and [H][N].
+// with their scaled squared norms (|k|^2 / sigma^2) in [H][M] and [H][N] and
+// a 16-byte "augmentation" row per key holding |k|^2 split exactly into
+// bf16 parts (hi, mid, lo) (bf16 keys) or as one float (fp32 keys); an extra
+// MFMA k-step against (-1/2, -1/2, -1/2) then yields k.x - |k|^2 / 2.
 template <typename E> struct KeySpace {
   const E* bankK;
   const E* candK;
   const float* bankN;
   const float* candN;
+  const u32x4_t* bankA;
+  const u32x4_t* candA;
   int32_t M;
   int32_t N;
   int32_t d;
@@ -146,7 +151,45 @@ template <typename E> struct KeySpace {
   KVB_DEV float nrm(int h, int v) const {
     return v < M ? bankN[(int64_t)h * M + v] : candN[(int64_t)h * N + (v - M)];
   }
+  KVB_DEV const u32x4_t* aug(int h, int v) const {
+    return v < M ? bankA + ((int64_t)h * M + v) : candA + ((int64_t)h * N + (v - M));
+  }
 };
+
+// Per-head view of a KeySpace with compile-time row length: row addresses are
+// one select and one shift from two per-head bases.
+template <typename E, int D> struct HeadKeys {
+  const E* bank;      // bankK + h*M*D
+  const E* cand;      // candK + (h*N - M)*D  (indexed by the virtual index)
+  const u32x4_t* abank;
+  const u32x4_t* acand;
+  uint32_t lim;       // M + N
+  uint32_t M;
+  KVB_DEV HeadKeys(const KeySpace<E>& ks, int h)
+      : bank(ks.bankK + (int64_t)h * ks.M * D), cand(ks.candK + ((int64_t)h * ks.N - ks.M) * D),
+        abank(ks.bankA + (int64_t)h * ks.M), acand(ks.candA + ((int64_t)h * ks.N - ks.M)),
+        lim((uint32_t)(ks.M + ks.N)), M((uint32_t)ks.M) {}
+  KVB_DEV bool ok(int v) const { return (uint32_t)v < lim; }
+  KVB_DEV const E* row(int v) const { return ((uint32_t)v < M ? bank : cand) + (int64_t)(uint32_t)v * D; }
+  KVB_DEV const u32x4_t* aug(int v) const { return ((uint32_t)v < M ? abank : acand) + (uint32_t)v; }
+};
+
+// value the optimiser cannot see through (keeps a clamp a single max)
+KVB_DEV float opaque(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Work-groups are dealt round-robin to the 8 XCDs of the chip (dispatch
+// index p runs on XCD p % 8).  Remap so that XCD x processes one contiguous
+// range of the W logical work items: items that share data (same head) then
+// share one XCD's L2.  The map is a bijection for any W.
+constexpr int NUM_XCD = 8;
+KVB_DEV int xcd_remap(int p, int W) {
+  const int x = p % NUM_XCD, j = p / NUM_XCD;
+  const int q = W / NUM_XCD, rem = W % NUM_XCD;
+  return x * q + (x < rem ? x : rem) + j;
+}
 
 // 16-byte load through the global address space (generic pointers that are
 // known to point to device memory; keeps the load off the LDS counter)

@@ -5,213 +5,310 @@
 // Density-Constrained Bank Update") and appendix B.1: the interaction of two
 // post-RoPE keys is a softened inverse power of their squared distance; the
 // exact update touches bank x candidate pairs, admitted x evicted pairs and
-// admitted x admitted pairs.  Squared distances come from bf16 MFMA dot
-// products: |a - b|^2 = |a|^2 + |b|^2 - 2 a.b with fp32 accumulation.
+// admitted x admitted pairs.
+//
+// Squared distances come from 32x32 MFMA dot products with fp32
+// accumulation.  One extra k-step multiplies the column key's squared norm
+// (split exactly into three bf16 parts) by -1/2, so the MFMA returns
+// R = x.y - |y|^2/2 and the softened distance is
+//   t = eps + |x - y|^2 / sigma^2 = fma(R, -2/sigma^2, |x|^2/sigma^2 + eps),
+// leaving fma, max, the reciprocal/power and one add per pair on the VALU.
 #include "kvb_common.hpp"
 #include "kvb_launch.hpp"
 
 namespace kvb {
 
+// LDS row layout (elements): [0, D) key, [D, D+AUGE) augmentation, zero pad.
+template <typename E> struct Aug;
+template <> struct Aug<uint16_t> {
+  static constexpr int AUGE = 8;                    // 16 bytes
+  template <int D> static constexpr int ldr() { return D + 24; }   // 304 B rows at D=128
+  KVB_DEV static s16x8_t xfrag(int lane) {          // (-1/2, -1/2, -1/2, 0, ...) for k-slice 0
+    const short m = (short)0xBF00;                  // bf16(-0.5)
+    return (lane >> 5) == 0 ? s16x8_t{m, m, m, 0, 0, 0, 0, 0} : s16x8_t{};
+  }
+  KVB_DEV static int aug_off(int lane) { return (lane >> 5) * 8; }
+};
+template <> struct Aug<float> {
+  static constexpr int AUGE = 4;
+  template <int D> static constexpr int ldr() { return D + 4; }
+  KVB_DEV static float xfrag(int lane) { return (lane >> 5) == 0 ? -0.5f : 0.0f; }
+  KVB_DEV static int aug_off(int lane) { return lane >> 5; }
+};
+
 // ---------------------------------------------------------------------------
 // squared norms: one group of CPR lanes per row, 16-byte chunks
 // ---------------------------------------------------------------------------
 template <typename E, int CPR>
-__global__ __launch_bounds__(256) void norms_kernel(const E* __restrict__ keys, int64_t nrows, int d,
-                                                    float scale, float* __restrict__ out) {
+__global__ __launch_bounds__(256) void norms_kernel(const E* __restrict__ keys, int64_t nrows, int d, float scale,
+                                                    float* __restrict__ out, u32x4_t* __restrict__ aug) {
   constexpr int EPC = 16 / sizeof(E);
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t row = gid / CPR;
   const int c = (int)(gid % CPR);
   float s = 0.0f;
   if (row < nrows) {
-    const E* p = keys + row * d + c * EPC;
-    const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(p);
+    const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(keys + row * d + c * EPC);
     const E* e = reinterpret_cast<const E*>(&raw);
 #pragma unroll
     for (int j = 0; j < EPC; ++j) {
-      float x = Ops<E>::to_f32(e[j]);
+      const float x = Ops<E>::to_f32(e[j]);
       s = __builtin_fmaf(x, x, s);
     }
   }
 #pragma unroll
   for (int o = CPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-  if (row < nrows && c == 0) out[row] = s * scale;
+  if (row < nrows && c == 0) {
+    out[row] = s * scale;
+    u32x4_t a = {0u, 0u, 0u, 0u};
+    if constexpr (sizeof(E) == 2) {
+      const uint16_t hi = f32_to_bf16(s);
+      const float r1 = s - bf16_to_f32(hi);
+      const uint16_t mid = f32_to_bf16(r1);
+      const uint16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+      a[0] = (uint32_t)hi | ((uint32_t)mid << 16);
+      a[1] = (uint32_t)lo;
+    } else {
+      a[0] = __float_as_uint(s);
+    }
+    aug[row] = a;
+  }
 }
 
-hipError_t launch_norms(const void* keys, int et, int H, int rows, int d, float scale, float* out,
+hipError_t launch_norms(const void* keys, int et, int H, int rows, int d, float scale, float* out, void* aug,
                         hipStream_t st) {
   const int64_t nrows = (int64_t)H * rows;
   if (nrows == 0) return hipSuccess;
   const int esz = et == ET_BF16 ? 2 : 4;
   const int cpr = d * esz / 16;
-  const int64_t threads = nrows * cpr;
-  const dim3 grid((unsigned)((threads + 255) / 256));
+  const dim3 grid((unsigned)((nrows * cpr + 255) / 256));
+  u32x4_t* a = (u32x4_t*)aug;
   if (et == ET_BF16) {
-    if (cpr == 8) hipLaunchKernelGGL((norms_kernel<uint16_t, 8>), grid, dim3(256), 0, st, (const uint16_t*)keys, nrows, d, scale, out);
-    else hipLaunchKernelGGL((norms_kernel<uint16_t, 16>), grid, dim3(256), 0, st, (const uint16_t*)keys, nrows, d, scale, out);
+    if (cpr == 8) hipLaunchKernelGGL((norms_kernel<uint16_t, 8>), grid, dim3(256), 0, st, (const uint16_t*)keys, nrows, d, scale, out, a);
+    else hipLaunchKernelGGL((norms_kernel<uint16_t, 16>), grid, dim3(256), 0, st, (const uint16_t*)keys, nrows, d, scale, out, a);
   } else {
-    if (cpr == 16) hipLaunchKernelGGL((norms_kernel<float, 16>), grid, dim3(256), 0, st, (const float*)keys, nrows, d, scale, out);
-    else hipLaunchKernelGGL((norms_kernel<float, 32>), grid, dim3(256), 0, st, (const float*)keys, nrows, d, scale, out);
+    if (cpr == 16) hipLaunchKernelGGL((norms_kernel<float, 16>), grid, dim3(256), 0, st, (const float*)keys, nrows, d, scale, out, a);
+    else hipLaunchKernelGGL((norms_kernel<float, 32>), grid, dim3(256), 0, st, (const float*)keys, nrows, d, scale, out, a);
   }
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// tile staging: TR key rows of D elements gathered by virtual index into LDS
-// (row stride LDR elements), 16-byte chunks, 256 threads.
+// tile staging: TR key rows (+ their augmentation) gathered by virtual index
+// into LDS rows of LDR elements; 256 threads, 16-byte chunks.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int TR>
+template <typename E, int D, int TR, int LDR>
 struct TileLoader {
   static constexpr int EPC = 16 / sizeof(E);     // elements per chunk
-  static constexpr int CPR = D / EPC;            // chunks per row
+  static constexpr int CPR = D / EPC;            // key chunks per row
   static constexpr int RPP = 256 / CPR;          // rows per pass
   static constexpr int PASSES = TR / RPP;
   static_assert(TR % RPP == 0, "tile rows");
+  static_assert(TR <= 256, "aug rows");
   u32x4_t reg[PASSES];
+  u32x4_t areg;
 
-  // v_of(r) returns the virtual row index of tile row r or -1 (zero fill)
-  template <typename KS, typename F>
-  KVB_DEV void load(const KS& ks, int h, F v_of) {
+  // v_of(r): virtual row index of tile row r, or -1 (zero fill)
+  template <typename F>
+  KVB_DEV void load(const HeadKeys<E, D>& hk, F v_of) {
     const int t = threadIdx.x;
     const int c = t % CPR;
 #pragma unroll
     for (int i = 0; i < PASSES; ++i) {
-      const int r = t / CPR + i * RPP;
-      const int v = v_of(r);
-      if (v >= 0) reg[i] = *reinterpret_cast<const u32x4_t*>(ks.row(h, v) + c * EPC);
-      else reg[i] = u32x4_t{0u, 0u, 0u, 0u};
+      const int v = v_of(t / CPR + i * RPP);
+      reg[i] = v >= 0 ? gload16(hk.row(v) + c * EPC) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    if (t < TR) {
+      const int v = v_of(t);
+      areg = v >= 0 ? gload16(hk.aug(v)) : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-  template <int LDR>
   KVB_DEV void store(E* lds) const {
     const int t = threadIdx.x;
     const int c = t % CPR;
 #pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-      const int r = t / CPR + i * RPP;
-      *reinterpret_cast<u32x4_t*>(lds + r * LDR + c * EPC) = reg[i];
+    for (int i = 0; i < PASSES; ++i)
+      *reinterpret_cast<u32x4_t*>(lds + (t / CPR + i * RPP) * LDR + c * EPC) = reg[i];
+    if (t < TR) *reinterpret_cast<u32x4_t*>(lds + t * LDR + D) = areg;
+  }
+  // zero the padding after the augmentation (read by the upper k-slice lanes)
+  KVB_DEV static void zero_pad(E* lds) {
+    constexpr int padE = LDR - D - 16 / (int)sizeof(E);
+    if constexpr (padE > 0) {
+      for (int r = threadIdx.x; r < TR; r += 256)
+        for (int j = 0; j < padE; ++j) lds[r * LDR + D + 16 / (int)sizeof(E) + j] = E{};
     }
   }
 };
 
 // ---------------------------------------------------------------------------
-// gram row sums.  Work-group: 4 waves x 16 rows; column tiles of 64 staged
-// through LDS (double buffered).  A operand = column keys (LDS), B operand =
-// the wave's 16 row keys (registers).  Lane accumulates phi for its row
-// (lane & 15) over columns 4*(lane>>4)+i of each 16-column subtile.
+// gram row sums: out[i] = sum_{j in cols} phi(row_i, col_j).
+// Work-group: 4 waves x 64 rows (two 32-row blocks per wave, A operand in
+// registers); column tiles of 64 (two 32-column subtiles, B operand) staged
+// through LDS, double buffered.  Lane (h = lane>>5, n = lane&31) accumulates
+// rows 8(i>>2) + 4h + (i&3) of each block against column n; a final
+// butterfly over n sums the columns.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int MODE, bool SELF>
-__global__ __launch_bounds__(256) void gram_kernel(KeySpace<E> ks, VList rows, VList cols, float* __restrict__ out,
+__global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows, VList cols, float* __restrict__ out,
                                                    int64_t out_hstride, int64_t split_stride, PhiConst pc,
                                                    uint64_t active) {
   using O = Ops<E>;
-  constexpr int LDR = D + O::PAD;
+  using A = Aug<E>;
+  constexpr int LDR = A::template ldr<D>();
   constexpr int TC = 64;
-  constexpr int NK = D / O::K16;
+  constexpr int NK = D / O::K32;
   __shared__ __attribute__((aligned(16))) E sY[2][TC * LDR];
-  __shared__ float sYn[2][TC];
   __shared__ int sYv[2][TC];
 
-  const int h = blockIdx.y;
+  // XCD-aware order: logical items (head, split, row tile), head-major
+  const int R = gridDim.x, S = gridDim.z;
+  const int lin = xcd_remap(blockIdx.x + R * (blockIdx.y + gridDim.y * blockIdx.z), R * gridDim.y * S);
+  const int h = lin / (S * R);
+  const int zs = (lin / R) % S;
   if (!head_on(active, h)) return;
+  const HeadKeys<E, D> hk(ks, h);
   const int nrows = vlist_count(rows, h);
-  const int r0 = blockIdx.x * 64;
+  const int r0 = (lin % R) * 256;
   if (r0 >= nrows) return;
   const int ncols = vlist_count(cols, h);
   const int ntiles = (ncols + TC - 1) / TC;
   const int per = (ntiles + (int)gridDim.z - 1) / (int)gridDim.z;
-  const int t0 = blockIdx.z * per;
+  const int t0 = zs * per;
   const int t1 = min(ntiles, t0 + per);
 
   const int lane = lane_id(), w = wave_id();
-  const int myrow = r0 + w * 16 + (lane & 15);
-  const int rv0 = myrow < nrows ? vlist_at(rows, h, myrow) : -1;
-  const bool rvalid = ks.ok(rv0);
-  const int rv = rvalid ? rv0 : -1;
+  const int hh = lane >> 5, nn = lane & 31;
+  const int wrow = r0 + w * 64;
 
-  typename O::frag xf[NK];
-  {
-    const E* xp = rvalid ? ks.row(h, rv) : nullptr;
+  typename O::frag xf[2][NK];
+  float xs[2][16];
 #pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      if (rvalid) xf[k] = O::load(xp + O::off16(k, lane));
-      else xf[k] = typename O::frag{};
+  for (int xb = 0; xb < 2; ++xb) {
+    const int r = wrow + 32 * xb + nn;
+    int v = r < nrows ? vlist_at(rows, h, r) : -1;
+    v = hk.ok(v) ? v : -1;
+    const E* xp = v >= 0 ? hk.row(v) : nullptr;
+#pragma unroll
+    for (int k = 0; k < NK; ++k) xf[xb][k] = v >= 0 ? O::load(xp + O::off32(k, lane)) : typename O::frag{};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = 8 * (i >> 2) + 4 * hh + (i & 3);
+      const int rr = wrow + 32 * xb + m;
+      int vm = rr < nrows ? vlist_at(rows, h, rr) : -1;
+      vm = hk.ok(vm) ? vm : -1;
+      xs[xb][i] = (vm >= 0 ? ks.nrm(h, vm) : 0.0f) + pc.eps;
     }
   }
-  const float xs = rvalid ? ks.nrm(h, rv) + pc.eps : pc.eps;
-  float acc = 0.0f;
+  const typename O::frag xa = A::xfrag(lane);
+  float acc[2][16];
+#pragma unroll
+  for (int xb = 0; xb < 2; ++xb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[xb][i] = 0.0f;
 
-  TileLoader<E, D, TC> ld;
+  TileLoader<E, D, TC, LDR> ld;
+  TileLoader<E, D, TC, LDR>::zero_pad(sY[0]);
+  TileLoader<E, D, TC, LDR>::zero_pad(sY[1]);
   auto vof = [&](int tile) {
     return [&, tile](int r) -> int {
       const int c = tile * TC + r;
       const int v = c < ncols ? vlist_at(cols, h, c) : -1;
-      return ks.ok(v) ? v : -1;
+      return hk.ok(v) ? v : -1;
     };
   };
   if (t0 < t1) {
-    ld.load(ks, h, vof(t0));
-    ld.template store<LDR>(sY[0]);
-    if (threadIdx.x < TC) {
-      const int c = t0 * TC + threadIdx.x;
-      int v = c < ncols ? vlist_at(cols, h, c) : -1;
-      v = ks.ok(v) ? v : -1;
-      sYn[0][threadIdx.x] = v >= 0 ? ks.nrm(h, v) : 0.0f;
-      sYv[0][threadIdx.x] = v;
-    }
+    ld.load(hk, vof(t0));
+    ld.store(sY[0]);
+    if (threadIdx.x < TC) sYv[0][threadIdx.x] = vof(t0)(threadIdx.x);
   }
   __syncthreads();
   for (int tile = t0; tile < t1; ++tile) {
     const int cur = (tile - t0) & 1;
     const bool more = tile + 1 < t1;
-    float nn = 0.0f;
     int nv = -1;
     if (more) {
-      ld.load(ks, h, vof(tile + 1));
-      if (threadIdx.x < TC) {
-        const int c = (tile + 1) * TC + threadIdx.x;
-        nv = c < ncols ? vlist_at(cols, h, c) : -1;
-        nv = ks.ok(nv) ? nv : -1;
-        nn = nv >= 0 ? ks.nrm(h, nv) : 0.0f;
-      }
+      ld.load(hk, vof(tile + 1));
+      if (threadIdx.x < TC) nv = vof(tile + 1)(threadIdx.x);
     }
-    const bool full = (tile + 1) * TC <= ncols;
-    const E* Y = sY[cur];
 #pragma unroll
-    for (int s = 0; s < TC / 16; ++s) {
-      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-      const E* yp = Y + (16 * s + (lane & 15)) * LDR;
+    for (int sub = 0; sub < TC / 32; ++sub) {
+      const E* yp = sY[cur] + (32 * sub + nn) * LDR;
+      const int yv = sYv[cur][32 * sub + nn];
+      f32x16_t cc[2];
 #pragma unroll
-      for (int k = 0; k < NK; ++k) c = O::mma16(O::load(yp + O::off16(k, lane)), xf[k], c);
+      for (int i = 0; i < 16; ++i) { cc[0][i] = 0.0f; cc[1][i] = 0.0f; }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int yi = 16 * s + 4 * (lane >> 4) + i;
-        float f = phi_pair<MODE>(c[i], xs + sYn[cur][yi], pc);
-        if (SELF || !full) {
-          const int yv = sYv[cur][yi];
-          const bool ok = yv >= 0 && (!SELF || yv != rv);
-          f = ok ? f : 0.0f;
+      for (int k = 0; k < NK; ++k) {
+        const typename O::frag yk = O::load(yp + O::off32(k, lane));
+        cc[0] = O::mma32(xf[0][k], yk, cc[0]);
+        cc[1] = O::mma32(xf[1][k], yk, cc[1]);
+      }
+      {
+        const typename O::frag ya = O::load(yp + D + A::aug_off(lane));
+        cc[0] = O::mma32(xa, ya, cc[0]);
+        cc[1] = O::mma32(xa, ya, cc[1]);
+      }
+      // an absent column clamps t to +inf, where every phi mode but p = 0 is 0
+      const float lo = opaque(yv >= 0 ? pc.eps : __builtin_inff());
+#pragma unroll
+      for (int xb = 0; xb < 2; ++xb) {
+        const f32x16_t c = cc[xb];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float t = __builtin_fmaf(c[i], pc.c2, xs[xb][i]);
+          t = fmaxf(t, lo);
+          float f = phi_of_t<MODE>(t, pc.neg_half_p);
+          if constexpr (MODE == PHI_P0) f = yv >= 0 ? f : 0.0f;
+          if constexpr (SELF) {
+            // self-exclusion: rows and columns are the same list, so a pair is
+            // its own partner exactly when the list positions coincide
+            const bool self = (tile * TC + 32 * sub + nn) == (wrow + 32 * xb + 8 * (i >> 2) + 4 * hh + (i & 3));
+            f = self ? 0.0f : f;
+          }
+          acc[xb][i] += f;
         }
-        acc += f;
       }
     }
     if (more) {
-      ld.template store<LDR>(sY[cur ^ 1]);
-      if (threadIdx.x < TC) {
-        sYn[cur ^ 1][threadIdx.x] = nn;
-        sYv[cur ^ 1][threadIdx.x] = nv;
-      }
+      ld.store(sY[cur ^ 1]);
+      if (threadIdx.x < TC) sYv[cur ^ 1][threadIdx.x] = nv;
     }
     __syncthreads();
   }
-  acc += __shfl_xor(acc, 16);
-  acc += __shfl_xor(acc, 32);
-  if (rvalid && (lane >> 4) == 0) out[(int64_t)h * out_hstride + (int64_t)blockIdx.z * split_stride + myrow] = acc;
+  // sum over the 32 columns held by the half-wave
+#pragma unroll
+  for (int xb = 0; xb < 2; ++xb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float v = acc[xb][i];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 8);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 1);
+      acc[xb][i] = v;
+    }
+  if (nn == 0) {
+#pragma unroll
+    for (int xb = 0; xb < 2; ++xb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = wrow + 32 * xb + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if (r < nrows) out[(int64_t)h * out_hstride + (int64_t)zs * split_stride + r] = acc[xb][i];
+      }
+  }
+}
+
+template <typename E>
+static KeySpace<E> key_space(const KeysDesc& k) {
+  return KeySpace<E>{(const E*)k.bankK, (const E*)k.candK, k.bankN, k.candN, (const u32x4_t*)k.bankA,
+                     (const u32x4_t*)k.candA, k.M, k.N, k.d};
 }
 
 template <typename E, int D, int MODE>
 static void gram_dispatch_self(const GramLaunch& g, dim3 grid, hipStream_t st) {
-  KeySpace<E> ks{(const E*)g.k.bankK, (const E*)g.k.candK, g.k.bankN, g.k.candN, g.k.M, g.k.N, g.k.d};
+  const KeySpace<E> ks = key_space<E>(g.k);
   if (g.self_excl)
     hipLaunchKernelGGL((gram_kernel<E, D, MODE, true>), grid, dim3(256), 0, st, ks, g.rows, g.cols, g.out,
                        g.out_hstride, g.split_stride, g.pc, g.active);
@@ -233,7 +330,7 @@ static void gram_dispatch_mode(const GramLaunch& g, dim3 grid, hipStream_t st) {
 
 hipError_t launch_gram(const GramLaunch& g, hipStream_t st) {
   if (g.rows.n <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((g.rows.n + 63) / 64), (unsigned)g.k.H, (unsigned)(g.splits > 0 ? g.splits : 1));
+  const dim3 grid((unsigned)((g.rows.n + 255) / 256), (unsigned)g.k.H, (unsigned)(g.splits > 0 ? g.splits : 1));
   if (g.k.et == ET_BF16) {
     if (g.k.d == 128) gram_dispatch_mode<uint16_t, 128>(g, grid, st);
     else gram_dispatch_mode<uint16_t, 64>(g, grid, st);
@@ -268,14 +365,15 @@ hipError_t launch_sum_splits(const float* src, int64_t src_hstride, int64_t spli
 // For bank state b and prefix length k the projected density is
 //   S_b(k) = rho_b + sum_{j<k} phi(b, c_{order[j]}).
 // The candidate axis is cut into 32-candidate subtiles; a 32x32 MFMA tile
-// (A = candidates, B = bank rows) gives lane l the 16 values of bank row
-// (l & 31) for candidates 8q + 4h + r (q = 0..3, h = l >> 5, r = 0..3), i.e.
-// eight groups of four in candidate order, alternating between the lane and
-// its partner l ^ 32.  The canonical running sum inside a subtile is
+// (A = candidates from LDS, B = bank rows in registers, plus the norm
+// augmentation step) gives lane l the 16 values of bank row (l & 31) for
+// candidates 8q + 4h + r (q = 0..3, h = l >> 5, r = 0..3), i.e. eight groups
+// of four in candidate order, alternating between the lane and its partner
+// l ^ 32.  The canonical running sum inside a subtile is
 //   carry + (E_G + P_G(r)),  E_0 = 0, E_{G+1} = E_G + T_G,
 // with T_G and P_G the sequential sums of group G; the carry advances by E_8.
 // This value is monotone in k, identical in the scan and the sum pass, and
-// its subtile totals are what the checkpoints store.
+// its subtile-boundary values are what the checkpoints store.
 //
 // scan pass: t_b = smallest k with S_b(k) > tau * rho0_b (kmax+1 if none).
 // sum pass:  rhoP_b = S_b(k*) starting from the nearest checkpoint.
@@ -288,17 +386,20 @@ __global__ __launch_bounds__(256) void scan_kernel(KeySpace<E> ks, const float* 
                                                    int32_t* __restrict__ t_out, const int32_t* __restrict__ kstar_p,
                                                    float* __restrict__ rhoP, PhiConst pc) {
   using O = Ops<E>;
-  constexpr int LDR = D + O::PAD;
+  using A = Aug<E>;
+  constexpr int LDR = A::template ldr<D>();
   constexpr int TC = 64;               // candidates per LDS stage (two subtiles)
   constexpr int NK = D / O::K32;
   __shared__ __attribute__((aligned(16))) E sC[2][TC * LDR];
-  __shared__ float sCn[2][TC];
 
-  const int h = blockIdx.y;
+  const int R = gridDim.x;
+  const int lin = xcd_remap(blockIdx.x + R * blockIdx.y, R * gridDim.y);
+  const int h = lin / R;
   if (!head_on(active, h)) return;
+  const HeadKeys<E, D> hk(ks, h);
   const int M = ks.M;
   const int n = count[h];
-  const int b0 = blockIdx.x * 128;
+  const int b0 = (lin % R) * 128;
   if (b0 >= n) return;
   const int lane = lane_id(), w = wave_id();
   const int hh = lane >> 5;
@@ -317,7 +418,7 @@ __global__ __launch_bounds__(256) void scan_kernel(KeySpace<E> ks, const float* 
   int t_b = kmax + 1;
   if constexpr (SUM) {
     kst = *kstar_p;
-    // mandatory rows (t_b <= k*) are evicted; their projected density is unused
+    // crossed rows (t_b <= k*) are evicted; their projected density is unused
     need = valid && kst > 0 && t_out[hb] > kst;
     if (!__syncthreads_or(need)) {
       if (valid) rhoP[hb] = r_b;
@@ -339,16 +440,15 @@ __global__ __launch_bounds__(256) void scan_kernel(KeySpace<E> ks, const float* 
   {
     const E* bp = ks.bankK + hb * D;
 #pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      if (valid) bf[k] = O::load(bp + O::off32(k, lane));
-      else bf[k] = typename O::frag{};
-    }
+    for (int k = 0; k < NK; ++k) bf[k] = valid ? O::load(bp + O::off32(k, lane)) : typename O::frag{};
   }
+  const typename O::frag ba = A::xfrag(lane);
   const float xs = valid ? ks.bankN[hb] + pc.eps : pc.eps;
 
-  // LDS stages hold 64 candidates = subtiles 2*stage, 2*stage + 1
   const int st_begin = sub_begin / 2, st_end = (sub_end + 1) / 2;
-  TileLoader<E, D, TC> ld;
+  TileLoader<E, D, TC, LDR> ld;
+  TileLoader<E, D, TC, LDR>::zero_pad(sC[0]);
+  TileLoader<E, D, TC, LDR>::zero_pad(sC[1]);
   auto vof = [&](int stage) {
     return [&, stage](int r) -> int {
       const int j = stage * TC + r;
@@ -357,27 +457,14 @@ __global__ __launch_bounds__(256) void scan_kernel(KeySpace<E> ks, const float* 
     };
   };
   if (st_begin < st_end) {
-    ld.load(ks, h, vof(st_begin));
-    ld.template store<LDR>(sC[0]);
-    if (threadIdx.x < TC) {
-      const int j = st_begin * TC + threadIdx.x;
-      const unsigned c = j < kmax ? (unsigned)order[(int64_t)h * ks.N + j] : 0xFFFFFFFFu;
-      sCn[0][threadIdx.x] = c < (unsigned)ks.N ? ks.candN[(int64_t)h * ks.N + c] : 0.0f;
-    }
+    ld.load(hk, vof(st_begin));
+    ld.store(sC[0]);
   }
   __syncthreads();
   for (int stg = st_begin; stg < st_end; ++stg) {
     const int cur = (stg - st_begin) & 1;
     const bool more = stg + 1 < st_end;
-    float nn = 0.0f;
-    if (more) {
-      ld.load(ks, h, vof(stg + 1));
-      if (threadIdx.x < TC) {
-        const int j = (stg + 1) * TC + threadIdx.x;
-        const unsigned c = j < kmax ? (unsigned)order[(int64_t)h * ks.N + j] : 0xFFFFFFFFu;
-        nn = c < (unsigned)ks.N ? ks.candN[(int64_t)h * ks.N + c] : 0.0f;
-      }
-    }
+    if (more) ld.load(hk, vof(stg + 1));
     const bool wave_busy = __any(!done);
     if (wave_busy) {
 #pragma unroll
@@ -393,13 +480,21 @@ __global__ __launch_bounds__(256) void scan_kernel(KeySpace<E> ks, const float* 
         const E* cpp = sC[cur] + (32 * half + (lane & 31)) * LDR;
 #pragma unroll
         for (int k = 0; k < NK; ++k) acc = O::mma32(O::load(cpp + O::off32(k, lane)), bf[k], acc);
+        acc = O::mma32(O::load(cpp + D + A::aug_off(lane)), ba, acc);
         float v[16];
         const int pos0 = 32 * sub;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int m = 8 * (i >> 2) + 4 * hh + (i & 3);
-          const float f = phi_pair<MODE>(acc[i], xs + sCn[cur][32 * half + m], pc);
-          v[i] = (pos0 + m < kmax) ? f : 0.0f;
+          float t = __builtin_fmaf(acc[i], pc.c2, xs);
+          t = fmaxf(t, pc.eps);
+          v[i] = phi_of_t<MODE>(t, pc.neg_half_p);
+        }
+        if (pos0 + 32 > kmax) {   // last subtile: drop positions past kmax
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int m = 8 * (i >> 2) + 4 * hh + (i & 3);
+            v[i] = (pos0 + m < kmax) ? v[i] : 0.0f;
+          }
         }
         float T[4];
 #pragma unroll
@@ -415,9 +510,12 @@ __global__ __launch_bounds__(256) void scan_kernel(KeySpace<E> ks, const float* 
           Eg[G + 1] = Eg[G] + tg;
         }
         if constexpr (!SUM) {
-          if (!done) {
-            const float s_end = carry + Eg[8];
-            if (s_end > thr) {
+          const float s_end = carry + Eg[8];
+          const bool cross = !done && (s_end > thr);
+          // rows cross once; the exact position search runs only in waves where
+          // some row crosses in this subtile (both lanes of a row agree)
+          if (__any(cross)) {
+            if (cross) {
               int first = 1 << 30;
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
@@ -433,10 +531,10 @@ __global__ __launch_bounds__(256) void scan_kernel(KeySpace<E> ks, const float* 
               const int other = __shfl_xor(first, 32);
               first = min(first, other);
               t_b = pos0 + first + 1;
-              done = true;
             }
-            carry = s_end;
           }
+          if (!done) carry = s_end;
+          done = done || cross;
         } else {
           if (sub < sub_end - 1) {
             carry = carry + Eg[8];
@@ -444,7 +542,6 @@ __global__ __launch_bounds__(256) void scan_kernel(KeySpace<E> ks, const float* 
             const int j = (kst - 1) - pos0;         // element index inside the subtile
             const int q = j >> 3, jh = (j >> 2) & 1, r = j & 3;
             float P = 0.0f;
-            float S = 0.0f;
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
               float PP = 0.0f;
@@ -454,17 +551,14 @@ __global__ __launch_bounds__(256) void scan_kernel(KeySpace<E> ks, const float* 
                 if (qq == q && rr == r) P = PP;
               }
             }
-            S = carry + (Eg[2 * q + jh] + P);
+            const float S = carry + (Eg[2 * q + jh] + P);
             const float So = __shfl_xor(S, 32);
             carry = (hh == jh) ? S : So;
           }
         }
       }
     }
-    if (more) {
-      ld.template store<LDR>(sC[cur ^ 1]);
-      if (threadIdx.x < TC) sCn[cur ^ 1][threadIdx.x] = nn;
-    }
+    if (more) ld.store(sC[cur ^ 1]);
     if constexpr (!SUM) {
       if (!__syncthreads_or(!done)) {
         // every row of the work-group has crossed: later checkpoints are
@@ -483,7 +577,7 @@ __global__ __launch_bounds__(256) void scan_kernel(KeySpace<E> ks, const float* 
 
 template <typename E, int D, int MODE>
 static void scan_dispatch(const ScanLaunch& a, bool sum, dim3 grid, hipStream_t st) {
-  KeySpace<E> ks{(const E*)a.k.bankK, (const E*)a.k.candK, a.k.bankN, a.k.candN, a.k.M, a.k.N, a.k.d};
+  const KeySpace<E> ks = key_space<E>(a.k);
   if (sum)
     hipLaunchKernelGGL((scan_kernel<E, D, MODE, true>), grid, dim3(256), 0, st, ks, a.rho, a.rho0, a.count,
                        a.order, a.active, a.kmax, a.tau, a.cps, a.ncp, a.cp, a.t_out, a.kstar, a.rhoP, a.pc);

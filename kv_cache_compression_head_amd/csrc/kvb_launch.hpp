@@ -13,12 +13,14 @@ struct KeysDesc {            // one layer's keys in two buffers (see KeySpace)
   const void* candK;
   const float* bankN;
   const float* candN;
+  const void* bankA;         // 16 bytes per row
+  const void* candA;
   int32_t M, N, d, H;
   int32_t et;
 };
 
-// |k|^2 * scale for rows [H][rows][d]
-hipError_t launch_norms(const void* keys, int et, int H, int rows, int d, float scale, float* out,
+// out[r] = |k_r|^2 * scale and aug[r] = exact split of |k_r|^2, rows [H][rows][d]
+hipError_t launch_norms(const void* keys, int et, int H, int rows, int d, float scale, float* out, void* aug,
                         hipStream_t s);
 
 // out[h*out_hstride + split*split_stride + i] = sum_{j in cols} phi(row_i, col_j)
@@ -89,6 +91,9 @@ struct SelectLaunch {
   int32_t* n_ev;             // [H]
   int32_t* n_mand;           // [H]
   uint32_t* status;          // device status word
+  int32_t* fixl;             // [H][M] column list of the admitted-state fix-up
+  int32_t* n_fix;            // [H]
+  int32_t* fmode;            // [H] 1: fixl = survivors (direct sum), 0: fixl = evicted (subtract)
 };
 hipError_t launch_kstar(const SelectLaunch& a, hipStream_t s);
 hipError_t launch_evict(const SelectLaunch& a, hipStream_t s);
@@ -106,7 +111,8 @@ struct ApplyLaunch {
   const int32_t* evl; const int32_t* n_ev;
   const float* rhoP;          // [H][M]
   const float* acc_surv;      // [H][M] sum over evicted for survivors (by survivor position)
-  const float* acc_adm_ev;    // [H][kmax] sum over evicted for admitted
+  const float* acc_adm_ev;    // [H][kmax] sum over fixl for admitted
+  const int32_t* fmode;       // [H]
   const float* acc_adm_adm;   // [H][kmax] sum over other admitted for admitted
 };
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s);

@@ -307,6 +307,9 @@ __global__ __launch_bounds__(1024) void evict_kernel(SelectLaunch a) {
     }
   }
   const uint64_t thr = s_prefix;
+  // admitted states' densities: sum over the survivors directly when they are
+  // fewer than the evicted states, else D(c) minus the evicted interactions
+  const bool direct = (n - e) < e;
   // compaction in ascending slot order
   for (int base = 0; base < n; base += 1024) {
     const int b = base + tid;
@@ -325,8 +328,14 @@ __global__ __launch_bounds__(1024) void evict_kernel(SelectLaunch a) {
     int oe = 0, os = 0;
     for (int j = 0; j < w; ++j) { oe += wsum[j] >> 16; os += wsum[j] & 0xFFFF; }
     const int be0 = s_base_e, bs0 = s_base_s;
-    if (live && ev) a.evl[hb + be0 + oe + pe] = b;
-    if (live && !ev) a.surv[hb + bs0 + os + ps] = b;
+    if (live && ev) {
+      a.evl[hb + be0 + oe + pe] = b;
+      if (!direct) a.fixl[hb + be0 + oe + pe] = b;
+    }
+    if (live && !ev) {
+      a.surv[hb + bs0 + os + ps] = b;
+      if (direct) a.fixl[hb + bs0 + os + ps] = b;
+    }
     __syncthreads();
     if (tid == 0) {
       int te = 0, ts = 0;
@@ -340,6 +349,8 @@ __global__ __launch_bounds__(1024) void evict_kernel(SelectLaunch a) {
     a.n_ev[h] = s_base_e;
     a.n_surv[h] = s_base_s;
     a.n_mand[h] = nm;
+    a.n_fix[h] = direct ? s_base_s : s_base_e;
+    a.fmode[h] = direct ? 1 : 0;
     if (s_base_e != e) atomicOr(a.status, DEV_EVICT);
   }
 }
@@ -387,7 +398,8 @@ __global__ __launch_bounds__(256) void apply_adm_kernel(ApplyLaunch a) {
   *reinterpret_cast<u32x4_t*>(dst + c * 16) = *reinterpret_cast<const u32x4_t*>(src + c * 16);
   if (threadIdx.x % (2 * CPR) == 0) {
     const int64_t hk = (int64_t)h * a.kmax + j;
-    const float r = (a.D[(int64_t)h * a.N + cand] - a.acc_adm_ev[hk]) + a.acc_adm_adm[hk];
+    const float r = a.fmode[h] ? a.acc_adm_ev[hk] + a.acc_adm_adm[hk]
+                               : (a.D[(int64_t)h * a.N + cand] - a.acc_adm_ev[hk]) + a.acc_adm_adm[hk];
     a.rho[hb + slot] = r;
     a.rho0[hb + slot] = r;
     a.bank_tok[hb + slot] = a.cand_tok[cand];
