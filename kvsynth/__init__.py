@@ -240,6 +240,8 @@ class LayerGen:
 
     def keys(self, h: int, frames: Sequence[int], rope_t: Optional[Sequence[int]] = None) -> np.ndarray:
         frames = list(frames)
+        if not frames:
+            return np.zeros((0, self.wl.d), dtype=np.float32)
         if rope_t is None:
             rope_t = [0] * len(frames)
         k = self._rotate(self.prerope_keys(h, frames), rope_t)
@@ -253,6 +255,8 @@ class LayerGen:
 
     def queries(self, h: int, frames: Sequence[int], rope_t: Sequence[int]) -> np.ndarray:
         frames = list(frames)
+        if not frames:
+            return np.zeros((0, self.wl.d), dtype=np.float32)
         q = np.stack([_rng(self.seed, self.layer, h, _S_QRY, t).standard_normal((self.wl.F, self.wl.d))
                       for t in frames]) if frames else np.zeros((0, self.wl.F, self.wl.d))
         q = self._rotate(q, rope_t)

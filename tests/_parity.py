@@ -169,3 +169,109 @@ def replay_update(before: GpuBank, after: GpuBank, candK, candV, cand_tok, D_gpu
         np.testing.assert_allclose(after.rho[h, :hb.n], rho_new, rtol=rtol_rho, atol=1e-6)
         np.testing.assert_allclose(hb.rho0[is_new], rho_new[is_new], rtol=rtol_rho, atol=1e-6)
     return rep
+
+
+def sampled_update(before: GpuBank, after: GpuBank, candK, candV, cand_tok, D_gpu, delta_gpu, order_gpu,
+                   t_gpu, rhoP_gpu, kstar_gpu, n_mand_gpu, n_ev_gpu, prm: od.Params, heads: List[int],
+                   nsample: int = 48, full_order_heads=(), seed: int = 0, rtol=2e-5) -> Report:
+    """Full-size check: every integer decision is verified exactly from the
+    GPU's own outputs (order sortedness, k* from the crossing times, eviction
+    structure, bank contents and K/V pairing); floating-point stages are
+    compared with the oracle on sampled rows (and the full order on
+    ``full_order_heads``)."""
+    rng = np.random.default_rng(seed)
+    N = cand_tok.shape[0]
+    kmax = min(N, prm.M)
+    tok = cand_tok.astype(np.int64)
+    k = int(kstar_gpu)
+    rep = Report(kstar=k)
+    tl, ns = [], []
+    for h in heads:
+        n = int(before.count[h])
+        bK = before.K[h, :n]
+        pi = order_gpu[h].astype(np.int64)
+        # order: a permutation, non-decreasing in the GPU's delta, ties by token
+        assert np.array_equal(np.sort(pi), np.arange(N))
+        dg = delta_gpu[h][pi]
+        assert np.all(np.diff(dg) >= 0), "GPU order not sorted by its own delta"
+        eq = dg[1:] == dg[:-1]
+        assert np.all(tok[pi][1:][eq] > tok[pi][:-1][eq])
+        # disturbance on sampled candidates; delta = D / mean(D)
+        cs = rng.choice(N, size=min(nsample, N), replace=False)
+        Dref = od.phi_rowsum(np.asarray(candK[h][cs], np.float64), bK, prm)
+        np.testing.assert_allclose(D_gpu[h][cs], Dref, rtol=rtol, atol=1e-6)
+        mean = np.mean(D_gpu[h].astype(np.float64))
+        if n > 0 and mean > 0:
+            np.testing.assert_allclose(delta_gpu[h], D_gpu[h] / mean, rtol=1e-5)
+        if h in full_order_heads:
+            Dfull, deltafull = od.disturbance(bK, candK[h], prm)
+            np.testing.assert_allclose(D_gpu[h], Dfull, rtol=rtol, atol=1e-6)
+            rep.order_near_ties += check_order(pi, deltafull, tok)
+        # crossing times on sampled bank rows, on the GPU's order
+        rows = rng.choice(n, size=min(nsample, n), replace=False) if n else np.zeros(0, np.int64)
+        tg = t_gpu[h, :n].astype(np.int64)
+        if rows.size:
+            rho_rows = od.phi_rowsum(bK[rows], bK, prm) - od.phi(np.zeros(1), prm)[0]
+            np.testing.assert_allclose(before.rho[h, rows], rho_rows, rtol=1e-4, atol=1e-6)
+            csorted = np.asarray(candK[h], np.float64)[pi[:kmax]]
+            rep.crossing_near_ties += check_crossings(tg[rows], bK[rows], rho_rows, before.rho0[h, rows], csorted, prm)
+            # projected density at k* on sampled rows that did not cross
+            live = rows[tg[rows] > k] if k > 0 else rows
+            if live.size:
+                pr = od.projected_density(bK[live], od.phi_rowsum(bK[live], bK, prm) - od.phi(np.zeros(1), prm)[0],
+                                          csorted, k, prm)
+                np.testing.assert_allclose(rhoP_gpu[h, live], pr, rtol=1e-4, atol=1e-6)
+        tl.append(tg)
+        ns.append(n)
+    ks_ref, _ = od.feasible_prefix(tl, ns, prm.M, kmax)
+    assert ks_ref == k, f"k* {k} != prefix {ks_ref} on the GPU crossing times"
+    for h, tg in zip(heads, tl):
+        n = int(before.count[h])
+        e = max(0, n + k - prm.M) if k > 0 else 0
+        assert int(n_ev_gpu[h]) == e
+        mand = (tg <= k) if k > 0 else np.zeros(n, bool)
+        assert int(n_mand_gpu[h]) == int(mand.sum())
+        new_n = int(after.count[h])
+        assert new_n == n - e + k
+        pi = order_gpu[h].astype(np.int64)
+        new_toks = after.tok[h, :new_n]
+        assert len(set(new_toks.tolist())) == new_n, "duplicate token in bank"
+        old = before.tok[h, :n]
+        keep = np.isin(old, new_toks)
+        ev = ~keep
+        assert int(ev.sum()) == e and np.all(ev[mand])
+        # completion = densest non-crossed states on the GPU's projected density (ties: lower token)
+        rp = rhoP_gpu[h, :n].astype(np.float64)
+        rest_ev = ev & ~mand
+        rest_kp = keep & ~mand
+        if rest_ev.any() and rest_kp.any():
+            lo_i = np.lexsort((old[rest_ev], -rp[rest_ev]))[-1]
+            worst_ev = (rp[rest_ev][lo_i], old[rest_ev][lo_i])
+            hi_i = np.lexsort((old[rest_kp], -rp[rest_kp]))[0]
+            best_kp = (rp[rest_kp][hi_i], old[rest_kp][hi_i])
+            assert (worst_ev[0] > best_kp[0]) or (worst_ev[0] == best_kp[0] and worst_ev[1] < best_kp[1]), \
+                "eviction completion is not the densest set"
+        adm = tok[pi[:k]]
+        assert set(adm.tolist()) | set(old[keep].tolist()) == set(new_toks.tolist())
+        # exact K/V pairing of every live row
+        cpos = {int(t): i for i, t in enumerate(tok.tolist())}
+        opos = {int(t): i for i, t in enumerate(old.tolist())}
+        for i, t in enumerate(new_toks.tolist()):
+            if t in opos:
+                j = opos[t]
+                assert np.array_equal(after.K[h, i], before.K[h, j]) and np.array_equal(after.V[h, i], before.V[h, j])
+                assert after.rho0[h, i] == before.rho0[h, j]
+            else:
+                j = cpos[t]
+                assert np.array_equal(after.K[h, i], np.asarray(candK[h][j], np.float64))
+                assert np.array_equal(after.V[h, i], np.asarray(candV[h][j], np.float64))
+        # densities of sampled rows of the new bank
+        nK = after.K[h, :new_n]
+        rows = rng.choice(new_n, size=min(nsample, new_n), replace=False)
+        rd = od.phi_rowsum(nK[rows], nK, prm) - od.phi(np.zeros(1), prm)[0]
+        np.testing.assert_allclose(after.rho[h, rows], rd, rtol=1e-4, atol=1e-6)
+        isnew = ~np.isin(new_toks[rows], old)
+        np.testing.assert_allclose(after.rho0[h, rows][isnew], rd[isnew], rtol=1e-4, atol=1e-6)
+        rep.admitted.append(k)
+        rep.evicted.append(e)
+    return rep
