@@ -106,6 +106,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
     }
   }
 
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): query fragments resident before the loop
   f32x4_t o[NDB][2];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -116,7 +117,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
 
   // staging registers and cursors
   const bool vthr = tid < 16 * CPR;
-  const int kg = tid / CPR, dc = tid % CPR;          // V: keys 4kg..4kg+3, d 8dc..8dc+7
+  // V: thread covers keys 4kg..4kg+3 and d 8dc..8dc+7; consecutive lanes take
+  // consecutive key groups so the transposed 8-byte stores of 16 lanes fill
+  // one 128-byte V^T row segment (no bank conflicts)
+  const int kg = tid % 16, dc = tid / 16;
   u32x4_t rk[KPASS], rv[4];
   SegCursor ck[KPASS], cv[4];
   if (nseg > 0) {
@@ -126,20 +130,21 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
     for (int i = 0; i < 4; ++i) cv[i].init(s_pre, s_v);
   }
 
+  // rows past the end of the KV re-read the last row: their scores are
+  // masked to -inf and their (finite) values get weight 0, so the loads need
+  // no branches
   auto fetch = [&](int kbase) {
 #pragma unroll
     for (int i = 0; i < KPASS; ++i) {
       const int r = tid / CPR + (256 / CPR) * i;
-      const int j = kbase + r;
-      if (j < Lkv) rk[i] = gload16(ck[i].row(s_pre, s_k, nseg, j, D) + (tid % CPR) * 8);
-      else rk[i] = u32x4_t{0u, 0u, 0u, 0u};
+      const int j = min(kbase + r, Lkv - 1);
+      rk[i] = gload16(ck[i].row(s_pre, s_k, nseg, j, D) + (tid % CPR) * 8);
     }
     if (vthr) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = kbase + 4 * kg + i;
-        if (j < Lkv) rv[i] = gload16(cv[i].row(s_pre, s_v, nseg, j, D) + dc * 8);
-        else rv[i] = u32x4_t{0u, 0u, 0u, 0u};
+        const int j = min(kbase + 4 * kg + i, Lkv - 1);
+        rv[i] = gload16(cv[i].row(s_pre, s_v, nseg, j, D) + dc * 8);
       }
     }
   };

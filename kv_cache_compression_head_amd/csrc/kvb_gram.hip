@@ -107,21 +107,27 @@ struct TileLoader {
   static_assert(TR <= 256, "aug rows");
   u32x4_t reg[PASSES];
   u32x4_t areg;
+  int vi[PASSES];
+  int va;
 
-  // v_of(r): virtual row index of tile row r, or -1 (zero fill)
+  // step 1: virtual row indices of the rows this thread stages (v_of(r) is the
+  // index of tile row r or -1 for zero fill); done one tile ahead so that
+  // index-list loads never serialise with the key loads
   template <typename F>
-  KVB_DEV void load(const HeadKeys<E, D>& hk, F v_of) {
+  KVB_DEV void index(F v_of) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) vi[i] = v_of(t / CPR + i * RPP);
+    va = t < TR ? v_of(t) : -1;
+  }
+  // step 2: issue the 16-byte key and augmentation loads
+  KVB_DEV void load(const HeadKeys<E, D>& hk) {
     const int t = threadIdx.x;
     const int c = t % CPR;
 #pragma unroll
-    for (int i = 0; i < PASSES; ++i) {
-      const int v = v_of(t / CPR + i * RPP);
-      reg[i] = v >= 0 ? gload16(hk.row(v) + c * EPC) : u32x4_t{0u, 0u, 0u, 0u};
-    }
-    if (t < TR) {
-      const int v = v_of(t);
-      areg = v >= 0 ? gload16(hk.aug(v)) : u32x4_t{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < PASSES; ++i)
+      reg[i] = vi[i] >= 0 ? gload16(hk.row(vi[i]) + c * EPC) : u32x4_t{0u, 0u, 0u, 0u};
+    if (t < TR) areg = va >= 0 ? gload16(hk.aug(va)) : u32x4_t{0u, 0u, 0u, 0u};
   }
   KVB_DEV void store(E* lds) const {
     const int t = threadIdx.x;
@@ -217,10 +223,15 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows
       return hk.ok(v) ? v : -1;
     };
   };
+  // all row fragments and norms in registers before the loop: the loop's
+  // waits then only concern the tile prefetches
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   if (t0 < t1) {
-    ld.load(hk, vof(t0));
+    ld.index(vof(t0));
+    ld.load(hk);
     ld.store(sY[0]);
-    if (threadIdx.x < TC) sYv[0][threadIdx.x] = vof(t0)(threadIdx.x);
+    if (threadIdx.x < TC) sYv[0][threadIdx.x] = ld.va;
+    if (t0 + 1 < t1) ld.index(vof(t0 + 1));
   }
   __syncthreads();
   for (int tile = t0; tile < t1; ++tile) {
@@ -228,8 +239,9 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows
     const bool more = tile + 1 < t1;
     int nv = -1;
     if (more) {
-      ld.load(hk, vof(tile + 1));
-      if (threadIdx.x < TC) nv = vof(tile + 1)(threadIdx.x);
+      ld.load(hk);
+      nv = ld.va;
+      if (tile + 2 < t1) ld.index(vof(tile + 2));
     }
 #pragma unroll
     for (int sub = 0; sub < TC / 32; ++sub) {
@@ -456,15 +468,21 @@ __global__ __launch_bounds__(256) void scan_kernel(KeySpace<E> ks, const float* 
       return c < (unsigned)ks.N ? M + (int)c : -1;
     };
   };
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): bank fragments resident
   if (st_begin < st_end) {
-    ld.load(hk, vof(st_begin));
+    ld.index(vof(st_begin));
+    ld.load(hk);
     ld.store(sC[0]);
+    if (st_begin + 1 < st_end) ld.index(vof(st_begin + 1));
   }
   __syncthreads();
   for (int stg = st_begin; stg < st_end; ++stg) {
     const int cur = (stg - st_begin) & 1;
     const bool more = stg + 1 < st_end;
-    if (more) ld.load(hk, vof(stg + 1));
+    if (more) {
+      ld.load(hk);
+      if (stg + 2 < st_end) ld.index(vof(stg + 2));
+    }
     const bool wave_busy = __any(!done);
     if (wave_busy) {
 #pragma unroll
