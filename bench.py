@@ -32,6 +32,14 @@ if ROOT not in sys.path:
 METRIC = "ms/chunk/layer + attention TFLOP/s (% of bf16 peak) at 480P and 1080P, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+# fp32 VALU lane-operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+PEAK_VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+# VALU issue slots per Soft-Riesz pair at p = 2 (fma, max, reciprocal at half
+# rate = 2 slots, accumulate)
+VALU_SLOTS_PER_PAIR = 5.0
+ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_kernel_480p_hbm_traffic.md")
+ATTN_SOURCES = ("kv_cache_compression_head_amd/csrc/kvb_attention.hip",
+                "kv_cache_compression_head_amd/csrc/kvb_common.hpp")
 
 
 def log(msg):
@@ -94,6 +102,45 @@ def one_step(lc, snap, inp, lay, Q, O, ev=None):
         ev[4].record()
 
 
+def attention_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_attention_traffic(config: str):
+    """HBM bytes per attention launch from the committed FETCH_SIZE /
+    WRITE_SIZE profile, or None when that profile was taken on other kernel
+    sources (or another workload)."""
+    try:
+        with open(ATTN_TRAFFIC_FILE) as fh:
+            kv = dict(l.split(":", 1) for l in fh.read().splitlines() if l.startswith("record."))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("record.workload") != config or kv.get("record.kernel_sources_sha256") != attention_source_digest():
+        return None
+    return int(kv["record.traffic_bytes_per_launch"])
+
+
+def copy_calibration(mib: int, copies: int):
+    """A plain device-to-device copy of known size, the yardstick for the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(copies):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                      "copies": copies}), flush=True)
+
+
 def cpu_baseline(name: str, seed: int = 0, heads=(0,)):
     """The fp64 oracle on a bounded sample: the same layer-chunk for a subset
     of heads (prefix computed over that subset), extrapolated to all heads."""
@@ -148,6 +195,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="480p", choices=["480p", "1080p"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter yardstick) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no "
@@ -155,6 +204,9 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 4)
+        return
     import kv_cache_compression_head_amd as kb
     kb.load_library()
     wl, lc, snap, inp, lay, Q, O = setup(args.config)
@@ -187,7 +239,22 @@ def main():
     attn_bytes = sum(2 * wl.Lq * wl.d * 2 + 2 * l * wl.d * 2 for l in lkv)
     roof = {"kernel": "attn_bf16_kernel (chunk_attention)", "bound": "mfma", "achieved": round(attn_tflops, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None, "algorithmic_flop_per_launch": attn_flop, "algorithmic_bytes_per_launch": attn_bytes}
+            "traffic": recorded_attention_traffic(args.config), "algorithmic_flop_per_launch": attn_flop,
+            "algorithmic_bytes_per_launch": attn_bytes}
+    # Soft-Riesz pair counts of the density stages (the algorithmic work; the
+    # crossing scan's figure is its upper bound n * min(N, M))
+    n0 = int(snap.count.min().cpu())
+    N = inp["candK"].shape[1]
+    ev = lc.out.n_evicted.cpu().tolist()
+    score_pairs = wl.H * n0 * N
+    upd_pairs = sum(n0 * min(N, wl.M) + (n0 - e) * e + kstar * min(e, n0 - e) + kstar * (kstar - 1) // 2 for e in ev)
+
+    def pair_roof(pairs, ms):
+        rate = pairs / (ms * 1e-3)
+        return {"pairs": pairs, "pairs_per_s": rate, "mfma_equiv_tflops": round(rate * 2 * wl.d / 1e12, 2),
+                "frac_bf16_peak": round(rate * 2 * wl.d / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "frac_valu_bound": round(rate * VALU_SLOTS_PER_PAIR / PEAK_VALU_LANE_OPS, 4)}
+    density_roof = {"score": pair_roof(score_pairs, avg["score"]), "update": pair_roof(upd_pairs, avg["update"])}
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, 1 of 12 heads)")
@@ -205,7 +272,7 @@ def main():
                                f"tau={wl.tau}, sigma={wl.sigma}, p={wl.p}"},
         "stages_ms": {k: round(v, 4) for k, v in avg.items()},
         "attention_tflops": round(attn_tflops, 2), "attention_frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-        "k_star": kstar, "roofline": roof, "cpu_baseline": cpu,
+        "k_star": kstar, "roofline": roof, "density_stages": density_roof, "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
 
