@@ -176,12 +176,26 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
   return KVB_OK;
 }
 
+// Column splits for a gram launch.  Work-groups cost the same (one column
+// range each), so the time is about rounds * columns-per-work-group, where a
+// round is one work-group per slot (two per compute unit at the kernel's
+// register use); pick the split count (up to MAX_SPLITS) that minimises it.
 int choose_splits(int H, int rows, int ncols) {
-  const int wgs = H * ((rows + 255) / 256);
-  const int tiles = (ncols + 63) / 64;
-  int s = 1;
-  while (s < MAX_SPLITS && wgs * s < 1024 && s * 2 <= tiles) s *= 2;
-  return s;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  const int64_t slots = 2LL * cus;
+  const int64_t wgs = (int64_t)H * ((rows + 255) / 256);
+  const int64_t tiles = (ncols + 63) / 64;
+  int best = 1;
+  int64_t best_cost = INT64_MAX;
+  for (int s = 1; s <= MAX_SPLITS && s <= tiles; ++s) {
+    const int64_t cost = ((wgs * s + slots - 1) / slots) * ((tiles + s - 1) / s);
+    if (cost < best_cost) { best_cost = cost; best = s; }
+  }
+  return best;
 }
 
 // one gram launch over rows_ub rows and at most cols_ub columns, with the

@@ -18,22 +18,86 @@
 
 namespace kvb {
 
-// LDS row layout (elements): [0, D) key, [D, D+AUGE) augmentation, zero pad.
+// Norm augmentation.  Every key row carries a 16-byte augmentation row
+// written by norms_kernel:
+//   bf16 keys: (h, m, l, -1/2, -1/2, -1/2, 0, 0), |k|^2 = h + m + l exactly
+//              (three bf16 parts), used as the y side of one extra k-step;
+//   fp32 keys: (|k|^2, -1/2, 0, 0).
+// The x side of that k-step is built in registers from the x row's own
+// augmentation: (-1/2, -1/2, -1/2, xh, xm, xl, 0, 0) (bf16) or -1/2 / |x|^2
+// (fp32, one element per k-slice), so the MFMA accumulates
+//   R = x.y - |x|^2/2 - |y|^2/2 = -|x - y|^2 / 2.
 template <typename E> struct Aug;
 template <> struct Aug<uint16_t> {
-  static constexpr int AUGE = 8;                    // 16 bytes
-  template <int D> static constexpr int ldr() { return D + 24; }   // 304 B rows at D=128
-  KVB_DEV static s16x8_t xfrag(int lane) {          // (-1/2, -1/2, -1/2, 0, ...) for k-slice 0
-    const short m = (short)0xBF00;                  // bf16(-0.5)
-    return (lane >> 5) == 0 ? s16x8_t{m, m, m, 0, 0, 0, 0, 0} : s16x8_t{};
+  KVB_DEV static s16x8_t xfrag(u32x4_t a, int lane) {
+    if (lane >> 5) return s16x8_t{};
+    const u32x4_t r = {0xBF00BF00u, 0xBF00u | (a[0] << 16), (a[0] >> 16) | (a[1] << 16), 0u};
+    return __builtin_bit_cast(s16x8_t, r);
   }
-  KVB_DEV static int aug_off(int lane) { return (lane >> 5) * 8; }
+  // y side: the stored row (the upper k-slice pairs with zeros on the x side)
+  KVB_DEV static s16x8_t yfrag(const u32x4_t& a, int) { return __builtin_bit_cast(s16x8_t, a); }
 };
 template <> struct Aug<float> {
-  static constexpr int AUGE = 4;
-  template <int D> static constexpr int ldr() { return D + 4; }
-  KVB_DEV static float xfrag(int lane) { return (lane >> 5) == 0 ? -0.5f : 0.0f; }
-  KVB_DEV static int aug_off(int lane) { return lane >> 5; }
+  KVB_DEV static float xfrag(u32x4_t a, int lane) { return (lane >> 5) ? __uint_as_float(a[0]) : -0.5f; }
+  KVB_DEV static float yfrag(const u32x4_t& a, int lane) { return __uint_as_float((lane >> 5) ? a[1] : a[0]); }
+};
+
+// LDS key tiles: rows of D elements with no padding; the 16-byte chunks of
+// row r are XOR-swizzled so that the 16 rows read by one quarter-wave hit 16
+// different 16-byte bank groups.
+template <typename E, int D> struct Tile {
+  static constexpr int EPC = 16 / (int)sizeof(E);   // elements per chunk
+  static constexpr int CPR = D / EPC;               // chunks per row
+  KVB_DEV static int swz(int r) {
+    if constexpr (sizeof(E) == 2) {
+      if constexpr (CPR == 16) return r & 15;
+      else return (r >> 1) & 7;
+    } else {
+      return 0;
+    }
+  }
+  // element offset of element e of row r (e is a fragment start)
+  KVB_DEV static int at(int r, int e) { return r * D + (((e / EPC) ^ swz(r)) * EPC) + e % EPC; }
+};
+
+// 16-byte global -> LDS copy that bypasses registers: lane l of the wave
+// writes 16 bytes at lds + 16 l
+KVB_DEV void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Stages TC key rows (gathered by virtual index) and their augmentation rows
+// into LDS with direct-to-LDS loads.  256 threads; thread (w, lane) copies
+// chunks (w * PASSW + i) * 64 + lane; wave 0 copies the augmentation rows.
+// Absent rows (index -1) copy row `fb` (any existing row) and are masked by
+// the caller through the stored index.
+template <typename E, int D, int TC>
+struct DmaTile {
+  using T = Tile<E, D>;
+  static constexpr int PASSW = TC * T::CPR / 256;
+  static_assert((TC * T::CPR) % 256 == 0 && TC == 64, "tile shape");
+  int vi[PASSW];
+  int va;
+  template <typename F>
+  KVB_DEV void index(F v_of) {
+    const int lane = lane_id(), w = wave_id();
+#pragma unroll
+    for (int i = 0; i < PASSW; ++i) vi[i] = v_of(((w * PASSW + i) * 64 + lane) / T::CPR);
+    va = w == 0 ? v_of(lane) : -1;
+  }
+  KVB_DEV void issue(const HeadKeys<E, D>& hk, E* sY, u32x4_t* sA, int fb) const {
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());
+#pragma unroll
+    for (int i = 0; i < PASSW; ++i) {
+      const int s = (w * PASSW + i) * 64 + lane;
+      const int r = s / T::CPR, c = s % T::CPR;
+      const int v = vi[i] >= 0 ? vi[i] : fb;
+      dma16(hk.row(v) + (c ^ T::swz(r)) * T::EPC, sY + (w * PASSW + i) * 64 * T::EPC);
+    }
+    if (w == 0) dma16(hk.aug(va >= 0 ? va : fb), sA);
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -67,9 +131,11 @@ __global__ __launch_bounds__(256) void norms_kernel(const E* __restrict__ keys, 
       const uint16_t mid = f32_to_bf16(r1);
       const uint16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
       a[0] = (uint32_t)hi | ((uint32_t)mid << 16);
-      a[1] = (uint32_t)lo;
+      a[1] = (uint32_t)lo | (0xBF00u << 16);      // bf16(-1/2)
+      a[2] = 0xBF00BF00u;
     } else {
       a[0] = __float_as_uint(s);
+      a[1] = __float_as_uint(-0.5f);
     }
     aug[row] = a;
   }
@@ -94,60 +160,6 @@ hipError_t launch_norms(const void* keys, int et, int H, int rows, int d, float 
 }
 
 // ---------------------------------------------------------------------------
-// tile staging: TR key rows (+ their augmentation) gathered by virtual index
-// into LDS rows of LDR elements; 256 threads, 16-byte chunks.
-// ---------------------------------------------------------------------------
-template <typename E, int D, int TR, int LDR>
-struct TileLoader {
-  static constexpr int EPC = 16 / sizeof(E);     // elements per chunk
-  static constexpr int CPR = D / EPC;            // key chunks per row
-  static constexpr int RPP = 256 / CPR;          // rows per pass
-  static constexpr int PASSES = TR / RPP;
-  static_assert(TR % RPP == 0, "tile rows");
-  static_assert(TR <= 256, "aug rows");
-  u32x4_t reg[PASSES];
-  u32x4_t areg;
-  int vi[PASSES];
-  int va;
-
-  // step 1: virtual row indices of the rows this thread stages (v_of(r) is the
-  // index of tile row r or -1 for zero fill); done one tile ahead so that
-  // index-list loads never serialise with the key loads
-  template <typename F>
-  KVB_DEV void index(F v_of) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < PASSES; ++i) vi[i] = v_of(t / CPR + i * RPP);
-    va = t < TR ? v_of(t) : -1;
-  }
-  // step 2: issue the 16-byte key and augmentation loads
-  KVB_DEV void load(const HeadKeys<E, D>& hk) {
-    const int t = threadIdx.x;
-    const int c = t % CPR;
-#pragma unroll
-    for (int i = 0; i < PASSES; ++i)
-      reg[i] = vi[i] >= 0 ? gload16(hk.row(vi[i]) + c * EPC) : u32x4_t{0u, 0u, 0u, 0u};
-    if (t < TR) areg = va >= 0 ? gload16(hk.aug(va)) : u32x4_t{0u, 0u, 0u, 0u};
-  }
-  KVB_DEV void store(E* lds) const {
-    const int t = threadIdx.x;
-    const int c = t % CPR;
-#pragma unroll
-    for (int i = 0; i < PASSES; ++i)
-      *reinterpret_cast<u32x4_t*>(lds + (t / CPR + i * RPP) * LDR + c * EPC) = reg[i];
-    if (t < TR) *reinterpret_cast<u32x4_t*>(lds + t * LDR + D) = areg;
-  }
-  // zero the padding after the augmentation (read by the upper k-slice lanes)
-  KVB_DEV static void zero_pad(E* lds) {
-    constexpr int padE = LDR - D - 16 / (int)sizeof(E);
-    if constexpr (padE > 0) {
-      for (int r = threadIdx.x; r < TR; r += 256)
-        for (int j = 0; j < padE; ++j) lds[r * LDR + D + 16 / (int)sizeof(E) + j] = E{};
-    }
-  }
-};
-
-// ---------------------------------------------------------------------------
 // gram row sums: out[i] = sum_{j in cols} phi(row_i, col_j).
 // Work-group: 4 waves x 64 rows (two 32-row blocks per wave, A operand in
 // registers); column tiles of 64 (two 32-column subtiles, B operand) staged
@@ -161,10 +173,11 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows
                                                    uint64_t active) {
   using O = Ops<E>;
   using A = Aug<E>;
-  constexpr int LDR = A::template ldr<D>();
+  using T = Tile<E, D>;
   constexpr int TC = 64;
   constexpr int NK = D / O::K32;
-  __shared__ __attribute__((aligned(16))) E sY[2][TC * LDR];
+  __shared__ __attribute__((aligned(16))) E sY[2][TC * D];
+  __shared__ __attribute__((aligned(16))) u32x4_t sA[2][TC];
   __shared__ int sYv[2][TC];
 
   // XCD-aware order: logical items (head, split, row tile), head-major
@@ -182,40 +195,31 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows
   const int per = (ntiles + (int)gridDim.z - 1) / (int)gridDim.z;
   const int t0 = zs * per;
   const int t1 = min(ntiles, t0 + per);
+  const int fb = ks.M > 0 ? 0 : ks.M;   // an existing row: bank slot 0, else candidate 0
 
   const int lane = lane_id(), w = wave_id();
   const int hh = lane >> 5, nn = lane & 31;
   const int wrow = r0 + w * 64;
 
   typename O::frag xf[2][NK];
-  float xs[2][16];
+  typename O::frag xa[2];
 #pragma unroll
   for (int xb = 0; xb < 2; ++xb) {
     const int r = wrow + 32 * xb + nn;
     int v = r < nrows ? vlist_at(rows, h, r) : -1;
     v = hk.ok(v) ? v : -1;
-    const E* xp = v >= 0 ? hk.row(v) : nullptr;
+    const E* xp = hk.row(v >= 0 ? v : fb);
 #pragma unroll
     for (int k = 0; k < NK; ++k) xf[xb][k] = v >= 0 ? O::load(xp + O::off32(k, lane)) : typename O::frag{};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = 8 * (i >> 2) + 4 * hh + (i & 3);
-      const int rr = wrow + 32 * xb + m;
-      int vm = rr < nrows ? vlist_at(rows, h, rr) : -1;
-      vm = hk.ok(vm) ? vm : -1;
-      xs[xb][i] = (vm >= 0 ? ks.nrm(h, vm) : 0.0f) + pc.eps;
-    }
+    xa[xb] = v >= 0 ? A::xfrag(gload16(hk.aug(v)), lane) : typename O::frag{};
   }
-  const typename O::frag xa = A::xfrag(lane);
   float acc[2][16];
 #pragma unroll
   for (int xb = 0; xb < 2; ++xb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[xb][i] = 0.0f;
 
-  TileLoader<E, D, TC, LDR> ld;
-  TileLoader<E, D, TC, LDR>::zero_pad(sY[0]);
-  TileLoader<E, D, TC, LDR>::zero_pad(sY[1]);
+  DmaTile<E, D, TC> ld;
   auto vof = [&](int tile) {
     return [&, tile](int r) -> int {
       const int c = tile * TC + r;
@@ -223,69 +227,66 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows
       return hk.ok(v) ? v : -1;
     };
   };
-  // all row fragments and norms in registers before the loop: the loop's
-  // waits then only concern the tile prefetches
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): row fragments resident
   if (t0 < t1) {
     ld.index(vof(t0));
-    ld.load(hk);
-    ld.store(sY[0]);
+    ld.issue(hk, sY[0], sA[0], fb);
     if (threadIdx.x < TC) sYv[0][threadIdx.x] = ld.va;
     if (t0 + 1 < t1) ld.index(vof(t0 + 1));
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   for (int tile = t0; tile < t1; ++tile) {
     const int cur = (tile - t0) & 1;
-    const bool more = tile + 1 < t1;
-    int nv = -1;
-    if (more) {
-      ld.load(hk);
-      nv = ld.va;
+    if (tile + 1 < t1) {
+      // buffer cur^1 was last read before the previous barrier
+      ld.issue(hk, sY[cur ^ 1], sA[cur ^ 1], fb);
+      if (threadIdx.x < TC) sYv[cur ^ 1][threadIdx.x] = ld.va;
       if (tile + 2 < t1) ld.index(vof(tile + 2));
     }
 #pragma unroll
     for (int sub = 0; sub < TC / 32; ++sub) {
-      const E* yp = sY[cur] + (32 * sub + nn) * LDR;
-      const int yv = sYv[cur][32 * sub + nn];
+      const int rr = 32 * sub + nn;
+      const int yv = sYv[cur][rr];
+      const int cpos = tile * TC + 32 * sub;       // list position of this subtile's column 0
       f32x16_t cc[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) { cc[0][i] = 0.0f; cc[1][i] = 0.0f; }
 #pragma unroll
       for (int k = 0; k < NK; ++k) {
-        const typename O::frag yk = O::load(yp + O::off32(k, lane));
+        const typename O::frag yk = O::load(sY[cur] + T::at(rr, O::off32(k, lane)));
         cc[0] = O::mma32(xf[0][k], yk, cc[0]);
         cc[1] = O::mma32(xf[1][k], yk, cc[1]);
       }
       {
-        const typename O::frag ya = O::load(yp + D + A::aug_off(lane));
-        cc[0] = O::mma32(xa, ya, cc[0]);
-        cc[1] = O::mma32(xa, ya, cc[1]);
+        const typename O::frag ya = A::yfrag(sA[cur][rr], lane);
+        cc[0] = O::mma32(xa[0], ya, cc[0]);
+        cc[1] = O::mma32(xa[1], ya, cc[1]);
       }
       // an absent column clamps t to +inf, where every phi mode but p = 0 is 0
       const float lo = opaque(yv >= 0 ? pc.eps : __builtin_inff());
 #pragma unroll
       for (int xb = 0; xb < 2; ++xb) {
         const f32x16_t c = cc[xb];
+        // self-exclusion (rows and columns are the same list): a pair is its
+        // own partner exactly when the list positions coincide, which needs
+        // the subtile's column range to meet the block's row range
+        const int rpos = wrow + 32 * xb;
+        const bool diag = SELF && cpos == rpos;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float t = __builtin_fmaf(c[i], pc.c2, xs[xb][i]);
+          float t = __builtin_fmaf(c[i], pc.c2, pc.eps);
           t = fmaxf(t, lo);
           float f = phi_of_t<MODE>(t, pc.neg_half_p);
           if constexpr (MODE == PHI_P0) f = yv >= 0 ? f : 0.0f;
           if constexpr (SELF) {
-            // self-exclusion: rows and columns are the same list, so a pair is
-            // its own partner exactly when the list positions coincide
-            const bool self = (tile * TC + 32 * sub + nn) == (wrow + 32 * xb + 8 * (i >> 2) + 4 * hh + (i & 3));
-            f = self ? 0.0f : f;
+            if (diag) f = (nn == 8 * (i >> 2) + 4 * hh + (i & 3)) ? 0.0f : f;
           }
           acc[xb][i] += f;
         }
       }
     }
-    if (more) {
-      ld.store(sY[cur ^ 1]);
-      if (threadIdx.x < TC) sYv[cur ^ 1][threadIdx.x] = nv;
-    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // next tile resident in LDS
     __syncthreads();
   }
   // sum over the 32 columns held by the half-wave
@@ -391,7 +392,7 @@ hipError_t launch_sum_splits(const float* src, int64_t src_hstride, int64_t spli
 // sum pass:  rhoP_b = S_b(k*) starting from the nearest checkpoint.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int MODE, bool SUM>
-__global__ __launch_bounds__(256) void scan_kernel(KeySpace<E> ks, const float* __restrict__ rho,
+__global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const float* __restrict__ rho,
                                                    const float* __restrict__ rho0, const int32_t* __restrict__ count,
                                                    const int32_t* __restrict__ order, uint64_t active,
                                                    int kmax, float tau, int cps, int ncp, float* __restrict__ cp,
@@ -399,10 +400,11 @@ __global__ __launch_bounds__(256) void scan_kernel(KeySpace<E> ks, const float* 
                                                    float* __restrict__ rhoP, PhiConst pc) {
   using O = Ops<E>;
   using A = Aug<E>;
-  constexpr int LDR = A::template ldr<D>();
+  using T = Tile<E, D>;
   constexpr int TC = 64;               // candidates per LDS stage (two subtiles)
   constexpr int NK = D / O::K32;
-  __shared__ __attribute__((aligned(16))) E sC[2][TC * LDR];
+  __shared__ __attribute__((aligned(16))) E sC[2][TC * D];
+  __shared__ __attribute__((aligned(16))) u32x4_t sA[2][TC];
 
   const int R = gridDim.x;
   const int lin = xcd_remap(blockIdx.x + R * blockIdx.y, R * gridDim.y);
@@ -449,18 +451,16 @@ __global__ __launch_bounds__(256) void scan_kernel(KeySpace<E> ks, const float* 
   }
 
   typename O::frag bf[NK];
+  typename O::frag ba;
   {
     const E* bp = ks.bankK + hb * D;
 #pragma unroll
     for (int k = 0; k < NK; ++k) bf[k] = valid ? O::load(bp + O::off32(k, lane)) : typename O::frag{};
+    ba = valid ? A::xfrag(gload16(ks.bankA + hb), lane) : typename O::frag{};
   }
-  const typename O::frag ba = A::xfrag(lane);
-  const float xs = valid ? ks.bankN[hb] + pc.eps : pc.eps;
 
   const int st_begin = sub_begin / 2, st_end = (sub_end + 1) / 2;
-  TileLoader<E, D, TC, LDR> ld;
-  TileLoader<E, D, TC, LDR>::zero_pad(sC[0]);
-  TileLoader<E, D, TC, LDR>::zero_pad(sC[1]);
+  DmaTile<E, D, TC> ld;
   auto vof = [&](int stage) {
     return [&, stage](int r) -> int {
       const int j = stage * TC + r;
@@ -468,19 +468,23 @@ __global__ __launch_bounds__(256) void scan_kernel(KeySpace<E> ks, const float* 
       return c < (unsigned)ks.N ? M + (int)c : -1;
     };
   };
+  // candidates are always present in a stage's used positions; rows past
+  // kmax copy a fallback row and are masked below
+  const int fb = M;                      // candidate 0 (N > 0 whenever kmax > 0)
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): bank fragments resident
   if (st_begin < st_end) {
     ld.index(vof(st_begin));
-    ld.load(hk);
-    ld.store(sC[0]);
+    ld.issue(hk, sC[0], sA[0], fb);
     if (st_begin + 1 < st_end) ld.index(vof(st_begin + 1));
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   for (int stg = st_begin; stg < st_end; ++stg) {
     const int cur = (stg - st_begin) & 1;
     const bool more = stg + 1 < st_end;
     if (more) {
-      ld.load(hk);
+      // buffer cur^1 was last read before the previous barrier
+      ld.issue(hk, sC[cur ^ 1], sA[cur ^ 1], fb);
       if (stg + 2 < st_end) ld.index(vof(stg + 2));
     }
     const bool wave_busy = __any(!done);
@@ -495,15 +499,15 @@ __global__ __launch_bounds__(256) void scan_kernel(KeySpace<E> ks, const float* 
         f32x16_t acc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-        const E* cpp = sC[cur] + (32 * half + (lane & 31)) * LDR;
+        const int cr = 32 * half + (lane & 31);
 #pragma unroll
-        for (int k = 0; k < NK; ++k) acc = O::mma32(O::load(cpp + O::off32(k, lane)), bf[k], acc);
-        acc = O::mma32(O::load(cpp + D + A::aug_off(lane)), ba, acc);
+        for (int k = 0; k < NK; ++k) acc = O::mma32(O::load(sC[cur] + T::at(cr, O::off32(k, lane))), bf[k], acc);
+        acc = O::mma32(A::yfrag(sA[cur][cr], lane), ba, acc);
         float v[16];
         const int pos0 = 32 * sub;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float t = __builtin_fmaf(acc[i], pc.c2, xs);
+          float t = __builtin_fmaf(acc[i], pc.c2, pc.eps);
           t = fmaxf(t, pc.eps);
           v[i] = phi_of_t<MODE>(t, pc.neg_half_p);
         }
@@ -576,7 +580,7 @@ __global__ __launch_bounds__(256) void scan_kernel(KeySpace<E> ks, const float* 
         }
       }
     }
-    if (more) ld.store(sC[cur ^ 1]);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // next stage resident in LDS
     if constexpr (!SUM) {
       if (!__syncthreads_or(!done)) {
         // every row of the work-group has crossed: later checkpoints are
