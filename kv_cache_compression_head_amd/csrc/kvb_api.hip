@@ -100,6 +100,9 @@ PhiConst phi_const(const kvb_params& P) {
   c.c2 = -2.0f * c.inv_s2;
   c.eps = P.p > 0.0f ? P.eps : 0.0f;
   c.neg_half_p = -0.5f * P.p;
+  int e2 = 0;
+  const float s2 = P.sigma * P.sigma;
+  c.direct = (P.p == 2.0f && frexpf(c.inv_s2, &e2) == 0.5f && c.inv_s2 * s2 == 1.0f && c.eps >= 1e-2f) ? 1 : 0;
   return c;
 }
 
@@ -263,8 +266,8 @@ int kvbank_score(const kvb_layer_desc* L, const kvb_bank* bank, const void* cand
     float* nC = at<float>(ws, lo.normC);
     void* aB = at<void>(ws, lo.augB);
     void* aC = at<void>(ws, lo.augC);
-    HIPCHK(launch_norms(bank->K, et, H, M, d, pc.inv_s2, nB, aB, st));
-    HIPCHK(launch_norms(cand_k, et, H, N, d, pc.inv_s2, nC, aC, st));
+    HIPCHK(launch_norms(bank->K, et, H, M, d, pc.inv_s2, et == ET_BF16 && pc.direct, nB, aB, st));
+    HIPCHK(launch_norms(cand_k, et, H, N, d, pc.inv_s2, et == ET_BF16 && pc.direct, nC, aC, st));
     GramLaunch g{};
     g.k = KeysDesc{bank->K, cand_k, nB, nC, aB, aC, M, N, d, H, et};
     g.rows = VList{nullptr, nullptr, 0, 0, 0, M, N, 0};
@@ -372,8 +375,8 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
     float* nC = at<float>(ws, lo.normC);
     void* aB = at<void>(ws, lo.augB);
     void* aC = at<void>(ws, lo.augC);
-    HIPCHK(launch_norms(bank->K, et, H, M, d, pc.inv_s2, nB, aB, st));
-    HIPCHK(launch_norms(cand_k, et, H, N, d, pc.inv_s2, nC, aC, st));
+    HIPCHK(launch_norms(bank->K, et, H, M, d, pc.inv_s2, et == ET_BF16 && pc.direct, nB, aB, st));
+    HIPCHK(launch_norms(cand_k, et, H, N, d, pc.inv_s2, et == ET_BF16 && pc.direct, nC, aC, st));
     const KeysDesc kd{bank->K, cand_k, nB, nC, aB, aC, M, N, d, H, et};
     ScanLaunch s{};
     s.k = kd; s.rho = bank->rho; s.rho0 = bank->rho0; s.count = bank->count; s.order = order;

@@ -86,6 +86,11 @@ struct PhiConst {
   float inv_s2;   // 1 / sigma^2
   float eps;
   float neg_half_p;
+  // "direct" form: sigma^2 is a power of two (so x * -2/sigma^2 and the
+  // scaled norms are exact in bf16 parts) and eps >= 1e-2 (so rounding can
+  // never bring t = eps + d2/sigma^2 near zero): the MFMA then returns t
+  // itself and the clamp is needed only on ragged tiles
+  int32_t direct;
 };
 
 template <int MODE> KVB_DEV float phi_of_t(float t, float neg_half_p) {
@@ -176,6 +181,12 @@ template <typename E, int D> struct HeadKeys {
 
 // value the optimiser cannot see through (keeps a clamp a single max)
 KVB_DEV float opaque(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+// same for an integer: values derived from it are recomputed where used
+// instead of being hoisted out of a loop and kept in registers
+KVB_DEV int opaque_i(int x) {
   asm volatile("" : "+v"(x));
   return x;
 }

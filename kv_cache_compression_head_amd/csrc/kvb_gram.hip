@@ -36,6 +36,32 @@ template <> struct Aug<uint16_t> {
   }
   // y side: the stored row (the upper k-slice pairs with zeros on the x side)
   KVB_DEV static s16x8_t yfrag(const u32x4_t& a, int) { return __builtin_bit_cast(s16x8_t, a); }
+  // direct form: stored rows are (h', m', l', 1, 1, 1, 1, 1) with h' + m' + l'
+  // = |k|^2 / sigma^2; the x side is (1, 1, 1, xh', xm', xl', eh, em) and, in
+  // the upper k-slice, eps's third part against the last 1, so the norm step
+  // adds |y|^2/sigma^2 + |x|^2/sigma^2 + eps exactly
+  KVB_DEV static s16x8_t xfrag_direct(u32x4_t a, int lane, u32x4_t e) {
+    const u32x4_t r = (lane >> 5) ? u32x4_t{0u, 0u, 0u, e[2] << 16}
+                                  : u32x4_t{0x3F803F80u, 0x3F80u | (a[0] << 16), (a[0] >> 16) | (a[1] << 16),
+                                            e[0] | (e[1] << 16)};
+    return __builtin_bit_cast(s16x8_t, r);
+  }
+  // bf16 parts (hi, mid, lo) of eps, exact for any float
+  KVB_DEV static u32x4_t eps_parts(float eps) {
+    const uint16_t hi = f32_to_bf16(eps);
+    const float r1 = eps - bf16_to_f32(hi);
+    const uint16_t mid = f32_to_bf16(r1);
+    const uint16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+    return u32x4_t{hi, mid, lo, 0u};
+  }
+  // x * s for a power of two s: exact in bf16 (keys are far from the
+  // exponent limits)
+  KVB_DEV static s16x8_t scale(s16x8_t x, float sc) {
+    s16x8_t r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (short)f32_to_bf16(bf16_to_f32((uint16_t)x[j]) * sc);
+    return r;
+  }
 };
 template <> struct Aug<float> {
   KVB_DEV static float xfrag(u32x4_t a, int lane) { return (lane >> 5) ? __uint_as_float(a[0]) : -0.5f; }
@@ -69,9 +95,17 @@ KVB_DEV void dma16(const void* g, void* lds) {
 
 // Stages TC key rows (gathered by virtual index) and their augmentation rows
 // into LDS with direct-to-LDS loads.  256 threads; thread (w, lane) copies
-// chunks (w * PASSW + i) * 64 + lane; wave 0 copies the augmentation rows.
-// Absent rows (index -1) copy row `fb` (any existing row) and are masked by
-// the caller through the stored index.
+// chunks (w * PASSW + i) * 64 + lane; wave 0 copies the augmentation rows
+// and records each row's index (-1 when absent) in sV when given.
+//
+// Indices come in two steps so that reading an index list never stalls the
+// copies in flight: index() keeps the raw list entries of a tile (plain
+// loads, nothing computed from them), issue() turns them into row indices
+// one tile later.  raw(c) reads list position c (clamped by the caller);
+// fix(c, raw) returns the virtual row index of position c or -1.  Absent
+// rows copy row `fb` (any existing row).
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+
 template <typename E, int D, int TC>
 struct DmaTile {
   using T = Tile<E, D>;
@@ -79,24 +113,32 @@ struct DmaTile {
   static_assert((TC * T::CPR) % 256 == 0 && TC == 64, "tile shape");
   int vi[PASSW];
   int va;
+  // Per-lane offsets are recomputed from an opaque lane id at each use: kept
+  // live across the loop they would cost registers the MFMA loop needs.
   template <typename F>
-  KVB_DEV void index(F v_of) {
-    const int lane = lane_id(), w = wave_id();
+  KVB_DEV void index(int tile, F raw) {
+    const int lane = opaque_i(lane_id());
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());
 #pragma unroll
-    for (int i = 0; i < PASSW; ++i) vi[i] = v_of(((w * PASSW + i) * 64 + lane) / T::CPR);
-    va = w == 0 ? v_of(lane) : -1;
+    for (int i = 0; i < PASSW; ++i) vi[i] = raw(tile * TC + ((w * PASSW + i) * 64 + lane) / T::CPR);
+    va = w == 0 ? raw(tile * TC + lane) : 0;
   }
-  KVB_DEV void issue(const HeadKeys<E, D>& hk, E* sY, u32x4_t* sA, int fb) const {
-    const int lane = lane_id();
+  template <typename G>
+  KVB_DEV void issue(int tile, G fix, const HeadKeys<E, D>& hk, E* sY, u32x4_t* sA, int* sV, int fb) const {
+    const int lane = opaque_i(lane_id());
     const int w = __builtin_amdgcn_readfirstlane(wave_id());
 #pragma unroll
     for (int i = 0; i < PASSW; ++i) {
       const int s = (w * PASSW + i) * 64 + lane;
       const int r = s / T::CPR, c = s % T::CPR;
-      const int v = vi[i] >= 0 ? vi[i] : fb;
-      dma16(hk.row(v) + (c ^ T::swz(r)) * T::EPC, sY + (w * PASSW + i) * 64 * T::EPC);
+      const int v = fix(tile * TC + r, vi[i]);
+      dma16(hk.row(v >= 0 ? v : fb) + (c ^ T::swz(r)) * T::EPC, sY + (w * PASSW + i) * 64 * T::EPC);
     }
-    if (w == 0) dma16(hk.aug(va >= 0 ? va : fb), sA);
+    if (w == 0) {
+      const int v = fix(tile * TC + lane, va);
+      if (sV != nullptr) sV[lane] = v;
+      dma16(hk.aug(v >= 0 ? v : fb), sA);
+    }
   }
 };
 
@@ -105,7 +147,7 @@ struct DmaTile {
 // ---------------------------------------------------------------------------
 template <typename E, int CPR>
 __global__ __launch_bounds__(256) void norms_kernel(const E* __restrict__ keys, int64_t nrows, int d, float scale,
-                                                    float* __restrict__ out, u32x4_t* __restrict__ aug) {
+                                                    int direct, float* __restrict__ out, u32x4_t* __restrict__ aug) {
   constexpr int EPC = 16 / sizeof(E);
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t row = gid / CPR;
@@ -126,13 +168,20 @@ __global__ __launch_bounds__(256) void norms_kernel(const E* __restrict__ keys, 
     out[row] = s * scale;
     u32x4_t a = {0u, 0u, 0u, 0u};
     if constexpr (sizeof(E) == 2) {
-      const uint16_t hi = f32_to_bf16(s);
-      const float r1 = s - bf16_to_f32(hi);
+      const float q = direct ? s * scale : s;       // scale is a power of two in the direct form
+      const uint16_t hi = f32_to_bf16(q);
+      const float r1 = q - bf16_to_f32(hi);
       const uint16_t mid = f32_to_bf16(r1);
       const uint16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
       a[0] = (uint32_t)hi | ((uint32_t)mid << 16);
-      a[1] = (uint32_t)lo | (0xBF00u << 16);      // bf16(-1/2)
-      a[2] = 0xBF00BF00u;
+      if (direct) {
+        a[1] = (uint32_t)lo | (0x3F80u << 16);    // bf16(1)
+        a[2] = 0x3F803F80u;
+        a[3] = 0x3F803F80u;
+      } else {
+        a[1] = (uint32_t)lo | (0xBF00u << 16);    // bf16(-1/2)
+        a[2] = 0xBF00BF00u;
+      }
     } else {
       a[0] = __float_as_uint(s);
       a[1] = __float_as_uint(-0.5f);
@@ -141,8 +190,8 @@ __global__ __launch_bounds__(256) void norms_kernel(const E* __restrict__ keys, 
   }
 }
 
-hipError_t launch_norms(const void* keys, int et, int H, int rows, int d, float scale, float* out, void* aug,
-                        hipStream_t st) {
+hipError_t launch_norms(const void* keys, int et, int H, int rows, int d, float scale, bool direct, float* out,
+                        void* aug, hipStream_t st) {
   const int64_t nrows = (int64_t)H * rows;
   if (nrows == 0) return hipSuccess;
   const int esz = et == ET_BF16 ? 2 : 4;
@@ -150,11 +199,11 @@ hipError_t launch_norms(const void* keys, int et, int H, int rows, int d, float 
   const dim3 grid((unsigned)((nrows * cpr + 255) / 256));
   u32x4_t* a = (u32x4_t*)aug;
   if (et == ET_BF16) {
-    if (cpr == 8) hipLaunchKernelGGL((norms_kernel<uint16_t, 8>), grid, dim3(256), 0, st, (const uint16_t*)keys, nrows, d, scale, out, a);
-    else hipLaunchKernelGGL((norms_kernel<uint16_t, 16>), grid, dim3(256), 0, st, (const uint16_t*)keys, nrows, d, scale, out, a);
+    if (cpr == 8) hipLaunchKernelGGL((norms_kernel<uint16_t, 8>), grid, dim3(256), 0, st, (const uint16_t*)keys, nrows, d, scale, (int)direct, out, a);
+    else hipLaunchKernelGGL((norms_kernel<uint16_t, 16>), grid, dim3(256), 0, st, (const uint16_t*)keys, nrows, d, scale, (int)direct, out, a);
   } else {
-    if (cpr == 16) hipLaunchKernelGGL((norms_kernel<float, 16>), grid, dim3(256), 0, st, (const float*)keys, nrows, d, scale, out, a);
-    else hipLaunchKernelGGL((norms_kernel<float, 32>), grid, dim3(256), 0, st, (const float*)keys, nrows, d, scale, out, a);
+    if (cpr == 16) hipLaunchKernelGGL((norms_kernel<float, 16>), grid, dim3(256), 0, st, (const float*)keys, nrows, d, scale, 0, out, a);
+    else hipLaunchKernelGGL((norms_kernel<float, 32>), grid, dim3(256), 0, st, (const float*)keys, nrows, d, scale, 0, out, a);
   }
   return hipGetLastError();
 }
@@ -167,7 +216,7 @@ hipError_t launch_norms(const void* keys, int et, int H, int rows, int d, float 
 // rows 8(i>>2) + 4h + (i&3) of each block against column n; a final
 // butterfly over n sums the columns.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int MODE, bool SELF>
+template <typename E, int D, int MODE, bool SELF, bool CLIST, bool DIRECT>
 __global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows, VList cols, float* __restrict__ out,
                                                    int64_t out_hstride, int64_t split_stride, PhiConst pc,
                                                    uint64_t active) {
@@ -176,9 +225,12 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows
   using T = Tile<E, D>;
   constexpr int TC = 64;
   constexpr int NK = D / O::K32;
-  __shared__ __attribute__((aligned(16))) E sY[2][TC * D];
-  __shared__ __attribute__((aligned(16))) u32x4_t sA[2][TC];
-  __shared__ int sYv[2][TC];
+  __shared__ __attribute__((aligned(16))) E sY0[TC * D];
+  __shared__ __attribute__((aligned(16))) E sY1[TC * D];
+  __shared__ __attribute__((aligned(16))) u32x4_t sA0[TC];
+  __shared__ __attribute__((aligned(16))) u32x4_t sA1[TC];
+  __shared__ int sV0[TC];
+  __shared__ int sV1[TC];
 
   // XCD-aware order: logical items (head, split, row tile), head-major
   const int R = gridDim.x, S = gridDim.z;
@@ -211,7 +263,14 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows
     const E* xp = hk.row(v >= 0 ? v : fb);
 #pragma unroll
     for (int k = 0; k < NK; ++k) xf[xb][k] = v >= 0 ? O::load(xp + O::off32(k, lane)) : typename O::frag{};
-    xa[xb] = v >= 0 ? A::xfrag(gload16(hk.aug(v)), lane) : typename O::frag{};
+    if constexpr (DIRECT) {
+      // x' = x * (-2/sigma^2) (exact): the MFMA then returns t itself
+#pragma unroll
+      for (int k = 0; k < NK; ++k) xf[xb][k] = A::scale(xf[xb][k], pc.c2);
+      xa[xb] = v >= 0 ? A::xfrag_direct(gload16(hk.aug(v)), lane, A::eps_parts(pc.eps)) : typename O::frag{};
+    } else {
+      xa[xb] = v >= 0 ? A::xfrag(gload16(hk.aug(v)), lane) : typename O::frag{};
+    }
   }
   float acc[2][16];
 #pragma unroll
@@ -220,46 +279,43 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows
     for (int i = 0; i < 16; ++i) acc[xb][i] = 0.0f;
 
   DmaTile<E, D, TC> ld;
-  auto vof = [&](int tile) {
-    return [&, tile](int r) -> int {
-      const int c = tile * TC + r;
-      const int v = c < ncols ? vlist_at(cols, h, c) : -1;
-      return hk.ok(v) ? v : -1;
-    };
+  // list position c -> raw entry (a plain load for index lists, the position
+  // itself for ranges) -> virtual row index (-1 past the end)
+  const int32_t* cidx = CLIST ? cols.idx + (int64_t)h * cols.idx_hstride : nullptr;
+  auto raw = [&](int c) -> int { return CLIST ? cidx[min(c, ncols - 1)] : c; };
+  auto fix = [&](int c, int e) -> int {
+    const int v = CLIST ? e + cols.add : cols.base + e;
+    return (c < ncols && hk.ok(v)) ? v : -1;
   };
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): row fragments resident
-  if (t0 < t1) {
-    ld.index(vof(t0));
-    ld.issue(hk, sY[0], sA[0], fb);
-    if (threadIdx.x < TC) sYv[0][threadIdx.x] = ld.va;
-    if (t0 + 1 < t1) ld.index(vof(t0 + 1));
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  for (int tile = t0; tile < t1; ++tile) {
-    const int cur = (tile - t0) & 1;
+  // one tile: prefetch the next tile into the other buffer set, then the
+  // MFMA products and interactions on this one.  The two buffer sets are
+  // distinct LDS objects, so the compiler can tell that the direct-to-LDS
+  // copy in flight does not alias the reads of the current tile.
+  // PLAIN (direct form, every column of the tile present): t needs no clamp
+  auto step = [&](auto plain_tag, int tile, const E* cY, const u32x4_t* cA, const int* cV, E* nY, u32x4_t* nA,
+                  int* nV) {
+    constexpr bool PLAIN = decltype(plain_tag)::value;
     if (tile + 1 < t1) {
-      // buffer cur^1 was last read before the previous barrier
-      ld.issue(hk, sY[cur ^ 1], sA[cur ^ 1], fb);
-      if (threadIdx.x < TC) sYv[cur ^ 1][threadIdx.x] = ld.va;
-      if (tile + 2 < t1) ld.index(vof(tile + 2));
+      // the next set was last read before the previous barrier
+      ld.issue(tile + 1, fix, hk, nY, nA, nV, fb);
+      if (tile + 2 < t1) ld.index(tile + 2, raw);
     }
 #pragma unroll
     for (int sub = 0; sub < TC / 32; ++sub) {
       const int rr = 32 * sub + nn;
-      const int yv = sYv[cur][rr];
+      const int yv = cV[rr];
       const int cpos = tile * TC + 32 * sub;       // list position of this subtile's column 0
       f32x16_t cc[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) { cc[0][i] = 0.0f; cc[1][i] = 0.0f; }
 #pragma unroll
       for (int k = 0; k < NK; ++k) {
-        const typename O::frag yk = O::load(sY[cur] + T::at(rr, O::off32(k, lane)));
+        const typename O::frag yk = O::load(cY + T::at(rr, O::off32(k, lane)));
         cc[0] = O::mma32(xf[0][k], yk, cc[0]);
         cc[1] = O::mma32(xf[1][k], yk, cc[1]);
       }
       {
-        const typename O::frag ya = A::yfrag(sA[cur][rr], lane);
+        const typename O::frag ya = A::yfrag(cA[rr], lane);
         cc[0] = O::mma32(xa[0], ya, cc[0]);
         cc[1] = O::mma32(xa[1], ya, cc[1]);
       }
@@ -275,8 +331,13 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows
         const bool diag = SELF && cpos == rpos;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float t = __builtin_fmaf(c[i], pc.c2, pc.eps);
-          t = fmaxf(t, lo);
+          float t;
+          if constexpr (DIRECT) {
+            t = PLAIN ? c[i] : fmaxf(c[i], lo);
+          } else {
+            t = __builtin_fmaf(c[i], pc.c2, pc.eps);
+            t = fmaxf(t, lo);
+          }
           float f = phi_of_t<MODE>(t, pc.neg_half_p);
           if constexpr (MODE == PHI_P0) f = yv >= 0 ? f : 0.0f;
           if constexpr (SELF) {
@@ -288,6 +349,25 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // next tile resident in LDS
     __syncthreads();
+  };
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): row fragments resident
+  if (t0 < t1) {
+    ld.index(t0, raw);
+    ld.issue(t0, fix, hk, sY0, sA0, sV0, fb);
+    if (t0 + 1 < t1) ld.index(t0 + 1, raw);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  // only the last tile of the column list can be ragged
+  const int tfull = DIRECT ? min(t1, ncols / TC) : t0;
+  int tile = t0;
+  for (; tile + 1 < tfull; tile += 2) {
+    step(BoolTag<true>{}, tile, sY0, sA0, sV0, sY1, sA1, sV1);
+    step(BoolTag<true>{}, tile + 1, sY1, sA1, sV1, sY0, sA0, sV0);
+  }
+  for (; tile < t1; ++tile) {
+    if (((tile - t0) & 1) == 0) step(BoolTag<false>{}, tile, sY0, sA0, sV0, sY1, sA1, sV1);
+    else step(BoolTag<false>{}, tile, sY1, sA1, sV1, sY0, sA0, sV0);
   }
   // sum over the 32 columns held by the half-wave
 #pragma unroll
@@ -319,25 +399,37 @@ static KeySpace<E> key_space(const KeysDesc& k) {
                      (const u32x4_t*)k.candA, k.M, k.N, k.d};
 }
 
-template <typename E, int D, int MODE>
+template <typename E, int D, int MODE, bool DIRECT>
 static void gram_dispatch_self(const GramLaunch& g, dim3 grid, hipStream_t st) {
   const KeySpace<E> ks = key_space<E>(g.k);
-  if (g.self_excl)
-    hipLaunchKernelGGL((gram_kernel<E, D, MODE, true>), grid, dim3(256), 0, st, ks, g.rows, g.cols, g.out,
-                       g.out_hstride, g.split_stride, g.pc, g.active);
+  // self-exclusion only arises with both sides the same index list
+  if (g.self_excl && g.cols.idx)
+    hipLaunchKernelGGL((gram_kernel<E, D, MODE, true, true, DIRECT>), grid, dim3(256), 0, st, ks, g.rows, g.cols,
+                       g.out, g.out_hstride, g.split_stride, g.pc, g.active);
+  else if (g.self_excl)
+    hipLaunchKernelGGL((gram_kernel<E, D, MODE, true, false, DIRECT>), grid, dim3(256), 0, st, ks, g.rows, g.cols,
+                       g.out, g.out_hstride, g.split_stride, g.pc, g.active);
+  else if (g.cols.idx)
+    hipLaunchKernelGGL((gram_kernel<E, D, MODE, false, true, DIRECT>), grid, dim3(256), 0, st, ks, g.rows, g.cols,
+                       g.out, g.out_hstride, g.split_stride, g.pc, g.active);
   else
-    hipLaunchKernelGGL((gram_kernel<E, D, MODE, false>), grid, dim3(256), 0, st, ks, g.rows, g.cols, g.out,
-                       g.out_hstride, g.split_stride, g.pc, g.active);
+    hipLaunchKernelGGL((gram_kernel<E, D, MODE, false, false, DIRECT>), grid, dim3(256), 0, st, ks, g.rows, g.cols,
+                       g.out, g.out_hstride, g.split_stride, g.pc, g.active);
 }
 
 template <typename E, int D>
 static void gram_dispatch_mode(const GramLaunch& g, dim3 grid, hipStream_t st) {
   switch (g.phi_mode) {
-    case PHI_P2: gram_dispatch_self<E, D, PHI_P2>(g, grid, st); break;
-    case PHI_P0: gram_dispatch_self<E, D, PHI_P0>(g, grid, st); break;
-    case PHI_P1: gram_dispatch_self<E, D, PHI_P1>(g, grid, st); break;
-    case PHI_P4: gram_dispatch_self<E, D, PHI_P4>(g, grid, st); break;
-    default: gram_dispatch_self<E, D, PHI_GEN>(g, grid, st); break;
+    case PHI_P2:
+      if constexpr (sizeof(E) == 2) {
+        if (g.pc.direct) { gram_dispatch_self<E, D, PHI_P2, true>(g, grid, st); break; }
+      }
+      gram_dispatch_self<E, D, PHI_P2, false>(g, grid, st);
+      break;
+    case PHI_P0: gram_dispatch_self<E, D, PHI_P0, false>(g, grid, st); break;
+    case PHI_P1: gram_dispatch_self<E, D, PHI_P1, false>(g, grid, st); break;
+    case PHI_P4: gram_dispatch_self<E, D, PHI_P4, false>(g, grid, st); break;
+    default: gram_dispatch_self<E, D, PHI_GEN, false>(g, grid, st); break;
   }
 }
 
@@ -391,7 +483,7 @@ hipError_t launch_sum_splits(const float* src, int64_t src_hstride, int64_t spli
 // scan pass: t_b = smallest k with S_b(k) > tau * rho0_b (kmax+1 if none).
 // sum pass:  rhoP_b = S_b(k*) starting from the nearest checkpoint.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int MODE, bool SUM>
+template <typename E, int D, int MODE, bool SUM, bool DIRECT>
 __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const float* __restrict__ rho,
                                                    const float* __restrict__ rho0, const int32_t* __restrict__ count,
                                                    const int32_t* __restrict__ order, uint64_t active,
@@ -403,8 +495,10 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
   using T = Tile<E, D>;
   constexpr int TC = 64;               // candidates per LDS stage (two subtiles)
   constexpr int NK = D / O::K32;
-  __shared__ __attribute__((aligned(16))) E sC[2][TC * D];
-  __shared__ __attribute__((aligned(16))) u32x4_t sA[2][TC];
+  __shared__ __attribute__((aligned(16))) E sC0[TC * D];
+  __shared__ __attribute__((aligned(16))) E sC1[TC * D];
+  __shared__ __attribute__((aligned(16))) u32x4_t sA0[TC];
+  __shared__ __attribute__((aligned(16))) u32x4_t sA1[TC];
 
   const int R = gridDim.x;
   const int lin = xcd_remap(blockIdx.x + R * blockIdx.y, R * gridDim.y);
@@ -456,40 +550,45 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
     const E* bp = ks.bankK + hb * D;
 #pragma unroll
     for (int k = 0; k < NK; ++k) bf[k] = valid ? O::load(bp + O::off32(k, lane)) : typename O::frag{};
-    ba = valid ? A::xfrag(gload16(ks.bankA + hb), lane) : typename O::frag{};
+    if constexpr (DIRECT) {
+#pragma unroll
+      for (int k = 0; k < NK; ++k) bf[k] = A::scale(bf[k], pc.c2);
+      ba = valid ? A::xfrag_direct(gload16(ks.bankA + hb), lane, A::eps_parts(pc.eps)) : typename O::frag{};
+    } else {
+      ba = valid ? A::xfrag(gload16(ks.bankA + hb), lane) : typename O::frag{};
+    }
   }
 
   const int st_begin = sub_begin / 2, st_end = (sub_end + 1) / 2;
   DmaTile<E, D, TC> ld;
-  auto vof = [&](int stage) {
-    return [&, stage](int r) -> int {
-      const int j = stage * TC + r;
-      const unsigned c = j < kmax ? (unsigned)order[(int64_t)h * ks.N + j] : 0xFFFFFFFFu;
-      return c < (unsigned)ks.N ? M + (int)c : -1;
-    };
-  };
+  // position j of the order -> raw entry -> virtual row index (-1 past kmax)
+  const int32_t* ord = order + (int64_t)h * ks.N;
+  auto raw = [&](int j) -> int { return ord[min(j, kmax - 1)]; };
+  auto fix = [&](int j, int e) -> int { return (j < kmax && (unsigned)e < (unsigned)ks.N) ? M + e : -1; };
   // candidates are always present in a stage's used positions; rows past
   // kmax copy a fallback row and are masked below
   const int fb = M;                      // candidate 0 (N > 0 whenever kmax > 0)
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): bank fragments resident
   if (st_begin < st_end) {
-    ld.index(vof(st_begin));
-    ld.issue(hk, sC[0], sA[0], fb);
-    if (st_begin + 1 < st_end) ld.index(vof(st_begin + 1));
+    ld.index(st_begin, raw);
+    ld.issue(st_begin, fix, hk, sC0, sA0, nullptr, fb);
+    if (st_begin + 1 < st_end) ld.index(st_begin + 1, raw);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  for (int stg = st_begin; stg < st_end; ++stg) {
-    const int cur = (stg - st_begin) & 1;
+  // one stage (returns false once every row of the work-group has crossed);
+  // the two buffer sets are distinct LDS objects, so the copy in flight is
+  // known not to alias the reads of the current stage
+  auto step = [&](int stg, const E* cC, const u32x4_t* cA, E* nC, u32x4_t* nA) -> bool {
     const bool more = stg + 1 < st_end;
     if (more) {
-      // buffer cur^1 was last read before the previous barrier
-      ld.issue(hk, sC[cur ^ 1], sA[cur ^ 1], fb);
-      if (stg + 2 < st_end) ld.index(vof(stg + 2));
+      // the next set was last read before the previous barrier
+      ld.issue(stg + 1, fix, hk, nC, nA, nullptr, fb);
+      if (stg + 2 < st_end) ld.index(stg + 2, raw);
     }
     const bool wave_busy = __any(!done);
     if (wave_busy) {
-#pragma unroll
+#pragma unroll 1
       for (int half = 0; half < 2; ++half) {
         const int sub = 2 * stg + half;
         if (sub < sub_begin || sub >= sub_end) continue;
@@ -501,14 +600,19 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
         for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
         const int cr = 32 * half + (lane & 31);
 #pragma unroll
-        for (int k = 0; k < NK; ++k) acc = O::mma32(O::load(sC[cur] + T::at(cr, O::off32(k, lane))), bf[k], acc);
-        acc = O::mma32(A::yfrag(sA[cur][cr], lane), ba, acc);
+        for (int k = 0; k < NK; ++k) acc = O::mma32(O::load(cC + T::at(cr, O::off32(k, lane))), bf[k], acc);
+        acc = O::mma32(A::yfrag(cA[cr], lane), ba, acc);
         float v[16];
         const int pos0 = 32 * sub;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float t = __builtin_fmaf(acc[i], pc.c2, pc.eps);
-          t = fmaxf(t, pc.eps);
+          // direct form: the MFMA returned t (no clamp needed, eps >= 1e-2);
+          // positions past kmax hold a stand-in row and are zeroed below
+          float t = acc[i];
+          if constexpr (!DIRECT) {
+            t = __builtin_fmaf(acc[i], pc.c2, pc.eps);
+            t = fmaxf(t, pc.eps);
+          }
           v[i] = phi_of_t<MODE>(t, pc.neg_half_p);
         }
         if (pos0 + 32 > kmax) {   // last subtile: drop positions past kmax
@@ -582,14 +686,17 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // next stage resident in LDS
     if constexpr (!SUM) {
-      if (!__syncthreads_or(!done)) {
-        // every row of the work-group has crossed: later checkpoints are
-        // never read (the sum pass skips rows with t_b <= k*)
-        break;
-      }
+      // every row of the work-group crossed: later checkpoints are never
+      // read (the sum pass skips rows with t_b <= k*)
+      return __syncthreads_or(!done) != 0;
     } else {
       __syncthreads();
+      return true;
     }
+  };
+  for (int stg = st_begin; stg < st_end; stg += 2) {
+    if (!step(stg, sC0, sA0, sC1, sA1)) break;
+    if (stg + 1 < st_end && !step(stg + 1, sC1, sA1, sC0, sA0)) break;
   }
   if (valid && hh == 0) {
     if constexpr (SUM) rhoP[hb] = need ? carry : r_b;
@@ -597,25 +704,30 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
   }
 }
 
-template <typename E, int D, int MODE>
+template <typename E, int D, int MODE, bool DIRECT>
 static void scan_dispatch(const ScanLaunch& a, bool sum, dim3 grid, hipStream_t st) {
   const KeySpace<E> ks = key_space<E>(a.k);
   if (sum)
-    hipLaunchKernelGGL((scan_kernel<E, D, MODE, true>), grid, dim3(256), 0, st, ks, a.rho, a.rho0, a.count,
+    hipLaunchKernelGGL((scan_kernel<E, D, MODE, true, DIRECT>), grid, dim3(256), 0, st, ks, a.rho, a.rho0, a.count,
                        a.order, a.active, a.kmax, a.tau, a.cps, a.ncp, a.cp, a.t_out, a.kstar, a.rhoP, a.pc);
   else
-    hipLaunchKernelGGL((scan_kernel<E, D, MODE, false>), grid, dim3(256), 0, st, ks, a.rho, a.rho0, a.count,
+    hipLaunchKernelGGL((scan_kernel<E, D, MODE, false, DIRECT>), grid, dim3(256), 0, st, ks, a.rho, a.rho0, a.count,
                        a.order, a.active, a.kmax, a.tau, a.cps, a.ncp, a.cp, a.t_out, a.kstar, a.rhoP, a.pc);
 }
 
 template <typename E, int D>
 static void scan_dispatch_mode(const ScanLaunch& a, bool sum, dim3 grid, hipStream_t st) {
   switch (a.phi_mode) {
-    case PHI_P2: scan_dispatch<E, D, PHI_P2>(a, sum, grid, st); break;
-    case PHI_P0: scan_dispatch<E, D, PHI_P0>(a, sum, grid, st); break;
-    case PHI_P1: scan_dispatch<E, D, PHI_P1>(a, sum, grid, st); break;
-    case PHI_P4: scan_dispatch<E, D, PHI_P4>(a, sum, grid, st); break;
-    default: scan_dispatch<E, D, PHI_GEN>(a, sum, grid, st); break;
+    case PHI_P2:
+      if constexpr (sizeof(E) == 2) {
+        if (a.pc.direct) { scan_dispatch<E, D, PHI_P2, true>(a, sum, grid, st); break; }
+      }
+      scan_dispatch<E, D, PHI_P2, false>(a, sum, grid, st);
+      break;
+    case PHI_P0: scan_dispatch<E, D, PHI_P0, false>(a, sum, grid, st); break;
+    case PHI_P1: scan_dispatch<E, D, PHI_P1, false>(a, sum, grid, st); break;
+    case PHI_P4: scan_dispatch<E, D, PHI_P4, false>(a, sum, grid, st); break;
+    default: scan_dispatch<E, D, PHI_GEN, false>(a, sum, grid, st); break;
   }
 }
 

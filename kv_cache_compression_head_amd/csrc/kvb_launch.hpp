@@ -19,9 +19,10 @@ struct KeysDesc {            // one layer's keys in two buffers (see KeySpace)
   int32_t et;
 };
 
-// out[r] = |k_r|^2 * scale and aug[r] = exact split of |k_r|^2, rows [H][rows][d]
-hipError_t launch_norms(const void* keys, int et, int H, int rows, int d, float scale, float* out, void* aug,
-                        hipStream_t s);
+// out[r] = |k_r|^2 * scale and aug[r] = the augmentation row of key r (exact
+// split of |k_r|^2, or of |k_r|^2 * scale in the direct form), rows [H][rows][d]
+hipError_t launch_norms(const void* keys, int et, int H, int rows, int d, float scale, bool direct, float* out,
+                        void* aug, hipStream_t s);
 
 // out[h*out_hstride + split*split_stride + i] = sum_{j in cols} phi(row_i, col_j)
 struct GramLaunch {

@@ -6,7 +6,7 @@ import math
 import numpy as np
 import pytest
 
-from kvsynth import WORKLOADS, LayerGen, Workload, frame_tokens
+from kvsynth import WORKLOADS, LayerGen, Workload, frame_tokens, round_bf16
 from oracle import density as od
 
 import gpu_common as gc
@@ -75,9 +75,10 @@ def test_tiny_full_admission():
     assert all(r.kstar == 48 for r in reps)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("p,tau", [(1.0, 1.3), (4.0, 1.3), (3.0, 1.2), (2.0, 1.05)])
-def test_tiny_phi_modes(p, tau):
-    wl = WORKLOADS["tiny"]
+def test_tiny_phi_modes(p, tau, dtype):
+    wl = dataclasses.replace(WORKLOADS["tiny"], dtype=dtype, name=f"tiny-{dtype}")
     _stream(wl, _prm(wl, p=p, tau=tau), attn=False)
 
 
@@ -103,6 +104,27 @@ def test_duplicate_rejected_on_gpu():
     assert 103 not in toks and {100, 101, 102, 5} <= toks
 
 
+def test_duplicate_rejected_on_gpu_bf16():
+    """The same invariant through the bf16 direct form (sigma^2 a power of
+    two): the duplicate's softened distance is exactly eps."""
+    wl = dataclasses.replace(WORKLOADS["tiny"], H=1, M=100, dtype="bf16", name="tiny-bf16")
+    prm = od.Params(M=100, tau=2.0)
+    lc = gc.layer_for(wl, prm)
+    d, n = 64, 60
+    K = (np.eye(d)[:n] * 200.0).astype(np.float32)[None]
+    # values as stored in bf16, so that the pairing check compares like with like
+    V = round_bf16(np.random.default_rng(0).normal(size=(1, n, d)).astype(np.float32))
+    gc.run_update(lc, None, wl, prm, (0, 0), [0], candK=K, candV=V, ctok=np.arange(n, dtype=np.int32))
+    cK = np.concatenate([np.eye(d)[n:n + 3] * 200.0, K[0, 5:6]]).astype(np.float32)[None]
+    cV = np.ones((1, 4, d), np.float32)
+    rep = gc.run_update(lc, None, wl, prm, (0, 0), [0], candK=cK, candV=cV,
+                        ctok=np.array([100, 101, 102, 103], np.int32))
+    assert rep.kstar == 3
+    bank = GpuBank.read(lc.bank)
+    toks = set(bank.tok[0, :bank.count[0]].tolist())
+    assert 103 not in toks and {100, 101, 102, 5} <= toks
+
+
 MID = Workload(name="mid", H=4, d=128, width=52, height=30, dtype="bf16", M=3120, tau=2.0,
                bank_updates=((1, 3), (3, 7)), window=(7, 9), chunk=(9, 12))
 
@@ -113,6 +135,13 @@ def test_mid_bf16_default():
 
 def test_mid_bf16_tight_tau():
     _stream(MID, _prm(MID, tau=1.02), attn=False, seed=1)
+
+
+@pytest.mark.parametrize("sigma,eps", [(7.0, 1.0), (8.0, 1e-3)])
+def test_mid_bf16_general_form(sigma, eps):
+    """bf16 keys where the Soft-Riesz argument is formed with a multiply-add
+    (sigma^2 not a power of two, or a small eps that needs the clamp)."""
+    _stream(MID, _prm(MID, sigma=sigma, eps=eps), max_abs=2e-2, mean_abs=2e-3, seed=2)
 
 
 def test_empty_update_and_zero_candidates():
