@@ -7,9 +7,10 @@
 // is the concatenation of the head's segments (order irrelevant).
 //
 // bf16 path: flash-style online softmax.  Work-group = 4 waves x 32 queries;
-// KV tiles of 64 keys staged in LDS (K row-major, V transposed), double
-// buffered: the next tile's global loads are in flight while the current
-// tile is multiplied.  Scores are computed transposed (S^T = K Q^T, 16x16x32
+// KV tiles of 64 keys staged in LDS, double buffered: K row-major with
+// XOR-swizzled 16-byte chunks, copied straight from global memory to LDS;
+// V transposed through registers.  The next tile's copies are in flight
+// while the current tile is multiplied.  Scores are computed transposed (S^T = K Q^T, 16x16x32
 // MFMA) so every lane holds keys of a single query; P^T feeds
 // O^T = V^T P^T directly as the B operand.  The running maximum is only
 // moved when a tile raises it by more than 2^8 (exact: numerator and
@@ -34,37 +35,24 @@ KVB_DEV uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// per-slot cursor over the segment prefix table (rows only move forward);
-// the current segment's bounds and base pointer stay in registers
-struct SegCursor {
-  int s, lo, hi;
-  const uint16_t* base;
-  KVB_DEV void init(const int* pre, const void* const* bases) {
-    s = 0; lo = pre[0]; hi = pre[1]; base = (const uint16_t*)bases[0];
-  }
-  KVB_DEV const uint16_t* row(const int* pre, const void* const* bases, int nseg, int j, int D) {
-    if (j >= hi) {
-      while (s + 1 < nseg && pre[s + 1] <= j) ++s;
-      lo = pre[s]; hi = pre[s + 1]; base = (const uint16_t*)bases[s];
-    }
-    return base + (int64_t)(j - lo) * D;
-  }
-};
-
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __restrict__ Q, void* __restrict__ O,
                                                            const SegEntry* __restrict__ segs,
                                                            const int32_t* __restrict__ nseg_p, int seg_cap, int Lq,
                                                            float scale_log2, int out_f32, int nqt) {
   using Op = Ops<uint16_t>;
-  constexpr int LDK = D + 8;              // K row stride (elements)
+  using T = Tile<uint16_t, D>;
   constexpr int LDV = ATT_TK + 4;         // V^T row stride (elements): 34 dwords, conflict-free b64 reads
   constexpr int NKS = D / 32;             // k-steps for S^T
   constexpr int NDB = D / 16;             // d blocks for O^T
-  constexpr int CPR = D / 8;              // 16-byte chunks per row
-  constexpr int KPASS = ATT_TK * CPR / 256;   // K chunks per thread
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][ATT_TK * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * LDV];
+  constexpr int CPR = T::CPR;             // 16-byte chunks per key row
+  constexpr int KPASS = ATT_TK * CPR / 256;   // K chunks copied per thread
+  // two buffer sets as distinct LDS objects: the direct-to-LDS copy of the
+  // next K tile is then known not to alias the reads of the current one
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[ATT_TK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[ATT_TK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[D * LDV];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[D * LDV];
   __shared__ int s_pre[ATT_MAXSEG + 1];
   __shared__ const void* s_k[ATT_MAXSEG];
   __shared__ const void* s_v[ATT_MAXSEG];
@@ -90,7 +78,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
     s_pre[nseg] = acc;
   }
   __syncthreads();
-  const int Lkv = s_pre[nseg];
+  const int Lkv = __builtin_amdgcn_readfirstlane(s_pre[nseg]);
 
   // query fragments (B operand of S^T = K Q^T)
   const int q0 = qt * ATT_QB + w * ATT_QW;
@@ -115,45 +103,58 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
   float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
   float l_run[2] = {0.f, 0.f};
 
-  // staging registers and cursors
+  // V staging: thread covers keys 4kg..4kg+3 and d 8dc..8dc+7; consecutive
+  // lanes take consecutive key groups so the transposed 8-byte stores of 16
+  // lanes fill one 128-byte V^T row segment (no bank conflicts)
   const bool vthr = tid < 16 * CPR;
-  // V: thread covers keys 4kg..4kg+3 and d 8dc..8dc+7; consecutive lanes take
-  // consecutive key groups so the transposed 8-byte stores of 16 lanes fill
-  // one 128-byte V^T row segment (no bank conflicts)
   const int kg = tid % 16, dc = tid / 16;
-  u32x4_t rk[KPASS], rv[4];
-  SegCursor ck[KPASS], cv[4];
-  if (nseg > 0) {
-#pragma unroll
-    for (int i = 0; i < KPASS; ++i) ck[i].init(s_pre, s_k);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) cv[i].init(s_pre, s_v);
-  }
+  u32x4_t rv[4];
 
-  // rows past the end of the KV re-read the last row: their scores are
-  // masked to -inf and their (finite) values get weight 0, so the loads need
-  // no branches
-  auto fetch = [&](int kbase) {
+  // Tile addressing.  A tile inside one segment (all but a handful per head)
+  // is one base pointer plus the row offset; a tile that straddles segments
+  // or the end resolves each row on its own (rows past the end re-read the
+  // last row: their scores are masked to -inf, their values get weight 0).
+  int useg = 0;   // uniform: segment holding the current tile start
+  auto slow_row = [&](int j, const void* const* bases) -> const uint16_t* {
+    j = min(j, Lkv - 1);
+    int s = 0;
+    while (s + 1 < nseg && s_pre[s + 1] <= j) ++s;
+    return (const uint16_t*)bases[s] + (int64_t)(j - s_pre[s]) * D;
+  };
+  auto fetch = [&](int kbase, uint16_t* sKn) {
+    while (useg + 1 < nseg && __builtin_amdgcn_readfirstlane(s_pre[useg + 1]) <= kbase) ++useg;
+    const int lo = __builtin_amdgcn_readfirstlane(s_pre[useg]);
+    const int hi = __builtin_amdgcn_readfirstlane(s_pre[useg + 1]);
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    // row addresses first (merging loaded registers across the two paths
+    // would force a wait on the loads), then the copies and loads
+    const uint16_t* kp[KPASS];
+    const uint16_t* vp[4];
+    if (kbase + ATT_TK <= hi) {
+      const uint16_t* kb = (const uint16_t*)s_k[useg] + (int64_t)(kbase - lo) * D;
+      const uint16_t* vb = (const uint16_t*)s_v[useg] + (int64_t)(kbase - lo) * D;
+#pragma unroll
+      for (int i = 0; i < KPASS; ++i) kp[i] = kb + (((wu * KPASS + i) * 64 + lane) / CPR) * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vp[i] = vb + (4 * kg + i) * D;
+    } else {
+#pragma unroll
+      for (int i = 0; i < KPASS; ++i) kp[i] = slow_row(kbase + ((wu * KPASS + i) * 64 + lane) / CPR, s_k);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vp[i] = slow_row(kbase + 4 * kg + i, s_v);
+    }
 #pragma unroll
     for (int i = 0; i < KPASS; ++i) {
-      const int r = tid / CPR + (256 / CPR) * i;
-      const int j = min(kbase + r, Lkv - 1);
-      rk[i] = gload16(ck[i].row(s_pre, s_k, nseg, j, D) + (tid % CPR) * 8);
+      const int sl = (wu * KPASS + i) * 64 + lane;
+      const int r = sl / CPR, c = sl % CPR;
+      dma16(kp[i] + (c ^ T::swz(r)) * 8, sKn + (wu * KPASS + i) * 64 * 8);
     }
     if (vthr) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = min(kbase + 4 * kg + i, Lkv - 1);
-        rv[i] = gload16(cv[i].row(s_pre, s_v, nseg, j, D) + dc * 8);
-      }
+      for (int i = 0; i < 4; ++i) rv[i] = gload16(vp[i] + dc * 8);
     }
   };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KPASS; ++i) {
-      const int r = tid / CPR + (256 / CPR) * i;
-      *reinterpret_cast<u32x4_t*>(&sK[buf][r * LDK + (tid % CPR) * 8]) = rk[i];
-    }
+  auto stage_v = [&](uint16_t* sVn) {
     if (vthr) {
       // transpose 4 keys x 8 d into 8 rows of V^T (4 keys each)
       const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&rv[0]);
@@ -165,22 +166,16 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
         uint2 pk;
         pk.x = (uint32_t)e0[x] | ((uint32_t)e1[x] << 16);
         pk.y = (uint32_t)e2[x] | ((uint32_t)e3[x] << 16);
-        *reinterpret_cast<uint2*>(&sV[buf][(8 * dc + x) * LDV + 4 * kg]) = pk;
+        *reinterpret_cast<uint2*>(&sVn[(8 * dc + x) * LDV + 4 * kg]) = pk;
       }
     }
   };
 
   const int ntile = (Lkv + ATT_TK - 1) / ATT_TK;
-  if (ntile > 0) {
-    fetch(0);
-    stage(0);
-  }
-  __syncthreads();
-  for (int tile = 0; tile < ntile; ++tile) {
-    const int cur = tile & 1;
+  auto step = [&](int tile, const uint16_t* sKc, const uint16_t* sVc, uint16_t* sKn, uint16_t* sVn) {
     const int kbase = tile * ATT_TK;
     const bool more = tile + 1 < ntile;
-    if (more) fetch(kbase + ATT_TK);
+    if (more) fetch(kbase + ATT_TK, sKn);
 
     // ---- S^T = K Q^T ----
     f32x4_t s[4][2];
@@ -188,10 +183,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
     for (int kb = 0; kb < 4; ++kb) {
       s[kb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       s[kb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kp = sK[cur] + (16 * kb + (lane & 15)) * LDK;
+      const int kr = 16 * kb + (lane & 15);
 #pragma unroll
       for (int k = 0; k < NKS; ++k) {
-        const s16x8_t a = Op::load(kp + Op::off16(k, lane));
+        const s16x8_t a = Op::load(sKc + T::at(kr, Op::off16(k, lane)));
         s[kb][0] = Op::mma16(a, qf[0][k], s[kb][0]);
         s[kb][1] = Op::mma16(a, qf[1][k], s[kb][1]);
       }
@@ -255,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
       const s16x8_t bb1 = __builtin_bit_cast(s16x8_t, b1);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const uint16_t* vp = sV[cur] + (16 * db + (lane & 15)) * LDV + 32 * hk + 4 * g;
+        const uint16_t* vp = sVc + (16 * db + (lane & 15)) * LDV + 32 * hk + 4 * g;
         const uint2 lo = *reinterpret_cast<const uint2*>(vp);
         const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
         const u32x4_t raw = {lo.x, lo.y, hi.x, hi.y};
@@ -264,8 +259,22 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
         o[db][1] = Op::mma16(a, bb1, o[db][1]);
       }
     }
-    if (more) stage(cur ^ 1);
+    // keep the V transpose (which waits for the V loads) after the products
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) stage_v(sVn);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // next K tile resident in LDS
     __syncthreads();
+  };
+
+  if (ntile > 0) {
+    fetch(0, sK0);
+    stage_v(sV0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  for (int tile = 0; tile < ntile; tile += 2) {
+    step(tile, sK0, sV0, sK1, sV1);
+    if (tile + 1 < ntile) step(tile + 1, sK1, sV1, sK0, sV0);
   }
 
   // ---- normalise and store: lane holds O[q][16db + 4g + i] ----

@@ -68,30 +68,7 @@ template <> struct Aug<float> {
   KVB_DEV static float yfrag(const u32x4_t& a, int lane) { return __uint_as_float((lane >> 5) ? a[1] : a[0]); }
 };
 
-// LDS key tiles: rows of D elements with no padding; the 16-byte chunks of
-// row r are XOR-swizzled so that the 16 rows read by one quarter-wave hit 16
-// different 16-byte bank groups.
-template <typename E, int D> struct Tile {
-  static constexpr int EPC = 16 / (int)sizeof(E);   // elements per chunk
-  static constexpr int CPR = D / EPC;               // chunks per row
-  KVB_DEV static int swz(int r) {
-    if constexpr (sizeof(E) == 2) {
-      if constexpr (CPR == 16) return r & 15;
-      else return (r >> 1) & 7;
-    } else {
-      return 0;
-    }
-  }
-  // element offset of element e of row r (e is a fragment start)
-  KVB_DEV static int at(int r, int e) { return r * D + (((e / EPC) ^ swz(r)) * EPC) + e % EPC; }
-};
-
-// 16-byte global -> LDS copy that bypasses registers: lane l of the wave
-// writes 16 bytes at lds + 16 l
-KVB_DEV void dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-}
+template <bool B> struct BoolTag { static constexpr bool value = B; };
 
 // Stages TC key rows (gathered by virtual index) and their augmentation rows
 // into LDS with direct-to-LDS loads.  256 threads; thread (w, lane) copies
@@ -104,8 +81,6 @@ KVB_DEV void dma16(const void* g, void* lds) {
 // one tile later.  raw(c) reads list position c (clamped by the caller);
 // fix(c, raw) returns the virtual row index of position c or -1.  Absent
 // rows copy row `fb` (any existing row).
-template <bool B> struct BoolTag { static constexpr bool value = B; };
-
 template <typename E, int D, int TC>
 struct DmaTile {
   using T = Tile<E, D>;
