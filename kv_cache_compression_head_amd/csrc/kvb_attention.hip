@@ -101,7 +101,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
-  float l_run[2] = {0.f, 0.f};
+  // softmax denominators, accumulated by MFMA from the same bf16 weights as
+  // the numerator (ones x P^T: every row of L holds the query's sum)
+  f32x4_t L[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  const s16x8_t ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80};
 
   // V staging: thread covers keys 4kg..4kg+3 and d 8dc..8dc+7; consecutive
   // lanes take consecutive key groups so the transposed 8-byte stores of 16
@@ -121,33 +124,50 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
     while (s + 1 < nseg && s_pre[s + 1] <= j) ++s;
     return (const uint16_t*)bases[s] + (int64_t)(j - s_pre[s]) * D;
   };
+  // byte offsets of this lane's K chunks inside a 64-row tile (swizzled
+  // source chunk of LDS slot (row, lane % CPR)), fixed for the kernel
+  uint32_t koff[KPASS];
+#pragma unroll
+  for (int i = 0; i < KPASS; ++i) {
+    const int sl = (w * KPASS + i) * 64 + lane;
+    const int r = sl / CPR, c = sl % CPR;
+    koff[i] = (uint32_t)(r * D + (c ^ T::swz(r)) * 8) * 2u;
+  }
   auto fetch = [&](int kbase, uint16_t* sKn) {
     while (useg + 1 < nseg && __builtin_amdgcn_readfirstlane(s_pre[useg + 1]) <= kbase) ++useg;
     const int lo = __builtin_amdgcn_readfirstlane(s_pre[useg]);
     const int hi = __builtin_amdgcn_readfirstlane(s_pre[useg + 1]);
     const int wu = __builtin_amdgcn_readfirstlane(w);
-    // row addresses first (merging loaded registers across the two paths
-    // would force a wait on the loads), then the copies and loads
-    const uint16_t* kp[KPASS];
+    // V row addresses first (merging loaded registers across the two paths
+    // would force a wait on the loads), then the loads
     const uint16_t* vp[4];
     if (kbase + ATT_TK <= hi) {
-      const uint16_t* kb = (const uint16_t*)s_k[useg] + (int64_t)(kbase - lo) * D;
-      const uint16_t* vb = (const uint16_t*)s_v[useg] + (int64_t)(kbase - lo) * D;
+      // whole tile inside one segment: K through a buffer resource on the
+      // segment (uniform base, per-lane offsets fixed for the kernel)
+      // (readfirstlane returns int: widen through uint32_t, never by sign)
+      const uint64_t kseg = (uint64_t)s_k[useg];
+      const uint32_t khi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(kseg >> 32));
+      const uint32_t klo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)kseg);
+      const void* kbase_ptr = (const void*)(((uint64_t)khi << 32) | (uint64_t)klo);
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(kbase_ptr), (short)0, (hi - lo) * D * 2, 0x00020000);
+      const int soff = (kbase - lo) * D * 2;
 #pragma unroll
-      for (int i = 0; i < KPASS; ++i) kp[i] = kb + (((wu * KPASS + i) * 64 + lane) / CPR) * D;
+      for (int i = 0; i < KPASS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk, (__attribute__((address_space(3))) void*)(sKn + (wu * KPASS + i) * 64 * 8), 16, (int)koff[i], soff, 0, 0);
+      const uint16_t* vb = (const uint16_t*)s_v[useg] + (int64_t)(kbase - lo) * D;
 #pragma unroll
       for (int i = 0; i < 4; ++i) vp[i] = vb + (4 * kg + i) * D;
     } else {
 #pragma unroll
-      for (int i = 0; i < KPASS; ++i) kp[i] = slow_row(kbase + ((wu * KPASS + i) * 64 + lane) / CPR, s_k);
+      for (int i = 0; i < KPASS; ++i) {
+        const int sl = (wu * KPASS + i) * 64 + lane;
+        const int r = sl / CPR, c = sl % CPR;
+        dma16(slow_row(kbase + r, s_k) + (c ^ T::swz(r)) * 8, sKn + (wu * KPASS + i) * 64 * 8);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) vp[i] = slow_row(kbase + 4 * kg + i, s_v);
-    }
-#pragma unroll
-    for (int i = 0; i < KPASS; ++i) {
-      const int sl = (wu * KPASS + i) * 64 + lane;
-      const int r = sl / CPR, c = sl % CPR;
-      dma16(kp[i] + (c ^ T::swz(r)) * 8, sKn + (wu * KPASS + i) * 64 * 8);
     }
     if (vthr) {
 #pragma unroll
@@ -171,6 +191,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
     }
   };
 
+  // element offsets of this lane's K fragments (row 16kb + (lane & 15) of a
+  // tile, chunk 4k + g): the swizzle of row 16kb + x equals that of x
+  int kread[NKS];
+#pragma unroll
+  for (int k = 0; k < NKS; ++k) kread[k] = T::at(lane & 15, Op::off16(k, lane));
+
   const int ntile = (Lkv + ATT_TK - 1) / ATT_TK;
   auto step = [&](int tile, const uint16_t* sKc, const uint16_t* sVc, uint16_t* sKn, uint16_t* sVn) {
     const int kbase = tile * ATT_TK;
@@ -183,10 +209,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
     for (int kb = 0; kb < 4; ++kb) {
       s[kb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       s[kb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int kr = 16 * kb + (lane & 15);
 #pragma unroll
       for (int k = 0; k < NKS; ++k) {
-        const s16x8_t a = Op::load(sKc + T::at(kr, Op::off16(k, lane)));
+        const s16x8_t a = Op::load(sKc + 16 * kb * D + kread[k]);
         s[kb][0] = Op::mma16(a, qf[0][k], s[kb][0]);
         s[kb][1] = Op::mma16(a, qf[1][k], s[kb][1]);
       }
@@ -218,7 +243,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
         const float mnew = fmaxf(m_run[qb], mt[qb]);
         const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew);
         m_run[qb] = mnew;
-        l_run[qb] *= alpha;
+        L[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[db][qb] *= alpha;
       }
@@ -227,19 +252,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const float nm = -m_run[qb];
-      float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         float p[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i], scale_log2, nm));
-          ls += p[i];
-        }
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i], scale_log2, nm));
         pk[qb][kb][0] = pack_bf16x2(p[0], p[1]);
         pk[qb][kb][1] = pack_bf16x2(p[2], p[3]);
       }
-      l_run[qb] += ls;
     }
     // ---- O^T += V^T P^T ----
 #pragma unroll
@@ -248,6 +268,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
       u32x4_t b1 = {pk[1][2 * hk][0], pk[1][2 * hk][1], pk[1][2 * hk + 1][0], pk[1][2 * hk + 1][1]};
       const s16x8_t bb0 = __builtin_bit_cast(s16x8_t, b0);
       const s16x8_t bb1 = __builtin_bit_cast(s16x8_t, b1);
+      L[0] = Op::mma16(ones, bb0, L[0]);
+      L[1] = Op::mma16(ones, bb1, L[1]);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const uint16_t* vp = sVc + (16 * db + (lane & 15)) * LDV + 32 * hk + 4 * g;
@@ -280,9 +302,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
   // ---- normalise and store: lane holds O[q][16db + 4g + i] ----
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float l = l_run[qb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = L[qb][0];
     const float inv = l > 0.f ? 1.0f / l : 0.0f;
     const int q = q0 + 16 * qb + (lane & 15);
     if (q < Lq) {
