@@ -71,7 +71,7 @@ template <> struct Aug<float> {
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 
 // Stages TC key rows (gathered by virtual index) and their augmentation rows
-// into LDS with direct-to-LDS loads.  256 threads; thread (w, lane) copies
+// into LDS with direct-to-LDS loads.  NT threads; thread (w, lane) copies
 // chunks (w * PASSW + i) * 64 + lane; wave 0 copies the augmentation rows
 // and records each row's index (-1 when absent) in sV when given.
 //
@@ -81,11 +81,11 @@ template <bool B> struct BoolTag { static constexpr bool value = B; };
 // one tile later.  raw(c) reads list position c (clamped by the caller);
 // fix(c, raw) returns the virtual row index of position c or -1.  Absent
 // rows copy row `fb` (any existing row).
-template <typename E, int D, int TC>
+template <typename E, int D, int TC, int NT = 256>
 struct DmaTile {
   using T = Tile<E, D>;
-  static constexpr int PASSW = TC * T::CPR / 256;
-  static_assert((TC * T::CPR) % 256 == 0 && TC == 64, "tile shape");
+  static constexpr int PASSW = TC * T::CPR / NT;
+  static_assert((TC * T::CPR) % NT == 0 && TC == 64, "tile shape");
   int vi[PASSW];
   int va;
   // Per-lane offsets are recomputed from an opaque lane id at each use: kept
@@ -185,16 +185,21 @@ hipError_t launch_norms(const void* keys, int et, int H, int rows, int d, float 
 
 // ---------------------------------------------------------------------------
 // gram row sums: out[i] = sum_{j in cols} phi(row_i, col_j).
-// Work-group: 4 waves x 64 rows (two 32-row blocks per wave, A operand in
-// registers); column tiles of 64 (two 32-column subtiles, B operand) staged
-// through LDS, double buffered.  Lane (h = lane>>5, n = lane&31) accumulates
-// rows 8(i>>2) + 4h + (i&3) of each block against column n; a final
-// butterfly over n sums the columns.
+// Work-group: 8 waves x 32 rows (A operand in registers, at most 128 VGPRs
+// so that four waves share each SIMD); column tiles of 64 (two 32-column
+// subtiles, B operand) staged through LDS, double buffered.  The two
+// subtiles' MFMA chains are independent, so the interactions of one overlap
+// the products of the other.  Lane (h = lane>>5, n = lane&31) accumulates
+// rows 8(i>>2) + 4h + (i&3) against column n; a final butterfly over n sums
+// the columns.
 // ---------------------------------------------------------------------------
+constexpr int GRAM_NT = 512;      // threads per work-group
+constexpr int GRAM_ROWS = 256;    // rows per work-group (32 per wave)
+
 template <typename E, int D, int MODE, bool SELF, bool CLIST, bool DIRECT>
-__global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows, VList cols, float* __restrict__ out,
-                                                   int64_t out_hstride, int64_t split_stride, PhiConst pc,
-                                                   uint64_t active) {
+__global__ __launch_bounds__(GRAM_NT, 4) void gram_kernel(KeySpace<E> ks, VList rows, VList cols,
+                                                         float* __restrict__ out, int64_t out_hstride,
+                                                         int64_t split_stride, PhiConst pc, uint64_t active) {
   using O = Ops<E>;
   using A = Aug<E>;
   using T = Tile<E, D>;
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows
   if (!head_on(active, h)) return;
   const HeadKeys<E, D> hk(ks, h);
   const int nrows = vlist_count(rows, h);
-  const int r0 = (lin % R) * 256;
+  const int r0 = (lin % R) * GRAM_ROWS;
   if (r0 >= nrows) return;
   const int ncols = vlist_count(cols, h);
   const int ntiles = (ncols + TC - 1) / TC;
@@ -226,34 +231,31 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows
 
   const int lane = lane_id(), w = wave_id();
   const int hh = lane >> 5, nn = lane & 31;
-  const int wrow = r0 + w * 64;
+  const int wrow = r0 + w * 32;
 
-  typename O::frag xf[2][NK];
-  typename O::frag xa[2];
-#pragma unroll
-  for (int xb = 0; xb < 2; ++xb) {
-    const int r = wrow + 32 * xb + nn;
+  typename O::frag xf[NK];
+  typename O::frag xa;
+  {
+    const int r = wrow + nn;
     int v = r < nrows ? vlist_at(rows, h, r) : -1;
     v = hk.ok(v) ? v : -1;
     const E* xp = hk.row(v >= 0 ? v : fb);
 #pragma unroll
-    for (int k = 0; k < NK; ++k) xf[xb][k] = v >= 0 ? O::load(xp + O::off32(k, lane)) : typename O::frag{};
+    for (int k = 0; k < NK; ++k) xf[k] = v >= 0 ? O::load(xp + O::off32(k, lane)) : typename O::frag{};
     if constexpr (DIRECT) {
       // x' = x * (-2/sigma^2) (exact): the MFMA then returns t itself
 #pragma unroll
-      for (int k = 0; k < NK; ++k) xf[xb][k] = A::scale(xf[xb][k], pc.c2);
-      xa[xb] = v >= 0 ? A::xfrag_direct(gload16(hk.aug(v)), lane, A::eps_parts(pc.eps)) : typename O::frag{};
+      for (int k = 0; k < NK; ++k) xf[k] = A::scale(xf[k], pc.c2);
+      xa = v >= 0 ? A::xfrag_direct(gload16(hk.aug(v)), lane, A::eps_parts(pc.eps)) : typename O::frag{};
     } else {
-      xa[xb] = v >= 0 ? A::xfrag(gload16(hk.aug(v)), lane) : typename O::frag{};
+      xa = v >= 0 ? A::xfrag(gload16(hk.aug(v)), lane) : typename O::frag{};
     }
   }
-  float acc[2][16];
+  float acc[16];
 #pragma unroll
-  for (int xb = 0; xb < 2; ++xb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[xb][i] = 0.0f;
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
 
-  DmaTile<E, D, TC> ld;
+  DmaTile<E, D, TC, GRAM_NT> ld;
   // list position c -> raw entry (a plain load for index lists, the position
   // itself for ranges) -> virtual row index (-1 past the end)
   const int32_t* cidx = CLIST ? cols.idx + (int64_t)h * cols.idx_hstride : nullptr;
@@ -262,10 +264,6 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows
     const int v = CLIST ? e + cols.add : cols.base + e;
     return (c < ncols && hk.ok(v)) ? v : -1;
   };
-  // one tile: prefetch the next tile into the other buffer set, then the
-  // MFMA products and interactions on this one.  The two buffer sets are
-  // distinct LDS objects, so the compiler can tell that the direct-to-LDS
-  // copy in flight does not alias the reads of the current tile.
   // PLAIN (direct form, every column of the tile present): t needs no clamp
   auto step = [&](auto plain_tag, int tile, const E* cY, const u32x4_t* cA, const int* cV, E* nY, u32x4_t* nA,
                   int* nV) {
@@ -275,51 +273,41 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows
       ld.issue(tile + 1, fix, hk, nY, nA, nV, fb);
       if (tile + 2 < t1) ld.index(tile + 2, raw);
     }
+    // both subtiles' products first (independent chains)
+    f32x16_t cc[2];
 #pragma unroll
-    for (int sub = 0; sub < TC / 32; ++sub) {
+    for (int sub = 0; sub < 2; ++sub) {
       const int rr = 32 * sub + nn;
-      const int yv = cV[rr];
-      const int cpos = tile * TC + 32 * sub;       // list position of this subtile's column 0
-      f32x16_t cc[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) { cc[0][i] = 0.0f; cc[1][i] = 0.0f; }
+      for (int i = 0; i < 16; ++i) cc[sub][i] = 0.0f;
 #pragma unroll
-      for (int k = 0; k < NK; ++k) {
-        const typename O::frag yk = O::load(cY + T::at(rr, O::off32(k, lane)));
-        cc[0] = O::mma32(xf[0][k], yk, cc[0]);
-        cc[1] = O::mma32(xf[1][k], yk, cc[1]);
-      }
-      {
-        const typename O::frag ya = A::yfrag(cA[rr], lane);
-        cc[0] = O::mma32(xa[0], ya, cc[0]);
-        cc[1] = O::mma32(xa[1], ya, cc[1]);
-      }
+      for (int k = 0; k < NK; ++k) cc[sub] = O::mma32(xf[k], O::load(cY + T::at(rr, O::off32(k, lane))), cc[sub]);
+      cc[sub] = O::mma32(xa, A::yfrag(cA[rr], lane), cc[sub]);
+    }
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int yv = cV[32 * sub + nn];
       // an absent column clamps t to +inf, where every phi mode but p = 0 is 0
       const float lo = opaque(yv >= 0 ? pc.eps : __builtin_inff());
+      // self-exclusion (rows and columns are the same list): a pair is its
+      // own partner exactly when the list positions coincide, which needs
+      // the subtile's column range to be the wave's row range
+      const bool diag = SELF && (tile * TC + 32 * sub) == wrow;
 #pragma unroll
-      for (int xb = 0; xb < 2; ++xb) {
-        const f32x16_t c = cc[xb];
-        // self-exclusion (rows and columns are the same list): a pair is its
-        // own partner exactly when the list positions coincide, which needs
-        // the subtile's column range to meet the block's row range
-        const int rpos = wrow + 32 * xb;
-        const bool diag = SELF && cpos == rpos;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float t;
-          if constexpr (DIRECT) {
-            t = PLAIN ? c[i] : fmaxf(c[i], lo);
-          } else {
-            t = __builtin_fmaf(c[i], pc.c2, pc.eps);
-            t = fmaxf(t, lo);
-          }
-          float f = phi_of_t<MODE>(t, pc.neg_half_p);
-          if constexpr (MODE == PHI_P0) f = yv >= 0 ? f : 0.0f;
-          if constexpr (SELF) {
-            if (diag) f = (nn == 8 * (i >> 2) + 4 * hh + (i & 3)) ? 0.0f : f;
-          }
-          acc[xb][i] += f;
+      for (int i = 0; i < 16; ++i) {
+        float t;
+        if constexpr (DIRECT) {
+          t = PLAIN ? cc[sub][i] : fmaxf(cc[sub][i], lo);
+        } else {
+          t = __builtin_fmaf(cc[sub][i], pc.c2, pc.eps);
+          t = fmaxf(t, lo);
         }
+        float f = phi_of_t<MODE>(t, pc.neg_half_p);
+        if constexpr (MODE == PHI_P0) f = yv >= 0 ? f : 0.0f;
+        if constexpr (SELF) {
+          if (diag) f = (nn == 8 * (i >> 2) + 4 * hh + (i & 3)) ? 0.0f : f;
+        }
+        acc[i] += f;
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // next tile resident in LDS
@@ -346,25 +334,21 @@ __global__ __launch_bounds__(256, 2) void gram_kernel(KeySpace<E> ks, VList rows
   }
   // sum over the 32 columns held by the half-wave
 #pragma unroll
-  for (int xb = 0; xb < 2; ++xb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float v = acc[xb][i];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 8);
-      v += __shfl_xor(v, 4);
-      v += __shfl_xor(v, 2);
-      v += __shfl_xor(v, 1);
-      acc[xb][i] = v;
-    }
+  for (int i = 0; i < 16; ++i) {
+    float v = acc[i];
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 8);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 1);
+    acc[i] = v;
+  }
   if (nn == 0) {
 #pragma unroll
-    for (int xb = 0; xb < 2; ++xb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = wrow + 32 * xb + 8 * (i >> 2) + 4 * hh + (i & 3);
-        if (r < nrows) out[(int64_t)h * out_hstride + (int64_t)zs * split_stride + r] = acc[xb][i];
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int r = wrow + 8 * (i >> 2) + 4 * hh + (i & 3);
+      if (r < nrows) out[(int64_t)h * out_hstride + (int64_t)zs * split_stride + r] = acc[i];
+    }
   }
 }
 
@@ -379,16 +363,16 @@ static void gram_dispatch_self(const GramLaunch& g, dim3 grid, hipStream_t st) {
   const KeySpace<E> ks = key_space<E>(g.k);
   // self-exclusion only arises with both sides the same index list
   if (g.self_excl && g.cols.idx)
-    hipLaunchKernelGGL((gram_kernel<E, D, MODE, true, true, DIRECT>), grid, dim3(256), 0, st, ks, g.rows, g.cols,
+    hipLaunchKernelGGL((gram_kernel<E, D, MODE, true, true, DIRECT>), grid, dim3(GRAM_NT), 0, st, ks, g.rows, g.cols,
                        g.out, g.out_hstride, g.split_stride, g.pc, g.active);
   else if (g.self_excl)
-    hipLaunchKernelGGL((gram_kernel<E, D, MODE, true, false, DIRECT>), grid, dim3(256), 0, st, ks, g.rows, g.cols,
+    hipLaunchKernelGGL((gram_kernel<E, D, MODE, true, false, DIRECT>), grid, dim3(GRAM_NT), 0, st, ks, g.rows, g.cols,
                        g.out, g.out_hstride, g.split_stride, g.pc, g.active);
   else if (g.cols.idx)
-    hipLaunchKernelGGL((gram_kernel<E, D, MODE, false, true, DIRECT>), grid, dim3(256), 0, st, ks, g.rows, g.cols,
+    hipLaunchKernelGGL((gram_kernel<E, D, MODE, false, true, DIRECT>), grid, dim3(GRAM_NT), 0, st, ks, g.rows, g.cols,
                        g.out, g.out_hstride, g.split_stride, g.pc, g.active);
   else
-    hipLaunchKernelGGL((gram_kernel<E, D, MODE, false, false, DIRECT>), grid, dim3(256), 0, st, ks, g.rows, g.cols,
+    hipLaunchKernelGGL((gram_kernel<E, D, MODE, false, false, DIRECT>), grid, dim3(GRAM_NT), 0, st, ks, g.rows, g.cols,
                        g.out, g.out_hstride, g.split_stride, g.pc, g.active);
 }
 
@@ -410,7 +394,8 @@ static void gram_dispatch_mode(const GramLaunch& g, dim3 grid, hipStream_t st) {
 
 hipError_t launch_gram(const GramLaunch& g, hipStream_t st) {
   if (g.rows.n <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((g.rows.n + 255) / 256), (unsigned)g.k.H, (unsigned)(g.splits > 0 ? g.splits : 1));
+  const dim3 grid((unsigned)((g.rows.n + GRAM_ROWS - 1) / GRAM_ROWS), (unsigned)g.k.H,
+                  (unsigned)(g.splits > 0 ? g.splits : 1));
   if (g.k.et == ET_BF16) {
     if (g.k.d == 128) gram_dispatch_mode<uint16_t, 128>(g, grid, st);
     else gram_dispatch_mode<uint16_t, 64>(g, grid, st);
@@ -446,14 +431,14 @@ hipError_t launch_sum_splits(const float* src, int64_t src_hstride, int64_t spli
 //   S_b(k) = rho_b + sum_{j<k} phi(b, c_{order[j]}).
 // The candidate axis is cut into 32-candidate subtiles; a 32x32 MFMA tile
 // (A = candidates from LDS, B = bank rows in registers, plus the norm
-// augmentation step) gives lane l the 16 values of bank row (l & 31) for
-// candidates 8q + 4h + r (q = 0..3, h = l >> 5, r = 0..3), i.e. eight groups
-// of four in candidate order, alternating between the lane and its partner
-// l ^ 32.  The canonical running sum inside a subtile is
-//   carry + (E_G + P_G(r)),  E_0 = 0, E_{G+1} = E_G + T_G,
-// with T_G and P_G the sequential sums of group G; the carry advances by E_8.
-// This value is monotone in k, identical in the scan and the sum pass, and
-// its subtile-boundary values are what the checkpoints store.
+// augmentation step) gives lane l the 16 values of bank row (l & 31).  The
+// candidates are placed in LDS so that lane half h = l >> 5 holds positions
+// 16h .. 16h + 15 of the subtile in order.  The canonical running sum is
+//   first half:  carry + P0(i),      second half:  (carry + tot0) + P1(i),
+// with P the sequential sums inside a half and tot0, tot1 the half totals
+// (exchanged between the two lanes of a row); the carry advances to
+// (carry + tot0) + tot1.  This value is monotone in k, identical in the scan
+// and the sum pass, and its subtile-boundary values are the checkpoints.
 //
 // scan pass: t_b = smallest k with S_b(k) > tau * rho0_b (kmax+1 if none).
 // sum pass:  rhoP_b = S_b(k*) starting from the nearest checkpoint.
@@ -538,8 +523,17 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
   DmaTile<E, D, TC> ld;
   // position j of the order -> raw entry -> virtual row index (-1 past kmax)
   const int32_t* ord = order + (int64_t)h * ks.N;
-  auto raw = [&](int j) -> int { return ord[min(j, kmax - 1)]; };
-  auto fix = [&](int j, int e) -> int { return (j < kmax && (unsigned)e < (unsigned)ks.N) ? M + e : -1; };
+  // LDS row r of a stage (subtile r / 32, MFMA row rho = r % 32 = 8q + 4h + r')
+  // holds order position 32 (r / 32) + 16 h + 4 q + r': the MFMA output then
+  // gives lane half h the 16 consecutive positions 16 h .. 16 h + 15
+  auto pos_of = [](int c) -> int {
+    const int rho = c & 31;
+    return (c & ~31) + 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3);
+  };
+  auto raw = [&](int c) -> int { return ord[min(pos_of(c), kmax - 1)]; };
+  auto fix = [&](int c, int e) -> int {
+    return (pos_of(c) < kmax && (unsigned)e < (unsigned)ks.N) ? M + e : -1;
+  };
   // candidates are always present in a stage's used positions; rows past
   // kmax copy a fallback row and are masked below
   const int fb = M;                      // candidate 0 (N > 0 whenever kmax > 0)
@@ -574,9 +568,15 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
         const int cr = 32 * half + (lane & 31);
+        // all fragment reads first, so their LDS latency overlaps
+        typename O::frag af[NK];
 #pragma unroll
-        for (int k = 0; k < NK; ++k) acc = O::mma32(O::load(cC + T::at(cr, O::off32(k, lane))), bf[k], acc);
-        acc = O::mma32(A::yfrag(cA[cr], lane), ba, acc);
+        for (int k = 0; k < NK; ++k) af[k] = O::load(cC + T::at(cr, O::off32(k, lane)));
+        const typename O::frag aa = A::yfrag(cA[cr], lane);
+#pragma unroll
+        for (int k = 0; k < NK; ++k) acc = O::mma32(af[k], bf[k], acc);
+        acc = O::mma32(aa, ba, acc);
+        // lane (row b, half hh) holds candidates pos0 + 16 hh + i, i = 0..15
         float v[16];
         const int pos0 = 32 * sub;
 #pragma unroll
@@ -592,69 +592,53 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
         }
         if (pos0 + 32 > kmax) {   // last subtile: drop positions past kmax
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int m = 8 * (i >> 2) + 4 * hh + (i & 3);
-            v[i] = (pos0 + m < kmax) ? v[i] : 0.0f;
-          }
+          for (int i = 0; i < 16; ++i) v[i] = (pos0 + 16 * hh + i < kmax) ? v[i] : 0.0f;
         }
-        float T[4];
+        // sequential half sums, exchanged between the two lanes of a row:
+        // after the swap every lane holds tot0 (first half) and tot1
+        float tot = v[0];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) T[q] = ((v[4 * q] + v[4 * q + 1]) + v[4 * q + 2]) + v[4 * q + 3];
-        float Tp[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) Tp[q] = __shfl_xor(T[q], 32);
-        float Eg[9];
-        Eg[0] = 0.0f;
-#pragma unroll
-        for (int G = 0; G < 8; ++G) {
-          const float tg = ((G & 1) == hh) ? T[G >> 1] : Tp[G >> 1];
-          Eg[G + 1] = Eg[G] + tg;
-        }
+        for (int i = 1; i < 16; ++i) tot += v[i];
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tot), __float_as_uint(tot), false, false);
+        const float tot0 = __uint_as_float(sw[0]), tot1 = __uint_as_float(sw[1]);
+        const float mid = carry + tot0;             // S at the end of the first half
+        const float s_end = mid + tot1;
+        const float base = hh ? mid : carry;        // S before this lane's first candidate
         if constexpr (!SUM) {
-          const float s_end = carry + Eg[8];
           const bool cross = !done && (s_end > thr);
           // rows cross once; the exact position search runs only in waves where
           // some row crosses in this subtile (both lanes of a row agree)
           if (__any(cross)) {
+            int first = 64;
             if (cross) {
-              int first = 1 << 30;
+              float P = 0.0f;
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                float P = 0.0f;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                  P = (r == 0) ? v[4 * q] : P + v[4 * q + r];
-                  const float S = carry + (Eg[2 * q + hh] + P);
-                  const int m = 8 * q + 4 * hh + r;
-                  if (S > thr && m < first) first = m;
-                }
+              for (int i = 0; i < 16; ++i) {
+                P = (i == 0) ? v[0] : P + v[i];
+                if (base + P > thr && first == 64) first = 16 * hh + i;
               }
-              const int other = __shfl_xor(first, 32);
-              first = min(first, other);
-              t_b = pos0 + first + 1;
             }
+            const auto fs = __builtin_amdgcn_permlane32_swap((unsigned)first, (unsigned)first, false, false);
+            first = min((int)fs[0], (int)fs[1]);
+            if (cross) t_b = pos0 + first + 1;
           }
           if (!done) carry = s_end;
           done = done || cross;
         } else {
           if (sub < sub_end - 1) {
-            carry = carry + Eg[8];
+            carry = s_end;
           } else {
-            const int j = (kst - 1) - pos0;         // element index inside the subtile
-            const int q = j >> 3, jh = (j >> 2) & 1, r = j & 3;
-            float P = 0.0f;
+            const int j = (kst - 1) - pos0;         // position of the last admitted candidate
+            const int jh = j >> 4, jj = j & 15;
+            float P = 0.0f, PP = 0.0f;
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-              float PP = 0.0f;
-#pragma unroll
-              for (int rr = 0; rr < 4; ++rr) {
-                PP = (rr == 0) ? v[4 * qq] : PP + v[4 * qq + rr];
-                if (qq == q && rr == r) P = PP;
-              }
+            for (int i = 0; i < 16; ++i) {
+              PP = (i == 0) ? v[0] : PP + v[i];
+              if (i == jj) P = PP;
             }
-            const float S = carry + (Eg[2 * q + jh] + P);
-            const float So = __shfl_xor(S, 32);
-            carry = (hh == jh) ? S : So;
+            const float S = base + P;               // meaningful in the lanes with hh == jh
+            const auto ss = __builtin_amdgcn_permlane32_swap(__float_as_uint(S), __float_as_uint(S), false, false);
+            carry = __uint_as_float(jh ? ss[1] : ss[0]);
           }
         }
       }
@@ -662,8 +646,11 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
     __builtin_amdgcn_s_waitcnt(0x0F70);   // next stage resident in LDS
     if constexpr (!SUM) {
       // every row of the work-group crossed: later checkpoints are never
-      // read (the sum pass skips rows with t_b <= k*)
-      return __syncthreads_or(!done) != 0;
+      // read (the sum pass skips rows with t_b <= k*); checked every fourth
+      // stage to keep one plain barrier per stage
+      if ((stg & 3) == 3) return __syncthreads_or(!done) != 0;
+      __syncthreads();
+      return true;
     } else {
       __syncthreads();
       return true;
