@@ -266,8 +266,7 @@ int kvbank_score(const kvb_layer_desc* L, const kvb_bank* bank, const void* cand
     float* nC = at<float>(ws, lo.normC);
     void* aB = at<void>(ws, lo.augB);
     void* aC = at<void>(ws, lo.augC);
-    HIPCHK(launch_norms(bank->K, et, H, M, d, pc.inv_s2, et == ET_BF16 && pc.direct, nB, aB, st));
-    HIPCHK(launch_norms(cand_k, et, H, N, d, pc.inv_s2, et == ET_BF16 && pc.direct, nC, aC, st));
+    HIPCHK(launch_norms(bank->K, M, nB, aB, cand_k, N, nC, aC, et, H, d, pc.inv_s2, et == ET_BF16 && pc.direct, st));
     GramLaunch g{};
     g.k = KeysDesc{bank->K, cand_k, nB, nC, aB, aC, M, N, d, H, et};
     g.rows = VList{nullptr, nullptr, 0, 0, 0, M, N, 0};
@@ -366,17 +365,21 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
   hipStream_t st = (hipStream_t)stream;
   const PhiConst pc = phi_const(L->params);
   const int pm = phi_mode_of(L->params.p);
-  HIPCHK(launch_fill_i32(out->n_mandatory, H, 0, st));
-  HIPCHK(launch_fill_i32(out->n_evicted, H, 0, st));
-  HIPCHK(launch_fill_i32(out->k_star, 1, 0, st));
+  {
+    // outputs, and the crossing-time histogram when the density path runs
+    const bool dens_run = hd.dens && N > 0;
+    int32_t* zp[4] = {out->n_mandatory, out->n_evicted, out->k_star,
+                      dens_run ? at<int32_t>(ws, lo.hist) : nullptr};
+    const int64_t zn[4] = {H, H, 1, (int64_t)H * (lo.kmax + 2)};
+    HIPCHK(launch_zero_i32(zp, zn, 4, st));
+  }
   if (hd.dens && N > 0) {
     const int kmax = lo.kmax;
     float* nB = at<float>(ws, lo.normB);
     float* nC = at<float>(ws, lo.normC);
     void* aB = at<void>(ws, lo.augB);
     void* aC = at<void>(ws, lo.augC);
-    HIPCHK(launch_norms(bank->K, et, H, M, d, pc.inv_s2, et == ET_BF16 && pc.direct, nB, aB, st));
-    HIPCHK(launch_norms(cand_k, et, H, N, d, pc.inv_s2, et == ET_BF16 && pc.direct, nC, aC, st));
+    HIPCHK(launch_norms(bank->K, M, nB, aB, cand_k, N, nC, aC, et, H, d, pc.inv_s2, et == ET_BF16 && pc.direct, st));
     const KeysDesc kd{bank->K, cand_k, nB, nC, aB, aC, M, N, d, H, et};
     ScanLaunch s{};
     s.k = kd; s.rho = bank->rho; s.rho0 = bank->rho0; s.count = bank->count; s.order = order;

@@ -121,12 +121,21 @@ struct DmaTile {
 // squared norms: one group of CPR lanes per row, 16-byte chunks
 // ---------------------------------------------------------------------------
 template <typename E, int CPR>
-__global__ __launch_bounds__(256) void norms_kernel(const E* __restrict__ keys, int64_t nrows, int d, float scale,
-                                                    int direct, float* __restrict__ out, u32x4_t* __restrict__ aug) {
+__global__ __launch_bounds__(256) void norms_kernel(const E* __restrict__ keysA, int64_t nA, float* __restrict__ outA,
+                                                    u32x4_t* __restrict__ augA, const E* __restrict__ keysB,
+                                                    int64_t nB, float* __restrict__ outB, u32x4_t* __restrict__ augB,
+                                                    int d, float scale, int direct) {
   constexpr int EPC = 16 / sizeof(E);
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = gid / CPR;
+  int64_t row = gid / CPR;
   const int c = (int)(gid % CPR);
+  // rows [0, nA) from the first key set, then [nA, nA + nB) from the second
+  const bool first = row < nA;
+  const E* keys = first ? keysA : keysB;
+  float* out = first ? outA : outB;
+  u32x4_t* aug = first ? augA : augB;
+  if (!first) row -= nA;
+  const int64_t nrows = first ? nA : nB;
   float s = 0.0f;
   if (row < nrows) {
     const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(keys + row * d + c * EPC);
@@ -165,23 +174,35 @@ __global__ __launch_bounds__(256) void norms_kernel(const E* __restrict__ keys, 
   }
 }
 
-hipError_t launch_norms(const void* keys, int et, int H, int rows, int d, float scale, bool direct, float* out,
-                        void* aug, hipStream_t st) {
-  const int64_t nrows = (int64_t)H * rows;
-  if (nrows == 0) return hipSuccess;
+hipError_t launch_norms(const void* keysA, int rowsA, float* outA, void* augA, const void* keysB, int rowsB,
+                        float* outB, void* augB, int et, int H, int d, float scale, bool direct, hipStream_t st) {
+  const int64_t nA = keysA ? (int64_t)H * rowsA : 0, nB = keysB ? (int64_t)H * rowsB : 0;
+  if (nA + nB == 0) return hipSuccess;
   const int esz = et == ET_BF16 ? 2 : 4;
   const int cpr = d * esz / 16;
-  const dim3 grid((unsigned)((nrows * cpr + 255) / 256));
-  u32x4_t* a = (u32x4_t*)aug;
+  const dim3 grid((unsigned)(((nA + nB) * cpr + 255) / 256));
   if (et == ET_BF16) {
-    if (cpr == 8) hipLaunchKernelGGL((norms_kernel<uint16_t, 8>), grid, dim3(256), 0, st, (const uint16_t*)keys, nrows, d, scale, (int)direct, out, a);
-    else hipLaunchKernelGGL((norms_kernel<uint16_t, 16>), grid, dim3(256), 0, st, (const uint16_t*)keys, nrows, d, scale, (int)direct, out, a);
+    const uint16_t* a = (const uint16_t*)keysA;
+    const uint16_t* b = (const uint16_t*)keysB;
+    if (cpr == 8)
+      hipLaunchKernelGGL((norms_kernel<uint16_t, 8>), grid, dim3(256), 0, st, a, nA, outA, (u32x4_t*)augA, b, nB, outB,
+                         (u32x4_t*)augB, d, scale, (int)direct);
+    else
+      hipLaunchKernelGGL((norms_kernel<uint16_t, 16>), grid, dim3(256), 0, st, a, nA, outA, (u32x4_t*)augA, b, nB, outB,
+                         (u32x4_t*)augB, d, scale, (int)direct);
   } else {
-    if (cpr == 16) hipLaunchKernelGGL((norms_kernel<float, 16>), grid, dim3(256), 0, st, (const float*)keys, nrows, d, scale, 0, out, a);
-    else hipLaunchKernelGGL((norms_kernel<float, 32>), grid, dim3(256), 0, st, (const float*)keys, nrows, d, scale, 0, out, a);
+    const float* a = (const float*)keysA;
+    const float* b = (const float*)keysB;
+    if (cpr == 16)
+      hipLaunchKernelGGL((norms_kernel<float, 16>), grid, dim3(256), 0, st, a, nA, outA, (u32x4_t*)augA, b, nB, outB,
+                         (u32x4_t*)augB, d, scale, 0);
+    else
+      hipLaunchKernelGGL((norms_kernel<float, 32>), grid, dim3(256), 0, st, a, nA, outA, (u32x4_t*)augA, b, nB, outB,
+                         (u32x4_t*)augB, d, scale, 0);
   }
   return hipGetLastError();
 }
+
 
 // ---------------------------------------------------------------------------
 // gram row sums: out[i] = sum_{j in cols} phi(row_i, col_j).

@@ -20,9 +20,10 @@ struct KeysDesc {            // one layer's keys in two buffers (see KeySpace)
 };
 
 // out[r] = |k_r|^2 * scale and aug[r] = the augmentation row of key r (exact
-// split of |k_r|^2, or of |k_r|^2 * scale in the direct form), rows [H][rows][d]
-hipError_t launch_norms(const void* keys, int et, int H, int rows, int d, float scale, bool direct, float* out,
-                        void* aug, hipStream_t s);
+// split of |k_r|^2, or of |k_r|^2 * scale in the direct form), for two key
+// sets [H][rowsA][d] and [H][rowsB][d] in one launch (a null set is skipped)
+hipError_t launch_norms(const void* keysA, int rowsA, float* outA, void* augA, const void* keysB, int rowsB,
+                        float* outB, void* augB, int et, int H, int d, float scale, bool direct, hipStream_t s);
 
 // out[h*out_hstride + split*split_stride + i] = sum_{j in cols} phi(row_i, col_j)
 struct GramLaunch {
@@ -65,6 +66,8 @@ hipError_t launch_scan(const ScanLaunch& a, bool sum_mode, hipStream_t s);
 
 // ---- selection / bookkeeping ----------------------------------------------
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+// zero count (<= 4) int32 arrays of the given lengths in one launch (null entries skipped)
+hipError_t launch_zero_i32(int32_t* const* ptrs, const int64_t* lens, int count, hipStream_t s);
 
 // keys for sorting: key = float_key(score[h][i]) << 32 | tie[i]; value = i
 hipError_t launch_sort(const float* score, int64_t score_hstride, const int32_t* tie, int64_t tie_hstride,

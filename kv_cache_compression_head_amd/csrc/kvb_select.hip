@@ -28,31 +28,60 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
   return hipGetLastError();
 }
 
+// up to four int32 arrays zeroed by one launch
+struct ZeroSet {
+  int32_t* p[4];
+  int64_t n[4];
+};
+__global__ void zero_i32x4_kernel(ZeroSet z) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (i < z.n[k]) { z.p[k][i] = 0; return; }
+    i -= z.n[k];
+  }
+}
+
+hipError_t launch_zero_i32(int32_t* const* ptrs, const int64_t* lens, int count, hipStream_t st) {
+  ZeroSet z{};
+  int64_t tot = 0;
+  for (int k = 0; k < 4; ++k) {
+    z.p[k] = k < count ? ptrs[k] : nullptr;
+    z.n[k] = (k < count && ptrs[k]) ? lens[k] : 0;
+    tot += z.n[k];
+  }
+  if (tot <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_i32x4_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, z);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // mean-normalised disturbance: delta = D / mean_c D (0 if bank empty or mean 0)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void delta_kernel(const float* __restrict__ D, const int32_t* __restrict__ count,
-                                                    uint64_t on, int n, float* __restrict__ delta) {
+__global__ __launch_bounds__(1024) void delta_kernel(const float* __restrict__ D, const int32_t* __restrict__ count,
+                                                     uint64_t on, int n, float* __restrict__ delta) {
   const int h = blockIdx.x;
   if (!head_on(on, h)) return;
-  __shared__ float red[256];
+  __shared__ float red[16];
+  const float* Dh = D + (int64_t)h * n;
+  // fixed-order partial sums: thread i adds elements i, i + 1024, ...
   float s = 0.0f;
-  for (int i = threadIdx.x; i < n; i += 256) s += D[(int64_t)h * n + i];
-  red[threadIdx.x] = s;
+  for (int i = threadIdx.x; i < n; i += 1024) s += Dh[i];
+  s = wave_sum(s);
+  if (lane_id() == 0) red[wave_id()] = s;
   __syncthreads();
-  for (int o = 128; o >= 1; o >>= 1) {
-    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
-    __syncthreads();
-  }
-  const float mean = red[0] / (float)n;
+  float tot = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) tot += red[k];
+  const float mean = tot / (float)n;
   const bool zero = count[h] <= 0 || !(mean > 0.0f);
-  for (int i = threadIdx.x; i < n; i += 256) delta[(int64_t)h * n + i] = zero ? 0.0f : D[(int64_t)h * n + i] / mean;
+  for (int i = threadIdx.x; i < n; i += 1024) delta[(int64_t)h * n + i] = zero ? 0.0f : Dh[i] / mean;
 }
 
 hipError_t launch_delta(const float* D, const int32_t* count, uint64_t on, int H, int n, float* delta,
                         hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(delta_kernel, dim3(H), dim3(256), 0, st, D, count, on, n, delta);
+  hipLaunchKernelGGL(delta_kernel, dim3(H), dim3(1024), 0, st, D, count, on, n, delta);
   return hipGetLastError();
 }
 
@@ -70,7 +99,7 @@ KVB_DEV uint64_t sort_key(const float* score, const int32_t* tie, int64_t tie_hs
   return ((uint64_t)hi << 32) | lo;
 }
 
-__global__ __launch_bounds__(256) void block_sort_kernel(const float* __restrict__ score, int64_t score_hstride,
+__global__ __launch_bounds__(1024) void block_sort_kernel(const float* __restrict__ score, int64_t score_hstride,
                                                          const int32_t* __restrict__ tie, int64_t tie_hstride,
                                                          uint64_t on, int n,
                                                          uint64_t* __restrict__ kout, int32_t* __restrict__ vout,
@@ -80,7 +109,7 @@ __global__ __launch_bounds__(256) void block_sort_kernel(const float* __restrict
   __shared__ uint64_t sk[SORT_BS];
   __shared__ int32_t sv[SORT_BS];
   const int base = blockIdx.x * SORT_BS;
-  for (int i = threadIdx.x; i < SORT_BS; i += 256) {
+  for (int i = threadIdx.x; i < SORT_BS; i += 1024) {
     const int g = base + i;
     if (g < n) {
       sk[i] = sort_key(score, tie, tie_hstride, h, g, score_hstride);
@@ -91,22 +120,22 @@ __global__ __launch_bounds__(256) void block_sort_kernel(const float* __restrict
     }
   }
   __syncthreads();
+  // bitonic network: one compare-exchange per thread and step
+  const int p = threadIdx.x;
   for (int k = 2; k <= SORT_BS; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int p = threadIdx.x; p < SORT_BS / 2; p += 256) {
-        const int i = (p / j) * 2 * j + (p % j);
-        const int l = i + j;
-        const bool up = ((i & k) == 0);
-        const uint64_t a = sk[i], b = sk[l];
-        if ((a > b) == up) {
-          sk[i] = b; sk[l] = a;
-          const int32_t t = sv[i]; sv[i] = sv[l]; sv[l] = t;
-        }
+      const int i = (p / j) * 2 * j + (p % j);
+      const int l = i + j;
+      const bool up = ((i & k) == 0);
+      const uint64_t a = sk[i], b = sk[l];
+      if ((a > b) == up) {
+        sk[i] = b; sk[l] = a;
+        const int32_t t = sv[i]; sv[i] = sv[l]; sv[l] = t;
       }
       __syncthreads();
     }
   }
-  for (int i = threadIdx.x; i < SORT_BS; i += 256) {
+  for (int i = threadIdx.x; i < SORT_BS; i += 1024) {
     const int g = base + i;
     if (g < n) {
       if (final_out) final_out[(int64_t)h * final_hstride + g] = sv[i];
@@ -154,7 +183,7 @@ hipError_t launch_sort(const float* score, int64_t score_hstride, const int32_t*
   if (n <= 0) return hipSuccess;
   const int nb = (n + SORT_BS - 1) / SORT_BS;
   const bool single = nb == 1;
-  hipLaunchKernelGGL(block_sort_kernel, dim3(nb, H), dim3(256), 0, st, score, score_hstride, tie, tie_hstride, on,
+  hipLaunchKernelGGL(block_sort_kernel, dim3(nb, H), dim3(SORT_BS / 2), 0, st, score, score_hstride, tie, tie_hstride, on,
                      n, k0, v0, single ? out : nullptr, out_hstride);
   if (single) return hipGetLastError();
   uint64_t* ka = k0; uint64_t* kb = k1;
@@ -189,23 +218,28 @@ __global__ __launch_bounds__(1024) void cumsum_kernel(int32_t* __restrict__ hist
                                                       int len) {
   const int h = blockIdx.x;
   if (!head_on(active, h)) return;
-  __shared__ int32_t s[1024];
-  int32_t carry = 0;
+  __shared__ int32_t ws[16];
   int32_t* p = hist + (int64_t)h * len;
-  for (int base = 0; base < len; base += 1024) {
-    const int i = base + threadIdx.x;
-    int32_t v = i < len ? p[i] : 0;
-    s[threadIdx.x] = v;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {
-      const int32_t add = (int)threadIdx.x >= o ? s[threadIdx.x - o] : 0;
-      __syncthreads();
-      s[threadIdx.x] += add;
-      __syncthreads();
-    }
-    if (i < len) p[i] = s[threadIdx.x] + carry;
-    carry += s[1023];
-    __syncthreads();
+  // thread t scans the contiguous chunk [t * per, (t + 1) * per)
+  const int per = (len + 1023) / 1024;
+  const int b0 = min(len, (int)threadIdx.x * per), b1 = min(len, b0 + per);
+  int32_t s = 0;
+  for (int i = b0; i < b1; ++i) s += p[i];
+  // exclusive prefix of the chunk sums: wave scan, then across waves
+  int32_t inc = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t v = __shfl_up(inc, o);
+    if (lane_id() >= o) inc += v;
+  }
+  if (lane_id() == 63) ws[wave_id()] = inc;
+  __syncthreads();
+  int32_t off = 0;
+  for (int k = 0; k < wave_id(); ++k) off += ws[k];
+  int32_t run = off + inc - s;
+  for (int i = b0; i < b1; ++i) {
+    run += p[i];
+    p[i] = run;
   }
 }
 
@@ -225,10 +259,8 @@ __global__ void feasible_kernel(const int32_t* __restrict__ cum, const int32_t* 
   if (ok) atomicMax(kstar, k);
 }
 
+// expects hist and kstar zeroed by the caller
 hipError_t launch_kstar(const SelectLaunch& a, hipStream_t st) {
-  hipError_t e;
-  if ((e = launch_fill_i32(a.hist, (int64_t)a.H * (a.kmax + 2), 0, st)) != hipSuccess) return e;
-  if ((e = launch_fill_i32(a.kstar, 1, 0, st)) != hipSuccess) return e;
   if (a.M > 0)
     hipLaunchKernelGGL(hist_kernel, dim3((a.M + 255) / 256, a.H), dim3(256), 0, st, a.t, a.count, a.active, a.M,
                        a.kmax, a.hist);
@@ -278,8 +310,11 @@ __global__ __launch_bounds__(1024) void evict_kernel(SelectLaunch a) {
   }
   if (tid == 0) s_rem = r;
   __syncthreads();
-  // radix select of the r-th largest key among non-crossed states
-  if (r > 0) {
+  // radix select of the r-th largest key among non-crossed states; none to
+  // pick (r = 0) or all of them (r = n - nm) need no select
+  if (r > 0 && r < n - nm) {
+    __shared__ int wsc[4];
+    __shared__ int s_sel;
     for (int pass = 0; pass < 8; ++pass) {
       const int shift = 56 - 8 * pass;
       for (int i = tid; i < 256; i += 1024) hist[i] = 0;
@@ -291,22 +326,39 @@ __global__ __launch_bounds__(1024) void evict_kernel(SelectLaunch a) {
         if ((key & msk) == pre) atomicAdd(&hist[(key >> shift) & 0xFF], 1);
       }
       __syncthreads();
-      if (tid == 0) {
-        int rem = s_rem;
-        int dsel = 0;
-        for (int dgt = 255; dgt >= 0; --dgt) {
-          const int c = hist[dgt];
-          if (c >= rem) { dsel = dgt; break; }
-          rem -= c;
+      // suffix counts S(d) = #keys with digit >= d: thread t < 256 takes digit
+      // 255 - t and scans in t; the selected digit has S(d) >= rem > S(d+1)
+      const int rem = s_rem;
+      const int d = 255 - tid;
+      int c = 0, inc = 0;
+      if (tid < 256) {
+        c = hist[d];
+        inc = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int v = __shfl_up(inc, o);
+          if (lane >= o) inc += v;
         }
-        s_rem = rem;
-        s_prefix = pre | ((uint64_t)dsel << shift);
+        if (lane == 63) wsc[w] = inc;
+      }
+      __syncthreads();
+      if (tid < 256) {
+        int off = 0;
+        for (int k = 0; k < w; ++k) off += wsc[k];
+        const int S = off + inc;
+        if (S >= rem && S - c < rem) { s_sel = d; s_rem = rem - (S - c); }
+      }
+      __syncthreads();
+      if (tid == 0) {
+        s_prefix = pre | ((uint64_t)s_sel << shift);
         s_mask = msk | (0xFFull << shift);
       }
       __syncthreads();
     }
   }
-  const uint64_t thr = s_prefix;
+  // keys >= thr are evicted among the non-crossed states (all of them when
+  // r covers every such state)
+  const uint64_t thr = (r >= n - nm) ? 0ull : s_prefix;
   // admitted states' densities: sum over the survivors directly when they are
   // fewer than the evicted states, else D(c) minus the evicted interactions
   const bool direct = (n - e) < e;
