@@ -578,25 +578,26 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
     }
     const bool wave_busy = __any(!done);
     if (wave_busy) {
-#pragma unroll 1
+      // both subtiles' products first (independent MFMA chains), then the
+      // interactions and prefix sums of each in order
+      f32x16_t accs[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int cr = 32 * half + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) accs[half][i] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NK; ++k) accs[half] = O::mma32(O::load(cC + T::at(cr, O::off32(k, lane))), bf[k], accs[half]);
+        accs[half] = O::mma32(A::yfrag(cA[cr], lane), ba, accs[half]);
+      }
+#pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int sub = 2 * stg + half;
         if (sub < sub_begin || sub >= sub_end) continue;
         if constexpr (!SUM) {
           if (sub % cps == 0 && sub > 0 && valid) cp[((int64_t)h * ncp + sub / cps) * M + b] = carry;
         }
-        f32x16_t acc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-        const int cr = 32 * half + (lane & 31);
-        // all fragment reads first, so their LDS latency overlaps
-        typename O::frag af[NK];
-#pragma unroll
-        for (int k = 0; k < NK; ++k) af[k] = O::load(cC + T::at(cr, O::off32(k, lane)));
-        const typename O::frag aa = A::yfrag(cA[cr], lane);
-#pragma unroll
-        for (int k = 0; k < NK; ++k) acc = O::mma32(af[k], bf[k], acc);
-        acc = O::mma32(aa, ba, acc);
+        const f32x16_t acc = accs[half];
         // lane (row b, half hh) holds candidates pos0 + 16 hh + i, i = 0..15
         float v[16];
         const int pos0 = 32 * sub;
