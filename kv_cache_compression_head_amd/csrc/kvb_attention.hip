@@ -204,6 +204,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
     if (more) fetch(kbase + ATT_TK, sKn);
 
     // ---- S^T = K Q^T ----
+    // MFMA issue at raised wave priority: the SIMD's other wave, between its
+    // own products, then gets the vector ALU for its softmax
+    __builtin_amdgcn_s_setprio(1);
     f32x4_t s[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -216,6 +219,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
         s[kb][1] = Op::mma16(a, qf[1][k], s[kb][1]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // ---- online softmax (log2 domain), lane owns query 16qb + (lane & 15) ----
     if (kbase + ATT_TK > Lkv) {
 #pragma unroll
