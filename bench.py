@@ -188,12 +188,85 @@ def cpu_baseline(name: str, seed: int = 0, heads=(0,)):
     return dt, threads, info.kstar
 
 
+def rollout_bench(steps: int, warmup_chunks: int):
+    """Streaming rollout timing: every chunk runs score + update + attention
+    for each of the 30 layers (480P, M = 9,360, 3 departing frames per
+    chunk).  One seeded layer stream supplies the inputs of all layers (each
+    layer keeps its own bank), so the inputs of a chunk are generated once;
+    the banks are first streamed through warmup_chunks chunks to reach the
+    steady state.  Returns (ms per chunk over all layers, details)."""
+    import numpy as np
+    import torch
+    import kv_cache_compression_head_amd as kb
+    from kv_cache_compression_head_amd.pipeline import LayerCache
+    from kv_cache_compression_head_amd.rollout import plan
+    from kvsynth import WORKLOADS, LayerGen, frame_tokens
+
+    wl = WORKLOADS["rollout"]
+    gen = LayerGen(wl, 0, 0)
+    kdt = torch.bfloat16
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(kdt).contiguous()
+
+    def chunk_inputs(c):
+        p = plan(c, wl.chunk_frames, wl.window_frames)
+        rt = lambda fr: [f - p.rope_base for f in fr]
+        x = {"N": len(p.departed) * wl.F}
+        if len(p.departed):
+            x["cK"], x["cV"] = dev(gen.keys_all(p.departed)), dev(gen.values_all(p.departed))
+            x["cT"] = torch.from_numpy(frame_tokens(wl, p.departed.start, p.departed.stop).astype(np.int32)).cuda()
+        lay = kb.KVLayout()
+        keep = []
+        if c > 0:
+            sk, sv = dev(gen.keys_all([0])), dev(gen.values_all([0]))
+            keep += [sk, sv]
+            lay.sink_k, lay.sink_v = sk, sv
+        if len(p.window):
+            wk, wv = dev(gen.keys_all(p.window, rt(p.window))), dev(gen.values_all(p.window))
+            keep += [wk, wv]
+            lay.win_k, lay.win_v, lay.win_start, lay.win_len = wk, wv, 0, len(p.window) * wl.F
+        ck, cv = dev(gen.keys_all(p.frames, rt(p.frames))), dev(gen.values_all(p.frames))
+        keep += [ck, cv]
+        lay.chunk_k, lay.chunk_v = ck, cv
+        x["lay"], x["keep"] = lay, keep
+        x["Q"] = dev(gen.queries_all(p.frames, rt(p.frames)))
+        return x
+
+    t = time.time()
+    chunks = [chunk_inputs(c) for c in range(warmup_chunks + steps)]
+    log(f"rollout inputs for {len(chunks)} chunks generated in {time.time() - t:.1f}s")
+    desc = kb.LayerDesc(H=wl.H, d=wl.d, M=wl.M, dtype=kb.KVB_BF16, frame_tokens=wl.F, labels=[0] * wl.H,
+                        tau=wl.tau, sigma=wl.sigma, eps=wl.eps, p=wl.p)
+    caches = [LayerCache(desc, seg_cap=8, max_N=3 * wl.F) for _ in range(wl.layers)]
+    O = torch.empty(wl.H, wl.Lq, wl.d, dtype=kdt, device="cuda")
+
+    def run_chunk(x):
+        for lc in caches:
+            if x["N"]:
+                lc.step(x["cK"], x["cV"], x["cT"], x["lay"])
+            else:
+                lc.update(None, None, None, None, None, x["lay"])
+            lc.attention(x["Q"], O)
+
+    for c in range(warmup_chunks):
+        run_chunk(chunks[c])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for c in range(warmup_chunks, warmup_chunks + steps):
+        run_chunk(chunks[c])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / steps
+    counts = caches[0].bank.count.cpu().tolist()
+    return ms, {"layers": wl.layers, "chunks_timed": steps, "first_timed_chunk": warmup_chunks,
+                "bank_count_layer0": counts, "k_star_last": int(caches[0].out.k_star.cpu()[0]),
+                "bank_bytes_per_layer": int(caches[0].bank.K.numel() * 2 * 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="480p", choices=["480p", "1080p"])
+    ap.add_argument("--config", default="480p", choices=["480p", "1080p", "rollout"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter yardstick) and exit")
@@ -209,6 +282,17 @@ def main():
         return
     import kv_cache_compression_head_amd as kb
     kb.load_library()
+    if args.config == "rollout":
+        ms, info = rollout_bench(args.steps, max(args.warmup, 6))
+        print(json.dumps({
+            "metric": METRIC, "value": round(ms, 3), "unit": "ms/chunk (30 layers)", "n_gpus": 1,
+            "steps": args.steps, "warmup": max(args.warmup, 6), "ms_per_step": round(ms, 3),
+            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": "rollout: 30 layers x 12 heads, 480P (1,560 tokens/frame), M=9360, 3 departing "
+                                   "frames per chunk, 6-frame window, 3-frame chunk; steady-state chunks"},
+            "ms_per_layer_chunk": round(ms / info["layers"], 4), "rollout": info}), flush=True)
+        return
     wl, lc, snap, inp, lay, Q, O = setup(args.config)
     log("setup done")
     for _ in range(args.warmup):
