@@ -7,10 +7,10 @@
 // is the concatenation of the head's segments (order irrelevant).
 //
 // bf16 path: flash-style online softmax.  Work-group = 4 waves x 32 queries;
-// KV tiles of 64 keys staged in LDS, double buffered: K row-major with
+// KV tiles of 64 keys staged in LDS, double buffered: K and V row-major with
 // XOR-swizzled 16-byte chunks, copied straight from global memory to LDS;
-// V transposed through registers.  The next tile's copies are in flight
-// while the current tile is multiplied.  Scores are computed transposed (S^T = K Q^T, 16x16x32
+// V^T fragments come from the transposing LDS read.  The next tile's copies
+// are in flight while the current tile is multiplied.  Scores are computed transposed (S^T = K Q^T, 16x16x32
 // MFMA) so every lane holds keys of a single query; P^T feeds
 // O^T = V^T P^T directly as the B operand.  The running maximum is only
 // moved when a tile raises it by more than 2^8 (exact: numerator and
@@ -35,24 +35,42 @@ KVB_DEV uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// XOR swizzle of the 16-byte chunks of a 64-row K or V tile in LDS.  With
+// 16 chunks per row (d = 128) the chunk of row r is XORed with
+// s(r) = ((r2 ^ r3) << 3) | (r1 r0 << 1) | r2: any 8 (or 16) aligned rows
+// take distinct values, so the 16-byte K fragment reads (one chunk of
+// consecutive rows) are conflict-free, and any 4 (or 8) aligned rows take
+// distinct chunk pairs, so the transposing V reads (two adjacent chunks of
+// 4 consecutive rows per 16 lanes) are too.  d = 64 keeps the 3 low bits.
+template <int CPR> KVB_DEV int att_swz(int r) {
+  const int base = ((r & 3) << 1) | ((r >> 2) & 1);
+  if constexpr (CPR == 16) return base | ((((r >> 2) ^ (r >> 3)) & 1) << 3);
+  else return base;
+}
+
+// LDS transpose read (gfx950): within each 16-lane group, lane 16G + i
+// receives element i & 3 of the 8 bytes addressed by lanes 16G + 4j + (i >> 2),
+// j = 0..3, as its elements j
+KVB_DEV s16x4_t lds_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __restrict__ Q, void* __restrict__ O,
                                                            const SegEntry* __restrict__ segs,
                                                            const int32_t* __restrict__ nseg_p, int seg_cap, int Lq,
                                                            float scale_log2, int out_f32, int nqt) {
   using Op = Ops<uint16_t>;
-  using T = Tile<uint16_t, D>;
-  constexpr int LDV = ATT_TK + 4;         // V^T row stride (elements): 34 dwords, conflict-free b64 reads
   constexpr int NKS = D / 32;             // k-steps for S^T
   constexpr int NDB = D / 16;             // d blocks for O^T
-  constexpr int CPR = T::CPR;             // 16-byte chunks per key row
-  constexpr int KPASS = ATT_TK * CPR / 256;   // K chunks copied per thread
+  constexpr int CPR = D / 8;              // 16-byte chunks per key row
+  constexpr int KPASS = ATT_TK * CPR / 256;   // chunks copied per thread and tile (each of K, V)
   // two buffer sets as distinct LDS objects: the direct-to-LDS copy of the
-  // next K tile is then known not to alias the reads of the current one
+  // next tile is then known not to alias the reads of the current one
   __shared__ __attribute__((aligned(16))) uint16_t sK0[ATT_TK * D];
   __shared__ __attribute__((aligned(16))) uint16_t sK1[ATT_TK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV0[D * LDV];
-  __shared__ __attribute__((aligned(16))) uint16_t sV1[D * LDV];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[ATT_TK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[ATT_TK * D];
   __shared__ int s_pre[ATT_MAXSEG + 1];
   __shared__ const void* s_k[ATT_MAXSEG];
   __shared__ const void* s_v[ATT_MAXSEG];
@@ -106,13 +124,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
   f32x4_t L[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
   const s16x8_t ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80};
 
-  // V staging: thread covers keys 4kg..4kg+3 and d 8dc..8dc+7; consecutive
-  // lanes take consecutive key groups so the transposed 8-byte stores of 16
-  // lanes fill one 128-byte V^T row segment (no bank conflicts)
-  const bool vthr = tid < 16 * CPR;
-  const int kg = tid % 16, dc = tid / 16;
-  u32x4_t rv[4];
-
   // Tile addressing.  A tile inside one segment (all but a handful per head)
   // is one base pointer plus the row offset; a tile that straddles segments
   // or the end resolves each row on its own (rows past the end re-read the
@@ -124,69 +135,49 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
     while (s + 1 < nseg && s_pre[s + 1] <= j) ++s;
     return (const uint16_t*)bases[s] + (int64_t)(j - s_pre[s]) * D;
   };
-  // byte offsets of this lane's K chunks inside a 64-row tile (swizzled
-  // source chunk of LDS slot (row, lane % CPR)), fixed for the kernel
+  // byte offsets (inside a 64-row tile) of the source chunks this lane copies
+  // to LDS slots (row, lane % CPR): the same for K and V, fixed for the kernel
   uint32_t koff[KPASS];
 #pragma unroll
   for (int i = 0; i < KPASS; ++i) {
     const int sl = (w * KPASS + i) * 64 + lane;
     const int r = sl / CPR, c = sl % CPR;
-    koff[i] = (uint32_t)(r * D + (c ^ T::swz(r)) * 8) * 2u;
+    koff[i] = (uint32_t)(r * D + (c ^ att_swz<CPR>(r)) * 8) * 2u;
   }
-  auto fetch = [&](int kbase, uint16_t* sKn) {
+  auto uniform_ptr = [](const void* p) -> void* {
+    // (readfirstlane returns int: widen through uint32_t, never by sign)
+    const uint64_t v = (uint64_t)p;
+    const uint32_t vh = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    const uint32_t vl = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    return (void*)(((uint64_t)vh << 32) | (uint64_t)vl);
+  };
+  auto fetch = [&](int kbase, uint16_t* sKn, uint16_t* sVn) {
     while (useg + 1 < nseg && __builtin_amdgcn_readfirstlane(s_pre[useg + 1]) <= kbase) ++useg;
     const int lo = __builtin_amdgcn_readfirstlane(s_pre[useg]);
     const int hi = __builtin_amdgcn_readfirstlane(s_pre[useg + 1]);
     const int wu = __builtin_amdgcn_readfirstlane(w);
-    // V row addresses first (merging loaded registers across the two paths
-    // would force a wait on the loads), then the loads
-    const uint16_t* vp[4];
     if (kbase + ATT_TK <= hi) {
-      // whole tile inside one segment: K through a buffer resource on the
-      // segment (uniform base, per-lane offsets fixed for the kernel)
-      // (readfirstlane returns int: widen through uint32_t, never by sign)
-      const uint64_t kseg = (uint64_t)s_k[useg];
-      const uint32_t khi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(kseg >> 32));
-      const uint32_t klo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)kseg);
-      const void* kbase_ptr = (const void*)(((uint64_t)khi << 32) | (uint64_t)klo);
-      const __amdgpu_buffer_rsrc_t rk =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(kbase_ptr), (short)0, (hi - lo) * D * 2, 0x00020000);
+      // whole tile inside one segment: buffer resources on the segment
+      // (uniform base, per-lane offsets fixed for the kernel)
+      const int nbytes = (hi - lo) * D * 2;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(s_k[useg]), (short)0, nbytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(s_v[useg]), (short)0, nbytes, 0x00020000);
       const int soff = (kbase - lo) * D * 2;
 #pragma unroll
-      for (int i = 0; i < KPASS; ++i)
+      for (int i = 0; i < KPASS; ++i) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rk, (__attribute__((address_space(3))) void*)(sKn + (wu * KPASS + i) * 64 * 8), 16, (int)koff[i], soff, 0, 0);
-      const uint16_t* vb = (const uint16_t*)s_v[useg] + (int64_t)(kbase - lo) * D;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vp[i] = vb + (4 * kg + i) * D;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rvs, (__attribute__((address_space(3))) void*)(sVn + (wu * KPASS + i) * 64 * 8), 16, (int)koff[i], soff, 0, 0);
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < KPASS; ++i) {
         const int sl = (wu * KPASS + i) * 64 + lane;
         const int r = sl / CPR, c = sl % CPR;
-        dma16(slow_row(kbase + r, s_k) + (c ^ T::swz(r)) * 8, sKn + (wu * KPASS + i) * 64 * 8);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vp[i] = slow_row(kbase + 4 * kg + i, s_v);
-    }
-    if (vthr) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rv[i] = gload16(vp[i] + dc * 8);
-    }
-  };
-  auto stage_v = [&](uint16_t* sVn) {
-    if (vthr) {
-      // transpose 4 keys x 8 d into 8 rows of V^T (4 keys each)
-      const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&rv[0]);
-      const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&rv[1]);
-      const uint16_t* e2 = reinterpret_cast<const uint16_t*>(&rv[2]);
-      const uint16_t* e3 = reinterpret_cast<const uint16_t*>(&rv[3]);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        uint2 pk;
-        pk.x = (uint32_t)e0[x] | ((uint32_t)e1[x] << 16);
-        pk.y = (uint32_t)e2[x] | ((uint32_t)e3[x] << 16);
-        *reinterpret_cast<uint2*>(&sVn[(8 * dc + x) * LDV + 4 * kg]) = pk;
+        const int e = (c ^ att_swz<CPR>(r)) * 8;
+        dma16(slow_row(kbase + r, s_k) + e, sKn + (wu * KPASS + i) * 64 * 8);
+        dma16(slow_row(kbase + r, s_v) + e, sVn + (wu * KPASS + i) * 64 * 8);
       }
     }
   };
@@ -195,13 +186,28 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
   // tile, chunk 4k + g): the swizzle of row 16kb + x equals that of x
   int kread[NKS];
 #pragma unroll
-  for (int k = 0; k < NKS; ++k) kread[k] = T::at(lane & 15, Op::off16(k, lane));
+  for (int k = 0; k < NKS; ++k) {
+    const int r = lane & 15;
+    kread[k] = r * D + (((4 * k + g) ^ att_swz<CPR>(r)) * 8);
+  }
+  // element offsets of this lane's 8-byte V pieces for the transposing reads:
+  // lane 16G + a reads row 4G + (a >> 2) (+ 32 hk, + 16 for the upper half),
+  // d = 16 db + 4 (a & 3) .. + 3; the read then hands lane 16G + i the values
+  // V[4G + j][16 db + i], j = 0..3 (the A operand of O^T = V^T P^T)
+  int vread[NDB];
+  {
+    const int a = lane & 15;
+    const int r = 4 * g + (a >> 2);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      vread[db] = r * D + (((2 * db + ((a & 3) >> 1)) ^ att_swz<CPR>(r)) * 8) + (a & 1) * 4;
+  }
 
   const int ntile = (Lkv + ATT_TK - 1) / ATT_TK;
   auto step = [&](int tile, const uint16_t* sKc, const uint16_t* sVc, uint16_t* sKn, uint16_t* sVn) {
     const int kbase = tile * ATT_TK;
     const bool more = tile + 1 < ntile;
-    if (more) fetch(kbase + ATT_TK, sKn);
+    if (more) fetch(kbase + ATT_TK, sKn, sVn);
 
     // ---- S^T = K Q^T ----
     // MFMA issue at raised wave priority: the SIMD's other wave, between its
@@ -266,6 +272,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
       }
     }
     // ---- O^T += V^T P^T ----
+    // B operand element j of lane 16G + i: key 32hk + 4G + j (j < 4) or
+    // 32hk + 16 + 4G + (j - 4); the transposing V reads follow that order
 #pragma unroll
     for (int hk = 0; hk < 2; ++hk) {
       u32x4_t b0 = {pk[0][2 * hk][0], pk[0][2 * hk][1], pk[0][2 * hk + 1][0], pk[0][2 * hk + 1][1]};
@@ -276,26 +284,19 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
       L[1] = Op::mma16(ones, bb1, L[1]);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const uint16_t* vp = sVc + (16 * db + (lane & 15)) * LDV + 32 * hk + 4 * g;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
-        const u32x4_t raw = {lo.x, lo.y, hi.x, hi.y};
-        const s16x8_t a = __builtin_bit_cast(s16x8_t, raw);
+        const uint16_t* vp = sVc + 32 * hk * D + vread[db];
+        const s16x4_t lo = lds_tr16(vp);
+        const s16x4_t hi = lds_tr16(vp + 16 * D);
+        const s16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         o[db][0] = Op::mma16(a, bb0, o[db][0]);
         o[db][1] = Op::mma16(a, bb1, o[db][1]);
       }
     }
-    // keep the V transpose (which waits for the V loads) after the products
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) stage_v(sVn);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // next K tile resident in LDS
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // next K and V tiles resident in LDS
     __syncthreads();
   };
 
-  if (ntile > 0) {
-    fetch(0, sK0);
-    stage_v(sV0);
-  }
+  if (ntile > 0) fetch(0, sK0, sV0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   for (int tile = 0; tile < ntile; tile += 2) {
@@ -373,8 +374,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t st) {
   if (a.Lq <= 0 || a.H <= 0) return hipSuccess;
   if (a.et == ET_BF16) {
-    const int nqt = (a.Lq + ATT_QB - 1) / ATT_QB;
     const float sl2 = a.scale * 1.4426950408889634f;
+    const int nqt = (a.Lq + ATT_QB - 1) / ATT_QB;
     const dim3 grid((unsigned)(nqt * a.H));
     if (a.d == 128)
       hipLaunchKernelGGL((attn_bf16_kernel<128>), grid, dim3(256), 0, st, (const uint16_t*)a.Q, a.O, a.segs, a.nseg,
