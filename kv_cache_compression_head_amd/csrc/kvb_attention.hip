@@ -15,6 +15,8 @@
 // O^T = V^T P^T directly as the B operand.  The running maximum is only
 // moved when a tile raises it by more than 2^8 (exact: numerator and
 // denominator share the stale maximum).
+#include <type_traits>
+
 #include "kvb_common.hpp"
 #include "kvb_launch.hpp"
 
@@ -114,21 +116,21 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
 
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): query fragments resident before the loop
   f32x4_t o[NDB][2];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
+  float m_run[2];
   // softmax denominators, accumulated by MFMA from the same bf16 weights as
   // the numerator (ones x P^T: every row of L holds the query's sum)
-  f32x4_t L[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  f32x4_t L[2];
   const s16x8_t ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80, 0x3F80};
 
   // Tile addressing.  A tile inside one segment (all but a handful per head)
   // is one base pointer plus the row offset; a tile that straddles segments
   // or the end resolves each row on its own (rows past the end re-read the
   // last row: their scores are masked to -inf, their values get weight 0).
-  int useg = 0;   // uniform: segment holding the current tile start
+  // The current segment's bounds and bases are kept in scalar registers;
+  // the LDS segment table is read only when a tile leaves the segment.
+  int ucur = 0, ulo = 0, uhi = -1;
+  const void* ubk = nullptr;
+  const void* ubv = nullptr;
   auto slow_row = [&](int j, const void* const* bases) -> const uint16_t* {
     j = min(j, Lkv - 1);
     int s = 0;
@@ -144,25 +146,30 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
     const int r = sl / CPR, c = sl % CPR;
     koff[i] = (uint32_t)(r * D + (c ^ att_swz<CPR>(r)) * 8) * 2u;
   }
-  auto uniform_ptr = [](const void* p) -> void* {
+  auto uniform_ptr = [](const void* p) -> const void* {
     // (readfirstlane returns int: widen through uint32_t, never by sign)
     const uint64_t v = (uint64_t)p;
     const uint32_t vh = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
     const uint32_t vl = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
-    return (void*)(((uint64_t)vh << 32) | (uint64_t)vl);
+    return (const void*)(((uint64_t)vh << 32) | (uint64_t)vl);
   };
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   auto fetch = [&](int kbase, uint16_t* sKn, uint16_t* sVn) {
-    while (useg + 1 < nseg && __builtin_amdgcn_readfirstlane(s_pre[useg + 1]) <= kbase) ++useg;
-    const int lo = __builtin_amdgcn_readfirstlane(s_pre[useg]);
-    const int hi = __builtin_amdgcn_readfirstlane(s_pre[useg + 1]);
-    const int wu = __builtin_amdgcn_readfirstlane(w);
-    if (kbase + ATT_TK <= hi) {
+    if (kbase < ulo || kbase + ATT_TK > uhi) {
+      if (kbase < ulo) ucur = 0;   // a new pass over the tiles
+      while (ucur + 1 < nseg && __builtin_amdgcn_readfirstlane(s_pre[ucur + 1]) <= kbase) ++ucur;
+      ulo = __builtin_amdgcn_readfirstlane(s_pre[ucur]);
+      uhi = __builtin_amdgcn_readfirstlane(s_pre[ucur + 1]);
+      ubk = uniform_ptr(s_k[ucur]);
+      ubv = uniform_ptr(s_v[ucur]);
+    }
+    if (kbase + ATT_TK <= uhi) {
       // whole tile inside one segment: buffer resources on the segment
       // (uniform base, per-lane offsets fixed for the kernel)
-      const int nbytes = (hi - lo) * D * 2;
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(s_k[useg]), (short)0, nbytes, 0x00020000);
-      const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(s_v[useg]), (short)0, nbytes, 0x00020000);
-      const int soff = (kbase - lo) * D * 2;
+      const int nbytes = (uhi - ulo) * D * 2;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ubk), (short)0, nbytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ubv), (short)0, nbytes, 0x00020000);
+      const int soff = (kbase - ulo) * D * 2;
 #pragma unroll
       for (int i = 0; i < KPASS; ++i) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -204,29 +211,53 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
   }
 
   const int ntile = (Lkv + ATT_TK - 1) / ATT_TK;
-  auto step = [&](int tile, const uint16_t* sKc, const uint16_t* sVc, uint16_t* sKn, uint16_t* sVn) {
+  // Softmax modes of one tile.  FIRST: the tile's maximum becomes the
+  // query's reference m (first tile of the fast pass).  FAST: weights
+  // 2^(s c - m) against that fixed reference, no maximum taken: exact
+  // whenever they stay finite (fp32 and bf16 reach 2^127), which the pass
+  // checks at the end.  SAFE: the reference follows the running maximum,
+  // moved only when a tile raises it by more than 2^8 (numerator and
+  // denominator are rescaled together).
+  constexpr int FIRST = 0, FAST = 1, SAFE = 2;
+  auto step = [&](auto mode_c, int tile, const uint16_t* sKc, const uint16_t* sVc, uint16_t* sKn, uint16_t* sVn) {
+    constexpr int mode = decltype(mode_c)::value;
     const int kbase = tile * ATT_TK;
     const bool more = tile + 1 < ntile;
     if (more) fetch(kbase + ATT_TK, sKn, sVn);
 
     // ---- S^T = K Q^T ----
     // MFMA issue at raised wave priority: the SIMD's other wave, between its
-    // own products, then gets the vector ALU for its softmax
+    // own products, then gets the vector ALU for its softmax.  Fragments of
+    // key block kb + 2 are read while block kb is multiplied.
     __builtin_amdgcn_s_setprio(1);
     f32x4_t s[4][2];
+    s16x8_t kf[2][NKS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int k = 0; k < NKS; ++k) kf[kb][k] = Op::load(sKc + 16 * kb * D + kread[k]);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       s[kb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       s[kb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < NKS; ++k) {
-        const s16x8_t a = Op::load(sKc + 16 * kb * D + kread[k]);
-        s[kb][0] = Op::mma16(a, qf[0][k], s[kb][0]);
-        s[kb][1] = Op::mma16(a, qf[1][k], s[kb][1]);
+        s[kb][0] = Op::mma16(kf[kb & 1][k], qf[0][k], s[kb][0]);
+        s[kb][1] = Op::mma16(kf[kb & 1][k], qf[1][k], s[kb][1]);
+      }
+      if (kb + 2 < 4) {
+#pragma unroll
+        for (int k = 0; k < NKS; ++k) kf[kb & 1][k] = Op::load(sKc + 16 * (kb + 2) * D + kread[k]);
       }
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NKS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NKS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NKS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NKS, 0);
     __builtin_amdgcn_s_setprio(0);
-    // ---- online softmax (log2 domain), lane owns query 16qb + (lane & 15) ----
+    // ---- softmax (log2 domain), lane owns query 16qb + (lane & 15) ----
     if (kbase + ATT_TK > Lkv) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -234,28 +265,37 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
         for (int i = 0; i < 4; ++i)
           if (kbase + 16 * kb + 4 * g + i >= Lkv) { s[kb][0][i] = -__builtin_inff(); s[kb][1][i] = -__builtin_inff(); }
     }
-    float mt[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx = s[0][qb][0];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      mt[qb] = mx * scale_log2;
-    }
-    const bool grow = (mt[0] > m_run[0] + ATT_RESCALE_LOG2) || (mt[1] > m_run[1] + ATT_RESCALE_LOG2);
-    if (__any(grow)) {
+    if constexpr (mode != FAST) {
+      float mt[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const float mnew = fmaxf(m_run[qb], mt[qb]);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew);
-        m_run[qb] = mnew;
-        L[qb] *= alpha;
+        float mx = s[0][qb][0];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db][qb] *= alpha;
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
+        const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+        const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+        mt[qb] = mx * scale_log2;
+      }
+      if constexpr (mode == FIRST) {
+        m_run[0] = mt[0];
+        m_run[1] = mt[1];
+      } else {
+        const bool grow = (mt[0] > m_run[0] + ATT_RESCALE_LOG2) || (mt[1] > m_run[1] + ATT_RESCALE_LOG2);
+        if (__any(grow)) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const float mnew = fmaxf(m_run[qb], mt[qb]);
+            const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew);
+            m_run[qb] = mnew;
+            L[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[db][qb] *= alpha;
+          }
+        }
       }
     }
     uint32_t pk[2][4][2];
@@ -295,13 +335,39 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
     __builtin_amdgcn_s_waitcnt(0x0F70);   // next K and V tiles resident in LDS
     __syncthreads();
   };
+  auto reset = [&]() {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[0] = m_run[1] = -__builtin_inff();
+    L[0] = L[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (ntile > 0) fetch(0, sK0, sV0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  };
 
-  if (ntile > 0) fetch(0, sK0, sV0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  for (int tile = 0; tile < ntile; tile += 2) {
-    step(tile, sK0, sV0, sK1, sV1);
-    if (tile + 1 < ntile) step(tile + 1, sK1, sV1, sK0, sV0);
+  // fast pass (tile t in buffer set t & 1)
+  reset();
+  if (ntile > 0) step(std::integral_constant<int, FIRST>{}, 0, sK0, sV0, sK1, sV1);
+  for (int tile = 1; tile < ntile; tile += 2) {
+    step(std::integral_constant<int, FAST>{}, tile, sK1, sV1, sK0, sV0);
+    if (tile + 1 < ntile) step(std::integral_constant<int, FAST>{}, tile + 1, sK0, sV0, sK1, sV1);
+  }
+  // a non-finite numerator or denominator anywhere in the work-group (a
+  // query whose scores rose by about 2^127 past its first tile's): redo the
+  // work-group's tiles with the running-maximum pass
+  float chk = L[0][0] + L[1][0];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) chk += (o[db][qb][0] + o[db][qb][1]) + (o[db][qb][2] + o[db][qb][3]);
+  if (__syncthreads_or(!__builtin_isfinite(chk))) {
+    reset();
+    for (int tile = 0; tile < ntile; tile += 2) {
+      step(std::integral_constant<int, SAFE>{}, tile, sK0, sV0, sK1, sV1);
+      if (tile + 1 < ntile) step(std::integral_constant<int, SAFE>{}, tile + 1, sK1, sV1, sK0, sV0);
+    }
   }
 
   // ---- normalise and store: lane holds O[q][16db + 4g + i] ----

@@ -32,9 +32,30 @@ def _seg_table(H, seg_cap, per_head):
     (64, 48, [[16, 64, 48], [16, 60, 48]], "f32"),
 ])
 def test_attention_ragged(d, Lq, lens, dtype):
+    _attention_case(d, Lq, lens, dtype)
+
+
+# Segments whose key scales differ by large factors: the running maximum of a
+# query moves by far more than 2^8 between tiles (up, then down), so the
+# online softmax has to rescale its accumulated numerator and denominator.
+# With scales of 40 the later scores exceed the first tile's by far more than
+# 2^127 (in the exponent), so weights against the first tile's maximum
+# overflow and the kernel must redo the tiles with the running maximum.
+@pytest.mark.parametrize("d,Lq,lens,kscale", [
+    (128, 300, [[130, 200, 64]], [0.05, 6.0, 0.5]),
+    (128, 257, [[64, 64, 70], [10, 300]], [0.1, 3.0, 8.0]),
+    (64, 100, [[200, 130]], [0.2, 7.0]),
+    (128, 200, [[64, 300], [70, 129, 5]], [0.05, 40.0, 0.3]),
+    (64, 90, [[100, 100]], [0.1, 40.0]),
+])
+def test_attention_rescale(d, Lq, lens, kscale):
+    _attention_case(d, Lq, lens, "bf16", kscale)
+
+
+def _attention_case(d, Lq, lens, dtype, kscale=None):
     import torch
     import kv_cache_compression_head_amd as kb
-    gc.banner(f"attention d={d} Lq={Lq} lens={lens} {dtype}")
+    gc.banner(f"attention d={d} Lq={Lq} lens={lens} {dtype} kscale={kscale}")
     rng = np.random.default_rng(d + Lq)
     H = len(lens)
     kdt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -47,8 +68,9 @@ def test_attention_ragged(d, Lq, lens, dtype):
     for h, ls in enumerate(lens):
         segs = []
         kk, vv = [], []
-        for ln in ls:
-            k = rnd(rng.normal(size=(ln, d)).astype(np.float32) * 1.5)
+        for i, ln in enumerate(ls):
+            ks = 1.5 if kscale is None else kscale[(i + h) % len(kscale)]
+            k = rnd(rng.normal(size=(ln, d)).astype(np.float32) * ks)
             v = rnd(rng.normal(size=(ln, d)).astype(np.float32))
             tk, tv = gc.dev(k, kdt), gc.dev(v, kdt)
             keep += [tk, tv]
