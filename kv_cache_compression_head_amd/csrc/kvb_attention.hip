@@ -57,6 +57,37 @@ KVB_DEV s16x4_t lds_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
 }
 
+// Global -> LDS copies of 16 bytes per lane, written as inline assembly so
+// that the compiler does not track them (its own tracking of copies through
+// the builtins costs about a tenth of the attention time here).  The kernel
+// orders them itself: s_waitcnt vmcnt(0) and a barrier before a copied tile
+// is read.  M0 holds the wave's LDS destination (lane l writes 16 bytes at
+// M0 + 16 l); nothing else in the attention kernels uses M0.  No outputs:
+// the data goes to LDS only.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+KVB_DEV void lds_copy_buf(i32x4_t rsrc, uint32_t voff, int soff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc),
+               "s"(soff)
+               : "memory");
+}
+KVB_DEV void lds_copy_glb(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g) : "memory");
+}
+// LDS byte address of p (wave-uniform)
+KVB_DEV uint32_t lds_addr(const void* p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)p);
+}
+// buffer resource on [base, base + nbytes): stride 0, raw buffer
+KVB_DEV i32x4_t buf_rsrc(const void* base, int nbytes) {
+  const uint64_t b = (uint64_t)base;
+  i32x4_t r;
+  r[0] = (int)(uint32_t)b;
+  r[1] = (int)((uint32_t)(b >> 32) & 0xffffu);
+  r[2] = nbytes;
+  r[3] = 0x00020000;
+  return r;
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __restrict__ Q, void* __restrict__ O,
                                                            const SegEntry* __restrict__ segs,
@@ -167,15 +198,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
       // whole tile inside one segment: buffer resources on the segment
       // (uniform base, per-lane offsets fixed for the kernel)
       const int nbytes = (uhi - ulo) * D * 2;
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ubk), (short)0, nbytes, 0x00020000);
-      const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ubv), (short)0, nbytes, 0x00020000);
+      const i32x4_t rk = buf_rsrc(ubk, nbytes), rvs = buf_rsrc(ubv, nbytes);
       const int soff = (kbase - ulo) * D * 2;
 #pragma unroll
       for (int i = 0; i < KPASS; ++i) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk, (__attribute__((address_space(3))) void*)(sKn + (wu * KPASS + i) * 64 * 8), 16, (int)koff[i], soff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rvs, (__attribute__((address_space(3))) void*)(sVn + (wu * KPASS + i) * 64 * 8), 16, (int)koff[i], soff, 0, 0);
+        lds_copy_buf(rk, koff[i], soff, lds_addr(sKn + (wu * KPASS + i) * 64 * 8));
+        lds_copy_buf(rvs, koff[i], soff, lds_addr(sVn + (wu * KPASS + i) * 64 * 8));
       }
     } else {
 #pragma unroll
@@ -183,8 +211,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
         const int sl = (wu * KPASS + i) * 64 + lane;
         const int r = sl / CPR, c = sl % CPR;
         const int e = (c ^ att_swz<CPR>(r)) * 8;
-        dma16(slow_row(kbase + r, s_k) + e, sKn + (wu * KPASS + i) * 64 * 8);
-        dma16(slow_row(kbase + r, s_v) + e, sVn + (wu * KPASS + i) * 64 * 8);
+        lds_copy_glb(slow_row(kbase + r, s_k) + e, lds_addr(sKn + (wu * KPASS + i) * 64 * 8));
+        lds_copy_glb(slow_row(kbase + r, s_v) + e, lds_addr(sVn + (wu * KPASS + i) * 64 * 8));
       }
     }
   };
