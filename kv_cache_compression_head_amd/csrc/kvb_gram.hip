@@ -71,9 +71,13 @@ template <> struct Aug<float> {
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 
 // Stages TC key rows (gathered by virtual index) and their augmentation rows
-// into LDS with direct-to-LDS loads.  NT threads; thread (w, lane) copies
-// chunks (w * PASSW + i) * 64 + lane; wave 0 copies the augmentation rows
-// and records each row's index (-1 when absent) in sV when given.
+// into LDS with direct-to-LDS loads.  NT threads in NW waves; copy i of wave
+// w fills tile rows (i NW + w) RPI .. + RPI - 1 (one contiguous KiB of LDS),
+// lane l taking row + l / CPR and LDS chunk l % CPR.  The rows of one lane
+// differ by multiples of NW RPI >= 16, which the swizzle ignores, so the
+// lane's source chunk offset is the same for every copy.  Wave 0 copies the
+// augmentation rows and records each row's index (-1 when absent) in sV
+// when given.
 //
 // Indices come in two steps so that reading an index list never stalls the
 // copies in flight: index() keeps the raw list entries of a tile (plain
@@ -84,33 +88,38 @@ template <bool B> struct BoolTag { static constexpr bool value = B; };
 template <typename E, int D, int TC, int NT = 256>
 struct DmaTile {
   using T = Tile<E, D>;
-  static constexpr int PASSW = TC * T::CPR / NT;
-  static_assert((TC * T::CPR) % NT == 0 && TC == 64, "tile shape");
+  static constexpr int NW = NT / 64;
+  static constexpr int RPI = 64 / T::CPR;           // rows per copy
+  static constexpr int PASSW = TC / (RPI * NW);     // copies per wave and tile
+  static_assert(TC == 64 && PASSW * RPI * NW == TC, "tile shape");
+  static_assert(sizeof(E) != 2 || (NW * RPI) % 16 == 0, "the swizzle must repeat across a lane's copies");
   int vi[PASSW];
   int va;
   // Per-lane offsets are recomputed from an opaque lane id at each use: kept
   // live across the loop they would cost registers the MFMA loop needs.
   template <typename F>
   KVB_DEV void index(int tile, F raw) {
-    const int lane = opaque_i(lane_id());
+    const unsigned lane = (unsigned)opaque_i(lane_id());
     const int w = __builtin_amdgcn_readfirstlane(wave_id());
+    const int r0 = (int)(lane / T::CPR);
 #pragma unroll
-    for (int i = 0; i < PASSW; ++i) vi[i] = raw(tile * TC + ((w * PASSW + i) * 64 + lane) / T::CPR);
-    va = w == 0 ? raw(tile * TC + lane) : 0;
+    for (int i = 0; i < PASSW; ++i) vi[i] = raw(tile * TC + (i * NW + w) * RPI + r0);
+    va = w == 0 ? raw(tile * TC + (int)lane) : 0;
   }
   template <typename G>
   KVB_DEV void issue(int tile, G fix, const HeadKeys<E, D>& hk, E* sY, u32x4_t* sA, int* sV, int fb) const {
-    const int lane = opaque_i(lane_id());
+    const unsigned lane = (unsigned)opaque_i(lane_id());
     const int w = __builtin_amdgcn_readfirstlane(wave_id());
+    const int r0 = (int)(lane / T::CPR), c = (int)(lane % T::CPR);
+    const int eoff = (c ^ T::swz(w * RPI + r0)) * T::EPC;
 #pragma unroll
     for (int i = 0; i < PASSW; ++i) {
-      const int s = (w * PASSW + i) * 64 + lane;
-      const int r = s / T::CPR, c = s % T::CPR;
+      const int r = (i * NW + w) * RPI + r0;
       const int v = fix(tile * TC + r, vi[i]);
-      dma16(hk.row(v >= 0 ? v : fb) + (c ^ T::swz(r)) * T::EPC, sY + (w * PASSW + i) * 64 * T::EPC);
+      dma16(hk.row(v >= 0 ? v : fb) + eoff, sY + (i * NW + w) * RPI * D);
     }
     if (w == 0) {
-      const int v = fix(tile * TC + lane, va);
+      const int v = fix(tile * TC + (int)lane, va);
       if (sV != nullptr) sV[lane] = v;
       dma16(hk.aug(v >= 0 ? v : fb), sA);
     }
@@ -558,11 +567,48 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
   // candidates are always present in a stage's used positions; rows past
   // kmax copy a fallback row and are masked below
   const int fb = M;                      // candidate 0 (N > 0 whenever kmax > 0)
+  // Full stages (every position below kmax): each row is candidate ord[j]
+  // and needs neither clamp nor check, so a copy address is one multiply-add
+  // on the list entry.  For bf16 keys the order position of a lane's copy i
+  // is 64 stage + jp + joff(i), with jp fixed for the kernel: copies of one
+  // lane are NW RPI = 16 (or 32) rows apart, and pos_of moves a row only
+  // inside its group of 32.
+  using LD = DmaTile<E, D, TC>;
+  constexpr bool FASTG = sizeof(E) == 2 && (LD::NW * LD::RPI == 16 || LD::NW * LD::RPI == 32);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int jp = pos_of(wu * LD::RPI + lane / T::CPR);
+  auto joff = [](int i) -> int { return LD::NW * LD::RPI == 16 ? 32 * (i >> 1) + 8 * (i & 1) : 32 * i; };
+  auto full = [&](int stg) -> bool { return (stg + 1) * TC <= kmax; };
+  auto index_fast = [&](int stg) {
+    const int32_t* op = ord + stg * TC + jp;
+#pragma unroll
+    for (int i = 0; i < LD::PASSW; ++i) ld.vi[i] = op[joff(i)];
+    ld.va = wu == 0 ? raw(stg * TC + lane) : 0;
+  };
+  const E* cand0 = hk.cand + (int64_t)M * D;   // candidate row 0
+  auto issue_fast = [&](int stg, E* nC, u32x4_t* nA) {
+    const int eoff = ((lane % T::CPR) ^ T::swz(wu * LD::RPI + lane / T::CPR)) * T::EPC;
+#pragma unroll
+    for (int i = 0; i < LD::PASSW; ++i)
+      dma16(cand0 + (int64_t)(uint32_t)ld.vi[i] * D + eoff, nC + (i * LD::NW + wu) * LD::RPI * D);
+    if (wu == 0) {
+      const int v = fix(stg * TC + lane, ld.va);
+      dma16(hk.aug(v >= 0 ? v : fb), nA);
+    }
+  };
+  auto load_index = [&](int stg) {
+    if (FASTG && full(stg)) index_fast(stg);
+    else ld.index(stg, raw);
+  };
+  auto load_issue = [&](int stg, E* nC, u32x4_t* nA) {
+    if (FASTG && full(stg)) issue_fast(stg, nC, nA);
+    else ld.issue(stg, fix, hk, nC, nA, nullptr, fb);
+  };
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): bank fragments resident
   if (st_begin < st_end) {
-    ld.index(st_begin, raw);
-    ld.issue(st_begin, fix, hk, sC0, sA0, nullptr, fb);
-    if (st_begin + 1 < st_end) ld.index(st_begin + 1, raw);
+    load_index(st_begin);
+    load_issue(st_begin, sC0, sA0);
+    if (st_begin + 1 < st_end) load_index(st_begin + 1);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
@@ -573,8 +619,8 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
     const bool more = stg + 1 < st_end;
     if (more) {
       // the next set was last read before the previous barrier
-      ld.issue(stg + 1, fix, hk, nC, nA, nullptr, fb);
-      if (stg + 2 < st_end) ld.index(stg + 2, raw);
+      load_issue(stg + 1, nC, nA);
+      if (stg + 2 < st_end) load_index(stg + 2);
     }
     const bool wave_busy = __any(!done);
     if (wave_busy) {
