@@ -285,7 +285,8 @@ __global__ __launch_bounds__(GRAM_NT, 4) void gram_kernel(KeySpace<E> ks, VList 
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
 
-  DmaTile<E, D, TC, GRAM_NT> ld;
+  using LD = DmaTile<E, D, TC, GRAM_NT>;
+  LD ld;
   // list position c -> raw entry (a plain load for index lists, the position
   // itself for ranges) -> virtual row index (-1 past the end)
   const int32_t* cidx = CLIST ? cols.idx + (int64_t)h * cols.idx_hstride : nullptr;
@@ -294,14 +295,67 @@ __global__ __launch_bounds__(GRAM_NT, 4) void gram_kernel(KeySpace<E> ks, VList 
     const int v = CLIST ? e + cols.add : cols.base + e;
     return (c < ncols && hk.ok(v)) ? v : -1;
   };
+  // Full tiles (every position below ncols) take a fast path: no clamp and
+  // no check per row.  A range tile that lies in one key set (bank or
+  // candidates) is consecutive rows: one uniform base plus this lane's row
+  // offset.  An index-list tile reads its entries with per-lane offsets
+  // fixed for the kernel.  The lane's row of copy i is (i NW + w) RPI + rl.
+  // Per-lane parts: kept live in the variants without self-exclusion; the
+  // self-excluding variants recompute them from an opaque lane id at each
+  // use (kept live there they cost registers the MFMA loop needs).
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const unsigned ln_keep = (unsigned)lane;
+  auto lane_part = [&]() -> unsigned { return SELF ? (unsigned)opaque_i(lane_id()) : ln_keep; };
+  auto full = [&](int tile) -> bool {
+    if ((tile + 1) * TC > ncols) return false;
+    if constexpr (CLIST) return true;
+    const int vlo = cols.base + tile * TC;   // one key set for the whole tile
+    return (vlo + TC <= (int)hk.M || vlo >= (int)hk.M) && vlo + TC <= (int)hk.lim;
+  };
+  auto load_index = [&](int tile) {
+    if (CLIST && full(tile)) {
+      const int rl = (int)(lane_part() / T::CPR);
+      const int32_t* ip = cidx + tile * TC + wu * LD::RPI + rl;
+#pragma unroll
+      for (int i = 0; i < LD::PASSW; ++i) ld.vi[i] = ip[i * LD::NW * LD::RPI];
+      ld.va = wu == 0 ? cidx[tile * TC + lane] : 0;
+    } else {
+      ld.index(tile, raw);
+    }
+  };
+  auto load_issue = [&](int tile, E* nY, u32x4_t* nA, int* nV) {
+    if (full(tile)) {
+      const unsigned ln = lane_part();
+      const int rl = (int)(ln / T::CPR);
+      const int eoff = ((int)(ln % T::CPR) ^ T::swz(wu * LD::RPI + rl)) * T::EPC;
+      if constexpr (CLIST) {
+#pragma unroll
+        for (int i = 0; i < LD::PASSW; ++i)
+          dma16(hk.row(ld.vi[i] + cols.add) + eoff, nY + (i * LD::NW + wu) * LD::RPI * D);
+      } else {
+        const int vlo = cols.base + tile * TC;
+        const E* base = hk.row(vlo) + (int64_t)(wu * LD::RPI + rl) * D + eoff;
+#pragma unroll
+        for (int i = 0; i < LD::PASSW; ++i)
+          dma16(base + (int64_t)i * LD::NW * LD::RPI * D, nY + (i * LD::NW + wu) * LD::RPI * D);
+      }
+      if (wu == 0) {
+        const int v = CLIST ? ld.va + cols.add : cols.base + tile * TC + lane;
+        nV[lane] = v;
+        dma16(hk.aug(v), nA);
+      }
+    } else {
+      ld.issue(tile, fix, hk, nY, nA, nV, fb);
+    }
+  };
   // PLAIN (direct form, every column of the tile present): t needs no clamp
   auto step = [&](auto plain_tag, int tile, const E* cY, const u32x4_t* cA, const int* cV, E* nY, u32x4_t* nA,
                   int* nV) {
     constexpr bool PLAIN = decltype(plain_tag)::value;
     if (tile + 1 < t1) {
       // the next set was last read before the previous barrier
-      ld.issue(tile + 1, fix, hk, nY, nA, nV, fb);
-      if (tile + 2 < t1) ld.index(tile + 2, raw);
+      load_issue(tile + 1, nY, nA, nV);
+      if (tile + 2 < t1) load_index(tile + 2);
     }
     // both subtiles' products first (independent chains)
     f32x16_t cc[2];
@@ -345,9 +399,9 @@ __global__ __launch_bounds__(GRAM_NT, 4) void gram_kernel(KeySpace<E> ks, VList 
   };
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): row fragments resident
   if (t0 < t1) {
-    ld.index(t0, raw);
-    ld.issue(t0, fix, hk, sY0, sA0, sV0, fb);
-    if (t0 + 1 < t1) ld.index(t0 + 1, raw);
+    load_index(t0);
+    load_issue(t0, sY0, sA0, sV0);
+    if (t0 + 1 < t1) load_index(t0 + 1);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
