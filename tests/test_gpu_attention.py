@@ -30,8 +30,11 @@ def _seg_table(H, seg_cap, per_head):
     (64, 129, [[33, 31], [1, 2, 3, 4, 5, 200], [640]], "bf16"),
     (128, 4680, [[1560, 9360, 3120, 1560, 4680]], "bf16"),
     (64, 48, [[16, 64, 48], [16, 60, 48]], "f32"),
+    (128, 700, [[0], [3000, 17], [], [64]], "bf16"),
 ])
 def test_attention_ragged(d, Lq, lens, dtype):
+    """Ragged segment tables; heads with no keys (an empty segment, or none)
+    give zeros."""
     _attention_case(d, Lq, lens, dtype)
 
 
@@ -78,18 +81,21 @@ def _attention_case(d, Lq, lens, dtype, kscale=None):
             kk.append(k)
             vv.append(v)
         per_head.append(segs)
-        Ks.append(np.concatenate(kk))
-        Vs.append(np.concatenate(vv))
+        Ks.append(np.concatenate(kk) if kk else np.zeros((0, d), np.float32))
+        Vs.append(np.concatenate(vv) if vv else np.zeros((0, d), np.float32))
     segs_t, nseg_t = _seg_table(H, seg_cap, per_head)
     Qd = gc.dev(Q, kdt)
     O = torch.empty(H, Lq, d, dtype=torch.float32, device="cuda")
-    kb.chunk_attention(H, d, Lq, kb.KVB_BF16 if dtype == "bf16" else kb.KVB_F32, Qd, segs_t, nseg_t, seg_cap, O,
-                       out_f32=True)
+    et = kb.KVB_BF16 if dtype == "bf16" else kb.KVB_F32
+    kb.chunk_attention(H, d, Lq, et, Qd, segs_t, nseg_t, seg_cap, O, out_f32=True)
     torch.cuda.synchronize()
     On = O.cpu().numpy()
     tol = (2e-2, 2e-3) if dtype == "bf16" else (1e-4, 1e-5)
     errs = []
     for h in range(H):
+        if Ks[h].shape[0] == 0:   # no keys: the kernels write zeros
+            assert np.all(On[h] == 0.0), f"head {h} without keys"
+            continue
         ref = oracle_attention(Q[h].astype(np.float64), Ks[h].astype(np.float64), Vs[h].astype(np.float64))
         errs.append(np.abs(On[h] - ref).reshape(-1))
     e = np.concatenate(errs)
