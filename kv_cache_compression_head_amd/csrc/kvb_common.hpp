@@ -195,6 +195,11 @@ template <typename E, int D> struct Tile {
   }
   // element offset of element e of row r (e is a fragment start)
   KVB_DEV static int at(int r, int e) { return r * D + (((e / EPC) ^ swz(r)) * EPC) + e % EPC; }
+  // at(r, e + f) from a0 = at(r, e), for a fragment step f whose chunk bits
+  // are disjoint from e's (f = off32(k, 0) against e = off32(0, lane)): the
+  // swizzle is an XOR on the chunk index and the row base has no bits below
+  // D, so stepping along the row is an XOR of the start offset
+  KVB_DEV static int at_step(int a0, int f) { return a0 ^ f; }
 };
 
 // 16-byte global -> LDS copy that bypasses registers: lane l of the wave

@@ -358,6 +358,16 @@ __global__ __launch_bounds__(GRAM_NT, 4) void gram_kernel(KeySpace<E> ks, VList 
       if (tile + 2 < t1) load_index(tile + 2);
     }
     // both subtiles' products first (independent chains)
+    // column fragment k of subtile sub: sub 32 D + at(n, off32(k, lane)),
+    // stepped from one start offset (the swizzle repeats every 32 rows);
+    // the start is rebuilt per tile so the compiler does not keep a register
+    // per fragment live across the loop
+    // (fp32 tiles have no swizzle: their offsets fold into immediates as is)
+    const int y0 = sizeof(E) == 2 ? opaque_i(T::at(nn, O::off32(0, lane))) : 0;
+    auto yoff = [&](int sub, int k) -> int {
+      if constexpr (sizeof(E) == 2) return 32 * sub * D + T::at_step(y0, O::off32(k, 0));
+      else return T::at(32 * sub + nn, O::off32(k, lane));
+    };
     f32x16_t cc[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -365,7 +375,8 @@ __global__ __launch_bounds__(GRAM_NT, 4) void gram_kernel(KeySpace<E> ks, VList 
 #pragma unroll
       for (int i = 0; i < 16; ++i) cc[sub][i] = 0.0f;
 #pragma unroll
-      for (int k = 0; k < NK; ++k) cc[sub] = O::mma32(xf[k], O::load(cY + T::at(rr, O::off32(k, lane))), cc[sub]);
+      for (int k = 0; k < NK; ++k)
+        cc[sub] = O::mma32(xf[k], O::load(cY + yoff(sub, k)), cc[sub]);
       cc[sub] = O::mma32(xa, A::yfrag(cA[rr], lane), cc[sub]);
     }
 #pragma unroll
@@ -680,6 +691,15 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
     if (wave_busy) {
       // both subtiles' products first (independent MFMA chains), then the
       // interactions and prefix sums of each in order
+      // candidate fragment k of subtile half: 32 half D + at(n, off32(k,
+      // lane)), stepped from one start offset rebuilt per stage (kept live
+      // across the walk, one register per fragment would spill)
+      // (fp32 tiles have no swizzle: their offsets fold into immediates)
+      const int c0 = sizeof(E) == 2 ? opaque_i(T::at(lane & 31, O::off32(0, lane))) : 0;
+      auto coff = [&](int half, int k) -> int {
+        if constexpr (sizeof(E) == 2) return 32 * half * D + T::at_step(c0, O::off32(k, 0));
+        else return T::at(32 * half + (lane & 31), O::off32(k, lane));
+      };
       f32x16_t accs[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -687,7 +707,8 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
 #pragma unroll
         for (int i = 0; i < 16; ++i) accs[half][i] = 0.0f;
 #pragma unroll
-        for (int k = 0; k < NK; ++k) accs[half] = O::mma32(O::load(cC + T::at(cr, O::off32(k, lane))), bf[k], accs[half]);
+        for (int k = 0; k < NK; ++k)
+          accs[half] = O::mma32(O::load(cC + coff(half, k)), bf[k], accs[half]);
         accs[half] = O::mma32(A::yfrag(cA[cr], lane), ba, accs[half]);
       }
 #pragma unroll
