@@ -192,9 +192,21 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
 /* Native attention of the chunk's queries over each head's segment table
  * (DensityKV card page Figure 2; Forcing-KV section 3.3):
  *   O_h = softmax(Q_h K_h^T * scale) V_h,  Q, O [H][Lq][d].
- * No workspace is used (ws may be NULL). */
+ * ws (device, optional, caller-owned, 256-byte aligned): with ws_bytes >=
+ * chunk_attention_workspace_size(A), the bf16 path balances its work over
+ * every slot of the GPU: items (head, 128-query tile) left over after whole
+ * rounds are cut along the keys into a main piece and a tail, whose fp32
+ * partials (o, reference, denominator) a second kernel merges.  ws = NULL
+ * runs one work-group per item.  Both give the same result up to rounding.
+ * A too-small non-NULL workspace is KVB_EWORKSPACE.  Calls that share one
+ * workspace must not overlap. */
 int chunk_attention(const kvb_attn_desc* A, const void* Q, const kvb_segment* segs, const int32_t* nseg, void* O,
                     void* ws, size_t ws_bytes, kvb_stream_t stream);
+
+/* Workspace bytes for chunk_attention's balanced grid (0: nothing to
+ * balance, or the fp32 path).  Depends on the current device's compute-unit
+ * count.  Host only; no device work. */
+int chunk_attention_workspace_size(const kvb_attn_desc* A, size_t* bytes);
 
 /* Message of the last non-OK status on this thread ("" if none). */
 const char* kvb_last_error(void);

@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 __all__ = [
     "KVB_BF16", "KVB_F32", "KVB_HEAD_DENSITY", "KVB_HEAD_STATIC", "KVB_HEAD_DYNAMIC",
     "KvbError", "load_library", "kvbank_workspace_size", "kvbank_score", "kvbank_update",
-    "chunk_attention", "kvb_last_error", "LayerDesc", "Bank", "KVLayout", "UpdateOut",
+    "chunk_attention", "chunk_attention_workspace_size", "kvb_last_error", "LayerDesc", "Bank", "KVLayout", "UpdateOut",
     "HEADER_FUNCTIONS",
 ]
 
@@ -25,7 +25,8 @@ LIB_PATH = os.path.join(_HERE, "libkvbank.so")
 KVB_BF16, KVB_F32 = 0, 1
 KVB_HEAD_DENSITY, KVB_HEAD_STATIC, KVB_HEAD_DYNAMIC = 0, 1, 2
 KVB_MAX_SEGMENTS = 256
-HEADER_FUNCTIONS = ("kvbank_workspace_size", "kvbank_score", "kvbank_update", "chunk_attention", "kvb_last_error")
+HEADER_FUNCTIONS = ("kvbank_workspace_size", "kvbank_score", "kvbank_update", "chunk_attention",
+                    "chunk_attention_workspace_size", "kvb_last_error")
 
 _c_i32, _c_f32, _c_f64, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 
@@ -90,7 +91,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                   _vp, _vp, ctypes.POINTER(kvb_kv_layout), ctypes.POINTER(kvb_update_out), _vp,
                                   ctypes.c_size_t, _vp]
     lib.chunk_attention.argtypes = [ctypes.POINTER(kvb_attn_desc), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
-    for f in ("kvbank_workspace_size", "kvbank_score", "kvbank_update", "chunk_attention"):
+    lib.chunk_attention_workspace_size.argtypes = [ctypes.POINTER(kvb_attn_desc), ctypes.POINTER(ctypes.c_size_t)]
+    for f in ("kvbank_workspace_size", "kvbank_score", "kvbank_update", "chunk_attention",
+              "chunk_attention_workspace_size"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kvb_last_error.restype = ctypes.c_char_p
     lib.kvb_last_error.argtypes = []
@@ -296,11 +299,26 @@ def kvbank_update(layer: LayerDesc, bank: Optional[Bank], cand_k, cand_v, cand_t
                              ctypes.byref(co), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
+def chunk_attention_workspace_size(H: int, d: int, Lq: int, dtype: int) -> int:
+    lib = load_library()
+    desc = kvb_attn_desc(int(H), int(d), int(Lq), int(dtype), 0.0, 1, 0, 0)
+    n = ctypes.c_size_t(0)
+    _check(lib.chunk_attention_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
 def chunk_attention(H: int, d: int, Lq: int, dtype: int, Q, segs, nseg, seg_cap: int, O, scale: float = 0.0,
-                    out_f32: bool = False, stream=None):
+                    out_f32: bool = False, stream=None, ws="auto"):
+    """ws: a device uint8 tensor of at least chunk_attention_workspace_size
+    bytes (balanced grid), None (one work-group per item), or "auto" (a
+    workspace tensor is allocated here)."""
     lib = load_library()
     kd = _kv_dtype(dtype)
     _req(Q, "Q", kd, (H, Lq, d))
     desc = kvb_attn_desc(int(H), int(d), int(Lq), int(dtype), float(scale), int(seg_cap), int(bool(out_f32)), 0)
-    _check(lib.chunk_attention(ctypes.byref(desc), _ptr(Q), _ptr(segs), _ptr(nseg), _ptr(O), None, 0,
-                               _stream(stream)))
+    if isinstance(ws, str):
+        import torch
+        n = chunk_attention_workspace_size(H, d, Lq, dtype)
+        ws = torch.empty(n, dtype=torch.uint8, device=Q.device) if n > 0 else None
+    _check(lib.chunk_attention(ctypes.byref(desc), _ptr(Q), _ptr(segs), _ptr(nseg), _ptr(O), _ptr(ws),
+                               0 if ws is None else ws.numel(), _stream(stream)))

@@ -443,7 +443,6 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
 
 int chunk_attention(const kvb_attn_desc* A, const void* Q, const kvb_segment* segs, const int32_t* nseg, void* O,
                     void* ws, size_t ws_bytes, kvb_stream_t stream) {
-  (void)ws; (void)ws_bytes;
   if (!A) return fail(KVB_EINVAL, "attention descriptor is NULL");
   if (A->H < 1 || A->H > KVB_MAX_HEADS) return fail(KVB_ESHAPE, "H=%d", A->H);
   if (A->d != 64 && A->d != 128) return fail(KVB_ESHAPE, "d=%d (supported: 64, 128)", A->d);
@@ -459,7 +458,24 @@ int chunk_attention(const kvb_attn_desc* A, const void* Q, const kvb_segment* se
   a.H = A->H; a.d = A->d; a.Lq = A->Lq; a.et = A->dtype; a.out_f32 = A->dtype == KVB_F32 ? 1 : (A->out_f32 ? 1 : 0);
   a.scale = A->scale > 0.0f ? A->scale : 1.0f / sqrtf((float)A->d);
   a.Q = Q; a.O = O; a.segs = reinterpret_cast<const SegEntry*>(segs); a.nseg = nseg; a.seg_cap = A->seg_cap;
+  if (ws) {
+    const AttnPlan p = attention_plan(A->H, A->d, A->Lq, A->dtype);
+    if (int rc = check_ws(ws, ws_bytes, (size_t)p.bytes)) return rc;
+    a.ws = ws;
+    a.ws_bytes = ws_bytes;
+  }
   HIPCHK(launch_attention(a, (hipStream_t)stream));
+  return ok();
+}
+
+static_assert(KVB_MAX_HEADS <= ATT_MAX_HEADS, "attention plan holds every head");
+
+int chunk_attention_workspace_size(const kvb_attn_desc* A, size_t* bytes) {
+  if (!A || !bytes) return fail(KVB_EINVAL, "NULL argument");
+  if (A->H < 1 || A->H > KVB_MAX_HEADS) return fail(KVB_ESHAPE, "H=%d", A->H);
+  if (A->d != 64 && A->d != 128) return fail(KVB_ESHAPE, "d=%d (supported: 64, 128)", A->d);
+  if (A->Lq < 0) return fail(KVB_ESHAPE, "Lq=%d", A->Lq);
+  *bytes = (size_t)attention_plan(A->H, A->d, A->Lq, A->dtype).bytes;
   return ok();
 }
 

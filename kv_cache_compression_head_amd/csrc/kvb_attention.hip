@@ -88,11 +88,26 @@ KVB_DEV i32x4_t buf_rsrc(const void* base, int nbytes) {
   return r;
 }
 
+// O[off .. off + 3] = v * inv, as fp32 or bf16
+KVB_DEV void attn_store(void* O, int out_f32, int64_t off, f32x4_t v, float inv) {
+  if (out_f32) {
+    const float4 r = {v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv};
+    *reinterpret_cast<float4*>((float*)O + off) = r;
+  } else {
+    uint2 r;
+    r.x = pack_bf16x2(v[0] * inv, v[1] * inv);
+    r.y = pack_bf16x2(v[2] * inv, v[3] * inv);
+    *reinterpret_cast<uint2*>((uint16_t*)O + off) = r;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __restrict__ Q, void* __restrict__ O,
                                                            const SegEntry* __restrict__ segs,
                                                            const int32_t* __restrict__ nseg_p, int seg_cap, int Lq,
-                                                           float scale_log2, int out_f32, int nqt) {
+                                                           float scale_log2, int out_f32, int nqt, int H,
+                                                           int rounds, int Ir, f32x4_t* __restrict__ part,
+                                                           int32_t* __restrict__ pflag) {
   using Op = Ops<uint16_t>;
   constexpr int NKS = D / 32;             // k-steps for S^T
   constexpr int NDB = D / 16;             // d blocks for O^T
@@ -108,44 +123,72 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
   __shared__ const void* s_k[ATT_MAXSEG];
   __shared__ const void* s_v[ATT_MAXSEG];
 
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);   // head-major items, one XCD per range
-  const int h = bid / nqt;
-  const int qt = bid % nqt;
+  const int G = gridDim.x;
+  const int bl = xcd_remap(blockIdx.x, G);   // head-major items, one XCD per range
   const int lane = lane_id(), w = wave_id();
   const int g = lane >> 4;
   const int tid = threadIdx.x;
 
-  int nseg = nseg_p[h];
-  nseg = nseg < ATT_MAXSEG ? nseg : ATT_MAXSEG;
-  if (tid == 0) {
-    int acc = 0;
-    for (int s = 0; s < nseg; ++s) {
-      const SegEntry e = segs[(int64_t)h * seg_cap + s];
-      s_pre[s] = acc;
-      s_k[s] = e.k;
-      s_v[s] = e.v;
-      acc += e.len;
+  // ---- work plan ----
+  // Items are (head, 128-query tile), head-major.  Without a partial buffer
+  // the grid has one work-group per item.  With one, the grid is one
+  // work-group per slot: `rounds` rounds of whole items, then the Ir items
+  // left over are balanced over all G work-groups.  Each of those keeps a
+  // main piece, key tiles [0, T), in the work-group of its own index (so
+  // the work-groups of a head sweep its keys together, as in the plain
+  // grid); the tails [T, n) go to the remaining G - Ir work-groups, each
+  // taking up to k consecutive items of one head (the same tail keys, read
+  // from L2 after the first).  T is the smallest length at or above the
+  // even share for which the tails fit, counting one tile of start-up per
+  // extra piece.  Every work-group derives the same T from the segment
+  // lengths.  Split items leave fp32 partials that attn_merge_kernel adds.
+  __shared__ int s_nt[ATT_MAX_HEADS];
+  __shared__ int s_T;
+  const int base = rounds * G;          // first left-over item
+  const int h0 = base / nqt;
+  int T = 0;
+  if (Ir > 0) {
+    if (w == 0) {
+      for (int hh = h0 + lane; hh < H; hh += 64) {
+        const int ns = min(nseg_p[hh], min(seg_cap, ATT_MAXSEG));
+        int64_t len = 0;
+        for (int s = 0; s < ns; ++s) len += segs[(int64_t)hh * seg_cap + s].len;
+        s_nt[hh] = (int)((len + ATT_TK - 1) / ATT_TK);
+      }
     }
-    s_pre[nseg] = acc;
+    __syncthreads();
+    if (w == 0) {
+      int64_t work = 0;
+      int ntmax = 0;
+      for (int hh = h0; hh < H; ++hh) {
+        const int cnt = (hh + 1) * nqt - max(hh * nqt, base);
+        work += (int64_t)cnt * s_nt[hh];
+        ntmax = max(ntmax, s_nt[hh]);
+      }
+      const int tlo = max(1, (int)((work + G - 1) / G));
+      const int tc = tlo + lane;   // candidate lengths, one per lane
+      int need = 0;
+      bool ok = true;
+      for (int hh = h0; hh < H; ++hh) {
+        const int cnt = (hh + 1) * nqt - max(hh * nqt, base);
+        const int r = s_nt[hh] - tc;
+        if (r > 0) {
+          const int k = tc / (r + 1);
+          if (k == 0) ok = false;
+          else need += (cnt + k - 1) / k;
+        }
+      }
+      ok = ok && need <= G - Ir;
+      const uint64_t m = __ballot(ok);
+      if (lane == 0) s_T = m ? tlo + (int)__builtin_ctzll(m) : ntmax;
+    }
+    __syncthreads();
+    T = __builtin_amdgcn_readfirstlane(s_T);
   }
-  __syncthreads();
-  const int Lkv = __builtin_amdgcn_readfirstlane(s_pre[nseg]);
 
-  // query fragments (B operand of S^T = K Q^T)
-  const int q0 = qt * ATT_QB + w * ATT_QW;
+  // per-piece state (set by `piece` below)
+  int h = -1, nseg = 0, Lkv = 0, q0 = 0, t_beg = 0, t_end = 0;
   s16x8_t qf[2][NKS];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int q = q0 + 16 * qb + (lane & 15);
-    const uint16_t* qp = Q + ((int64_t)h * Lq + (q < Lq ? q : 0)) * D;
-#pragma unroll
-    for (int k = 0; k < NKS; ++k) {
-      if (q < Lq) qf[qb][k] = Op::load(qp + Op::off16(k, lane));
-      else qf[qb][k] = s16x8_t{};
-    }
-  }
-
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): query fragments resident before the loop
   f32x4_t o[NDB][2];
   float m_run[2];
   // softmax denominators, accumulated by MFMA from the same bf16 weights as
@@ -185,7 +228,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
     return (const void*)(((uint64_t)vh << 32) | (uint64_t)vl);
   };
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  auto fetch = [&](int kbase, uint16_t* sKn, uint16_t* sVn) {
+  auto fetch = [&](int kbase, uint16_t* sKn, uint16_t* sVn) __attribute__((always_inline)) {
     if (kbase < ulo || kbase + ATT_TK > uhi) {
       if (kbase < ulo) ucur = 0;   // a new pass over the tiles
       while (ucur + 1 < nseg && __builtin_amdgcn_readfirstlane(s_pre[ucur + 1]) <= kbase) ++ucur;
@@ -238,7 +281,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
       vread[db] = r * D + (((2 * db + ((a & 3) >> 1)) ^ att_swz<CPR>(r)) * 8) + (a & 1) * 4;
   }
 
-  const int ntile = (Lkv + ATT_TK - 1) / ATT_TK;
   // Softmax modes of one tile.  FIRST: the tile's maximum becomes the
   // query's reference m (first tile of the fast pass).  FAST: weights
   // 2^(s c - m) against that fixed reference, no maximum taken: exact
@@ -247,10 +289,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
   // moved only when a tile raises it by more than 2^8 (numerator and
   // denominator are rescaled together).
   constexpr int FIRST = 0, FAST = 1, SAFE = 2;
-  auto step = [&](auto mode_c, int tile, const uint16_t* sKc, const uint16_t* sVc, uint16_t* sKn, uint16_t* sVn) {
+  auto step = [&](auto mode_c, int tile, const uint16_t* sKc, const uint16_t* sVc, uint16_t* sKn,
+                  uint16_t* sVn) __attribute__((always_inline)) {
     constexpr int mode = decltype(mode_c)::value;
     const int kbase = tile * ATT_TK;
-    const bool more = tile + 1 < ntile;
+    const bool more = tile + 1 < t_end;
     if (more) fetch(kbase + ATT_TK, sKn, sVn);
 
     // ---- S^T = K Q^T ----
@@ -363,61 +406,191 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
     __builtin_amdgcn_s_waitcnt(0x0F70);   // next K and V tiles resident in LDS
     __syncthreads();
   };
-  auto reset = [&]() {
+  auto reset = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     m_run[0] = m_run[1] = -__builtin_inff();
     L[0] = L[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (ntile > 0) fetch(0, sK0, sV0);
+    if (t_beg < t_end) fetch(t_beg * ATT_TK, sK0, sV0);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   };
 
-  // fast pass (tile t in buffer set t & 1)
-  reset();
-  if (ntile > 0) step(std::integral_constant<int, FIRST>{}, 0, sK0, sV0, sK1, sV1);
-  for (int tile = 1; tile < ntile; tile += 2) {
-    step(std::integral_constant<int, FAST>{}, tile, sK1, sV1, sK0, sV0);
-    if (tile + 1 < ntile) step(std::integral_constant<int, FAST>{}, tile + 1, sK0, sV0, sK1, sV1);
-  }
-  // a non-finite numerator or denominator anywhere in the work-group (a
-  // query whose scores rose by about 2^127 past its first tile's): redo the
-  // work-group's tiles with the running-maximum pass
-  float chk = L[0][0] + L[1][0];
+  // One piece: key tiles [t0, t1) of item (head, query tile).  slot < 0:
+  // the whole item, normalised into O; slot 0 / 1: the main piece / the
+  // tail of left-over item ir, stored unnormalised with its reference and
+  // denominator.  flag: the main piece (or whole left-over item) records
+  // whether the item was split.
+  auto piece = [&](int item, int t0, int t1, int slot, int ir) __attribute__((always_inline)) {
+    const int hn = item / nqt, qt = item % nqt;
+    if (hn != h) {
+      // every wave's last table read came before the previous barrier
+      h = hn;
+      nseg = min(nseg_p[h], min(seg_cap, ATT_MAXSEG));
+      if (tid == 0) {
+        int acc = 0;
+        for (int s = 0; s < nseg; ++s) {
+          const SegEntry e = segs[(int64_t)h * seg_cap + s];
+          s_pre[s] = acc;
+          s_k[s] = e.k;
+          s_v[s] = e.v;
+          acc += e.len;
+        }
+        s_pre[nseg] = acc;
+      }
+      __syncthreads();
+      Lkv = __builtin_amdgcn_readfirstlane(s_pre[nseg]);
+    }
+    ucur = 0;
+    ulo = 0;
+    uhi = -1;   // the next fetch seeks its segment
+    const int ntile = (Lkv + ATT_TK - 1) / ATT_TK;
+    t_beg = t0;
+    t_end = min(t1, ntile);
+
+    // query fragments (B operand of S^T = K Q^T)
+    q0 = qt * ATT_QB + w * ATT_QW;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int qb = 0; qb < 2; ++qb) {
+      const int q = q0 + 16 * qb + (lane & 15);
+      const uint16_t* qp = Q + ((int64_t)h * Lq + (q < Lq ? q : 0)) * D;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) chk += (o[db][qb][0] + o[db][qb][1]) + (o[db][qb][2] + o[db][qb][3]);
-  if (__syncthreads_or(!__builtin_isfinite(chk))) {
+      for (int k = 0; k < NKS; ++k) {
+        if (q < Lq) qf[qb][k] = Op::load(qp + Op::off16(k, lane));
+        else qf[qb][k] = s16x8_t{};
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): query fragments resident before the tiles
+
+    // fast pass (tile t in buffer set (t - t0) & 1)
     reset();
-    for (int tile = 0; tile < ntile; tile += 2) {
-      step(std::integral_constant<int, SAFE>{}, tile, sK0, sV0, sK1, sV1);
-      if (tile + 1 < ntile) step(std::integral_constant<int, SAFE>{}, tile + 1, sK1, sV1, sK0, sV0);
+    if (t_beg < t_end) step(std::integral_constant<int, FIRST>{}, t_beg, sK0, sV0, sK1, sV1);
+    for (int tile = t_beg + 1; tile < t_end; tile += 2) {
+      step(std::integral_constant<int, FAST>{}, tile, sK1, sV1, sK0, sV0);
+      if (tile + 1 < t_end) step(std::integral_constant<int, FAST>{}, tile + 1, sK0, sV0, sK1, sV1);
+    }
+    // a non-finite numerator or denominator anywhere in the work-group (a
+    // query whose scores rose by about 2^127 past its first tile's): redo the
+    // piece's tiles with the running-maximum pass
+    float chk = L[0][0] + L[1][0];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) chk += (o[db][qb][0] + o[db][qb][1]) + (o[db][qb][2] + o[db][qb][3]);
+    if (__syncthreads_or(!__builtin_isfinite(chk))) {
+      reset();
+      for (int tile = t_beg; tile < t_end; tile += 2) {
+        step(std::integral_constant<int, SAFE>{}, tile, sK0, sV0, sK1, sV1);
+        if (tile + 1 < t_end) step(std::integral_constant<int, SAFE>{}, tile + 1, sK1, sV1, sK0, sV0);
+      }
+    }
+
+    if (slot >= 0) {
+      // ---- partial: lane's o (NDB x 2 vectors), then {m0, m1, L0, L1} ----
+      f32x4_t* pp = part + (((int64_t)ir * 2 + slot) * 4 + w) * (2 * NDB + 1) * 64 + lane;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) pp[(2 * db + qb) * 64] = o[db][qb];
+      pp[2 * NDB * 64] = f32x4_t{m_run[0], m_run[1], L[0][0], L[1][0]};
+      if (slot == 0 && tid == 0) pflag[ir] = 1;
+      return;
+    }
+    if (ir >= 0 && tid == 0) pflag[ir] = 0;
+    // ---- normalise and store: lane holds O[q][16db + 4g + i] ----
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float l = L[qb][0];
+      const float inv = l > 0.f ? 1.0f / l : 0.0f;
+      const int q = q0 + 16 * qb + (lane & 15);
+      if (q < Lq) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          attn_store(O, out_f32, ((int64_t)h * Lq + q) * D + 16 * db + 4 * g, o[db][qb], inv);
+      }
+    }
+  };
+
+  // this work-group's tail range: items [tl_first, tl_first + tl_cnt) of
+  // one head, key tiles [T, tl_nt)
+  int tl_first = 0, tl_cnt = 0, tl_nt = 0;
+  if (Ir > 0 && bl >= Ir) {
+    int c = bl - Ir;
+    for (int hh = h0; hh < H; ++hh) {
+      const int cnt = (hh + 1) * nqt - max(hh * nqt, base);
+      const int r = s_nt[hh] - T;
+      if (r <= 0) continue;
+      const int k = T / (r + 1);
+      const int nh = (cnt + k - 1) / k;
+      if (c < nh) {
+        tl_first = max(hh * nqt, base) + c * k;
+        tl_cnt = min(cnt, (c + 1) * k) - c * k;
+        tl_nt = s_nt[hh];
+        break;
+      }
+      c -= nh;
     }
   }
+  // pieces in order: whole items of each round, then the main piece (or the
+  // whole left-over item) or the tails; one call site keeps one copy of the
+  // tile loop
+  const int npieces = rounds + (Ir > 0 ? (bl < Ir ? 1 : tl_cnt) : 0);
+  for (int pc = 0; pc < npieces; ++pc) {
+    int item, t0 = 0, t1 = 1 << 30, slot = -1, ir = -1;
+    if (pc < rounds) {
+      item = pc * G + bl;
+    } else if (bl < Ir) {
+      item = base + bl;
+      ir = bl;
+      const int nt = s_nt[item / nqt];
+      if (nt > T) {
+        t1 = T;
+        slot = 0;
+      }
+    } else {
+      item = tl_first + (pc - rounds);
+      ir = item - base;
+      t0 = T;
+      t1 = tl_nt;
+      slot = 1;
+    }
+    piece(item, t0, t1, slot, ir);
+  }
+}
 
-  // ---- normalise and store: lane holds O[q][16db + 4g + i] ----
+// Merge of the two pieces of a split item: weights against the larger of
+// the two references, o = (o0 a0 + o1 a1) / (L0 a0 + L1 a1).  One
+// work-group per left-over item, lanes laid out as in attn_bf16_kernel.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(void* __restrict__ O, const f32x4_t* __restrict__ part,
+                                                         const int32_t* __restrict__ pflag, int base, int nqt,
+                                                         int Lq, int out_f32) {
+  constexpr int NDB = D / 16;
+  const int ir = blockIdx.x;
+  if (pflag[ir] == 0) return;
+  const int item = base + ir, h = item / nqt, qt = item % nqt;
+  const int lane = lane_id(), w = wave_id(), g = lane >> 4;
+  const f32x4_t* p0 = part + (((int64_t)ir * 2 + 0) * 4 + w) * (2 * NDB + 1) * 64 + lane;
+  const f32x4_t* p1 = p0 + 4 * (2 * NDB + 1) * 64;
+  const f32x4_t s0 = p0[2 * NDB * 64], s1 = p1[2 * NDB * 64];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float l = L[qb][0];
+    const float m0 = s0[qb], m1 = s1[qb];
+    const float mx = fmaxf(m0, m1);
+    const float a0 = mx == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m0 - mx);
+    const float a1 = mx == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m1 - mx);
+    const float l = s0[2 + qb] * a0 + s1[2 + qb] * a1;
     const float inv = l > 0.f ? 1.0f / l : 0.0f;
-    const int q = q0 + 16 * qb + (lane & 15);
+    const int q = qt * ATT_QB + w * ATT_QW + 16 * qb + (lane & 15);
     if (q < Lq) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int d0 = 16 * db + 4 * g;
-        const int64_t off = ((int64_t)h * Lq + q) * D + d0;
-        if (out_f32) {
-          float4 v = {o[db][qb][0] * inv, o[db][qb][1] * inv, o[db][qb][2] * inv, o[db][qb][3] * inv};
-          *reinterpret_cast<float4*>((float*)O + off) = v;
-        } else {
-          uint2 pkv;
-          pkv.x = pack_bf16x2(o[db][qb][0] * inv, o[db][qb][1] * inv);
-          pkv.y = pack_bf16x2(o[db][qb][2] * inv, o[db][qb][3] * inv);
-          *reinterpret_cast<uint2*>((uint16_t*)O + off) = pkv;
-        }
+        const f32x4_t v0 = p0[(2 * db + qb) * 64], v1 = p1[(2 * db + qb) * 64];
+        const f32x4_t v = {v0[0] * a0 + v1[0] * a1, v0[1] * a0 + v1[1] * a1, v0[2] * a0 + v1[2] * a1,
+                           v0[3] * a0 + v1[3] * a1};
+        attn_store(O, out_f32, ((int64_t)h * Lq + q) * D + 16 * db + 4 * g, v, inv);
       }
     }
   }
@@ -440,7 +613,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 #pragma unroll
   for (int i = 0; i < D; ++i) acc[i] = 0.f;
   float m = -__builtin_inff(), l = 0.f;
-  const int ns = nseg_p[h];
+  const int ns = min(nseg_p[h], seg_cap);
   for (int s = 0; s < ns; ++s) {
     const SegEntry e = segs[(int64_t)h * seg_cap + s];
     const float* kp = (const float*)e.k;
@@ -465,18 +638,62 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
   for (int i = 0; i < D; ++i) op[i] = acc[i] * inv;
 }
 
+// Balanced-grid plan of a bf16 launch: G work-groups (one per slot, two per
+// compute unit at the kernel's register use), `rounds` rounds of whole
+// items, Ir left-over items whose partials need `bytes` of workspace.
+AttnPlan attention_plan(int H, int d, int Lq, int et) {
+  AttnPlan p{};
+  if (et != ET_BF16 || Lq <= 0 || H <= 0) return p;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  const int items = ((Lq + ATT_QB - 1) / ATT_QB) * H;
+  p.G = 2 * cus;
+  p.rounds = items / p.G;
+  p.Ir = items % p.G;
+  const int64_t per_item = 2LL * 4 * (2 * (d / 16) + 1) * 64 * 16;   // two pieces, 4 waves, float4 per lane
+  p.flag_bytes = ((int64_t)p.Ir * 4 + 255) / 256 * 256;
+  p.bytes = p.Ir > 0 ? p.flag_bytes + p.Ir * per_item : 0;
+  return p;
+}
+
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t st) {
   if (a.Lq <= 0 || a.H <= 0) return hipSuccess;
   if (a.et == ET_BF16) {
     const float sl2 = a.scale * 1.4426950408889634f;
     const int nqt = (a.Lq + ATT_QB - 1) / ATT_QB;
-    const dim3 grid((unsigned)(nqt * a.H));
+    const int items = nqt * a.H;
+    // balanced grid when a workspace is given (and there is a round to fill)
+    AttnPlan p = attention_plan(a.H, a.d, a.Lq, a.et);
+    const bool bal = a.ws != nullptr && a.ws_bytes >= (size_t)p.bytes && (p.Ir > 0 || p.rounds > 0);
+    int G = items, rounds = 1, Ir = 0;
+    int32_t* flag = nullptr;
+    f32x4_t* part = nullptr;
+    if (bal) {
+      G = p.G;
+      rounds = p.rounds;
+      Ir = p.Ir;
+      if (Ir > 0) {
+        flag = (int32_t*)a.ws;
+        part = (f32x4_t*)((char*)a.ws + p.flag_bytes);
+      }
+    }
     if (a.d == 128)
-      hipLaunchKernelGGL((attn_bf16_kernel<128>), grid, dim3(256), 0, st, (const uint16_t*)a.Q, a.O, a.segs, a.nseg,
-                         a.seg_cap, a.Lq, sl2, a.out_f32, nqt);
+      hipLaunchKernelGGL((attn_bf16_kernel<128>), dim3((unsigned)G), dim3(256), 0, st, (const uint16_t*)a.Q, a.O,
+                         a.segs, a.nseg, a.seg_cap, a.Lq, sl2, a.out_f32, nqt, a.H, rounds, Ir, part, flag);
     else
-      hipLaunchKernelGGL((attn_bf16_kernel<64>), grid, dim3(256), 0, st, (const uint16_t*)a.Q, a.O, a.segs, a.nseg,
-                         a.seg_cap, a.Lq, sl2, a.out_f32, nqt);
+      hipLaunchKernelGGL((attn_bf16_kernel<64>), dim3((unsigned)G), dim3(256), 0, st, (const uint16_t*)a.Q, a.O,
+                         a.segs, a.nseg, a.seg_cap, a.Lq, sl2, a.out_f32, nqt, a.H, rounds, Ir, part, flag);
+    if (Ir > 0) {
+      if (a.d == 128)
+        hipLaunchKernelGGL((attn_merge_kernel<128>), dim3((unsigned)Ir), dim3(256), 0, st, a.O, part, flag,
+                           rounds * G, nqt, a.Lq, a.out_f32);
+      else
+        hipLaunchKernelGGL((attn_merge_kernel<64>), dim3((unsigned)Ir), dim3(256), 0, st, a.O, part, flag,
+                           rounds * G, nqt, a.Lq, a.out_f32);
+    }
   } else {
     const dim3 grid((unsigned)((a.Lq + 63) / 64), (unsigned)a.H);
     if (a.d == 128)

@@ -11,7 +11,8 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import (KVB_BF16, KVB_F32, Bank, KVLayout, LayerDesc, UpdateOut, chunk_attention, kvb_segment,
+from . import (KVB_BF16, KVB_F32, Bank, KVLayout, LayerDesc, UpdateOut, chunk_attention,
+               chunk_attention_workspace_size, kvb_segment,
                kvbank_score, kvbank_update, kvbank_workspace_size)
 
 
@@ -29,6 +30,7 @@ class LayerCache:
         self.bank = Bank.empty(self.H, max(self.M, 1), self.d, self.kdt) if self.M > 0 else None
         self.out = UpdateOut.alloc(self.H, seg_cap, self.M, diagnostics)
         self.ws = None
+        self._aws = None
         self._ws_N = -1
         self._bufs = {}
         if max_N:
@@ -72,8 +74,12 @@ class LayerCache:
         H, Lq, d = Q.shape
         if O is None:
             O = torch.empty(H, Lq, d, dtype=torch.float32 if out_f32 else Q.dtype, device=Q.device)
+        # the balanced grid's partials: kept between calls, grown on demand
+        n = chunk_attention_workspace_size(H, d, Lq, self.desc.dtype)
+        if n > 0 and (self._aws is None or self._aws.numel() < n):
+            self._aws = torch.empty(n, dtype=torch.uint8, device=Q.device)
         chunk_attention(H, d, Lq, self.desc.dtype, Q, self.out.segs, self.out.nseg, self.out.seg_cap, O,
-                        out_f32=out_f32)
+                        out_f32=out_f32, ws=self._aws if n > 0 else None)
         return O
 
     # -- host views of the results (synchronising) --------------------------

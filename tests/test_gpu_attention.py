@@ -32,10 +32,13 @@ def _seg_table(H, seg_cap, per_head):
     (64, 48, [[16, 64, 48], [16, 60, 48]], "f32"),
     (128, 700, [[0], [3000, 17], [], [64]], "bf16"),
 ])
-def test_attention_ragged(d, Lq, lens, dtype):
+@pytest.mark.parametrize("ws", ["auto", None])
+def test_attention_ragged(d, Lq, lens, dtype, ws):
     """Ragged segment tables; heads with no keys (an empty segment, or none)
-    give zeros."""
-    _attention_case(d, Lq, lens, dtype)
+    give zeros.  ws "auto": the balanced grid (left-over items cut into a
+    main piece and a tail, merged from fp32 partials); None: one work-group
+    per item."""
+    _attention_case(d, Lq, lens, dtype, ws=ws)
 
 
 # Segments whose key scales differ by large factors: the running maximum of a
@@ -55,10 +58,10 @@ def test_attention_rescale(d, Lq, lens, kscale):
     _attention_case(d, Lq, lens, "bf16", kscale)
 
 
-def _attention_case(d, Lq, lens, dtype, kscale=None):
+def _attention_case(d, Lq, lens, dtype, kscale=None, ws="auto", heads=None, ret=False):
     import torch
     import kv_cache_compression_head_amd as kb
-    gc.banner(f"attention d={d} Lq={Lq} lens={lens} {dtype} kscale={kscale}")
+    gc.banner(f"attention d={d} Lq={Lq} lens={lens} {dtype} kscale={kscale} ws={ws}")
     rng = np.random.default_rng(d + Lq)
     H = len(lens)
     kdt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -87,12 +90,14 @@ def _attention_case(d, Lq, lens, dtype, kscale=None):
     Qd = gc.dev(Q, kdt)
     O = torch.empty(H, Lq, d, dtype=torch.float32, device="cuda")
     et = kb.KVB_BF16 if dtype == "bf16" else kb.KVB_F32
-    kb.chunk_attention(H, d, Lq, et, Qd, segs_t, nseg_t, seg_cap, O, out_f32=True)
+    kb.chunk_attention(H, d, Lq, et, Qd, segs_t, nseg_t, seg_cap, O, out_f32=True, ws=ws)
     torch.cuda.synchronize()
     On = O.cpu().numpy()
+    if ret:
+        return On
     tol = (2e-2, 2e-3) if dtype == "bf16" else (1e-4, 1e-5)
     errs = []
-    for h in range(H):
+    for h in (range(H) if heads is None else heads):
         if Ks[h].shape[0] == 0:   # no keys: the kernels write zeros
             assert np.all(On[h] == 0.0), f"head {h} without keys"
             continue
@@ -121,3 +126,44 @@ def test_attention_bf16_output_dtype():
         ref = oracle_attention(Q[h].astype(np.float64), K[h].astype(np.float64), V[h].astype(np.float64))
         e = np.abs(On[h] - ref)
         assert e.max() <= 2e-2 and e.mean() <= 2e-3
+
+
+def test_attention_balanced_rounds():
+    """More items than slots (8 heads x 65 query tiles = 520 on 512 slots):
+    a round of whole items, then the 8 left-over items balanced over every
+    work-group; heads of different lengths."""
+    lens = [[300 + 97 * h, 64 * h] for h in range(8)]
+    _attention_case(128, 8200, lens, "bf16")
+
+
+def test_attention_balanced_multi_tail():
+    """12 heads x 37 query tiles over 6,400 keys: the tails are short
+    enough that each tail work-group takes several items of one head.
+    Three heads against the oracle; every head against the one-work-group-
+    per-item grid."""
+    lens = [[1560, 3200, 1640] for _ in range(12)]
+    _attention_case(128, 4680, lens, "bf16", heads=[0, 6, 11])
+    a = _attention_case(128, 4680, lens, "bf16", ret=True)
+    b = _attention_case(128, 4680, lens, "bf16", ws=None, ret=True)
+    e = np.abs(a - b)
+    assert e.max() <= 1e-2 and e.mean() <= 1e-3, (e.max(), e.mean())
+
+
+def test_attention_balanced_d64():
+    """d = 64 on the balanced grid, with a ragged tail tile."""
+    _attention_case(64, 1000, [[900, 333], [1500], [64, 64, 7]], "bf16")
+
+
+def test_attention_workspace_size():
+    """The workspace covers the left-over items' partials: two pieces of
+    4 waves x (2 d/16 + 1) float4 per lane each, plus a flag per item."""
+    import kv_cache_compression_head_amd as kb
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for H, d, Lq in [(12, 128, 4680), (8, 128, 8200), (3, 64, 300)]:
+        items = -(-Lq // 128) * H
+        ir = items % (2 * cus)
+        per = 2 * 4 * (2 * (d // 16) + 1) * 64 * 16
+        want = 0 if ir == 0 else -(-ir * 4 // 256) * 256 + ir * per
+        assert kb.chunk_attention_workspace_size(H, d, Lq, kb.KVB_BF16) == want
+    assert kb.chunk_attention_workspace_size(12, 128, 4680, kb.KVB_F32) == 0
