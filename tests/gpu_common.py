@@ -67,9 +67,17 @@ def run_update(lc, gen: LayerGen, wl: Workload, prm: od.Params, frames: Tuple[in
     torch.cuda.synchronize()
     st = int(lc.out.status.cpu()[0])
     assert st == 0, f"device status {st:#x}"
+    # every disturbance, and every live slot's densities, finite (the
+    # oracle comparisons below sample rows; a padding row leaking into a
+    # list's last row would show here)
+    assert np.all(np.isfinite(D.cpu().numpy())), "non-finite disturbance"
     if not replay:
         return None
     after = GpuBank.read(lc.bank)
+    for h in range(after.count.shape[0]):
+        n = int(after.count[h])
+        assert np.all(np.isfinite(after.rho[h, :n])) and np.all(np.isfinite(after.rho0[h, :n])), \
+            f"non-finite density in head {h}"
     return replay_update(before, after, candK.astype(np.float64), candV.astype(np.float64), np.asarray(ctok),
                          D.cpu().numpy(), s.cpu().numpy(), o.cpu().numpy(), lc.out.t_cross.cpu().numpy(),
                          lc.out.rho_proj.cpu().numpy(), int(lc.out.k_star.cpu()[0]),
