@@ -321,7 +321,13 @@ def main():
     attn_tflops = attn_flop / (avg["attention"] * 1e-3) / 1e12
     # algorithmic bytes of the attention launch: Q + O + each head's K and V once
     attn_bytes = sum(2 * wl.Lq * wl.d * 2 + 2 * l * wl.d * 2 for l in lkv)
-    roof = {"kernel": "attn_bf16_kernel (chunk_attention)", "bound": "mfma", "achieved": round(attn_tflops, 2),
+    # the chunk_attention call: attn_bf16_kernel, plus attn_merge_kernel when
+    # the balanced grid splits items (timed together, as one call)
+    import kv_cache_compression_head_amd as kb
+    bal = kb.chunk_attention_workspace_size(wl.H, wl.d, wl.Lq, kb.KVB_BF16) > 0
+    kname = "attn_bf16_kernel + attn_merge_kernel" if bal else "attn_bf16_kernel"
+    roof = {"kernel": f"{kname} (chunk_attention)", "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": recorded_attention_traffic(args.config), "algorithmic_flop_per_launch": attn_flop,
             "algorithmic_bytes_per_launch": attn_bytes}

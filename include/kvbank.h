@@ -193,11 +193,13 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
  * (DensityKV card page Figure 2; Forcing-KV section 3.3):
  *   O_h = softmax(Q_h K_h^T * scale) V_h,  Q, O [H][Lq][d].
  * ws (device, optional, caller-owned, 256-byte aligned): with ws_bytes >=
- * chunk_attention_workspace_size(A), the bf16 path balances its work over
- * every slot of the GPU: items (head, 128-query tile) left over after whole
- * rounds are cut along the keys into a main piece and a tail, whose fp32
- * partials (o, reference, denominator) a second kernel merges.  ws = NULL
- * runs one work-group per item.  Both give the same result up to rounding.
+ * chunk_attention_workspace_size(A) > 0, the bf16 path balances its work
+ * over every slot of the GPU: items (head, 128-query tile) left over after
+ * whole rounds are cut along the keys into a main piece and a tail, whose
+ * fp32 partials (o, reference, denominator) a second kernel merges.  This is
+ * taken only when one work-group per item would leave the last round at
+ * least a fifth empty (the size is then 0 otherwise).  ws = NULL runs one
+ * work-group per item.  Both give the same result up to rounding.
  * A too-small non-NULL workspace is KVB_EWORKSPACE.  Calls that share one
  * workspace must not overlap. */
 int chunk_attention(const kvb_attn_desc* A, const void* Q, const kvb_segment* segs, const int32_t* nseg, void* O,

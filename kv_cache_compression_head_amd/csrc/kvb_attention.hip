@@ -640,7 +640,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 
 // Balanced-grid plan of a bf16 launch: G work-groups (one per slot, two per
 // compute unit at the kernel's register use), `rounds` rounds of whole
-// items, Ir left-over items whose partials need `bytes` of workspace.
+// items, Ir left-over items whose partials need `bytes` of workspace; `use`
+// says whether the balanced grid is taken at all.
 AttnPlan attention_plan(int H, int d, int Lq, int et) {
   AttnPlan p{};
   if (et != ET_BF16 || Lq <= 0 || H <= 0) return p;
@@ -653,9 +654,19 @@ AttnPlan attention_plan(int H, int d, int Lq, int et) {
   p.G = 2 * cus;
   p.rounds = items / p.G;
   p.Ir = items % p.G;
+  // Balance only a last round that the plain grid would leave at least a
+  // fifth empty.  A nearly full round gains nothing here: the chip runs
+  // this kernel at its power limit, so the idle slots' share of the budget
+  // already goes to the busy ones (measured at 87 % full: equal time, 1.7x
+  // the HBM traffic for partials and tail re-reads).
+  if (p.Ir == 0 || (int64_t)p.Ir * 5 >= (int64_t)p.G * 4) {
+    p.use = false;
+    return p;
+  }
+  p.use = true;
   const int64_t per_item = 2LL * 4 * (2 * (d / 16) + 1) * 64 * 16;   // two pieces, 4 waves, float4 per lane
   p.flag_bytes = ((int64_t)p.Ir * 4 + 255) / 256 * 256;
-  p.bytes = p.Ir > 0 ? p.flag_bytes + p.Ir * per_item : 0;
+  p.bytes = p.flag_bytes + p.Ir * per_item;
   return p;
 }
 
@@ -667,7 +678,7 @@ hipError_t launch_attention(const AttnLaunch& a, hipStream_t st) {
     const int items = nqt * a.H;
     // balanced grid when a workspace is given (and there is a round to fill)
     AttnPlan p = attention_plan(a.H, a.d, a.Lq, a.et);
-    const bool bal = a.ws != nullptr && a.ws_bytes >= (size_t)p.bytes && (p.Ir > 0 || p.rounds > 0);
+    const bool bal = p.use && a.ws != nullptr && a.ws_bytes >= (size_t)p.bytes;
     int G = items, rounds = 1, Ir = 0;
     int32_t* flag = nullptr;
     f32x4_t* part = nullptr;

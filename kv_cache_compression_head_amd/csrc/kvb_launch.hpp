@@ -160,7 +160,7 @@ struct AttnLaunch {
   const SegEntry* segs; const int32_t* nseg; int32_t seg_cap;
   void* ws; size_t ws_bytes;   // optional: enables the balanced grid (partials of split items)
 };
-struct AttnPlan { int G, rounds, Ir; int64_t flag_bytes, bytes; };
+struct AttnPlan { int G, rounds, Ir; bool use; int64_t flag_bytes, bytes; };
 constexpr int ATT_MAX_HEADS = 64;   // per-head tile counts of the balanced grid's plan live in LDS
 AttnPlan attention_plan(int H, int d, int Lq, int et);
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);

@@ -137,12 +137,12 @@ def test_attention_balanced_rounds():
 
 
 def test_attention_balanced_multi_tail():
-    """12 heads x 37 query tiles over 6,400 keys: the tails are short
-    enough that each tail work-group takes several items of one head.
-    Three heads against the oracle; every head against the one-work-group-
-    per-item grid."""
-    lens = [[1560, 3200, 1640] for _ in range(12)]
-    _attention_case(128, 4680, lens, "bf16", heads=[0, 6, 11])
+    """10 heads x 37 query tiles over 6,400 keys (370 items on 512 slots):
+    the tails are short enough that each tail work-group takes several items
+    of one head.  Three heads against the oracle; every head against the
+    one-work-group-per-item grid."""
+    lens = [[1560, 3200, 1640] for _ in range(10)]
+    _attention_case(128, 4680, lens, "bf16", heads=[0, 5, 9])
     a = _attention_case(128, 4680, lens, "bf16", ret=True)
     b = _attention_case(128, 4680, lens, "bf16", ws=None, ret=True)
     e = np.abs(a - b)
@@ -156,14 +156,16 @@ def test_attention_balanced_d64():
 
 def test_attention_workspace_size():
     """The workspace covers the left-over items' partials: two pieces of
-    4 waves x (2 d/16 + 1) float4 per lane each, plus a flag per item."""
+    4 waves x (2 d/16 + 1) float4 per lane each, plus a flag per item; none
+    when the last round of the plain grid is at least four fifths full."""
     import kv_cache_compression_head_amd as kb
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    for H, d, Lq in [(12, 128, 4680), (8, 128, 8200), (3, 64, 300)]:
+    for H, d, Lq in [(12, 128, 4680), (10, 128, 4680), (8, 128, 8200), (3, 64, 300), (12, 128, 24480)]:
         items = -(-Lq // 128) * H
         ir = items % (2 * cus)
         per = 2 * 4 * (2 * (d // 16) + 1) * 64 * 16
-        want = 0 if ir == 0 else -(-ir * 4 // 256) * 256 + ir * per
+        use = ir > 0 and ir * 5 < 2 * cus * 4
+        want = -(-ir * 4 // 256) * 256 + ir * per if use else 0
         assert kb.chunk_attention_workspace_size(H, d, Lq, kb.KVB_BF16) == want
     assert kb.chunk_attention_workspace_size(12, 128, 4680, kb.KVB_F32) == 0
