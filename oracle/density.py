@@ -34,6 +34,22 @@ Readings where the page is silent (each is listed in the design notes):
   rest (ties: lower token id first) until e(k*) states are chosen
 * admitted states get rho0 = their density in the new bank; survivors keep rho0
 
+Policy variants (the page's appendix E ablations; Params fields, defaults
+are the method above):
+
+* order "source": candidates in spatiotemporal source order, read as
+  ascending token id (frame, then row-major position), instead of by delta
+* baseline "refresh": after every update each state's baseline is its
+  density in the new bank (instead of frozen insertion-time baselines)
+* eviction "densest": the e(k*) states with the highest projected density
+  (ties: lower token id), crossed or not; "oldest": the crossed states, then
+  ascending token id (source-order completion)
+* prefix "head": every density head takes its own largest feasible k
+  instead of the layer's shared one
+* fill_below_capacity: a prefix length k with n + k <= M needs no density
+  check and evicts nothing (a reading of where the growth bound binds; the
+  page's default gates at every occupancy)
+
 Parity pins (tests/test_oracle_density.py): closed-form densities on collinear
 keys, permutation and rotation invariance, the A.1 logit-gap bound, FIFO
 reduction at p = 0 and tau = inf, full admission when capacity exceeds the
@@ -57,6 +73,12 @@ class Params:
     sigma: float = 8.0
     eps: float = 1.0
     p: float = 2.0
+    # policy variants (see the module header); defaults are the method
+    order: str = "delta"             # "delta" | "source"
+    baseline: str = "frozen"         # "frozen" | "refresh"
+    eviction: str = "threshold"      # "threshold" | "densest" | "oldest"
+    prefix: str = "shared"           # "shared" | "head"
+    fill_below_capacity: bool = False
 
 
 # ---------------------------------------------------------------------------
@@ -169,8 +191,11 @@ def disturbance(bankK: np.ndarray, candK: np.ndarray, prm: Params):
     return D, delta
 
 
-def candidate_order(delta: np.ndarray, tok: np.ndarray) -> np.ndarray:
-    """Permutation sorting candidates by ascending (delta, token id)."""
+def candidate_order(delta: np.ndarray, tok: np.ndarray, order: str = "delta") -> np.ndarray:
+    """Permutation sorting candidates by ascending (delta, token id), or by
+    token id alone for the source-order variant."""
+    if order == "source":
+        return np.argsort(np.asarray(tok, np.int64), kind="stable").astype(np.int64)
     return np.lexsort((np.asarray(tok, np.int64), np.asarray(delta, np.float64))).astype(np.int64)
 
 
@@ -210,39 +235,48 @@ def projected_density(bankK, rho, candK_sorted, k: int, prm: Params) -> np.ndarr
     return rho + phi_rowsum(bankK, np.asarray(candK_sorted, np.float64)[:k], prm)
 
 
-def feasible_prefix(ts: Sequence[np.ndarray], ns: Sequence[int], M: int, kmax: int):
-    """Largest k in [0, kmax] feasible for every density head.
-
-    |V_h(k)| = #{b : t_b <= k}; e_h(k) = max(0, n_h + k - M); feasible iff
-    |V_h(k)| <= e_h(k) for all h.  k = 0 is always feasible.
-    Returns (kstar, feasible[k] boolean array).
-    """
+def feasible_head(t: np.ndarray, n: int, M: int, kmax: int, fill_below_capacity: bool = False) -> np.ndarray:
+    """feasible[k], k in [0, kmax], for one head: |V(k)| = #{b : t_b <= k} <=
+    e(k) = max(0, n + k - M); with fill_below_capacity every k with
+    n + k <= M is feasible as well.  k = 0 is always feasible."""
     ks = np.arange(kmax + 1)
+    hist = np.bincount(np.minimum(t, kmax + 1), minlength=kmax + 2)[: kmax + 1]
+    Vk = np.cumsum(hist)
+    feas = Vk <= np.maximum(0, n + ks - M)
+    if fill_below_capacity:
+        feas |= n + ks <= M
+    feas[0] = True
+    return feas
+
+
+def feasible_prefix(ts: Sequence[np.ndarray], ns: Sequence[int], M: int, kmax: int,
+                    fill_below_capacity: bool = False):
+    """Largest k in [0, kmax] feasible for every density head (see
+    feasible_head).  Returns (kstar, feasible[k] boolean array)."""
     feas = np.ones(kmax + 1, dtype=bool)
     for t, n in zip(ts, ns):
-        hist = np.bincount(np.minimum(t, kmax + 1), minlength=kmax + 2)[: kmax + 1]
-        Vk = np.cumsum(hist)
-        ek = np.maximum(0, n + ks - M)
-        feas &= Vk <= ek
-    feas[0] = True
+        feas &= feasible_head(t, n, M, kmax, fill_below_capacity)
     return int(np.nonzero(feas)[0].max()), feas
 
 
-def eviction_set(proj_k: np.ndarray, crossed: np.ndarray, tok: np.ndarray, e: int) -> np.ndarray:
-    """Boolean mask: crossed states, then the highest projected densities.
+def eviction_set(proj_k: np.ndarray, crossed: np.ndarray, tok: np.ndarray, e: int,
+                 eviction: str = "threshold") -> np.ndarray:
+    """Boolean mask of e evicted states.
 
-    Among non-crossed states ties in projected density go to the lower token
-    id first.  The total count is e (the crossed set never exceeds e at a
-    feasible k).
+    "threshold": the crossed states, then the highest projected densities
+    (ties: lower token id first); "oldest": the crossed states, then
+    ascending token id; "densest": the e highest projected densities
+    (ties: lower token id), crossed or not.  The crossed set never exceeds e
+    at a feasible k.
     """
     n = proj_k.shape[0]
-    ev = np.array(crossed, dtype=bool, copy=True)
+    ev = np.zeros(n, bool) if eviction == "densest" else np.array(crossed, dtype=bool, copy=True)
     r = e - int(ev.sum())
     if r < 0:
         raise ValueError("crossed set exceeds the eviction count")
     if r > 0:
         rest = np.nonzero(~ev)[0]
-        o = np.lexsort((tok[rest], -proj_k[rest]))
+        o = np.argsort(tok[rest], kind="stable") if eviction == "oldest" else np.lexsort((tok[rest], -proj_k[rest]))
         ev[rest[o[:r]]] = True
     assert int(ev.sum()) == e and n >= e
     return ev
@@ -254,7 +288,7 @@ def eviction_set(proj_k: np.ndarray, crossed: np.ndarray, tok: np.ndarray, e: in
 
 @dataclasses.dataclass
 class UpdateInfo:
-    kstar: int
+    kstar: int                               # shared prefix (the largest per-head one with prefix "head")
     kmax: int
     D: List[Optional[np.ndarray]]
     delta: List[Optional[np.ndarray]]
@@ -266,6 +300,7 @@ class UpdateInfo:
     evicted: List[Optional[np.ndarray]]      # mask over old bank rows
     e: List[int]
     feasible: Optional[np.ndarray]
+    kstar_h: List[int] = dataclasses.field(default_factory=list)   # prefix applied per head
 
 
 def update_layer(banks: List[Optional[HeadBank]], candK: np.ndarray, candV: np.ndarray,
@@ -289,21 +324,32 @@ def update_layer(banks: List[Optional[HeadBank]], candK: np.ndarray, candV: np.n
     for h in heads:
         b = banks[h]
         D, delta = disturbance(b.K, candK[h], prm)
-        pi = candidate_order(delta, tok) if order is None else np.asarray(order[h], np.int64)
+        pi = candidate_order(delta, tok, prm.order) if order is None else np.asarray(order[h], np.int64)
         rho = density(b.K, prm)
         t, _ = crossing_times(b.K, rho, b.rho0, np.asarray(candK[h], np.float64)[pi[:kmax]], prm)
         info.D[h], info.delta[h], info.order[h], info.t[h], info.rho[h] = D, delta, pi, t, rho
-    ks, feas = feasible_prefix([info.t[h] for h in heads], [banks[h].n for h in heads], prm.M, kmax)
-    info.feasible = feas
-    info.kstar = ks if kstar is None else int(kstar)
-    k = info.kstar
+    fill = prm.fill_below_capacity
+    if prm.prefix == "head":
+        kh = {h: int(np.nonzero(feasible_head(info.t[h], banks[h].n, prm.M, kmax, fill))[0].max()) for h in heads}
+        if kstar is not None:
+            kh = {h: int(kstar[h]) if np.ndim(kstar) else int(kstar) for h in heads}
+        info.kstar = max(kh.values()) if kh else 0
+    else:
+        ks, feas = feasible_prefix([info.t[h] for h in heads], [banks[h].n for h in heads], prm.M, kmax, fill)
+        info.feasible = feas
+        info.kstar = ks if kstar is None else int(kstar)
+        kh = {h: info.kstar for h in heads}
+    info.kstar_h = [kh.get(h, 0) for h in range(H)]
     new = list(banks)
     for h in heads:
         b = banks[h]
+        k = kh[h]
         e = max(0, b.n + k - prm.M)
         proj_k = projected_density(b.K, info.rho[h], np.asarray(candK[h], np.float64)[info.order[h]], k, prm)
-        crossed = (info.t[h] <= k) if k > 0 else np.zeros(b.n, bool)
-        ev = eviction_set(proj_k, crossed, b.tok, e) if k > 0 else np.zeros(b.n, bool)
+        # no density check below capacity in the fill variant: nothing crossed counts
+        gated = k > 0 and not (fill and b.n + k <= prm.M)
+        crossed = (info.t[h] <= k) if gated else np.zeros(b.n, bool)
+        ev = eviction_set(proj_k, crossed, b.tok, e, prm.eviction) if k > 0 else np.zeros(b.n, bool)
         info.proj[h], info.crossed[h], info.evicted[h], info.e[h] = proj_k, crossed, ev, e
         adm = info.order[h][:k]
         keep = ~ev
@@ -311,7 +357,10 @@ def update_layer(banks: List[Optional[HeadBank]], candK: np.ndarray, candV: np.n
         V2 = np.concatenate([b.V[keep], np.asarray(candV[h], np.float64)[adm]])
         tok2 = np.concatenate([b.tok[keep], tok[adm]])
         rho_new = density(K2, prm)
-        rho0 = np.concatenate([b.rho0[keep], rho_new[keep.sum():]])
+        if prm.baseline == "refresh":
+            rho0 = rho_new
+        else:
+            rho0 = np.concatenate([b.rho0[keep], rho_new[keep.sum():]])
         new[h] = HeadBank(tok2, K2, V2, rho0)
     return new, info
 
@@ -322,7 +371,9 @@ def update_layer_brute(banks: List[Optional[HeadBank]], candK, candV, cand_tok, 
 
     For each k the projected density of every bank state is summed directly
     over the first k ordered candidates, with distances from explicit
-    differences; no running sums, no Gram form.
+    differences; no running sums, no Gram form.  Policy variants follow the
+    same Params fields, each written out with plain sorts and loops.
+    Returns (new_banks, kstar per head, orders).
     """
     H = len(banks)
     heads = [h for h in range(H) if banks[h] is not None] if heads is None else list(heads)
@@ -336,42 +387,56 @@ def update_layer_brute(banks: List[Optional[HeadBank]], candK, candV, cand_tok, 
         D = Dmat.sum(axis=1)
         mean = D.mean() if D.size else 0.0
         delta = D / mean if (b.n > 0 and mean > 0) else np.zeros(N)
-        orders[h] = np.array(sorted(range(N), key=lambda c: (delta[c], tok[c])), dtype=np.int64)
+        if prm.order == "source":
+            orders[h] = np.array(sorted(range(N), key=lambda c: tok[c]), dtype=np.int64)
+        else:
+            orders[h] = np.array(sorted(range(N), key=lambda c: (delta[c], tok[c])), dtype=np.int64)
         Bm = phi(sqdist_direct(b.K, b.K), prm)
         np.fill_diagonal(Bm, 0.0)
         rhos[h] = Bm.sum(axis=1)
 
+    def projected(h, k):
+        b = banks[h]
+        if k == 0:
+            return rhos[h].copy()
+        adm = np.asarray(candK[h], np.float64)[orders[h][:k]]
+        return rhos[h] + phi(sqdist_direct(b.K, adm), prm).sum(axis=1)
+
     def crossed_at(h, k):
         b = banks[h]
-        if k == 0 or not math.isfinite(prm.tau):
-            return np.zeros(b.n, bool), rhos[h].copy()
-        adm = np.asarray(candK[h], np.float64)[orders[h][:k]]
-        pr = rhos[h] + phi(sqdist_direct(b.K, adm), prm).sum(axis=1)
-        return pr > prm.tau * b.rho0, pr
+        below = prm.fill_below_capacity and b.n + k <= prm.M
+        if k == 0 or below or not math.isfinite(prm.tau):
+            return np.zeros(b.n, bool)
+        return projected(h, k) > prm.tau * b.rho0
 
-    kstar = 0
-    for k in range(kmax + 1):
-        ok = True
-        for h in heads:
-            c, _ = crossed_at(h, k)
-            if int(c.sum()) > max(0, banks[h].n + k - prm.M):
-                ok = False
-                break
-        if ok:
-            kstar = k
+    def ok(h, k):
+        if k == 0 or (prm.fill_below_capacity and banks[h].n + k <= prm.M):
+            return True
+        return int(crossed_at(h, k).sum()) <= max(0, banks[h].n + k - prm.M)
+
+    if prm.prefix == "head":
+        kst = {h: max(k for k in range(kmax + 1) if ok(h, k)) for h in heads}
+    else:
+        shared = max(k for k in range(kmax + 1) if all(ok(h, k) for h in heads))
+        kst = {h: shared for h in heads}
     new = list(banks)
     for h in heads:
         b = banks[h]
-        c, pr = crossed_at(h, kstar)
-        if kstar > 0:
-            adm_full = np.asarray(candK[h], np.float64)[orders[h][:kstar]]
-            pr = rhos[h] + phi(sqdist_direct(b.K, adm_full), prm).sum(axis=1)
-        e = max(0, b.n + kstar - prm.M)
-        ev = c.copy()
-        rest = sorted([i for i in range(b.n) if not ev[i]], key=lambda i: (-pr[i], b.tok[i]))
+        k = kst[h]
+        c, pr = crossed_at(h, k), projected(h, k)
+        e = max(0, b.n + k - prm.M)
+        if prm.eviction == "densest":
+            ev = np.zeros(b.n, bool)
+        else:
+            ev = c.copy()
+        rest = [i for i in range(b.n) if not ev[i]]
+        if prm.eviction == "oldest":
+            rest = sorted(rest, key=lambda i: b.tok[i])
+        else:
+            rest = sorted(rest, key=lambda i: (-pr[i], b.tok[i]))
         for i in rest[: e - int(ev.sum())]:
             ev[i] = True
-        adm = orders[h][:kstar]
+        adm = orders[h][:k]
         keep = ~ev
         K2 = np.concatenate([b.K[keep], np.asarray(candK[h], np.float64)[adm]])
         V2 = np.concatenate([b.V[keep], np.asarray(candV[h], np.float64)[adm]])
@@ -379,9 +444,9 @@ def update_layer_brute(banks: List[Optional[HeadBank]], candK, candV, cand_tok, 
         Bm = phi(sqdist_direct(K2, K2), prm)
         np.fill_diagonal(Bm, 0.0)
         rnew = Bm.sum(axis=1)
-        rho0 = np.concatenate([b.rho0[keep], rnew[keep.sum():]])
+        rho0 = rnew if prm.baseline == "refresh" else np.concatenate([b.rho0[keep], rnew[keep.sum():]])
         new[h] = HeadBank(tok2, K2, V2, rho0)
-    return new, kstar, orders
+    return new, kst, orders
 
 
 def bank_payload_bytes(L: int, H: int, M: int, dk: int, dv: int, elem_bytes: int = 2) -> int:
