@@ -82,13 +82,26 @@ typedef struct ihipStream_t* kvb_stream_t;   /* same type as hipStream_t */
 #define KVB_MAX_HEADS 64
 #define KVB_MAX_SEGMENTS 256  /* per head, attention side */
 
+/* DensityKV policy variants (DensityKV paper summary, appendix E
+ * ablations); 0 is the method: candidates by ascending (delta, token id),
+ * frozen insertion baselines, crossed states evicted first then the densest,
+ * one prefix length shared by the layer's density heads, density gating at
+ * every occupancy. */
+#define KVB_POL_SOURCE_ORDER     1u   /* candidates in source order: ascending token id */
+#define KVB_POL_REFRESH_BASELINE 2u   /* after each update every state's baseline = its new density */
+#define KVB_POL_EVICT_DENSEST    4u   /* evict the e highest projected densities, crossed or not */
+#define KVB_POL_EVICT_OLDEST     8u   /* crossed states, then ascending token id (source-order completion) */
+#define KVB_POL_HEAD_PREFIX     16u   /* each density head its own largest feasible prefix (k_star is [H]) */
+#define KVB_POL_FILL_BELOW_CAP  32u   /* no density check, no eviction, for prefixes with n + k <= M */
+#define KVB_POL_ALL             63u
+
 typedef struct kvb_params {
   float tau;          /* density growth bound, >= 1 (may be +inf) */
   float sigma;        /* Soft-Riesz bandwidth, > 0 */
   float eps;          /* softening, > 0 unless p == 0 */
   float p;            /* decay exponent, >= 0 */
   int32_t seg_len;    /* Forcing-KV segment length in tokens (divides F); used by dynamic heads */
-  int32_t reserved;
+  uint32_t policy;    /* OR of KVB_POL_* (density heads); EVICT_DENSEST and EVICT_OLDEST exclude each other */
   double retention;   /* Forcing-KV kept fraction r in [0, 1] */
 } kvb_params;
 
@@ -129,7 +142,7 @@ typedef struct kvb_segment {   /* one contiguous run of retained rows of one hea
 } kvb_segment;
 
 typedef struct kvb_update_out {   /* device pointers written by kvbank_update */
-  int32_t* k_star;        /* [1] shared admitted prefix length */
+  int32_t* k_star;        /* [1] shared admitted prefix length; [H] per head with KVB_POL_HEAD_PREFIX */
   int32_t* n_mandatory;   /* [H] states that crossed tau * rho0 at k* */
   int32_t* n_evicted;     /* [H] */
   uint32_t* status;       /* [1] OR of KVB_DEV_* bits (caller zeroes it) */

@@ -13,7 +13,9 @@ import os
 from typing import Optional, Sequence
 
 __all__ = [
-    "KVB_BF16", "KVB_F32", "KVB_HEAD_DENSITY", "KVB_HEAD_STATIC", "KVB_HEAD_DYNAMIC",
+    "KVB_BF16", "KVB_F32", "KVB_HEAD_DENSITY", "KVB_HEAD_STATIC", "KVB_HEAD_DYNAMIC", "KVB_POL_SOURCE_ORDER",
+    "KVB_POL_REFRESH_BASELINE", "KVB_POL_EVICT_DENSEST", "KVB_POL_EVICT_OLDEST", "KVB_POL_HEAD_PREFIX",
+    "KVB_POL_FILL_BELOW_CAP",
     "KvbError", "load_library", "kvbank_workspace_size", "kvbank_score", "kvbank_update",
     "chunk_attention", "chunk_attention_workspace_size", "kvb_last_error", "LayerDesc", "Bank", "KVLayout", "UpdateOut",
     "HEADER_FUNCTIONS",
@@ -24,6 +26,9 @@ LIB_PATH = os.path.join(_HERE, "libkvbank.so")
 
 KVB_BF16, KVB_F32 = 0, 1
 KVB_HEAD_DENSITY, KVB_HEAD_STATIC, KVB_HEAD_DYNAMIC = 0, 1, 2
+# DensityKV policy variants (kvb_params.policy); 0 is the method
+KVB_POL_SOURCE_ORDER, KVB_POL_REFRESH_BASELINE, KVB_POL_EVICT_DENSEST = 1, 2, 4
+KVB_POL_EVICT_OLDEST, KVB_POL_HEAD_PREFIX, KVB_POL_FILL_BELOW_CAP = 8, 16, 32
 KVB_MAX_SEGMENTS = 256
 HEADER_FUNCTIONS = ("kvbank_workspace_size", "kvbank_score", "kvbank_update", "chunk_attention",
                     "chunk_attention_workspace_size", "kvb_last_error")
@@ -33,7 +38,7 @@ _c_i32, _c_f32, _c_f64, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_double, c
 
 class kvb_params(ctypes.Structure):
     _fields_ = [("tau", _c_f32), ("sigma", _c_f32), ("eps", _c_f32), ("p", _c_f32),
-                ("seg_len", _c_i32), ("reserved", _c_i32), ("retention", _c_f64)]
+                ("seg_len", _c_i32), ("policy", ctypes.c_uint32), ("retention", _c_f64)]
 
 
 class kvb_layer_desc(ctypes.Structure):
@@ -129,11 +134,12 @@ class LayerDesc:
     p: float = 2.0
     seg_len: int = 0
     retention: float = 0.0
+    policy: int = 0          # OR of KVB_POL_*
 
     def c(self):
         lab = (ctypes.c_uint8 * max(1, len(self.labels)))(*[int(x) for x in self.labels])
-        prm = kvb_params(float(self.tau), float(self.sigma), float(self.eps), float(self.p), int(self.seg_len), 0,
-                         float(self.retention))
+        prm = kvb_params(float(self.tau), float(self.sigma), float(self.eps), float(self.p), int(self.seg_len),
+                         int(self.policy), float(self.retention))
         desc = kvb_layer_desc(int(self.H), int(self.d), int(self.M), int(self.dtype), int(self.frame_tokens), 0,
                               ctypes.cast(lab, ctypes.POINTER(ctypes.c_uint8)), prm)
         desc._keep = lab   # keep the label array alive with the descriptor
@@ -238,7 +244,8 @@ class UpdateOut:
     def alloc(H: int, seg_cap: int = 8, M: int = 0, diagnostics: bool = False):
         import torch
         dev = torch.device("cuda")
-        o = UpdateOut(torch.zeros(1, dtype=torch.int32, device=dev), torch.zeros(H, dtype=torch.int32, device=dev),
+        # k_star: [H] so that a per-head prefix (KVB_POL_HEAD_PREFIX) fits; a shared one is entry 0
+        o = UpdateOut(torch.zeros(H, dtype=torch.int32, device=dev), torch.zeros(H, dtype=torch.int32, device=dev),
                       torch.zeros(H, dtype=torch.int32, device=dev), torch.zeros(1, dtype=torch.int32, device=dev),
                       torch.zeros(H * seg_cap * ctypes.sizeof(kvb_segment), dtype=torch.uint8, device=dev),
                       torch.zeros(H, dtype=torch.int32, device=dev), int(seg_cap))

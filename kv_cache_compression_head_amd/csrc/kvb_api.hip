@@ -75,6 +75,9 @@ int check_layer(const kvb_layer_desc* L, int32_t N, Heads* hd) {
     if (!(P.p >= 0.0f) || !isfinite(P.p)) return fail(KVB_EPARAM, "p=%g must be >= 0", (double)P.p);
     if (P.p > 0.0f && (!(P.eps > 0.0f) || !isfinite(P.eps)))
       return fail(KVB_EPARAM, "eps=%g must be > 0 when p > 0", (double)P.eps);
+    if (P.policy & ~KVB_POL_ALL) return fail(KVB_EPARAM, "policy=%#x has unknown bits", P.policy);
+    if ((P.policy & KVB_POL_EVICT_DENSEST) && (P.policy & KVB_POL_EVICT_OLDEST))
+      return fail(KVB_EPARAM, "policy: EVICT_DENSEST and EVICT_OLDEST exclude each other");
   }
   if (hd->dyn) {
     if (P.seg_len <= 0 || L->frame_tokens % P.seg_len != 0)
@@ -288,7 +291,9 @@ int kvbank_score(const kvb_layer_desc* L, const kvb_bank* bank, const void* cand
     if (g.splits > 1)
       HIPCHK(launch_sum_splits(g.out, (int64_t)MAX_SPLITS * N, N, g.splits, out_D, N, H, N, st));
     HIPCHK(launch_delta(out_D, bank->count, hd.dens, H, N, out_score, st));
-    HIPCHK(launch_sort(out_score, N, cand_tok, 0, hd.dens, H, N, at<uint64_t>(ws, lo.k0), at<uint64_t>(ws, lo.k1),
+    // order: ascending (delta, token id), or token id alone (source order)
+    const float* key = (L->params.policy & KVB_POL_SOURCE_ORDER) ? nullptr : out_score;
+    HIPCHK(launch_sort(key, N, cand_tok, 0, hd.dens, H, N, at<uint64_t>(ws, lo.k0), at<uint64_t>(ws, lo.k1),
                        at<int32_t>(ws, lo.v0), at<int32_t>(ws, lo.v1), out_order, N, st));
   }
   if (hd.dyn) {
@@ -365,12 +370,14 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
   hipStream_t st = (hipStream_t)stream;
   const PhiConst pc = phi_const(L->params);
   const int pm = phi_mode_of(L->params.p);
+  const uint32_t pol = hd.dens ? L->params.policy : 0u;
+  const int ks_hs = (pol & KVB_POL_HEAD_PREFIX) ? 1 : 0;
   {
     // outputs, and the crossing-time histogram when the density path runs
     const bool dens_run = hd.dens && N > 0;
     int32_t* zp[4] = {out->n_mandatory, out->n_evicted, out->k_star,
                       dens_run ? at<int32_t>(ws, lo.hist) : nullptr};
-    const int64_t zn[4] = {H, H, 1, (int64_t)H * (lo.kmax + 2)};
+    const int64_t zn[4] = {H, H, ks_hs ? H : 1, (int64_t)H * (lo.kmax + 2)};
     HIPCHK(launch_zero_i32(zp, zn, 4, st));
   }
   if (hd.dens && N > 0) {
@@ -384,7 +391,10 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
     ScanLaunch s{};
     s.k = kd; s.rho = bank->rho; s.rho0 = bank->rho0; s.count = bank->count; s.order = order;
     s.active = hd.dens; s.kmax = kmax; s.tau = L->params.tau; s.cps = lo.cps; s.ncp = lo.ncp;
-    s.cp = at<float>(ws, lo.cp); s.kstar = out->k_star;
+    s.cp = at<float>(ws, lo.cp); s.kstar = out->k_star; s.kstar_hs = ks_hs;
+    // crossed states survive with densest-only eviction, and below capacity
+    // in the fill variant: their running sums and rho' are then needed
+    s.keep_crossed = (pol & (KVB_POL_EVICT_DENSEST | KVB_POL_FILL_BELOW_CAP)) ? 1 : 0;
     s.t_out = out->t_cross ? out->t_cross : at<int32_t>(ws, lo.t);
     s.rhoP = out->rho_proj ? out->rho_proj : at<float>(ws, lo.rhoP);
     s.pc = pc; s.phi_mode = pm;
@@ -392,6 +402,9 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
     SelectLaunch sel{};
     sel.H = H; sel.M = M; sel.kmax = kmax; sel.active = hd.dens; sel.count = bank->count;
     sel.t = s.t_out; sel.hist = at<int32_t>(ws, lo.hist); sel.kstar = out->k_star; sel.rhoP = s.rhoP;
+    sel.kstar_hs = ks_hs;
+    sel.fill = (pol & KVB_POL_FILL_BELOW_CAP) ? 1 : 0;
+    sel.evict_mode = (pol & KVB_POL_EVICT_DENSEST) ? 1 : (pol & KVB_POL_EVICT_OLDEST) ? 2 : 0;
     sel.bank_tok = bank->tok; sel.evict = at<uint8_t>(ws, lo.evict); sel.surv = at<int32_t>(ws, lo.surv);
     sel.evl = at<int32_t>(ws, lo.evl); sel.n_surv = at<int32_t>(ws, lo.nsurv); sel.n_ev = out->n_evicted;
     sel.n_mand = out->n_mandatory; sel.status = out->status;
@@ -405,7 +418,7 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
     const VList evl{sel.evl, sel.n_ev, M, 1, 0, 0, M, 0};
     const VList fxl{sel.fixl, sel.n_fix, M, 1, 0, 0, M, 0};
     const VList srv{sel.surv, sel.n_surv, M, 1, 0, 0, M, 0};
-    const VList adm{order, out->k_star, N, 0, M, 0, kmax, 0};
+    const VList adm{order, out->k_star, N, ks_hs, M, 0, kmax, 0};
     float* split = at<float>(ws, lo.split);
     const int64_t sstride = (N > M ? N : M);
     g.rows = srv; g.cols = evl; g.self_excl = 0;
@@ -418,7 +431,8 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
     ap.H = H; ap.M = M; ap.N = N; ap.d = d; ap.et = et; ap.kmax = kmax; ap.active = hd.dens;
     ap.bankK = bank->K; ap.bankV = bank->V; ap.bank_tok = bank->tok; ap.rho0 = bank->rho0; ap.rho = bank->rho;
     ap.count = bank->count; ap.candK = cand_k; ap.candV = cand_v; ap.cand_tok = cand_tok; ap.order = order;
-    ap.D = D; ap.kstar = out->k_star; ap.surv = sel.surv; ap.n_surv = sel.n_surv; ap.evl = sel.evl;
+    ap.D = D; ap.kstar = out->k_star; ap.kstar_hs = ks_hs;
+    ap.refresh = (pol & KVB_POL_REFRESH_BASELINE) ? 1 : 0; ap.surv = sel.surv; ap.n_surv = sel.n_surv; ap.evl = sel.evl;
     ap.n_ev = sel.n_ev; ap.rhoP = s.rhoP; ap.acc_surv = at<float>(ws, lo.accS);
     ap.acc_adm_ev = at<float>(ws, lo.accAE); ap.acc_adm_adm = at<float>(ws, lo.accAA); ap.fmode = sel.fmode;
     HIPCHK(launch_apply(ap, st));

@@ -544,7 +544,8 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
                                                    const int32_t* __restrict__ order, uint64_t active,
                                                    int kmax, float tau, int cps, int ncp, float* __restrict__ cp,
                                                    int32_t* __restrict__ t_out, const int32_t* __restrict__ kstar_p,
-                                                   float* __restrict__ rhoP, PhiConst pc) {
+                                                   int kstar_hs, int keep_crossed, float* __restrict__ rhoP,
+                                                   PhiConst pc) {
   using O = Ops<E>;
   using A = Aug<E>;
   using T = Tile<E, D>;
@@ -580,9 +581,10 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
   bool need = false;
   int t_b = kmax + 1;
   if constexpr (SUM) {
-    kst = *kstar_p;
-    // crossed rows (t_b <= k*) are evicted; their projected density is unused
-    need = valid && kst > 0 && t_out[hb] > kst;
+    kst = kstar_p[h * kstar_hs];
+    // crossed rows (t_b <= k*) are evicted and their projected density is
+    // unused, unless the policy lets crossed rows survive
+    need = valid && kst > 0 && (keep_crossed || t_out[hb] > kst);
     if (!__syncthreads_or(need)) {
       if (valid) rhoP[hb] = r_b;
       return;
@@ -687,7 +689,9 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
       load_issue(stg + 1, nC, nA);
       if (stg + 2 < st_end) load_index(stg + 2);
     }
-    const bool wave_busy = __any(!done);
+    // a wave whose rows have all crossed skips the stage, unless crossed
+    // rows may survive: the scan then keeps their running sums (checkpoints)
+    const bool wave_busy = (!SUM && keep_crossed) || __any(!done);
     if (wave_busy) {
       // both subtiles' products first (independent MFMA chains), then the
       // interactions and prefix sums of each in order
@@ -765,7 +769,9 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
             first = min((int)fs[0], (int)fs[1]);
             if (cross) t_b = pos0 + first + 1;
           }
-          if (!done) carry = s_end;
+          // a crossed row's running sum stops unless crossed rows may survive
+          // (the sum pass then resumes them from their checkpoints too)
+          if (!done || keep_crossed) carry = s_end;
           done = done || cross;
         } else {
           if (sub < sub_end - 1) {
@@ -791,7 +797,7 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
       // every row of the work-group crossed: later checkpoints are never
       // read (the sum pass skips rows with t_b <= k*); checked every fourth
       // stage to keep one plain barrier per stage
-      if ((stg & 3) == 3) return __syncthreads_or(!done) != 0;
+      if ((stg & 3) == 3 && !keep_crossed) return __syncthreads_or(!done) != 0;
       __syncthreads();
       return true;
     } else {
@@ -814,10 +820,12 @@ static void scan_dispatch(const ScanLaunch& a, bool sum, dim3 grid, hipStream_t 
   const KeySpace<E> ks = key_space<E>(a.k);
   if (sum)
     hipLaunchKernelGGL((scan_kernel<E, D, MODE, true, DIRECT>), grid, dim3(256), 0, st, ks, a.rho, a.rho0, a.count,
-                       a.order, a.active, a.kmax, a.tau, a.cps, a.ncp, a.cp, a.t_out, a.kstar, a.rhoP, a.pc);
+                       a.order, a.active, a.kmax, a.tau, a.cps, a.ncp, a.cp, a.t_out, a.kstar, a.kstar_hs,
+                       a.keep_crossed, a.rhoP, a.pc);
   else
     hipLaunchKernelGGL((scan_kernel<E, D, MODE, false, DIRECT>), grid, dim3(256), 0, st, ks, a.rho, a.rho0, a.count,
-                       a.order, a.active, a.kmax, a.tau, a.cps, a.ncp, a.cp, a.t_out, a.kstar, a.rhoP, a.pc);
+                       a.order, a.active, a.kmax, a.tau, a.cps, a.ncp, a.cp, a.t_out, a.kstar, a.kstar_hs,
+                       a.keep_crossed, a.rhoP, a.pc);
 }
 
 template <typename E, int D>

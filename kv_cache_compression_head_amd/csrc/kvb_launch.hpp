@@ -57,7 +57,9 @@ struct ScanLaunch {
   int32_t ncp;            // checkpoints per row
   float* cp;              // [H][ncp][M]
   int32_t* t_out;         // [H][M] (scan)
-  const int32_t* kstar;   // device scalar (sum)
+  const int32_t* kstar;   // device: [1] shared prefix, or [H] per head (sum)
+  int32_t kstar_hs;       // head stride of kstar: 0 shared, 1 per head
+  int32_t keep_crossed;   // 1: crossed rows may survive (their running sums and rho' are needed)
   float* rhoP;            // [H][M] (sum)
   PhiConst pc;
   int32_t phi_mode;
@@ -85,7 +87,10 @@ struct SelectLaunch {
   const int32_t* count;      // [H] bank occupancy
   const int32_t* t;          // [H][M] crossing times
   int32_t* hist;             // [H][kmax+2] scratch, becomes |V_h(k)|
-  int32_t* kstar;            // device scalar
+  int32_t* kstar;            // device: [1] shared prefix, or [H] per head
+  int32_t kstar_hs;          // 0 shared, 1 per head (each head its own largest feasible k)
+  int32_t fill;              // 1: no density gating while n + k <= M
+  int32_t evict_mode;        // 0 crossed then densest, 1 densest only, 2 crossed then oldest
   const float* rhoP;         // [H][M]
   const int32_t* bank_tok;   // [H][M]
   uint8_t* evict;            // [H][M]
@@ -110,7 +115,8 @@ struct ApplyLaunch {
   const void* candK; const void* candV; const int32_t* cand_tok;
   const int32_t* order;       // [H][N]
   const float* D;             // [H][N]
-  const int32_t* kstar;
+  const int32_t* kstar; int32_t kstar_hs;
+  int32_t refresh;            // 1: every live state's baseline becomes its new density
   const int32_t* surv; const int32_t* n_surv;
   const int32_t* evl; const int32_t* n_ev;
   const float* rhoP;          // [H][M]

@@ -94,7 +94,8 @@ constexpr int SORT_BS = 2048;
 
 KVB_DEV uint64_t sort_key(const float* score, const int32_t* tie, int64_t tie_hstride, int h, int i,
                           int64_t score_hstride) {
-  const uint32_t hi = float_key(score[(int64_t)h * score_hstride + i]);
+  // no score: the tie key alone (source order, by token id)
+  const uint32_t hi = score ? float_key(score[(int64_t)h * score_hstride + i]) : 0u;
   const uint32_t lo = tie ? (uint32_t)tie[(int64_t)h * tie_hstride + i] : (uint32_t)i;
   return ((uint64_t)hi << 32) | lo;
 }
@@ -243,20 +244,33 @@ __global__ __launch_bounds__(1024) void cumsum_kernel(int32_t* __restrict__ hist
   }
 }
 
+// head h admits the first k candidates: |V_h(k)| <= e_h(k), or (fill
+// variant) the k fit below capacity with no density check
+KVB_DEV bool head_feasible(const int32_t* cum, int n, int M, int kmax, int fill, int h, int k) {
+  if (k == 0 || (fill && n + k <= M)) return true;
+  return cum[(int64_t)h * (kmax + 2) + k] <= max(0, n + k - M);
+}
+
+// shared prefix: the largest k feasible for every density head
 __global__ void feasible_kernel(const int32_t* __restrict__ cum, const int32_t* __restrict__ count,
-                                uint64_t active, int H, int M, int kmax,
+                                uint64_t active, int H, int M, int kmax, int fill,
                                 int32_t* __restrict__ kstar) {
   const int k = blockIdx.x * blockDim.x + threadIdx.x;
   if (k > kmax) return;
   bool ok = true;
-  if (k > 0) {
-    for (int h = 0; h < H; ++h) {
-      if (!head_on(active, h)) continue;
-      const int e = max(0, count[h] + k - M);
-      if (cum[(int64_t)h * (kmax + 2) + k] > e) { ok = false; break; }
-    }
-  }
+  for (int h = 0; h < H && ok; ++h)
+    if (head_on(active, h)) ok = head_feasible(cum, count[h], M, kmax, fill, h, k);
   if (ok) atomicMax(kstar, k);
+}
+
+// per-head prefix: kstar[h] = the largest k feasible for head h
+__global__ void feasible_head_kernel(const int32_t* __restrict__ cum, const int32_t* __restrict__ count,
+                                     uint64_t active, int M, int kmax, int fill, int32_t* __restrict__ kstar) {
+  const int h = blockIdx.y;
+  if (!head_on(active, h)) return;
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k > kmax) return;
+  if (head_feasible(cum, count[h], M, kmax, fill, h, k)) atomicMax(kstar + h, k);
 }
 
 // expects hist and kstar zeroed by the caller
@@ -265,8 +279,12 @@ hipError_t launch_kstar(const SelectLaunch& a, hipStream_t st) {
     hipLaunchKernelGGL(hist_kernel, dim3((a.M + 255) / 256, a.H), dim3(256), 0, st, a.t, a.count, a.active, a.M,
                        a.kmax, a.hist);
   hipLaunchKernelGGL(cumsum_kernel, dim3(a.H), dim3(1024), 0, st, a.hist, a.active, a.kmax + 2);
-  hipLaunchKernelGGL(feasible_kernel, dim3((a.kmax + 1 + 255) / 256), dim3(256), 0, st, a.hist, a.count, a.active,
-                     a.H, a.M, a.kmax, a.kstar);
+  if (a.kstar_hs)
+    hipLaunchKernelGGL(feasible_head_kernel, dim3((a.kmax + 1 + 255) / 256, a.H), dim3(256), 0, st, a.hist, a.count,
+                       a.active, a.M, a.kmax, a.fill, a.kstar);
+  else
+    hipLaunchKernelGGL(feasible_kernel, dim3((a.kmax + 1 + 255) / 256), dim3(256), 0, st, a.hist, a.count,
+                       a.active, a.H, a.M, a.kmax, a.fill, a.kstar);
   return hipGetLastError();
 }
 
@@ -276,8 +294,11 @@ hipError_t launch_kstar(const SelectLaunch& a, hipStream_t st) {
 // select over 64-bit keys; then ballot/prefix-sum compaction of the evicted
 // and surviving slots, both in ascending slot order.
 // ---------------------------------------------------------------------------
-KVB_DEV uint64_t evict_key(float rp, int32_t tok) {
-  return ((uint64_t)float_key(rp) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)tok);
+// larger key = evicted first: (projected density desc, token asc), or the
+// token alone (oldest first) for source-order completion
+KVB_DEV uint64_t evict_key(float rp, int32_t tok, bool oldest) {
+  const uint64_t t = (uint64_t)(0xFFFFFFFFu - (uint32_t)tok);
+  return oldest ? t : (((uint64_t)float_key(rp) << 32) | t);
 }
 
 __global__ __launch_bounds__(1024) void evict_kernel(SelectLaunch a) {
@@ -288,8 +309,13 @@ __global__ __launch_bounds__(1024) void evict_kernel(SelectLaunch a) {
   const int64_t hb = (int64_t)h * M;
   if (!head_on(a.active, h)) return;
   const int n = a.count[h];
-  const int ks = *a.kstar;
+  const int ks = a.kstar[h * a.kstar_hs];
   const int e = ks > 0 ? max(0, n + ks - M) : 0;
+  // crossed states (t_b <= k*): counted unless the prefix fits below capacity
+  // in the fill variant; evicted first unless the eviction is densest-only
+  const bool gated = ks > 0 && !(a.fill && n + ks <= M);
+  const bool oldest = a.evict_mode == 2;
+  const bool force = a.evict_mode != 1;
   __shared__ int hist[256];
   __shared__ int s_nm;
   __shared__ uint64_t s_prefix, s_mask;
@@ -299,10 +325,11 @@ __global__ __launch_bounds__(1024) void evict_kernel(SelectLaunch a) {
   if (tid == 0) { s_nm = 0; s_prefix = 0; s_mask = 0; s_base_e = 0; s_base_s = 0; }
   __syncthreads();
   int nm_local = 0;
-  for (int b = tid; b < n; b += 1024) nm_local += (ks > 0 && a.t[hb + b] <= ks) ? 1 : 0;
+  for (int b = tid; b < n; b += 1024) nm_local += (gated && a.t[hb + b] <= ks) ? 1 : 0;
   atomicAdd(&s_nm, nm_local);
   __syncthreads();
-  const int nm = s_nm;
+  const int nm_crossed = s_nm;
+  const int nm = force ? nm_crossed : 0;   // forced evictions
   int r = e - nm;
   if (r < 0) {
     if (tid == 0) atomicOr(a.status, DEV_EVICT);
@@ -321,8 +348,8 @@ __global__ __launch_bounds__(1024) void evict_kernel(SelectLaunch a) {
       __syncthreads();
       const uint64_t pre = s_prefix, msk = s_mask;
       for (int b = tid; b < n; b += 1024) {
-        if (ks > 0 && a.t[hb + b] <= ks) continue;
-        const uint64_t key = evict_key(a.rhoP[hb + b], a.bank_tok[hb + b]);
+        if (force && gated && a.t[hb + b] <= ks) continue;
+        const uint64_t key = evict_key(a.rhoP[hb + b], a.bank_tok[hb + b], oldest);
         if ((key & msk) == pre) atomicAdd(&hist[(key >> shift) & 0xFF], 1);
       }
       __syncthreads();
@@ -367,8 +394,8 @@ __global__ __launch_bounds__(1024) void evict_kernel(SelectLaunch a) {
     const int b = base + tid;
     bool ev = false, live = b < n;
     if (live) {
-      const bool mand = ks > 0 && a.t[hb + b] <= ks;
-      ev = mand || (r > 0 && evict_key(a.rhoP[hb + b], a.bank_tok[hb + b]) >= thr);
+      const bool mand = force && gated && a.t[hb + b] <= ks;
+      ev = mand || (r > 0 && evict_key(a.rhoP[hb + b], a.bank_tok[hb + b], oldest) >= thr);
       a.evict[hb + b] = ev ? 1 : 0;
     }
     const uint64_t be = __ballot(live && ev);
@@ -400,7 +427,7 @@ __global__ __launch_bounds__(1024) void evict_kernel(SelectLaunch a) {
   if (tid == 0) {
     a.n_ev[h] = s_base_e;
     a.n_surv[h] = s_base_s;
-    a.n_mand[h] = nm;
+    a.n_mand[h] = nm_crossed;
     a.n_fix[h] = direct ? s_base_s : s_base_e;
     a.fmode[h] = direct ? 1 : 0;
     if (s_base_e != e) atomicOr(a.status, DEV_EVICT);
@@ -423,7 +450,9 @@ __global__ void apply_surv_kernel(ApplyLaunch a) {
   if (i >= a.n_surv[h]) return;
   const int64_t hb = (int64_t)h * a.M;
   const int slot = a.surv[hb + i];
-  a.rho[hb + slot] = a.rhoP[hb + slot] - a.acc_surv[hb + i];
+  const float r = a.rhoP[hb + slot] - a.acc_surv[hb + i];
+  a.rho[hb + slot] = r;
+  if (a.refresh) a.rho0[hb + slot] = r;
 }
 
 // 8 rows per 256-thread block; each row moves K and V (16-byte chunks)
@@ -431,7 +460,7 @@ template <int CPR>
 __global__ __launch_bounds__(256) void apply_adm_kernel(ApplyLaunch a) {
   const int h = blockIdx.y;
   if (!head_on(a.active, h)) return;
-  const int ks = *a.kstar;
+  const int ks = a.kstar[h * a.kstar_hs];
   constexpr int RPB = 256 / (2 * CPR);
   const int j = blockIdx.x * RPB + threadIdx.x / (2 * CPR);
   if (j >= ks) return;
@@ -461,7 +490,7 @@ __global__ __launch_bounds__(256) void apply_adm_kernel(ApplyLaunch a) {
 __global__ void commit_count_kernel(ApplyLaunch a) {
   const int h = threadIdx.x;
   if (h >= a.H || !head_on(a.active, h)) return;
-  a.count[h] = a.n_surv[h] + *a.kstar;
+  a.count[h] = a.n_surv[h] + a.kstar[h * a.kstar_hs];
 }
 
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t st) {

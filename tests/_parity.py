@@ -99,14 +99,32 @@ class Report:
     evicted: List[int] = field(default_factory=list)
 
 
+def check_evictions_oldest(ev_gpu: np.ndarray, mand: np.ndarray, tok: np.ndarray):
+    """Source-order completion: the crossed states, then the oldest (lowest
+    token id) of the rest; token ids are unique, so the set is exact."""
+    assert np.all(ev_gpu[mand]), "a crossed state was not evicted"
+    evd = ev_gpu & ~mand
+    kept = (~ev_gpu) & ~mand
+    if evd.any() and kept.any():
+        assert tok[evd].max() < tok[kept].min(), "completion is not the oldest states"
+
+
 def replay_update(before: GpuBank, after: GpuBank, candK, candV, cand_tok, D_gpu, delta_gpu, order_gpu,
                   t_gpu, rhoP_gpu, kstar_gpu, n_mand_gpu, n_ev_gpu, prm: od.Params, heads: List[int],
                   rtol_D=2e-5, rtol_rho=1e-4) -> Report:
-    """Stage-replay check of one layer update over the listed density heads."""
+    """Stage-replay check of one layer update over the listed density heads,
+    under the policy fields of prm.  kstar_gpu: the device's k_star array
+    (entry 0 the shared prefix, or one entry per head)."""
     N = cand_tok.shape[0]
     kmax = min(N, prm.M)
     tok = cand_tok.astype(np.int64)
-    k = int(kstar_gpu)
+    ks_arr = np.atleast_1d(np.asarray(kstar_gpu)).astype(np.int64)
+    per_head = prm.prefix == "head"
+    kof = (lambda h: int(ks_arr[h])) if per_head else (lambda h: int(ks_arr[0]))
+    k = int(ks_arr[heads].max()) if per_head else int(ks_arr[0])
+    fill = prm.fill_below_capacity
+    # crossed rows survive (and carry rho') under densest-only eviction and below capacity with fill
+    keep_crossed = prm.eviction == "densest" or fill
     rep = Report(kstar=k)
     tl, ns, cache = [], [], {}
     for h in heads:
@@ -118,7 +136,10 @@ def replay_update(before: GpuBank, after: GpuBank, candK, candV, cand_tok, D_gpu
         D, delta = od.disturbance(b.K, candK[h], prm)
         np.testing.assert_allclose(D_gpu[h], D, rtol=rtol_D, atol=1e-6)
         np.testing.assert_allclose(delta_gpu[h], delta, rtol=rtol_D, atol=1e-6)
-        rep.order_near_ties += check_order(order_gpu[h], delta, tok)
+        if prm.order == "source":
+            assert order_gpu[h].tolist() == np.argsort(tok, kind="stable").tolist(), "source order"
+        else:
+            rep.order_near_ties += check_order(order_gpu[h], delta, tok)
         # stage 2: crossing prefix lengths on the GPU's order
         pi = order_gpu[h].astype(np.int64)
         cs = np.asarray(candK[h], np.float64)[pi[:kmax]]
@@ -127,18 +148,26 @@ def replay_update(before: GpuBank, after: GpuBank, candK, candV, cand_tok, D_gpu
         tl.append(tg)
         ns.append(b.n)
         cache[h] = (b, rho_def, cs, pi, tg)
-    # stage 3: shared prefix from the GPU's crossing times (integer logic, exact)
-    ks_ref, _ = od.feasible_prefix(tl, ns, prm.M, kmax)
-    assert ks_ref == k, f"k* {k} != oracle prefix {ks_ref} on the GPU crossing times"
+    # stage 3: prefix lengths from the GPU's crossing times (integer logic, exact)
+    if per_head:
+        for h, tg_h, n_h in zip(heads, tl, ns):
+            kh = int(np.nonzero(od.feasible_head(tg_h, n_h, prm.M, kmax, fill))[0].max())
+            assert kh == kof(h), f"head {h}: k* {kof(h)} != oracle prefix {kh} on the GPU crossing times"
+    else:
+        ks_ref, _ = od.feasible_prefix(tl, ns, prm.M, kmax, fill)
+        assert ks_ref == k, f"k* {k} != oracle prefix {ks_ref} on the GPU crossing times"
     for h in heads:
         b, rho_def, cs, pi, tg = cache[h]
+        k = kof(h)
         e = max(0, b.n + k - prm.M) if k > 0 else 0
         assert int(n_ev_gpu[h]) == e, f"head {h}: evicted {int(n_ev_gpu[h])} != e {e}"
-        mand = (tg <= k) if k > 0 else np.zeros(b.n, bool)
-        assert int(n_mand_gpu[h]) == int(mand.sum()), f"head {h}: n_mandatory"
+        gated = k > 0 and not (fill and b.n + k <= prm.M)
+        crossed = (tg <= k) if gated else np.zeros(b.n, bool)
+        assert int(n_mand_gpu[h]) == int(crossed.sum()), f"head {h}: n_mandatory"
+        mand = crossed if prm.eviction != "densest" else np.zeros(b.n, bool)
         # stage 4: projected densities and eviction set
         proj = od.projected_density(b.K, rho_def, cs, k, prm)
-        live = ~mand
+        live = np.ones(b.n, bool) if keep_crossed else ~crossed
         np.testing.assert_allclose(rhoP_gpu[h, :b.n][live], proj[live], rtol=rtol_rho, atol=1e-6)
         new_n = int(after.count[h])
         assert new_n == b.n - e + k, f"head {h}: count {new_n} != {b.n - e + k}"
@@ -147,7 +176,10 @@ def replay_update(before: GpuBank, after: GpuBank, candK, candV, cand_tok, D_gpu
         assert set(adm_toks.tolist()) <= new_toks, f"head {h}: admitted tokens missing"
         ev_gpu = np.array([t not in new_toks for t in b.tok.tolist()], dtype=bool)
         assert int(ev_gpu.sum()) == e
-        check_evictions(ev_gpu, mand, proj)
+        if prm.eviction == "oldest":
+            check_evictions_oldest(ev_gpu, mand, b.tok)
+        else:
+            check_evictions(ev_gpu, mand, proj)
         rep.admitted.append(k)
         rep.evicted.append(e)
         # stage 5: new bank -- exact pairing, frozen baselines, densities
@@ -159,7 +191,8 @@ def replay_update(before: GpuBank, after: GpuBank, candK, candV, cand_tok, D_gpu
             if t in oldpos:
                 j = oldpos[t]
                 assert np.array_equal(hb.K[i], b.K[j]) and np.array_equal(hb.V[i], b.V[j]), "survivor row moved"
-                assert hb.rho0[i] == b.rho0[j], "survivor baseline changed"
+                if prm.baseline == "frozen":
+                    assert hb.rho0[i] == b.rho0[j], "survivor baseline changed"
             else:
                 is_new[i] = True
                 j = cpos[t]
@@ -168,6 +201,8 @@ def replay_update(before: GpuBank, after: GpuBank, candK, candV, cand_tok, D_gpu
         rho_new = od.density(hb.K, prm)
         np.testing.assert_allclose(after.rho[h, :hb.n], rho_new, rtol=rtol_rho, atol=1e-6)
         np.testing.assert_allclose(hb.rho0[is_new], rho_new[is_new], rtol=rtol_rho, atol=1e-6)
+        if prm.baseline == "refresh":
+            np.testing.assert_allclose(hb.rho0, rho_new, rtol=rtol_rho, atol=1e-6)
     return rep
 
 

@@ -29,12 +29,26 @@ def kv_dtype(wl: Workload):
     return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
 
 
+def policy_bits(prm: od.Params) -> int:
+    """The C ABI's policy word for the oracle's policy fields."""
+    import kv_cache_compression_head_amd as kb
+    bits = 0
+    bits |= kb.KVB_POL_SOURCE_ORDER if prm.order == "source" else 0
+    bits |= kb.KVB_POL_REFRESH_BASELINE if prm.baseline == "refresh" else 0
+    bits |= kb.KVB_POL_EVICT_DENSEST if prm.eviction == "densest" else 0
+    bits |= kb.KVB_POL_EVICT_OLDEST if prm.eviction == "oldest" else 0
+    bits |= kb.KVB_POL_HEAD_PREFIX if prm.prefix == "head" else 0
+    bits |= kb.KVB_POL_FILL_BELOW_CAP if prm.fill_below_capacity else 0
+    return bits
+
+
 def layer_for(wl: Workload, prm: od.Params, labels=None, seg_cap=8, diagnostics=True, seg_len=0, retention=0.0):
     import kv_cache_compression_head_amd as kb
     from kv_cache_compression_head_amd.pipeline import LayerCache
     desc = kb.LayerDesc(H=wl.H, d=wl.d, M=prm.M, dtype=kb.KVB_BF16 if wl.dtype == "bf16" else kb.KVB_F32,
                         frame_tokens=wl.F, labels=list(labels) if labels is not None else [0] * wl.H,
-                        tau=prm.tau, sigma=prm.sigma, eps=prm.eps, p=prm.p, seg_len=seg_len, retention=retention)
+                        tau=prm.tau, sigma=prm.sigma, eps=prm.eps, p=prm.p, seg_len=seg_len, retention=retention,
+                        policy=policy_bits(prm))
     return LayerCache(desc, seg_cap=seg_cap, diagnostics=diagnostics)
 
 
@@ -80,7 +94,7 @@ def run_update(lc, gen: LayerGen, wl: Workload, prm: od.Params, frames: Tuple[in
             f"non-finite density in head {h}"
     return replay_update(before, after, candK.astype(np.float64), candV.astype(np.float64), np.asarray(ctok),
                          D.cpu().numpy(), s.cpu().numpy(), o.cpu().numpy(), lc.out.t_cross.cpu().numpy(),
-                         lc.out.rho_proj.cpu().numpy(), int(lc.out.k_star.cpu()[0]),
+                         lc.out.rho_proj.cpu().numpy(), lc.out.k_star.cpu().numpy(),
                          lc.out.n_mandatory.cpu().numpy(), lc.out.n_evicted.cpu().numpy(), prm, heads)
 
 

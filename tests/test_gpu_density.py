@@ -154,3 +154,42 @@ def test_empty_update_and_zero_candidates():
     torch.cuda.synchronize()
     assert int(lc.bank.count.sum().cpu()) == 0
     assert lc.out.nseg.cpu().tolist() == [0, 0]
+
+
+# DensityKV policy variants (the page's appendix E ablations), each checked
+# stage by stage against the oracle's rules for that variant
+POLICY_CASES = {
+    "source": dict(order="source"),
+    "refresh": dict(baseline="refresh"),
+    "densest": dict(eviction="densest"),
+    "oldest": dict(eviction="oldest"),
+    "head": dict(prefix="head"),
+    "fill": dict(fill_below_capacity=True),
+    "all": dict(order="source", baseline="refresh", eviction="oldest", prefix="head", fill_below_capacity=True),
+    "densest-fill-head": dict(eviction="densest", fill_below_capacity=True, prefix="head"),
+}
+
+
+@pytest.mark.parametrize("name", list(POLICY_CASES))
+def test_tiny_policy_variants(name):
+    wl = WORKLOADS["tiny"]
+    for tau in (1.3, 2.0):
+        _stream(wl, _prm(wl, tau=tau, **POLICY_CASES[name]), attn=False, seed=4)
+
+
+@pytest.mark.parametrize("name", ["source", "refresh", "densest", "oldest", "head", "fill", "all"])
+def test_mid_bf16_policy_variants(name):
+    _stream(MID, _prm(MID, tau=1.05, **POLICY_CASES[name]), attn=False, seed=3)
+
+
+def test_tiny_source_order_oldest_is_a_window():
+    """tau = inf, source order, oldest-first completion, p = 2: the bank is
+    the M most recent tokens after every update (a sliding window for any
+    interaction)."""
+    wl = WORKLOADS["tiny"]
+    prm = _prm(wl, tau=math.inf, order="source", eviction="oldest")
+    _, lc = _stream(wl, prm, attn=False)
+    bank = GpuBank.read(lc.bank)
+    last = wl.bank_updates[-1][1] * wl.F
+    for h in range(wl.H):
+        assert sorted(bank.tok[h, :bank.count[h]].tolist()) == list(range(last - 64, last))
