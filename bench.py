@@ -46,7 +46,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def setup(name: str, seed: int = 0):
+def setup(name: str, seed: int = 0, policy: int = 0, tau=None):
     import numpy as np
     import torch
     import kv_cache_compression_head_amd as kb
@@ -54,6 +54,9 @@ def setup(name: str, seed: int = 0):
     from kvsynth import WORKLOADS, LayerGen, frame_tokens
 
     wl = WORKLOADS[name]
+    if tau is not None:
+        import dataclasses
+        wl = dataclasses.replace(wl, tau=float(tau))
     gen = LayerGen(wl, seed, 0)
     kdt = torch.bfloat16
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(kdt).contiguous()
@@ -74,7 +77,7 @@ def setup(name: str, seed: int = 0):
     Q = dev(gen.queries_all(range(q0, q1), rc))
     log(f"inputs generated in {time.time() - t:.1f}s")
     desc = kb.LayerDesc(H=wl.H, d=wl.d, M=wl.M, dtype=kb.KVB_BF16, frame_tokens=wl.F, labels=[0] * wl.H,
-                        tau=wl.tau, sigma=wl.sigma, eps=wl.eps, p=wl.p)
+                        tau=wl.tau, sigma=wl.sigma, eps=wl.eps, p=wl.p, policy=policy)
     lc = LayerCache(desc, seg_cap=8, max_N=max(inp["candK"].shape[1], inp["bankK"].shape[1]))
     # cold bank: frames b0..b1 admitted together into the empty bank
     lc.step(inp["bankK"], inp["bankV"], inp["bankT"], lay)
@@ -270,6 +273,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter yardstick) and exit")
+    ap.add_argument("--policy", type=int, default=0,
+                    help="DensityKV policy variant bits (KVB_POL_*; 0 = the method)")
+    ap.add_argument("--tau", type=float, default=None, help="override the workload's density growth bound")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no "
@@ -293,7 +299,10 @@ def main():
                                    "frames per chunk, 6-frame window, 3-frame chunk; steady-state chunks"},
             "ms_per_layer_chunk": round(ms / info["layers"], 4), "rollout": info}), flush=True)
         return
-    wl, lc, snap, inp, lay, Q, O = setup(args.config)
+    if (args.policy or args.tau is not None) and not args.no_cpu_baseline:
+        print("bench.py: --policy / --tau measure variants; run them with --no-cpu-baseline", file=sys.stderr)
+        sys.exit(2)
+    wl, lc, snap, inp, lay, Q, O = setup(args.config, policy=args.policy, tau=args.tau)
     log("setup done")
     for _ in range(args.warmup):
         one_step(lc, snap, inp, lay, Q, O)
@@ -366,7 +375,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{args.config}: one layer-chunk, H={wl.H}, d={wl.d}, F={wl.F}, M={wl.M}, "
                                f"N={inp['candK'].shape[1]}, Lq={wl.Lq}, window={wl.window[1] - wl.window[0]} frames, "
-                               f"tau={wl.tau}, sigma={wl.sigma}, p={wl.p}"},
+                               f"tau={wl.tau}, sigma={wl.sigma}, p={wl.p}"
+                               + (f", policy={args.policy}" if args.policy else "")},
         "stages_ms": {k: round(v, 4) for k, v in avg.items()},
         "attention_tflops": round(attn_tflops, 2), "attention_frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "k_star": kstar, "roofline": roof, "density_stages": density_roof, "cpu_baseline": cpu,
