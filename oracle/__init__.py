@@ -22,7 +22,10 @@ Sources (page title, then section / equation):
   3.5 (implementation sketch).
 * DensityKV card page, Figure 2 (sink + bank + local window attended together
   through native attention).
+* DensityKV paper summary, supplementary "Post-RoPE Attention Geometry"
+  (memory keys carry temporal rotary coordinate 0): the memory-key
+  re-rotation in ``rope``.
 
 Parity status per function is listed in each module header.
 """
-from . import density, attention, forcing  # noqa: F401
+from . import density, attention, forcing, rope  # noqa: F401
