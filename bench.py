@@ -129,6 +129,39 @@ def recorded_attention_traffic(config: str):
     return int(kv["record.traffic_bytes_per_launch"])
 
 
+def memory_keys_bench(wl, iters: int = 20):
+    """Timing of the memory-key write path on the workload's window: the
+    oldest 3 of its frames leave the ring (re-rotated to temporal coordinate
+    0, values copied) and 3 arriving frames take their slots.  HBM-bound:
+    bytes per launch = read departing K,V + write candidates + read arriving
+    + write ring = 4 x 2 x H x rows x d x 2."""
+    import torch
+    import kv_cache_compression_head_amd as kb
+    W = wl.window[1] - wl.window[0]
+    n = 3 * wl.F
+    cap = W * wl.F
+    g = torch.Generator(device="cuda").manual_seed(0)
+    mk = lambda r: torch.randn(wl.H, r, wl.d, device="cuda", generator=g).to(torch.bfloat16)
+    rk, rv, nk, nv = mk(cap), mk(cap), mk(n), mk(n)
+    ck, cv = torch.empty_like(nk), torch.empty_like(nv)
+    desc = kb.LayerDesc(H=wl.H, d=wl.d, M=wl.M, dtype=kb.KVB_BF16, frame_tokens=wl.F, labels=[0] * wl.H)
+    call = lambda i: kb.kvbank_window_advance(desc, rk, rv, (i * n) % cap, n, 1, ck, cv, nk, nv)
+    for i in range(3):
+        call(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(iters):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    nbytes = 4 * 2 * wl.H * n * wl.d * 2
+    return {"kernel": "window_advance_kernel (kvbank_window_advance)", "rows": n, "ms": round(ms, 4),
+            "bytes_per_launch": nbytes, "GB/s": round(nbytes / ms / 1e6, 1),
+            "frac_hbm_peak": round(nbytes / ms / 1e6 / 8000.0, 4)}
+
+
 def copy_calibration(mib: int, copies: int):
     """A plain device-to-device copy of known size, the yardstick for the
     FETCH_SIZE / WRITE_SIZE counters."""
@@ -354,6 +387,7 @@ def main():
                 "frac_bf16_peak": round(rate * 2 * wl.d / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "frac_valu_bound": round(rate * VALU_SLOTS_PER_PAIR / PEAK_VALU_LANE_OPS, 4)}
     density_roof = {"score": pair_roof(score_pairs, avg["score"]), "update": pair_roof(upd_pairs, avg["update"])}
+    mem_keys = memory_keys_bench(wl)
     cpu = None
     if not args.no_cpu_baseline:
         # a bounded sample of about 10-30 s of CPU work: one head first, then
@@ -379,7 +413,8 @@ def main():
                                + (f", policy={args.policy}" if args.policy else "")},
         "stages_ms": {k: round(v, 4) for k, v in avg.items()},
         "attention_tflops": round(attn_tflops, 2), "attention_frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-        "k_star": kstar, "roofline": roof, "density_stages": density_roof, "cpu_baseline": cpu,
+        "k_star": kstar, "roofline": roof, "density_stages": density_roof, "memory_keys": mem_keys,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
 

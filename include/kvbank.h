@@ -223,6 +223,30 @@ int chunk_attention(const kvb_attn_desc* A, const void* Q, const kvb_segment* se
  * count.  Host only; no device work. */
 int chunk_attention_workspace_size(const kvb_attn_desc* A, size_t* bytes);
 
+/* Memory-key write path (DensityKV paper summary, supplementary "Post-RoPE
+ * Attention Geometry": memory keys carry temporal rotary coordinate 0 and keep
+ * their spatial coordinates; Method, "Online Density-Constrained Bank
+ * Update": the candidates are the frames that leave the local window).
+ * The n_rows ring rows from position start (mod ring_cap) leave the window;
+ * row r belongs to departing frame r / F (F = L->frame_tokens), whose keys
+ * carry temporal coordinate t_first + r / F.
+ *   ring_k, ring_v [H][ring_cap][d] device, L->dtype; updated in place when
+ *                   new_k/new_v are given
+ *   cand_k [H][n_rows][d]: the row's key with each temporal rotary pair
+ *                   (x_2i, x_2i+1), i < n_t = d/2 - 2 floor(d/6), turned by
+ *                   -t * rope_base^(-i / n_t) (interleaved pairs, temporal
+ *                   first); the other elements copied bit for bit
+ *   cand_v [H][n_rows][d]: the row's value, bit for bit
+ *   new_k, new_v [H][n_rows][d] (optional, both or neither): written into the
+ *                   departed slots after they are read (the arriving frames)
+ * Device buffers are caller-owned; cand_* must not overlap ring_* or new_*.
+ * n_rows = 0 is a no-op.  Errors: KVB_EINVAL null or misaligned (16 B)
+ * pointer; KVB_ESHAPE n_rows > ring_cap, start outside [0, ring_cap),
+ * n_rows not a multiple of F; KVB_EPARAM rope_base <= 1 or not finite. */
+int kvbank_window_advance(const kvb_layer_desc* L, void* ring_k, void* ring_v, int32_t ring_cap, int32_t start,
+                          int32_t n_rows, int32_t t_first, float rope_base, const void* new_k, const void* new_v,
+                          void* cand_k, void* cand_v, kvb_stream_t stream);
+
 /* Message of the last non-OK status on this thread ("" if none). */
 const char* kvb_last_error(void);
 

@@ -17,7 +17,7 @@ __all__ = [
     "KVB_POL_REFRESH_BASELINE", "KVB_POL_EVICT_DENSEST", "KVB_POL_EVICT_OLDEST", "KVB_POL_HEAD_PREFIX",
     "KVB_POL_FILL_BELOW_CAP",
     "KvbError", "load_library", "kvbank_workspace_size", "kvbank_score", "kvbank_update",
-    "chunk_attention", "chunk_attention_workspace_size", "kvb_last_error", "LayerDesc", "Bank", "KVLayout", "UpdateOut",
+    "chunk_attention", "chunk_attention_workspace_size", "kvbank_window_advance", "kvb_last_error", "LayerDesc", "Bank", "KVLayout", "UpdateOut",
     "HEADER_FUNCTIONS",
 ]
 
@@ -31,7 +31,7 @@ KVB_POL_SOURCE_ORDER, KVB_POL_REFRESH_BASELINE, KVB_POL_EVICT_DENSEST = 1, 2, 4
 KVB_POL_EVICT_OLDEST, KVB_POL_HEAD_PREFIX, KVB_POL_FILL_BELOW_CAP = 8, 16, 32
 KVB_MAX_SEGMENTS = 256
 HEADER_FUNCTIONS = ("kvbank_workspace_size", "kvbank_score", "kvbank_update", "chunk_attention",
-                    "chunk_attention_workspace_size", "kvb_last_error")
+                    "chunk_attention_workspace_size", "kvbank_window_advance", "kvb_last_error")
 
 _c_i32, _c_f32, _c_f64, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 
@@ -97,8 +97,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                   ctypes.c_size_t, _vp]
     lib.chunk_attention.argtypes = [ctypes.POINTER(kvb_attn_desc), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.chunk_attention_workspace_size.argtypes = [ctypes.POINTER(kvb_attn_desc), ctypes.POINTER(ctypes.c_size_t)]
+    lib.kvbank_window_advance.argtypes = [ctypes.POINTER(kvb_layer_desc), _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                          _c_f32, _vp, _vp, _vp, _vp, _vp]
     for f in ("kvbank_workspace_size", "kvbank_score", "kvbank_update", "chunk_attention",
-              "chunk_attention_workspace_size"):
+              "chunk_attention_workspace_size", "kvbank_window_advance"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kvb_last_error.restype = ctypes.c_char_p
     lib.kvb_last_error.argtypes = []
@@ -329,3 +331,24 @@ def chunk_attention(H: int, d: int, Lq: int, dtype: int, Q, segs, nseg, seg_cap:
         ws = torch.empty(n, dtype=torch.uint8, device=Q.device) if n > 0 else None
     _check(lib.chunk_attention(ctypes.byref(desc), _ptr(Q), _ptr(segs), _ptr(nseg), _ptr(O), _ptr(ws),
                                0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def kvbank_window_advance(layer: LayerDesc, ring_k, ring_v, start: int, n_rows: int, t_first: int, cand_k, cand_v,
+                          new_k=None, new_v=None, rope_base: float = 10000.0, stream=None):
+    """Departing window rows -> bank candidates at temporal coordinate 0;
+    arriving rows (optional) into the freed ring slots.  ring_* [H][cap][d],
+    cand_* / new_* [H][n_rows][d], all of the layer's dtype."""
+    lib = load_library()
+    kd = _kv_dtype(layer.dtype)
+    cap = int(ring_k.shape[1])
+    _req(ring_k, "ring_k", kd, (layer.H, cap, layer.d))
+    _req(ring_v, "ring_v", kd, (layer.H, cap, layer.d))
+    _req(cand_k, "cand_k", kd, (layer.H, n_rows, layer.d))
+    _req(cand_v, "cand_v", kd, (layer.H, n_rows, layer.d))
+    if new_k is not None:
+        _req(new_k, "new_k", kd, (layer.H, n_rows, layer.d))
+        _req(new_v, "new_v", kd, (layer.H, n_rows, layer.d))
+    desc = layer.c()
+    _check(lib.kvbank_window_advance(ctypes.byref(desc), _ptr(ring_k), _ptr(ring_v), cap, int(start), int(n_rows),
+                                     int(t_first), float(rope_base), _ptr(new_k), _ptr(new_v), _ptr(cand_k),
+                                     _ptr(cand_v), _stream(stream)))

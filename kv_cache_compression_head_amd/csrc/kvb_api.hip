@@ -482,6 +482,34 @@ int chunk_attention(const kvb_attn_desc* A, const void* Q, const kvb_segment* se
   return ok();
 }
 
+int kvbank_window_advance(const kvb_layer_desc* L, void* ring_k, void* ring_v, int32_t ring_cap, int32_t start,
+                          int32_t n_rows, int32_t t_first, float rope_base, const void* new_k, const void* new_v,
+                          void* cand_k, void* cand_v, kvb_stream_t stream) {
+  if (!L) return fail(KVB_EINVAL, "layer descriptor is NULL");
+  if (L->H < 1 || L->H > KVB_MAX_HEADS) return fail(KVB_ESHAPE, "H=%d", L->H);
+  if (L->d != 64 && L->d != 128) return fail(KVB_ESHAPE, "d=%d (supported: 64, 128)", L->d);
+  if (L->dtype != KVB_BF16 && L->dtype != KVB_F32) return fail(KVB_EDTYPE, "dtype=%d", L->dtype);
+  if (L->frame_tokens <= 0) return fail(KVB_ESHAPE, "frame_tokens=%d", L->frame_tokens);
+  if (!(rope_base > 1.0f) || !isfinite(rope_base)) return fail(KVB_EPARAM, "rope_base=%g", (double)rope_base);
+  if (n_rows < 0 || ring_cap < 0 || n_rows > ring_cap || n_rows % L->frame_tokens != 0)
+    return fail(KVB_ESHAPE, "n_rows=%d ring_cap=%d frame_tokens=%d", n_rows, ring_cap, L->frame_tokens);
+  if (n_rows == 0) return ok();
+  if (start < 0 || start >= ring_cap) return fail(KVB_ESHAPE, "start=%d ring_cap=%d", start, ring_cap);
+  if ((new_k == nullptr) != (new_v == nullptr)) return fail(KVB_EINVAL, "new_k and new_v: both or neither");
+  REQ_PTR(ring_k, 16, "ring_k");
+  REQ_PTR(ring_v, 16, "ring_v");
+  REQ_PTR(cand_k, 16, "cand_k");
+  REQ_PTR(cand_v, 16, "cand_v");
+  if (new_k) { REQ_PTR(new_k, 16, "new_k"); REQ_PTR(new_v, 16, "new_v"); }
+  WindowLaunch w{};
+  w.ring_k = ring_k; w.ring_v = ring_v; w.cap = ring_cap; w.start = start; w.n_rows = n_rows;
+  w.F = L->frame_tokens; w.t_first = t_first; w.H = L->H; w.d = L->d; w.et = L->dtype;
+  w.log2_base = log2((double)rope_base);
+  w.new_k = new_k; w.new_v = new_v; w.cand_k = cand_k; w.cand_v = cand_v;
+  HIPCHK(launch_window_advance(w, (hipStream_t)stream));
+  return ok();
+}
+
 static_assert(KVB_MAX_HEADS <= ATT_MAX_HEADS, "attention plan holds every head");
 
 int chunk_attention_workspace_size(const kvb_attn_desc* A, size_t* bytes) {

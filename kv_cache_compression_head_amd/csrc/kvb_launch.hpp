@@ -166,6 +166,16 @@ struct AttnLaunch {
   const SegEntry* segs; const int32_t* nseg; int32_t seg_cap;
   void* ws; size_t ws_bytes;   // optional: enables the balanced grid (partials of split items)
 };
+// ---- memory-key write path (window ring advance) ---------------------------
+struct WindowLaunch {
+  void* ring_k; void* ring_v;       // [H][cap][d]
+  int32_t cap, start, n_rows, F, t_first, H, d, et;
+  double log2_base;                 // log2 of the rotary base
+  const void* new_k; const void* new_v;   // [H][n_rows][d] or null
+  void* cand_k; void* cand_v;             // [H][n_rows][d]
+};
+hipError_t launch_window_advance(const WindowLaunch& a, hipStream_t s);
+
 struct AttnPlan { int G, rounds, Ir; bool use; int64_t flag_bytes, bytes; };
 constexpr int ATT_MAX_HEADS = 64;   // per-head tile counts of the balanced grid's plan live in LDS
 AttnPlan attention_plan(int H, int d, int Lq, int et);

@@ -115,3 +115,28 @@ def test_struct_layouts_match_the_c_header(tmp_path):
         assert int(got[f"{name} size"]) == ctypes.sizeof(cls), name
         for f, _ in cls._fields_:
             assert int(got[f"{name}.{f}"]) == getattr(cls, f).offset, f"{name}.{f}"
+
+
+def test_window_advance_rejects_before_launch():
+    """kvbank_window_advance checks shapes, parameters and pointers on the
+    host; n_rows = 0 is a no-op (nothing launched, no pointer read)."""
+    lib = kb.load_library()
+    d = _desc().c()                      # F = 16
+    wa = lib.kvbank_window_advance
+    ok = dict(ring_k=16, ring_v=32, cap=64, start=0, n=32, t0=1, base=10000.0, nk=None, nv=None, ck=48, cv=64)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return wa(ctypes.byref(d), a["ring_k"], a["ring_v"], a["cap"], a["start"], a["n"], a["t0"], a["base"],
+                  a["nk"], a["nv"], a["ck"], a["cv"], None)
+    assert call(n=0, ring_k=None, ring_v=None, ck=None, cv=None) == 0
+    assert call(n=24) == -2                 # not a multiple of F
+    assert call(n=80) == -2                 # more rows than the ring holds
+    assert call(start=64) == -2             # start outside the ring
+    assert call(base=1.0) == -4
+    assert call(base=math.inf) == -4
+    assert call(nk=16) == -1                # new_k without new_v
+    assert call(ck=17) == -1                # misaligned
+    assert call(cv=None) == -1
+    assert kb.kvb_last_error()
