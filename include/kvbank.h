@@ -93,7 +93,11 @@ typedef struct ihipStream_t* kvb_stream_t;   /* same type as hipStream_t */
 #define KVB_POL_EVICT_OLDEST     8u   /* crossed states, then ascending token id (source-order completion) */
 #define KVB_POL_HEAD_PREFIX     16u   /* each density head its own largest feasible prefix (k_star is [H]) */
 #define KVB_POL_FILL_BELOW_CAP  32u   /* no density check, no eviction, for prefixes with n + k <= M */
-#define KVB_POL_ALL             63u
+/* Forcing-KV dynamic heads (notes page, section 3.4 as printed): BottomK
+ * within each frame, floor(r * n) of its n = F / seg_len segments, instead of
+ * one BottomK over all (frame, segment) items */
+#define KVB_POL_FRAME_BOTTOMK   64u
+#define KVB_POL_ALL            127u
 
 typedef struct kvb_params {
   float tau;          /* density growth bound, >= 1 (may be +inf) */
@@ -101,7 +105,7 @@ typedef struct kvb_params {
   float eps;          /* softening, > 0 unless p == 0 */
   float p;            /* decay exponent, >= 0 */
   int32_t seg_len;    /* Forcing-KV segment length in tokens (divides F); used by dynamic heads */
-  uint32_t policy;    /* OR of KVB_POL_* (density heads); EVICT_DENSEST and EVICT_OLDEST exclude each other */
+  uint32_t policy;    /* OR of KVB_POL_*; EVICT_DENSEST and EVICT_OLDEST exclude each other */
   double retention;   /* Forcing-KV kept fraction r in [0, 1] */
 } kvb_params;
 

@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 __all__ = [
     "KVB_BF16", "KVB_F32", "KVB_HEAD_DENSITY", "KVB_HEAD_STATIC", "KVB_HEAD_DYNAMIC", "KVB_POL_SOURCE_ORDER",
     "KVB_POL_REFRESH_BASELINE", "KVB_POL_EVICT_DENSEST", "KVB_POL_EVICT_OLDEST", "KVB_POL_HEAD_PREFIX",
-    "KVB_POL_FILL_BELOW_CAP",
+    "KVB_POL_FILL_BELOW_CAP", "KVB_POL_FRAME_BOTTOMK",
     "KvbError", "load_library", "kvbank_workspace_size", "kvbank_score", "kvbank_update",
     "chunk_attention", "chunk_attention_workspace_size", "kvbank_window_advance", "kvb_last_error", "LayerDesc", "Bank", "KVLayout", "UpdateOut",
     "HEADER_FUNCTIONS",
@@ -29,6 +29,7 @@ KVB_HEAD_DENSITY, KVB_HEAD_STATIC, KVB_HEAD_DYNAMIC = 0, 1, 2
 # DensityKV policy variants (kvb_params.policy); 0 is the method
 KVB_POL_SOURCE_ORDER, KVB_POL_REFRESH_BASELINE, KVB_POL_EVICT_DENSEST = 1, 2, 4
 KVB_POL_EVICT_OLDEST, KVB_POL_HEAD_PREFIX, KVB_POL_FILL_BELOW_CAP = 8, 16, 32
+KVB_POL_FRAME_BOTTOMK = 64
 KVB_MAX_SEGMENTS = 256
 HEADER_FUNCTIONS = ("kvbank_workspace_size", "kvbank_score", "kvbank_update", "chunk_attention",
                     "chunk_attention_workspace_size", "kvbank_window_advance", "kvb_last_error")

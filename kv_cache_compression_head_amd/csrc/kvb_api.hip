@@ -75,10 +75,10 @@ int check_layer(const kvb_layer_desc* L, int32_t N, Heads* hd) {
     if (!(P.p >= 0.0f) || !isfinite(P.p)) return fail(KVB_EPARAM, "p=%g must be >= 0", (double)P.p);
     if (P.p > 0.0f && (!(P.eps > 0.0f) || !isfinite(P.eps)))
       return fail(KVB_EPARAM, "eps=%g must be > 0 when p > 0", (double)P.eps);
-    if (P.policy & ~KVB_POL_ALL) return fail(KVB_EPARAM, "policy=%#x has unknown bits", P.policy);
-    if ((P.policy & KVB_POL_EVICT_DENSEST) && (P.policy & KVB_POL_EVICT_OLDEST))
-      return fail(KVB_EPARAM, "policy: EVICT_DENSEST and EVICT_OLDEST exclude each other");
   }
+  if (P.policy & ~KVB_POL_ALL) return fail(KVB_EPARAM, "policy=%#x has unknown bits", P.policy);
+  if ((P.policy & KVB_POL_EVICT_DENSEST) && (P.policy & KVB_POL_EVICT_OLDEST))
+    return fail(KVB_EPARAM, "policy: EVICT_DENSEST and EVICT_OLDEST exclude each other");
   if (hd->dyn) {
     if (P.seg_len <= 0 || L->frame_tokens % P.seg_len != 0)
       return fail(KVB_EPARAM, "seg_len=%d must divide frame_tokens=%d", P.seg_len, L->frame_tokens);
@@ -305,8 +305,17 @@ int kvbank_score(const kvb_layer_desc* L, const kvb_bank* bank, const void* cand
     c.cosbuf = at<float>(ws, lo.cos); c.scores = out_score; c.score_hstride = N;
     HIPCHK(launch_segment_cosine(c, st));
     const int items = T * (F / seg);
-    HIPCHK(launch_sort(out_score, N, nullptr, 0, hd.dyn, H, items, at<uint64_t>(ws, lo.k0), at<uint64_t>(ws, lo.k1),
-                       at<int32_t>(ws, lo.v0), at<int32_t>(ws, lo.v1), out_order, N, st));
+    if (L->params.policy & KVB_POL_FRAME_BOTTOMK) {
+      // per-frame BottomK: items sorted by their rank inside their frame (then
+      // by index), so that the first T floor(r n) are every frame's lowest
+      float* rank = at<float>(ws, lo.cos);   // the cosine scratch is free again
+      HIPCHK(launch_frame_rank(out_score + (int64_t)hd.dyn_list[0] * N, items, F / seg, rank, st));
+      HIPCHK(launch_sort(rank, 0, nullptr, 0, hd.dyn, H, items, at<uint64_t>(ws, lo.k0), at<uint64_t>(ws, lo.k1),
+                         at<int32_t>(ws, lo.v0), at<int32_t>(ws, lo.v1), out_order, N, st));
+    } else {
+      HIPCHK(launch_sort(out_score, N, nullptr, 0, hd.dyn, H, items, at<uint64_t>(ws, lo.k0),
+                         at<uint64_t>(ws, lo.k1), at<int32_t>(ws, lo.v0), at<int32_t>(ws, lo.v1), out_order, N, st));
+    }
   }
   return ok();
 }
@@ -345,7 +354,12 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
   int items = 0, keep = 0;
   if (hd.dyn) {
     items = (N / F) * (F / L->params.seg_len);
-    keep = (int)floor(L->params.retention * (double)items);
+    if (L->params.policy & KVB_POL_FRAME_BOTTOMK) {
+      const int nseg = F / L->params.seg_len;
+      keep = (N / F) * (int)floor(L->params.retention * (double)nseg);
+    } else {
+      keep = (int)floor(L->params.retention * (double)items);
+    }
   }
   {
     int need = 0;

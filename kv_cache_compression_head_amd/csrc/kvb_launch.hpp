@@ -77,6 +77,10 @@ hipError_t launch_sort(const float* score, int64_t score_hstride, const int32_t*
                        int32_t* vbuf0, int32_t* vbuf1, int32_t* out_order, int64_t out_hstride,
                        hipStream_t s);
 
+// rank[i] = position of item i inside its frame of nseg items, ascending by
+// (score, index), as a float sort key
+hipError_t launch_frame_rank(const float* score, int items, int nseg, float* rank, hipStream_t s);
+
 // per head: mean of D over n, delta = D / mean (0 if bank empty or mean 0)
 hipError_t launch_delta(const float* D, const int32_t* count, uint64_t head_on, int H, int n,
                         float* delta, hipStream_t s);

@@ -200,6 +200,29 @@ hipError_t launch_sort(const float* score, int64_t score_hstride, const int32_t*
 }
 
 // ---------------------------------------------------------------------------
+// per-frame rank of a Forcing-KV segment score (frames hold a handful of
+// segments: a direct count per item)
+// ---------------------------------------------------------------------------
+__global__ void frame_rank_kernel(const float* __restrict__ score, int items, int nseg, float* __restrict__ rank) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= items) return;
+  const int f0 = (i / nseg) * nseg;
+  const float s = score[i];
+  int r = 0;
+  for (int j = f0; j < f0 + nseg; ++j) {
+    const float sj = score[j];
+    r += (sj < s || (sj == s && j < i)) ? 1 : 0;
+  }
+  rank[i] = (float)r;
+}
+
+hipError_t launch_frame_rank(const float* score, int items, int nseg, float* rank, hipStream_t st) {
+  if (items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(frame_rank_kernel, dim3((items + 255) / 256), dim3(256), 0, st, score, items, nseg, rank);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // shared prefix length k*
 // ---------------------------------------------------------------------------
 __global__ void hist_kernel(const int32_t* __restrict__ t, const int32_t* __restrict__ count,

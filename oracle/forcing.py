@@ -19,6 +19,10 @@ Video Diffusion Models" (paper notes).
   the dynamic heads; the selection is one global BottomK over all (frame,
   segment) items; kept items are gathered in token order.
 
+Variant (section 3.4 as printed): BottomK within each frame, keeping
+floor(r * n) of its n segments (ties: lower index); with the appendix
+defaults n = 6, r = 0.3 that is one segment per frame.
+
 Readings: cos(a, b) = a.b / max(|a| |b|, 1e-8); r is the kept fraction and
 the kept count is floor(r * items) computed in double precision; ties in the
 BottomK go to the lower item index.
@@ -68,6 +72,18 @@ def bottomk(scores: np.ndarray, r: float) -> np.ndarray:
     k = keep_count(r, scores.shape[0])
     order = np.lexsort((np.arange(scores.shape[0]), np.asarray(scores, np.float64)))
     return np.sort(order[:k])
+
+
+def bottomk_per_frame(scores: np.ndarray, r: float, nseg: int) -> np.ndarray:
+    """Per frame, the floor(r * nseg) lowest scores of its nseg segments
+    (ties: lower index); kept item indices ascending."""
+    scores = np.asarray(scores, np.float64)
+    k = keep_count(r, nseg)
+    kept = []
+    for t in range(scores.shape[0] // nseg):
+        s = scores[t * nseg:(t + 1) * nseg]
+        kept.extend(t * nseg + i for i in sorted(range(nseg), key=lambda i: (s[i], i))[:k])
+    return np.array(sorted(kept), dtype=np.int64)
 
 
 def kept_token_rows(kept: np.ndarray, F: int, seg_len: int) -> np.ndarray:

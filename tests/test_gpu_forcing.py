@@ -15,10 +15,10 @@ from _parity import check_order
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl, seed=0, rows=None):
+def _run(wl, seed=0, rows=None, per_frame=False):
     import torch
     import kv_cache_compression_head_amd as kb
-    gc.banner(f"forcing {wl.name} seg_len={wl.seg_len} r={wl.retention} seed={seed}")
+    gc.banner(f"forcing {wl.name} seg_len={wl.seg_len} r={wl.retention} seed={seed} per_frame={per_frame}")
     gen = LayerGen(wl, seed, 0)
     labels = head_labels(wl, seed)
     F, H, d = wl.F, wl.H, wl.d
@@ -33,13 +33,15 @@ def _run(wl, seed=0, rows=None):
     Q = gen.queries_all(ch_f, ch_f)
     T = len(hist_f)
     items = T * (F // wl.seg_len)
-    keep = of.keep_count(wl.retention, items)
+    nseg = F // wl.seg_len
+    keep = T * of.keep_count(wl.retention, nseg) if per_frame else of.keep_count(wl.retention, items)
     seg_cap = min(256, 2 + keep + 1)
     from kvsynth import Workload
     prm_M = 0
     import kv_cache_compression_head_amd.pipeline as pl
     desc = kb.LayerDesc(H=H, d=d, M=prm_M, dtype=kb.KVB_BF16, frame_tokens=F, labels=labels.tolist(),
-                        seg_len=wl.seg_len, retention=wl.retention)
+                        seg_len=wl.seg_len, retention=wl.retention,
+                        policy=kb.KVB_POL_FRAME_BOTTOMK if per_frame else 0)
     lc = pl.LayerCache(desc, seg_cap=seg_cap)
     kdt = torch.bfloat16
     N = T * F
@@ -59,8 +61,15 @@ def _run(wl, seed=0, rows=None):
     s_np, o_np = s.cpu().numpy(), o.cpu().numpy()
     for h in dyn:
         np.testing.assert_allclose(s_np[h, :items], ref, rtol=2e-5, atol=2e-6)
-        check_order(o_np[h, :items], ref, np.arange(items))
+        if not per_frame:
+            check_order(o_np[h, :items], ref, np.arange(items))
     kept = np.sort(o_np[dyn[0], :keep])
+    if per_frame:
+        # the per-frame selection, decided on the GPU's own scores (fp32),
+        # is exactly the oracle's rule applied to them
+        for h in dyn:
+            assert np.sort(o_np[h, :keep]).tolist() == of.bottomk_per_frame(s_np[h, :items], wl.retention,
+                                                                             nseg).tolist()
     # segment tables
     segs = lc.segments()
     esz = 2
@@ -112,3 +121,13 @@ def test_forcing_small_shapes():
     wl = dataclasses.replace(WORKLOADS["fkv480p"], width=8, height=4, H=4, n_static=2, seg_len=8, retention=0.5,
                              history=(1, 6), chunk=(6, 9), name="fkv-small")
     _run(wl)
+
+
+@pytest.mark.parametrize("r", [0.3, 0.33, 0.5])
+def test_forcing_per_frame_bottomk(r):
+    """Section 3.4 as printed: six segments per frame, floor(r 6) kept in
+    every frame (one at the appendix's r = 0.3 and the YAML's 0.33)."""
+    wl = dataclasses.replace(WORKLOADS["fkv480p"], seg_len=260, retention=r, name=f"fkv-frame-{r}")
+    kept = _run(wl, rows=np.arange(0, wl.Lq, 37), per_frame=True)
+    T = wl.history[1] - wl.history[0]
+    assert len(kept) == T * int(np.floor(r * 6))

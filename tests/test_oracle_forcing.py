@@ -66,3 +66,30 @@ def test_static_rows_match_transition_formula():
         rows = of.static_rows(T, F)
         absolute = rows + hist_start_frame * F
         assert absolute.tolist() == list(range((i * C - 1) * F, i * C * F))
+
+
+def test_per_frame_bottomk():
+    """Section 3.4 as printed: each frame keeps floor(r n) of its n
+    segments, the lowest scores (ties to the lower index).  One frame is the
+    global BottomK; r = 1 keeps all, r = 0 none; n = 1 with r < 1 keeps
+    none (the degenerate case of one segment per frame)."""
+    rng = np.random.default_rng(3)
+    n = 6
+    s = rng.uniform(size=5 * n)
+    for r in (0.3, 0.33, 0.5, 0.99):
+        kept = of.bottomk_per_frame(s, r, n)
+        k = int(np.floor(r * n))
+        assert len(kept) == 5 * k
+        for t in range(5):
+            mine = [i for i in kept if t * n <= i < (t + 1) * n]
+            assert len(mine) == k
+            rest = [i for i in range(t * n, (t + 1) * n) if i not in mine]
+            if mine and rest:
+                assert max(s[mine]) <= min(s[rest])
+    np.testing.assert_array_equal(of.bottomk_per_frame(s[:n], 0.5, n), of.bottomk(s[:n], 0.5))
+    assert of.bottomk_per_frame(s, 1.0, n).tolist() == list(range(5 * n))
+    assert of.bottomk_per_frame(s, 0.0, n).size == 0
+    assert of.bottomk_per_frame(s, 0.9, 1).size == 0
+    # ties: equal scores keep the lower index
+    tie = np.array([0.5, 0.5, 0.1, 0.5, 0.2, 0.5])
+    assert of.bottomk_per_frame(tie, 0.5, 6).tolist() == [0, 2, 4]
