@@ -23,6 +23,14 @@ Variant (section 3.4 as printed): BottomK within each frame, keeping
 floor(r * n) of its n segments (ties: lower index); with the appendix
 defaults n = 6, r = 0.3 that is one segment per frame.
 
+Section 3.2 (offline head profiling): with A the attention mass of the
+profiling chunk's queries on the whole key set (total), the generated chunk,
+the transition frame and the sink frame, a head is static when
+(A_generate + A_transition) / (A_total - A_sink) > alpha (0.8 in the
+appendix), else dynamic.  Reading: A_region = sum over the chunk's queries of
+the softmax weights on that region's keys (so A_total = number of queries);
+the comparison is the formula's strict '>' (the printed sketch uses '>=').
+
 Readings: cos(a, b) = a.b / max(|a| |b|, 1e-8); r is the kept fraction and
 the kept count is floor(r * items) computed in double precision; ties in the
 BottomK go to the lower item index.
@@ -91,6 +99,34 @@ def kept_token_rows(kept: np.ndarray, F: int, seg_len: int) -> np.ndarray:
     nseg = F // seg_len
     rows = [np.arange(seg_len) + (i // nseg) * F + (i % nseg) * seg_len for i in np.asarray(kept)]
     return np.concatenate(rows) if rows else np.zeros(0, dtype=np.int64)
+
+
+REGION_OTHER, REGION_SINK, REGION_TRANSITION, REGION_GENERATE = 0, 1, 2, 3
+
+
+def attention_mass(Q: np.ndarray, K: np.ndarray, region: np.ndarray, scale: float = None) -> np.ndarray:
+    """[4] masses (other, sink, transition, generate): sums over queries of the
+    softmax(Q K^T scale) weights on each region's keys."""
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    region = np.asarray(region)
+    if scale is None:
+        scale = 1.0 / math.sqrt(Q.shape[1])
+    s = (Q @ K.T) * scale
+    s -= s.max(axis=1, keepdims=True)
+    P = np.exp(s)
+    P /= P.sum(axis=1, keepdims=True)
+    return np.array([P[:, region == r].sum() for r in range(4)])
+
+
+def head_score(mass: np.ndarray) -> float:
+    """(A_generate + A_transition) / (A_total - A_sink)."""
+    total = float(np.sum(mass))
+    return (mass[REGION_GENERATE] + mass[REGION_TRANSITION]) / (total - mass[REGION_SINK])
+
+
+def head_is_static(mass: np.ndarray, alpha: float = 0.8) -> bool:
+    return head_score(mass) > alpha
 
 
 def static_rows(T: int, F: int) -> np.ndarray:

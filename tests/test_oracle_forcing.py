@@ -93,3 +93,37 @@ def test_per_frame_bottomk():
     # ties: equal scores keep the lower index
     tie = np.array([0.5, 0.5, 0.1, 0.5, 0.2, 0.5])
     assert of.bottomk_per_frame(tie, 0.5, 6).tolist() == [0, 2, 4]
+
+
+def test_attention_mass_closed_form_and_brute_force():
+    """Section 3.2 masses.  Equal logits (Q = 0) spread every query's weight
+    evenly: A_region = Lq * |region| / Lkv.  A_total is the query count.
+    A per-query Python loop agrees; so does attention with one-hot values."""
+    rng = np.random.default_rng(0)
+    Lq, d = 7, 16
+    region = np.array([1] * 4 + [0] * 10 + [2] * 4 + [3] * 6)
+    K = rng.normal(size=(region.size, d))
+    m = of.attention_mass(np.zeros((Lq, d)), K, region)
+    np.testing.assert_allclose(m, [Lq * np.sum(region == r) / region.size for r in range(4)], rtol=1e-14)
+    Q = rng.normal(size=(Lq, d)) * 2
+    m = of.attention_mass(Q, K, region)
+    assert abs(m.sum() - Lq) < 1e-12
+    brute = np.zeros(4)
+    for q in range(Lq):
+        e = [np.exp(sum(Q[q, i] * K[k, i] for i in range(d)) / 4.0) for k in range(region.size)]
+        z = sum(e)
+        for k in range(region.size):
+            brute[region[k]] += e[k] / z
+    np.testing.assert_allclose(m, brute, rtol=1e-12)
+    onehot = np.eye(4)[region]
+    np.testing.assert_allclose(attention(Q, K, onehot).sum(axis=0), m, rtol=1e-12)
+
+
+def test_head_score_and_label():
+    """score = (A_gen + A_trans) / (A_total - A_sink), static when > alpha
+    (strict, as in the formula)."""
+    assert of.head_score(np.array([1.0, 5.0, 1.0, 3.0])) == 4.0 / 5.0
+    assert not of.head_is_static(np.array([1.0, 5.0, 1.0, 3.0]), 0.8)
+    assert of.head_is_static(np.array([0.5, 5.0, 1.0, 3.5]), 0.8)
+    # sink mass cancels out: the same ratio whatever the sink holds
+    assert of.head_score(np.array([1.0, 0.0, 1.0, 3.0])) == of.head_score(np.array([1.0, 9.0, 1.0, 3.0]))
