@@ -162,6 +162,52 @@ def memory_keys_bench(wl, iters: int = 20):
             "frac_hbm_peak": round(nbytes / ms / 1e6 / 8000.0, 4)}
 
 
+def head_profile_bench(wl, iters: int = 3):
+    """Timing of the Forcing-KV offline head profiling on the workload's
+    attention shape: the chunk's queries over sink + history + transition +
+    chunk keys (one call: one-hot fill, table rewrite, the attention kernels
+    with one-hot values, the per-head reduction)."""
+    import numpy as np
+    import torch
+    import kv_cache_compression_head_amd as kb
+    H, d, F, Lq = wl.H, wl.d, wl.F, wl.Lq
+    W = wl.window[1] - wl.window[0]
+    sizes = [(1, F), (0, wl.M + (W - 1) * F), (2, F), (3, Lq)]   # sink, bank + older window, transition, chunk
+    g = torch.Generator(device="cuda").manual_seed(1)
+    Q = torch.randn(H, Lq, d, device="cuda", generator=g).to(torch.bfloat16)
+    Ks = [torch.randn(H, n, d, device="cuda", generator=g).to(torch.bfloat16) for _, n in sizes]
+    seg_cap = 4
+    arr = (kb.kvb_segment * (H * seg_cap))()
+    reg = np.zeros((H, seg_cap), np.int32)
+    for h in range(H):
+        for i, ((r, n), K) in enumerate(zip(sizes, Ks)):
+            arr[h * seg_cap + i] = kb.kvb_segment(K[h].data_ptr(), 0, n, 0)
+            reg[h, i] = r
+    segs = torch.from_numpy(np.frombuffer(bytes(arr), dtype=np.uint8).copy()).to("cuda")
+    nseg = torch.full((H,), seg_cap, dtype=torch.int32, device="cuda")
+    region = torch.from_numpy(reg).to("cuda")
+    max_len = max(n for _, n in sizes)
+    ws = torch.empty(kb.forcing_head_profile_workspace_size(H, d, Lq, kb.KVB_BF16, seg_cap, max_len),
+                     dtype=torch.uint8, device="cuda")
+    score = torch.empty(H, dtype=torch.float32, device="cuda")
+    label = torch.empty(H, dtype=torch.uint8, device="cuda")
+    call = lambda: kb.forcing_head_profile(H, d, Lq, kb.KVB_BF16, Q, segs, nseg, seg_cap, region, max_len, score,
+                                           label, ws=ws)
+    call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(iters):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    lkv = sum(n for _, n in sizes)
+    flop = 4.0 * H * Lq * lkv * d
+    return {"call": "forcing_head_profile", "ms": round(ms, 4), "Lkv": lkv,
+            "TFLOP/s": round(flop / ms / 1e9, 1), "frac_bf16_peak": round(flop / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+
+
 def copy_calibration(mib: int, copies: int):
     """A plain device-to-device copy of known size, the yardstick for the
     FETCH_SIZE / WRITE_SIZE counters."""
@@ -388,6 +434,7 @@ def main():
                 "frac_valu_bound": round(rate * VALU_SLOTS_PER_PAIR / PEAK_VALU_LANE_OPS, 4)}
     density_roof = {"score": pair_roof(score_pairs, avg["score"]), "update": pair_roof(upd_pairs, avg["update"])}
     mem_keys = memory_keys_bench(wl)
+    profile = head_profile_bench(wl)
     cpu = None
     if not args.no_cpu_baseline:
         # a bounded sample of about 10-30 s of CPU work: one head first, then
@@ -414,6 +461,7 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in avg.items()},
         "attention_tflops": round(attn_tflops, 2), "attention_frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "k_star": kstar, "roofline": roof, "density_stages": density_roof, "memory_keys": mem_keys,
+        "head_profile": profile,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -251,6 +251,31 @@ int kvbank_window_advance(const kvb_layer_desc* L, void* ring_k, void* ring_v, i
                           int32_t n_rows, int32_t t_first, float rope_base, const void* new_k, const void* new_v,
                           void* cand_k, void* cand_v, kvb_stream_t stream);
 
+/* Offline head profiling (Forcing-KV notes page, section 3.2).  Per head,
+ * the sums over the chunk's Lq queries of their softmax(Q K^T * scale)
+ * weights on each region of the head's key set: A_other, A_sink,
+ * A_transition, A_generate; score = (A_generate + A_transition) /
+ * (A_total - A_sink); the head is static when score > alpha (0.8 on the
+ * page), else dynamic.
+ *   A: H, d, Lq, dtype, scale and seg_cap as for chunk_attention
+ *   Q [H][Lq][d]; segs/nseg: the head's key segments (v pointers unused)
+ *   region [H][seg_cap] int32 device: 0 other history, 1 sink, 2 transition,
+ *          3 generate (the chunk itself)
+ *   max_len: at least every segment's length (sizes the workspace)
+ *   out_mass [H][4] float device, optional: A_other, A_sink, A_transition,
+ *          A_generate; out_score [H] float; out_label [H] uint8:
+ *          KVB_HEAD_STATIC or KVB_HEAD_DYNAMIC.  A head with a segment
+ *          longer than max_len or a region outside 0..3 gets score NaN and
+ *          label 0xFF (nothing is read past the workspace).
+ *   ws: forcing_head_profile_workspace_size bytes, caller-owned.
+ * Runs the attention kernels with one-hot values (the mass of region r is
+ * column r of the output).  Errors: as for chunk_attention, plus EPARAM for
+ * alpha outside [0, 1]. */
+int forcing_head_profile_workspace_size(const kvb_attn_desc* A, int32_t max_len, size_t* bytes);
+int forcing_head_profile(const kvb_attn_desc* A, const void* Q, const kvb_segment* segs, const int32_t* nseg,
+                         const int32_t* region, int32_t max_len, float alpha, float* out_mass, float* out_score,
+                         uint8_t* out_label, void* ws, size_t ws_bytes, kvb_stream_t stream);
+
 /* Message of the last non-OK status on this thread ("" if none). */
 const char* kvb_last_error(void);
 

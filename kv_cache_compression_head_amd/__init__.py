@@ -17,7 +17,8 @@ __all__ = [
     "KVB_POL_REFRESH_BASELINE", "KVB_POL_EVICT_DENSEST", "KVB_POL_EVICT_OLDEST", "KVB_POL_HEAD_PREFIX",
     "KVB_POL_FILL_BELOW_CAP", "KVB_POL_FRAME_BOTTOMK",
     "KvbError", "load_library", "kvbank_workspace_size", "kvbank_score", "kvbank_update",
-    "chunk_attention", "chunk_attention_workspace_size", "kvbank_window_advance", "kvb_last_error", "LayerDesc", "Bank", "KVLayout", "UpdateOut",
+    "chunk_attention", "chunk_attention_workspace_size", "kvbank_window_advance", "forcing_head_profile",
+    "forcing_head_profile_workspace_size", "kvb_last_error", "LayerDesc", "Bank", "KVLayout", "UpdateOut",
     "HEADER_FUNCTIONS",
 ]
 
@@ -32,7 +33,8 @@ KVB_POL_EVICT_OLDEST, KVB_POL_HEAD_PREFIX, KVB_POL_FILL_BELOW_CAP = 8, 16, 32
 KVB_POL_FRAME_BOTTOMK = 64
 KVB_MAX_SEGMENTS = 256
 HEADER_FUNCTIONS = ("kvbank_workspace_size", "kvbank_score", "kvbank_update", "chunk_attention",
-                    "chunk_attention_workspace_size", "kvbank_window_advance", "kvb_last_error")
+                    "chunk_attention_workspace_size", "kvbank_window_advance", "forcing_head_profile_workspace_size",
+                    "forcing_head_profile", "kvb_last_error")
 
 _c_i32, _c_f32, _c_f64, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 
@@ -100,8 +102,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.chunk_attention_workspace_size.argtypes = [ctypes.POINTER(kvb_attn_desc), ctypes.POINTER(ctypes.c_size_t)]
     lib.kvbank_window_advance.argtypes = [ctypes.POINTER(kvb_layer_desc), _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                           _c_f32, _vp, _vp, _vp, _vp, _vp]
+    lib.forcing_head_profile_workspace_size.argtypes = [ctypes.POINTER(kvb_attn_desc), _c_i32,
+                                                        ctypes.POINTER(ctypes.c_size_t)]
+    lib.forcing_head_profile.argtypes = [ctypes.POINTER(kvb_attn_desc), _vp, _vp, _vp, _vp, _c_i32, _c_f32, _vp, _vp,
+                                         _vp, _vp, ctypes.c_size_t, _vp]
     for f in ("kvbank_workspace_size", "kvbank_score", "kvbank_update", "chunk_attention",
-              "chunk_attention_workspace_size", "kvbank_window_advance"):
+              "chunk_attention_workspace_size", "kvbank_window_advance", "forcing_head_profile_workspace_size",
+              "forcing_head_profile"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kvb_last_error.restype = ctypes.c_char_p
     lib.kvb_last_error.argtypes = []
@@ -353,3 +360,28 @@ def kvbank_window_advance(layer: LayerDesc, ring_k, ring_v, start: int, n_rows: 
     _check(lib.kvbank_window_advance(ctypes.byref(desc), _ptr(ring_k), _ptr(ring_v), cap, int(start), int(n_rows),
                                      int(t_first), float(rope_base), _ptr(new_k), _ptr(new_v), _ptr(cand_k),
                                      _ptr(cand_v), _stream(stream)))
+
+
+def forcing_head_profile_workspace_size(H: int, d: int, Lq: int, dtype: int, seg_cap: int, max_len: int) -> int:
+    lib = load_library()
+    desc = kvb_attn_desc(int(H), int(d), int(Lq), int(dtype), 0.0, int(seg_cap), 1, 0)
+    n = ctypes.c_size_t(0)
+    _check(lib.forcing_head_profile_workspace_size(ctypes.byref(desc), int(max_len), ctypes.byref(n)))
+    return int(n.value)
+
+
+def forcing_head_profile(H: int, d: int, Lq: int, dtype: int, Q, segs, nseg, seg_cap: int, region, max_len: int,
+                         score, label, mass=None, alpha: float = 0.8, scale: float = 0.0, ws=None, stream=None):
+    """Per-head attention masses, score and static/dynamic label (see
+    forcing_head_profile in the C header).  ws: a device uint8 tensor of
+    forcing_head_profile_workspace_size bytes, or None to allocate one."""
+    lib = load_library()
+    _req(Q, "Q", _kv_dtype(dtype), (H, Lq, d))
+    desc = kvb_attn_desc(int(H), int(d), int(Lq), int(dtype), float(scale), int(seg_cap), 1, 0)
+    if ws is None:
+        import torch
+        ws = torch.empty(forcing_head_profile_workspace_size(H, d, Lq, dtype, seg_cap, max_len), dtype=torch.uint8,
+                         device=Q.device)
+    _check(lib.forcing_head_profile(ctypes.byref(desc), _ptr(Q), _ptr(segs), _ptr(nseg), _ptr(region), int(max_len),
+                                    float(alpha), _ptr(mass), _ptr(score), _ptr(label), _ptr(ws), ws.numel(),
+                                    _stream(stream)))

@@ -496,6 +496,64 @@ int chunk_attention(const kvb_attn_desc* A, const void* Q, const kvb_segment* se
   return ok();
 }
 
+// workspace of forcing_head_profile: one-hot blocks, segment table, O, flags
+struct ProfileLayout { int64_t ind, segs, O, bad, total; };
+static ProfileLayout profile_layout(const kvb_attn_desc* A, int32_t max_len) {
+  ProfileLayout p{};
+  int64_t off = 0;
+  const int esz = A->dtype == KVB_BF16 ? 2 : 4;
+  auto bump = [&](int64_t bytes) { const int64_t o = off; off += (bytes + 255) / 256 * 256; return o; };
+  p.ind = bump(4LL * max_len * A->d * esz);
+  p.segs = bump((int64_t)A->H * A->seg_cap * (int64_t)sizeof(SegEntry));
+  p.O = bump((int64_t)A->H * A->Lq * A->d * 4);
+  p.bad = bump((int64_t)A->H * 4);
+  p.total = off;
+  return p;
+}
+
+static int check_profile_desc(const kvb_attn_desc* A, int32_t max_len) {
+  if (!A) return fail(KVB_EINVAL, "attention descriptor is NULL");
+  if (A->H < 1 || A->H > KVB_MAX_HEADS) return fail(KVB_ESHAPE, "H=%d", A->H);
+  if (A->d != 64 && A->d != 128) return fail(KVB_ESHAPE, "d=%d (supported: 64, 128)", A->d);
+  if (A->dtype != KVB_BF16 && A->dtype != KVB_F32) return fail(KVB_EDTYPE, "dtype=%d", A->dtype);
+  if (A->Lq < 1) return fail(KVB_ESHAPE, "Lq=%d", A->Lq);
+  if (A->seg_cap < 1 || A->seg_cap > KVB_MAX_SEGMENTS) return fail(KVB_ESHAPE, "seg_cap=%d", A->seg_cap);
+  if (max_len < 0) return fail(KVB_ESHAPE, "max_len=%d", max_len);
+  return KVB_OK;
+}
+
+int forcing_head_profile_workspace_size(const kvb_attn_desc* A, int32_t max_len, size_t* bytes) {
+  if (int rc = check_profile_desc(A, max_len)) return rc;
+  if (!bytes) return fail(KVB_EINVAL, "bytes is NULL");
+  *bytes = (size_t)profile_layout(A, max_len).total;
+  return ok();
+}
+
+int forcing_head_profile(const kvb_attn_desc* A, const void* Q, const kvb_segment* segs, const int32_t* nseg,
+                         const int32_t* region, int32_t max_len, float alpha, float* out_mass, float* out_score,
+                         uint8_t* out_label, void* ws, size_t ws_bytes, kvb_stream_t stream) {
+  if (int rc = check_profile_desc(A, max_len)) return rc;
+  if (!(alpha >= 0.0f && alpha <= 1.0f)) return fail(KVB_EPARAM, "alpha=%g not in [0,1]", (double)alpha);
+  const ProfileLayout lo = profile_layout(A, max_len);
+  if (int rc = check_ws(ws, ws_bytes, (size_t)lo.total)) return rc;
+  REQ_PTR(Q, 16, "Q");
+  REQ_PTR(segs, 8, "segs");
+  REQ_PTR(nseg, 4, "nseg");
+  REQ_PTR(region, 4, "region");
+  REQ_PTR(out_score, 4, "out_score");
+  REQ_PTR(out_label, 1, "out_label");
+  if (out_mass && !aligned(out_mass, 4)) return fail(KVB_EINVAL, "out_mass is not 4-byte aligned");
+  ProfileLaunch p{};
+  p.a.H = A->H; p.a.d = A->d; p.a.Lq = A->Lq; p.a.et = A->dtype; p.a.out_f32 = 1;
+  p.a.scale = A->scale > 0.0f ? A->scale : 1.0f / sqrtf((float)A->d);
+  p.a.Q = Q; p.a.segs = reinterpret_cast<const SegEntry*>(segs); p.a.nseg = nseg; p.a.seg_cap = A->seg_cap;
+  p.region = region; p.max_len = max_len; p.alpha = alpha;
+  p.ind = at<void>(ws, lo.ind); p.segs_out = at<SegEntry>(ws, lo.segs); p.O = at<float>(ws, lo.O);
+  p.bad = at<int32_t>(ws, lo.bad); p.mass = out_mass; p.score = out_score; p.label = out_label;
+  HIPCHK(launch_head_profile(p, (hipStream_t)stream));
+  return ok();
+}
+
 int kvbank_window_advance(const kvb_layer_desc* L, void* ring_k, void* ring_v, int32_t ring_cap, int32_t start,
                           int32_t n_rows, int32_t t_first, float rope_base, const void* new_k, const void* new_v,
                           void* cand_k, void* cand_v, kvb_stream_t stream) {

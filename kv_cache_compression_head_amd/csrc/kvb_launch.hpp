@@ -170,6 +170,22 @@ struct AttnLaunch {
   const SegEntry* segs; const int32_t* nseg; int32_t seg_cap;
   void* ws; size_t ws_bytes;   // optional: enables the balanced grid (partials of split items)
 };
+// ---- offline head profiling (Forcing-KV) ------------------------------------
+struct ProfileLaunch {
+  AttnLaunch a;             // queries, segment table (keys), shapes
+  const int32_t* region;    // [H][seg_cap]: 0 other, 1 sink, 2 transition, 3 generate
+  int32_t max_len;          // rows of each one-hot block (>= every segment length)
+  float alpha;
+  void* ind;                // workspace: [4][max_len][d] one-hot rows
+  SegEntry* segs_out;       // workspace: [H][seg_cap]
+  float* O;                 // workspace: [H][Lq][d] fp32
+  int32_t* bad;             // workspace: [H]
+  float* mass;              // optional [H][4]
+  float* score;             // [H]
+  uint8_t* label;           // [H]
+};
+hipError_t launch_head_profile(const ProfileLaunch& p, hipStream_t s);
+
 // ---- memory-key write path (window ring advance) ---------------------------
 struct WindowLaunch {
   void* ring_k; void* ring_v;       // [H][cap][d]

@@ -140,3 +140,19 @@ def test_window_advance_rejects_before_launch():
     assert call(ck=17) == -1                # misaligned
     assert call(cv=None) == -1
     assert kb.kvb_last_error()
+
+
+def test_head_profile_rejects_before_launch():
+    lib = kb.load_library()
+    a = kb.kvb_attn_desc(2, 64, 40, 1, 0.0, 4, 1, 0)
+    n = ctypes.c_size_t(0)
+    assert lib.forcing_head_profile_workspace_size(ctypes.byref(a), 100, ctypes.byref(n)) == 0 and n.value > 0
+    prof = lib.forcing_head_profile
+    # alpha outside [0, 1]
+    assert prof(ctypes.byref(a), 16, 16, 16, 16, 100, ctypes.c_float(1.5), None, 16, 16, 16, n.value, None) == -4
+    # workspace too small
+    assert prof(ctypes.byref(a), 16, 16, 16, 16, 100, ctypes.c_float(0.8), None, 16, 16, 16, n.value - 1, None) == -5
+    # bad d, negative max_len
+    b = kb.kvb_attn_desc(2, 96, 40, 1, 0.0, 4, 1, 0)
+    assert lib.forcing_head_profile_workspace_size(ctypes.byref(b), 100, ctypes.byref(n)) == -2
+    assert lib.forcing_head_profile_workspace_size(ctypes.byref(a), -1, ctypes.byref(n)) == -2
