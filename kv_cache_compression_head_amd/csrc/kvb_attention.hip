@@ -6,7 +6,7 @@
 // keys without a mask.  O_h = softmax(Q_h K_h^T * scale) V_h, where K_h/V_h
 // is the concatenation of the head's segments (order irrelevant).
 //
-// bf16 path: flash-style online softmax.  Work-group = 4 waves x 32 queries;
+// bf16 path: flash-style online softmax.  Work-group = 8 waves x 32 queries;
 // KV tiles of 64 keys staged in LDS, double buffered: K and V row-major with
 // XOR-swizzled 16-byte chunks, copied straight from global memory to LDS;
 // V^T fragments come from the transposing LDS read.  The next tile's copies
@@ -22,9 +22,14 @@
 
 namespace kvb {
 
-constexpr int ATT_TK = 64;          // keys per tile
-constexpr int ATT_QW = 32;          // queries per wave
-constexpr int ATT_QB = 128;         // queries per work-group
+// Eight waves of 32 queries share each K/V tile in LDS: half the L2 -> LDS
+// traffic per flop of four waves, which matters because the chip runs this
+// kernel at its power limit (one work-group per CU, two waves per SIMD).
+constexpr int ATT_NW = 8;            // waves per work-group
+constexpr int ATT_NT = 64 * ATT_NW;  // threads per work-group
+constexpr int ATT_TK = 64;           // keys per tile
+constexpr int ATT_QW = 32;           // queries per wave
+constexpr int ATT_QB = 32 * ATT_NW;  // queries per work-group
 constexpr int ATT_MAXSEG = 256;     // segments cached in LDS
 constexpr float ATT_RESCALE_LOG2 = 8.0f;
 
@@ -102,7 +107,7 @@ KVB_DEV void attn_store(void* O, int out_f32, int64_t off, f32x4_t v, float inv)
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __restrict__ Q, void* __restrict__ O,
+__global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __restrict__ Q, void* __restrict__ O,
                                                            const SegEntry* __restrict__ segs,
                                                            const int32_t* __restrict__ nseg_p, int seg_cap, int Lq,
                                                            float scale_log2, int out_f32, int nqt, int H,
@@ -112,7 +117,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
   constexpr int NKS = D / 32;             // k-steps for S^T
   constexpr int NDB = D / 16;             // d blocks for O^T
   constexpr int CPR = D / 8;              // 16-byte chunks per key row
-  constexpr int KPASS = ATT_TK * CPR / 256;   // chunks copied per thread and tile (each of K, V)
+  constexpr int KPASS = ATT_TK * CPR / ATT_NT;   // chunks copied per thread and tile (each of K, V)
   // two buffer sets as distinct LDS objects: the direct-to-LDS copy of the
   // next tile is then known not to alias the reads of the current one
   __shared__ __attribute__((aligned(16))) uint16_t sK0[ATT_TK * D];
@@ -489,7 +494,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
 
     if (slot >= 0) {
       // ---- partial: lane's o (NDB x 2 vectors), then {m0, m1, L0, L1} ----
-      f32x4_t* pp = part + (((int64_t)ir * 2 + slot) * 4 + w) * (2 * NDB + 1) * 64 + lane;
+      f32x4_t* pp = part + (((int64_t)ir * 2 + slot) * ATT_NW + w) * (2 * NDB + 1) * 64 + lane;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -564,7 +569,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const uint16_t* __res
 // the two references, o = (o0 a0 + o1 a1) / (L0 a0 + L1 a1).  One
 // work-group per left-over item, lanes laid out as in attn_bf16_kernel.
 template <int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(void* __restrict__ O, const f32x4_t* __restrict__ part,
+__global__ __launch_bounds__(ATT_NT) void attn_merge_kernel(void* __restrict__ O, const f32x4_t* __restrict__ part,
                                                          const int32_t* __restrict__ pflag, int base, int nqt,
                                                          int Lq, int out_f32) {
   constexpr int NDB = D / 16;
@@ -572,8 +577,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(void* __restrict__ O, c
   if (pflag[ir] == 0) return;
   const int item = base + ir, h = item / nqt, qt = item % nqt;
   const int lane = lane_id(), w = wave_id(), g = lane >> 4;
-  const f32x4_t* p0 = part + (((int64_t)ir * 2 + 0) * 4 + w) * (2 * NDB + 1) * 64 + lane;
-  const f32x4_t* p1 = p0 + 4 * (2 * NDB + 1) * 64;
+  const f32x4_t* p0 = part + (((int64_t)ir * 2 + 0) * ATT_NW + w) * (2 * NDB + 1) * 64 + lane;
+  const f32x4_t* p1 = p0 + ATT_NW * (2 * NDB + 1) * 64;
   const f32x4_t s0 = p0[2 * NDB * 64], s1 = p1[2 * NDB * 64];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -651,7 +656,7 @@ AttnPlan attention_plan(int H, int d, int Lq, int et) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
   }
   const int items = ((Lq + ATT_QB - 1) / ATT_QB) * H;
-  p.G = 2 * cus;
+  p.G = (8 / ATT_NW) * cus;    // two waves per SIMD
   p.rounds = items / p.G;
   p.Ir = items % p.G;
   // Balance only a last round that the plain grid would leave at least a
@@ -664,7 +669,7 @@ AttnPlan attention_plan(int H, int d, int Lq, int et) {
     return p;
   }
   p.use = true;
-  const int64_t per_item = 2LL * 4 * (2 * (d / 16) + 1) * 64 * 16;   // two pieces, 4 waves, float4 per lane
+  const int64_t per_item = 2LL * ATT_NW * (2 * (d / 16) + 1) * 64 * 16;   // two pieces, every wave, float4 per lane
   p.flag_bytes = ((int64_t)p.Ir * 4 + 255) / 256 * 256;
   p.bytes = p.flag_bytes + p.Ir * per_item;
   return p;
@@ -692,17 +697,17 @@ hipError_t launch_attention(const AttnLaunch& a, hipStream_t st) {
       }
     }
     if (a.d == 128)
-      hipLaunchKernelGGL((attn_bf16_kernel<128>), dim3((unsigned)G), dim3(256), 0, st, (const uint16_t*)a.Q, a.O,
+      hipLaunchKernelGGL((attn_bf16_kernel<128>), dim3((unsigned)G), dim3(ATT_NT), 0, st, (const uint16_t*)a.Q, a.O,
                          a.segs, a.nseg, a.seg_cap, a.Lq, sl2, a.out_f32, nqt, a.H, rounds, Ir, part, flag);
     else
-      hipLaunchKernelGGL((attn_bf16_kernel<64>), dim3((unsigned)G), dim3(256), 0, st, (const uint16_t*)a.Q, a.O,
+      hipLaunchKernelGGL((attn_bf16_kernel<64>), dim3((unsigned)G), dim3(ATT_NT), 0, st, (const uint16_t*)a.Q, a.O,
                          a.segs, a.nseg, a.seg_cap, a.Lq, sl2, a.out_f32, nqt, a.H, rounds, Ir, part, flag);
     if (Ir > 0) {
       if (a.d == 128)
-        hipLaunchKernelGGL((attn_merge_kernel<128>), dim3((unsigned)Ir), dim3(256), 0, st, a.O, part, flag,
+        hipLaunchKernelGGL((attn_merge_kernel<128>), dim3((unsigned)Ir), dim3(ATT_NT), 0, st, a.O, part, flag,
                            rounds * G, nqt, a.Lq, a.out_f32);
       else
-        hipLaunchKernelGGL((attn_merge_kernel<64>), dim3((unsigned)Ir), dim3(256), 0, st, a.O, part, flag,
+        hipLaunchKernelGGL((attn_merge_kernel<64>), dim3((unsigned)Ir), dim3(ATT_NT), 0, st, a.O, part, flag,
                            rounds * G, nqt, a.Lq, a.out_f32);
     }
   } else {

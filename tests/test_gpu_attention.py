@@ -129,7 +129,7 @@ def test_attention_bf16_output_dtype():
 
 
 def test_attention_balanced_rounds():
-    """More items than slots (8 heads x 65 query tiles = 520 on 512 slots):
+    """More items than slots (8 heads x 33 query tiles = 264 on 256 slots):
     a round of whole items, then the 8 left-over items balanced over every
     work-group; heads of different lengths."""
     lens = [[300 + 97 * h, 64 * h] for h in range(8)]
@@ -137,7 +137,7 @@ def test_attention_balanced_rounds():
 
 
 def test_attention_balanced_multi_tail():
-    """10 heads x 37 query tiles over 6,400 keys (370 items on 512 slots):
+    """10 heads x 19 query tiles over 6,400 keys (190 items on 256 slots):
     the tails are short enough that each tail work-group takes several items
     of one head.  Three heads against the oracle; every head against the
     one-work-group-per-item grid."""
@@ -156,16 +156,17 @@ def test_attention_balanced_d64():
 
 def test_attention_workspace_size():
     """The workspace covers the left-over items' partials: two pieces of
-    4 waves x (2 d/16 + 1) float4 per lane each, plus a flag per item; none
-    when the last round of the plain grid is at least four fifths full."""
+    8 waves x (2 d/16 + 1) float4 per lane each, plus a flag per item; none
+    when the last round of the plain grid is at least four fifths full
+    (one work-group of 256 queries per compute unit)."""
     import kv_cache_compression_head_amd as kb
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for H, d, Lq in [(12, 128, 4680), (10, 128, 4680), (8, 128, 8200), (3, 64, 300), (12, 128, 24480)]:
-        items = -(-Lq // 128) * H
-        ir = items % (2 * cus)
-        per = 2 * 4 * (2 * (d // 16) + 1) * 64 * 16
-        use = ir > 0 and ir * 5 < 2 * cus * 4
+        items = -(-Lq // 256) * H
+        ir = items % cus
+        per = 2 * 8 * (2 * (d // 16) + 1) * 64 * 16
+        use = ir > 0 and ir * 5 < cus * 4
         want = -(-ir * 4 // 256) * 256 + ir * per if use else 0
         assert kb.chunk_attention_workspace_size(H, d, Lq, kb.KVB_BF16) == want
     assert kb.chunk_attention_workspace_size(12, 128, 4680, kb.KVB_F32) == 0
