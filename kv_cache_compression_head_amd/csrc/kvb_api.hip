@@ -114,7 +114,7 @@ constexpr int MAX_SPLITS = 8;
 
 struct Layout {
   size_t normB, normC, augB, augC, k0, k1, v0, v1, t, cp, hist, rhoP, evict, surv, evl, fixl, nsurv, nfix,
-      fmode, accS, accAE, accAA, cos, split, total;
+      fmode, accS, accAE, accAA, colAA, cos, split, total;
   int kmax, cps, ncp;
 };
 
@@ -155,6 +155,8 @@ Layout layout_of(const kvb_layer_desc* L, int32_t N) {
   o.accS = bump(&off, H * M * 4);
   o.accAE = bump(&off, H * (int64_t)o.kmax * 4);
   o.accAA = bump(&off, H * (int64_t)o.kmax * 4);
+  // column-sum slices of the symmetric admitted x admitted Gram
+  o.colAA = bump(&off, H * (int64_t)((o.kmax + GRAM_ROW_BLOCK - 1) / GRAM_ROW_BLOCK) * o.kmax * 4);
   o.cos = bump(&off, (int64_t)N * 4);
   o.split = bump(&off, H * (int64_t)MAX_SPLITS * (N > L->M ? N : L->M) * 4);
   o.total = off;
@@ -204,12 +206,40 @@ int choose_splits(int H, int rows, int ncols) {
   return best;
 }
 
+// The symmetric self-Gram: row block b takes the tiles from 4b on, so the
+// work-groups are uneven; the cost of s splits is the larger of the longest
+// work-group and the average load per slot.
+int choose_splits_sym(int H, int n) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  const int64_t slots = cus;   // one work-group per CU in this variant
+  const int64_t tiles = (n + 63) / 64;
+  const int blocks = (n + GRAM_ROW_BLOCK - 1) / GRAM_ROW_BLOCK;
+  int best = 1;
+  int64_t best_cost = INT64_MAX;
+  for (int s = 1; s <= MAX_SPLITS && s <= tiles; ++s) {
+    int64_t total = 0, longest = 0;
+    for (int b = 0; b < blocks; ++b) {
+      const int64_t t = (tiles - (int64_t)b * (GRAM_ROW_BLOCK / 64) + s - 1) / s;
+      total += t * s;
+      longest = t > longest ? t : longest;
+    }
+    const int64_t avg = (H * total + slots - 1) / slots;
+    const int64_t cost = longest > avg ? longest : avg;
+    if (cost < best_cost) { best_cost = cost; best = s; }
+  }
+  return best;
+}
+
 // one gram launch over rows_ub rows and at most cols_ub columns, with the
 // column range split over work-groups when the row tiles alone cannot fill
 // the device; split partials are summed in a fixed order
 hipError_t run_gram(GramLaunch g, int H, int rows_ub, int cols_ub, float* dst, int64_t dst_hstride, float* split,
                     int64_t split_n, hipStream_t st) {
-  g.splits = choose_splits(H, rows_ub, cols_ub);
+  g.splits = g.colsum ? choose_splits_sym(H, rows_ub) : choose_splits(H, rows_ub, cols_ub);
   if (g.splits > 1) {
     g.out = split;
     g.out_hstride = (int64_t)MAX_SPLITS * split_n;
@@ -439,8 +469,14 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
     HIPCHK(run_gram(g, H, M, kmax, at<float>(ws, lo.accS), M, split, sstride, st));
     g.rows = adm; g.cols = fxl;
     HIPCHK(run_gram(g, H, kmax, M, at<float>(ws, lo.accAE), kmax, split, sstride, st));
+    // admitted x admitted is symmetric: each unordered pair once, the
+    // mirrored half through column sums added back in order
     g.rows = adm; g.cols = adm; g.self_excl = 1;
+    g.colsum = at<float>(ws, lo.colAA); g.col_ld = kmax;
     HIPCHK(run_gram(g, H, kmax, kmax, at<float>(ws, lo.accAA), kmax, split, sstride, st));
+    HIPCHK(launch_sym_combine(at<float>(ws, lo.accAA), kmax, g.colsum, kmax,
+                              (kmax + GRAM_ROW_BLOCK - 1) / GRAM_ROW_BLOCK, adm, hd.dens, H, kmax, st));
+    g.colsum = nullptr;
     ApplyLaunch ap{};
     ap.H = H; ap.M = M; ap.N = N; ap.d = d; ap.et = et; ap.kmax = kmax; ap.active = hd.dens;
     ap.bankK = bank->K; ap.bankV = bank->V; ap.bank_tok = bank->tok; ap.rho0 = bank->rho0; ap.rho = bank->rho;

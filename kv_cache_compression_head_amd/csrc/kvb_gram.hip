@@ -227,9 +227,13 @@ constexpr int GRAM_NT = 512;      // threads per work-group
 constexpr int GRAM_ROWS = 256;    // rows per work-group (32 per wave)
 
 template <typename E, int D, int MODE, bool SELF, bool CLIST, bool DIRECT>
-__global__ __launch_bounds__(GRAM_NT, 4) void gram_kernel(KeySpace<E> ks, VList rows, VList cols,
+// The admitted x admitted variant (self-excluding index list) keeps the
+// column-sum terms live besides the row sums: it runs one work-group per CU
+// so that they fit in registers.
+__global__ __launch_bounds__(GRAM_NT, (SELF && CLIST) ? 2 : 4) void gram_kernel(KeySpace<E> ks, VList rows, VList cols,
                                                          float* __restrict__ out, int64_t out_hstride,
-                                                         int64_t split_stride, PhiConst pc, uint64_t active) {
+                                                         int64_t split_stride, PhiConst pc, uint64_t active,
+                                                         float* __restrict__ colsum, int64_t col_ld) {
   using O = Ops<E>;
   using A = Aug<E>;
   using T = Tile<E, D>;
@@ -241,6 +245,11 @@ __global__ __launch_bounds__(GRAM_NT, 4) void gram_kernel(KeySpace<E> ks, VList 
   __shared__ __attribute__((aligned(16))) u32x4_t sA1[TC];
   __shared__ int sV0[TC];
   __shared__ int sV1[TC];
+  // symmetric self-Gram (rows and columns the same list, colsum given): a
+  // work-group takes only the column tiles from its own row block on; the
+  // diagonal block adds row sums, the tiles right of it also column sums,
+  // which stand for the mirrored pairs of the later rows
+  __shared__ float sColP[SELF ? GRAM_NT / 64 : 1][SELF ? 2 : 1][SELF ? 64 : 1];
 
   // XCD-aware order: logical items (head, split, row tile), head-major
   const int R = gridDim.x, S = gridDim.z;
@@ -254,14 +263,24 @@ __global__ __launch_bounds__(GRAM_NT, 4) void gram_kernel(KeySpace<E> ks, VList 
   if (r0 >= nrows) return;
   const int ncols = vlist_count(cols, h);
   const int ntiles = (ncols + TC - 1) / TC;
-  const int per = (ntiles + (int)gridDim.z - 1) / (int)gridDim.z;
-  const int t0 = zs * per;
+  const bool sym = SELF && colsum != nullptr;
+  const int tb = sym ? r0 / TC : 0;                  // first column tile of this work-group
+  const int tdiag = tb + GRAM_ROWS / TC;             // first tile right of the diagonal block
+  const int per = (max(ntiles - tb, 0) + (int)gridDim.z - 1) / (int)gridDim.z;
+  const int t0 = tb + zs * per;
   const int t1 = min(ntiles, t0 + per);
   const int fb = ks.M > 0 ? 0 : ks.M;   // an existing row: bank slot 0, else candidate 0
 
   const int lane = lane_id(), w = wave_id();
   const int hh = lane >> 5, nn = lane & 31;
   const int wrow = r0 + w * 32;
+  if (t0 >= t1) {
+    // no column tile in this split (an empty column list, say): the partial
+    // row sums are zero, and no row fragment needs loading
+    if (lane < 32 && wrow + lane < nrows)
+      out[(int64_t)h * out_hstride + (int64_t)zs * split_stride + wrow + lane] = 0.0f;
+    return;
+  }
 
   typename O::frag xf[NK];
   typename O::frag xa;
@@ -388,6 +407,10 @@ __global__ __launch_bounds__(GRAM_NT, 4) void gram_kernel(KeySpace<E> ks, VList 
       // own partner exactly when the list positions coincide, which needs
       // the subtile's column range to be the wave's row range
       const bool diag = SELF && (tile * TC + 32 * sub) == wrow;
+      // column sums (symmetric self-Gram, right of the diagonal block). Rows
+      // and columns are one list, so such a tile only exists for a full row
+      // block: no padding row enters these sums.
+      float cs = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float t;
@@ -403,6 +426,23 @@ __global__ __launch_bounds__(GRAM_NT, 4) void gram_kernel(KeySpace<E> ks, VList 
           if (diag) f = (nn == 8 * (i >> 2) + 4 * hh + (i & 3)) ? 0.0f : f;
         }
         acc[i] += f;
+        if constexpr (SELF) cs += f;
+      }
+      if constexpr (SELF) {
+        if (sym && tile >= tdiag) sColP[w][hh][32 * sub + nn] = cs;
+      }
+    }
+    if constexpr (SELF) {
+      if (sym && tile >= tdiag) {
+        // the tile's column sums over the work-group's rows, one slice per row block
+        __syncthreads();
+        if ((int)threadIdx.x < TC) {
+          float cs = 0.0f;
+#pragma unroll
+          for (int ww = 0; ww < GRAM_NT / 64; ++ww) cs += sColP[ww][0][threadIdx.x] + sColP[ww][1][threadIdx.x];
+          const int c = tile * TC + (int)threadIdx.x;
+          if (c < ncols) colsum[((int64_t)h * R + r0 / GRAM_ROWS) * col_ld + c] = cs;
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // next tile resident in LDS
@@ -459,16 +499,16 @@ static void gram_dispatch_self(const GramLaunch& g, dim3 grid, hipStream_t st) {
   // self-exclusion only arises with both sides the same index list
   if (g.self_excl && g.cols.idx)
     hipLaunchKernelGGL((gram_kernel<E, D, MODE, true, true, DIRECT>), grid, dim3(GRAM_NT), 0, st, ks, g.rows, g.cols,
-                       g.out, g.out_hstride, g.split_stride, g.pc, g.active);
+                       g.out, g.out_hstride, g.split_stride, g.pc, g.active, g.colsum, g.col_ld);
   else if (g.self_excl)
     hipLaunchKernelGGL((gram_kernel<E, D, MODE, true, false, DIRECT>), grid, dim3(GRAM_NT), 0, st, ks, g.rows, g.cols,
-                       g.out, g.out_hstride, g.split_stride, g.pc, g.active);
+                       g.out, g.out_hstride, g.split_stride, g.pc, g.active, g.colsum, g.col_ld);
   else if (g.cols.idx)
     hipLaunchKernelGGL((gram_kernel<E, D, MODE, false, true, DIRECT>), grid, dim3(GRAM_NT), 0, st, ks, g.rows, g.cols,
-                       g.out, g.out_hstride, g.split_stride, g.pc, g.active);
+                       g.out, g.out_hstride, g.split_stride, g.pc, g.active, g.colsum, g.col_ld);
   else
     hipLaunchKernelGGL((gram_kernel<E, D, MODE, false, false, DIRECT>), grid, dim3(GRAM_NT), 0, st, ks, g.rows, g.cols,
-                       g.out, g.out_hstride, g.split_stride, g.pc, g.active);
+                       g.out, g.out_hstride, g.split_stride, g.pc, g.active, g.colsum, g.col_ld);
 }
 
 template <typename E, int D>
@@ -509,6 +549,27 @@ __global__ void sum_splits_kernel(const float* __restrict__ src, int64_t src_hst
   float s = 0.0f;
   for (int k = 0; k < splits; ++k) s += src[(int64_t)h * src_hstride + k * split_stride + i];
   dst[(int64_t)h * dst_hstride + i] = s;
+}
+
+__global__ void sym_combine_kernel(float* __restrict__ dst, int64_t dst_hstride, const float* __restrict__ colsum,
+                                   int64_t col_ld, int nblocks, VList rows, uint64_t active) {
+  const int h = blockIdx.y;
+  if (!head_on(active, h)) return;
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= vlist_count(rows, h)) return;
+  const int jb = min(j / GRAM_ROWS, nblocks);
+  float s = dst[(int64_t)h * dst_hstride + j];
+  for (int b = 0; b < jb; ++b) s += colsum[((int64_t)h * nblocks + b) * col_ld + j];
+  dst[(int64_t)h * dst_hstride + j] = s;
+}
+
+hipError_t launch_sym_combine(float* dst, int64_t dst_hstride, const float* colsum, int64_t col_ld, int nblocks,
+                              VList rows, uint64_t active, int H, int n, hipStream_t st) {
+  static_assert(GRAM_ROWS == GRAM_ROW_BLOCK, "row block of the Gram work-group");
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sym_combine_kernel, dim3((n + 255) / 256, H), dim3(256), 0, st, dst, dst_hstride, colsum, col_ld,
+                     nblocks, rows, active);
+  return hipGetLastError();
 }
 
 hipError_t launch_sum_splits(const float* src, int64_t src_hstride, int64_t split_stride, int splits, float* dst,

@@ -37,8 +37,17 @@ struct GramLaunch {
   PhiConst pc;
   int32_t phi_mode;
   uint64_t active;        // bit h: head computed
+  // symmetric self-Gram (self_excl, rows == cols): column-sum slices
+  // [H][row blocks][col_ld]; null computes every ordered pair
+  float* colsum;
+  int64_t col_ld;
 };
 hipError_t launch_gram(const GramLaunch& g, hipStream_t s);
+// dst[h][j] += sum over row blocks b < j / 256 of colsum[h][b][j], in order of b,
+// for j below the row list's count (the symmetric self-Gram's mirrored pairs)
+hipError_t launch_sym_combine(float* dst, int64_t dst_hstride, const float* colsum, int64_t col_ld, int nblocks,
+                              VList rows, uint64_t active, int H, int n, hipStream_t s);
+constexpr int GRAM_ROW_BLOCK = 256;   // rows per Gram work-group
 
 // sum split partials in order: dst[h*dst_hstride+i] = sum_s src[h*src_hstride + s*split_stride + i]
 hipError_t launch_sum_splits(const float* src, int64_t src_hstride, int64_t split_stride, int splits,
