@@ -144,6 +144,14 @@ def test_mid_bf16_general_form(sigma, eps):
     _stream(MID, _prm(MID, sigma=sigma, eps=eps), max_abs=2e-2, mean_abs=2e-3, seed=2)
 
 
+def test_mid_f32_head_prefix():
+    """fp32 keys over many 256-row blocks with a different admitted count per
+    head (per-head prefix, early crossings): the symmetric admitted Gram's
+    column sums and their ordered combine on the fp32 path."""
+    wl = dataclasses.replace(MID, dtype="f32", name="mid-f32")
+    _stream(wl, _prm(wl, tau=1.05, prefix="head"), attn=False, seed=5)
+
+
 def test_empty_update_and_zero_candidates():
     import torch
     import kv_cache_compression_head_amd as kb
