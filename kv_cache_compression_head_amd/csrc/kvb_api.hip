@@ -156,7 +156,7 @@ Layout layout_of(const kvb_layer_desc* L, int32_t N) {
   o.accAE = bump(&off, H * (int64_t)o.kmax * 4);
   o.accAA = bump(&off, H * (int64_t)o.kmax * 4);
   // column-sum slices of the symmetric admitted x admitted Gram
-  o.colAA = bump(&off, H * (int64_t)((o.kmax + GRAM_ROW_BLOCK - 1) / GRAM_ROW_BLOCK) * o.kmax * 4);
+  o.colAA = bump(&off, H * sym_head_floats(o.kmax) * 4);
   o.cos = bump(&off, (int64_t)N * 4);
   o.split = bump(&off, H * (int64_t)MAX_SPLITS * (N > L->M ? N : L->M) * 4);
   o.total = off;

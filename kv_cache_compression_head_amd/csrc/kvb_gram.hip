@@ -441,7 +441,8 @@ __global__ __launch_bounds__(GRAM_NT, (SELF && CLIST) ? 2 : 4) void gram_kernel(
 #pragma unroll
           for (int ww = 0; ww < GRAM_NT / 64; ++ww) cs += sColP[ww][0][threadIdx.x] + sColP[ww][1][threadIdx.x];
           const int c = tile * TC + (int)threadIdx.x;
-          if (c < ncols) colsum[((int64_t)h * R + r0 / GRAM_ROWS) * col_ld + c] = cs;
+          const int b = r0 / GRAM_ROWS;
+          if (c < ncols) colsum[h * sym_head_floats(col_ld) + sym_col_off(col_ld, b) + (c - (b + 1) * GRAM_ROWS)] = cs;
         }
       }
     }
@@ -559,7 +560,8 @@ __global__ void sym_combine_kernel(float* __restrict__ dst, int64_t dst_hstride,
   if (j >= vlist_count(rows, h)) return;
   const int jb = min(j / GRAM_ROWS, nblocks);
   float s = dst[(int64_t)h * dst_hstride + j];
-  for (int b = 0; b < jb; ++b) s += colsum[((int64_t)h * nblocks + b) * col_ld + j];
+  const float* ch = colsum + h * sym_head_floats(col_ld);
+  for (int b = 0; b < jb; ++b) s += ch[sym_col_off(col_ld, b) + (j - (b + 1) * GRAM_ROWS)];
   dst[(int64_t)h * dst_hstride + j] = s;
 }
 

@@ -37,17 +37,31 @@ struct GramLaunch {
   PhiConst pc;
   int32_t phi_mode;
   uint64_t active;        // bit h: head computed
-  // symmetric self-Gram (self_excl, rows == cols): column-sum slices
-  // [H][row blocks][col_ld]; null computes every ordered pair
+  // symmetric self-Gram (self_excl, rows == cols): column-sum slices in the
+  // triangular layout below, for a list bounded by col_ld entries; null
+  // computes every ordered pair
   float* colsum;
   int64_t col_ld;
 };
 hipError_t launch_gram(const GramLaunch& g, hipStream_t s);
-// dst[h][j] += sum over row blocks b < j / 256 of colsum[h][b][j], in order of b,
-// for j below the row list's count (the symmetric self-Gram's mirrored pairs)
+// dst[h][j] += sum over row blocks b < j / 256 of the column sum of block b at
+// column j, in order of b, for j below the row list's count (the symmetric
+// self-Gram's mirrored pairs)
 hipError_t launch_sym_combine(float* dst, int64_t dst_hstride, const float* colsum, int64_t col_ld, int nblocks,
                               VList rows, uint64_t active, int H, int n, hipStream_t s);
 constexpr int GRAM_ROW_BLOCK = 256;   // rows per Gram work-group
+// Triangular column-sum layout for a list bounded by n: row block b keeps only
+// the columns right of its diagonal block, [(b+1) 256, n), and the blocks are
+// packed one after another, so block b starts at sum_{b'<b} (n - (b'+1) 256).
+// Column c of block b is at sym_col_off(n, b) + c - (b+1) 256; one head holds
+// sym_head_floats(n) floats.
+__host__ __device__ inline int64_t sym_col_off(int64_t n, int b) {
+  return (int64_t)b * n - (int64_t)(GRAM_ROW_BLOCK / 2) * b * (b + 1);
+}
+__host__ __device__ inline int64_t sym_head_floats(int64_t n) {
+  const int nb = (int)((n + GRAM_ROW_BLOCK - 1) / GRAM_ROW_BLOCK);
+  return nb > 1 ? sym_col_off(n, nb - 1) : 0;
+}
 
 // sum split partials in order: dst[h*dst_hstride+i] = sum_s src[h*src_hstride + s*split_stride + i]
 hipError_t launch_sum_splits(const float* src, int64_t src_hstride, int64_t split_stride, int splits,
