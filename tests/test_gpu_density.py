@@ -152,6 +152,14 @@ def test_mid_f32_head_prefix():
     _stream(wl, _prm(wl, tau=1.05, prefix="head"), attn=False, seed=5)
 
 
+def test_mid_bf16_d64():
+    """Head dimension 64 in bf16 over many 256-row blocks: the d = 64 Gram,
+    scan and symmetric admitted Gram, and the d = 64 attention kernel on the
+    layer's segment table."""
+    wl = dataclasses.replace(MID, d=64, name="mid-d64")
+    _stream(wl, _prm(wl, tau=1.1), max_abs=2e-2, mean_abs=2e-3, seed=6)
+
+
 def test_empty_update_and_zero_candidates():
     import torch
     import kv_cache_compression_head_amd as kb
