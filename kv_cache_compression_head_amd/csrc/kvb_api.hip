@@ -215,7 +215,7 @@ int choose_splits_sym(int H, int n) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
   }
-  const int64_t slots = cus;   // one work-group per CU in this variant
+  const int64_t slots = 3LL * cus;   // three four-wave work-groups per CU in this variant
   const int64_t tiles = (n + 63) / 64;
   const int blocks = (n + GRAM_ROW_BLOCK - 1) / GRAM_ROW_BLOCK;
   int best = 1;

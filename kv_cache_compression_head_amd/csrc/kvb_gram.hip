@@ -225,12 +225,16 @@ hipError_t launch_norms(const void* keysA, int rowsA, float* outA, void* augA, c
 // ---------------------------------------------------------------------------
 constexpr int GRAM_NT = 512;      // threads per work-group
 constexpr int GRAM_ROWS = 256;    // rows per work-group (32 per wave)
+// The admitted x admitted variant (self-excluding index list) keeps the
+// column-sum terms live besides the row sums: more registers than four waves
+// per SIMD leave, so it runs four-wave work-groups of 128 rows, three waves
+// per SIMD.
+constexpr int SYM_NT = 256;
+static_assert(SYM_NT / 2 == GRAM_ROW_BLOCK, "rows per work-group of the symmetric self-Gram");
+template <bool SELF, bool CLIST> constexpr int gram_nt() { return (SELF && CLIST) ? SYM_NT : GRAM_NT; }
 
 template <typename E, int D, int MODE, bool SELF, bool CLIST, bool DIRECT>
-// The admitted x admitted variant (self-excluding index list) keeps the
-// column-sum terms live besides the row sums: it runs one work-group per CU
-// so that they fit in registers.
-__global__ __launch_bounds__(GRAM_NT, (SELF && CLIST) ? 2 : 4) void gram_kernel(KeySpace<E> ks, VList rows, VList cols,
+__global__ __launch_bounds__((gram_nt<SELF, CLIST>()), ((SELF && CLIST) ? 3 : 4)) void gram_kernel(KeySpace<E> ks, VList rows, VList cols,
                                                          float* __restrict__ out, int64_t out_hstride,
                                                          int64_t split_stride, PhiConst pc, uint64_t active,
                                                          float* __restrict__ colsum, int64_t col_ld) {
@@ -249,7 +253,9 @@ __global__ __launch_bounds__(GRAM_NT, (SELF && CLIST) ? 2 : 4) void gram_kernel(
   // work-group takes only the column tiles from its own row block on; the
   // diagonal block adds row sums, the tiles right of it also column sums,
   // which stand for the mirrored pairs of the later rows
-  __shared__ float sColP[SELF ? GRAM_NT / 64 : 1][SELF ? 2 : 1][SELF ? 64 : 1];
+  constexpr int NT = gram_nt<SELF, CLIST>();
+  constexpr int ROWS = NT / 2;   // 32 rows per wave
+  __shared__ float sColP[SELF ? NT / 64 : 1][SELF ? 2 : 1][SELF ? 64 : 1];
 
   // XCD-aware order: logical items (head, split, row tile), head-major
   const int R = gridDim.x, S = gridDim.z;
@@ -259,13 +265,13 @@ __global__ __launch_bounds__(GRAM_NT, (SELF && CLIST) ? 2 : 4) void gram_kernel(
   if (!head_on(active, h)) return;
   const HeadKeys<E, D> hk(ks, h);
   const int nrows = vlist_count(rows, h);
-  const int r0 = (lin % R) * GRAM_ROWS;
+  const int r0 = (lin % R) * ROWS;
   if (r0 >= nrows) return;
   const int ncols = vlist_count(cols, h);
   const int ntiles = (ncols + TC - 1) / TC;
   const bool sym = SELF && colsum != nullptr;
   const int tb = sym ? r0 / TC : 0;                  // first column tile of this work-group
-  const int tdiag = tb + GRAM_ROWS / TC;             // first tile right of the diagonal block
+  const int tdiag = tb + ROWS / TC;             // first tile right of the diagonal block
   const int per = (max(ntiles - tb, 0) + (int)gridDim.z - 1) / (int)gridDim.z;
   const int t0 = tb + zs * per;
   const int t1 = min(ntiles, t0 + per);
@@ -304,7 +310,7 @@ __global__ __launch_bounds__(GRAM_NT, (SELF && CLIST) ? 2 : 4) void gram_kernel(
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
 
-  using LD = DmaTile<E, D, TC, GRAM_NT>;
+  using LD = DmaTile<E, D, TC, NT>;
   LD ld;
   // list position c -> raw entry (a plain load for index lists, the position
   // itself for ranges) -> virtual row index (-1 past the end)
@@ -439,10 +445,10 @@ __global__ __launch_bounds__(GRAM_NT, (SELF && CLIST) ? 2 : 4) void gram_kernel(
         if ((int)threadIdx.x < TC) {
           float cs = 0.0f;
 #pragma unroll
-          for (int ww = 0; ww < GRAM_NT / 64; ++ww) cs += sColP[ww][0][threadIdx.x] + sColP[ww][1][threadIdx.x];
+          for (int ww = 0; ww < NT / 64; ++ww) cs += sColP[ww][0][threadIdx.x] + sColP[ww][1][threadIdx.x];
           const int c = tile * TC + (int)threadIdx.x;
-          const int b = r0 / GRAM_ROWS;
-          if (c < ncols) colsum[h * sym_head_floats(col_ld) + sym_col_off(col_ld, b) + (c - (b + 1) * GRAM_ROWS)] = cs;
+          const int b = r0 / ROWS;
+          if (c < ncols) colsum[h * sym_head_floats(col_ld) + sym_col_off(col_ld, b) + (c - (b + 1) * ROWS)] = cs;
         }
       }
     }
@@ -498,10 +504,11 @@ template <typename E, int D, int MODE, bool DIRECT>
 static void gram_dispatch_self(const GramLaunch& g, dim3 grid, hipStream_t st) {
   const KeySpace<E> ks = key_space<E>(g.k);
   // self-exclusion only arises with both sides the same index list
-  if (g.self_excl && g.cols.idx)
-    hipLaunchKernelGGL((gram_kernel<E, D, MODE, true, true, DIRECT>), grid, dim3(GRAM_NT), 0, st, ks, g.rows, g.cols,
+  if (g.self_excl && g.cols.idx) {
+    grid.x = (unsigned)((g.rows.n + SYM_NT / 2 - 1) / (SYM_NT / 2));
+    hipLaunchKernelGGL((gram_kernel<E, D, MODE, true, true, DIRECT>), grid, dim3(SYM_NT), 0, st, ks, g.rows, g.cols,
                        g.out, g.out_hstride, g.split_stride, g.pc, g.active, g.colsum, g.col_ld);
-  else if (g.self_excl)
+  } else if (g.self_excl)
     hipLaunchKernelGGL((gram_kernel<E, D, MODE, true, false, DIRECT>), grid, dim3(GRAM_NT), 0, st, ks, g.rows, g.cols,
                        g.out, g.out_hstride, g.split_stride, g.pc, g.active, g.colsum, g.col_ld);
   else if (g.cols.idx)
@@ -552,24 +559,30 @@ __global__ void sum_splits_kernel(const float* __restrict__ src, int64_t src_hst
   dst[(int64_t)h * dst_hstride + i] = s;
 }
 
+// Four lanes per column: lane q sums a quarter of the blocks in order, and the
+// quarters are added as (q0 + q1) + (q2 + q3), a fixed order.
 __global__ void sym_combine_kernel(float* __restrict__ dst, int64_t dst_hstride, const float* __restrict__ colsum,
                                    int64_t col_ld, int nblocks, VList rows, uint64_t active) {
   const int h = blockIdx.y;
   if (!head_on(active, h)) return;
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= vlist_count(rows, h)) return;
-  const int jb = min(j / GRAM_ROWS, nblocks);
-  float s = dst[(int64_t)h * dst_hstride + j];
+  const int j = blockIdx.x * (blockDim.x / 4) + (int)(threadIdx.x >> 2);
+  const int q = (int)(threadIdx.x & 3);
+  if (j >= vlist_count(rows, h)) return;   // the column's four lanes leave together
+  const int jb = min(j / GRAM_ROW_BLOCK, nblocks);
+  const int per = (jb + 3) / 4;
+  const int b0 = min(q * per, jb), b1 = min(b0 + per, jb);
   const float* ch = colsum + h * sym_head_floats(col_ld);
-  for (int b = 0; b < jb; ++b) s += ch[sym_col_off(col_ld, b) + (j - (b + 1) * GRAM_ROWS)];
-  dst[(int64_t)h * dst_hstride + j] = s;
+  float s = 0.0f;
+  for (int b = b0; b < b1; ++b) s += ch[sym_col_off(col_ld, b) + (j - (b + 1) * GRAM_ROW_BLOCK)];
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  if (q == 0) dst[(int64_t)h * dst_hstride + j] += s;
 }
 
 hipError_t launch_sym_combine(float* dst, int64_t dst_hstride, const float* colsum, int64_t col_ld, int nblocks,
                               VList rows, uint64_t active, int H, int n, hipStream_t st) {
-  static_assert(GRAM_ROWS == GRAM_ROW_BLOCK, "row block of the Gram work-group");
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(sym_combine_kernel, dim3((n + 255) / 256, H), dim3(256), 0, st, dst, dst_hstride, colsum, col_ld,
+  hipLaunchKernelGGL(sym_combine_kernel, dim3((n + 63) / 64, H), dim3(256), 0, st, dst, dst_hstride, colsum, col_ld,
                      nblocks, rows, active);
   return hipGetLastError();
 }

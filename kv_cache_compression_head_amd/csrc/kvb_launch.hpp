@@ -44,16 +44,16 @@ struct GramLaunch {
   int64_t col_ld;
 };
 hipError_t launch_gram(const GramLaunch& g, hipStream_t s);
-// dst[h][j] += sum over row blocks b < j / 256 of the column sum of block b at
-// column j, in order of b, for j below the row list's count (the symmetric
+// dst[h][j] += sum over row blocks b < j / 128 of the column sum of block b at
+// column j, in a fixed order, for j below the row list's count (the symmetric
 // self-Gram's mirrored pairs)
 hipError_t launch_sym_combine(float* dst, int64_t dst_hstride, const float* colsum, int64_t col_ld, int nblocks,
                               VList rows, uint64_t active, int H, int n, hipStream_t s);
-constexpr int GRAM_ROW_BLOCK = 256;   // rows per Gram work-group
+constexpr int GRAM_ROW_BLOCK = 128;   // rows per work-group of the symmetric self-Gram
 // Triangular column-sum layout for a list bounded by n: row block b keeps only
-// the columns right of its diagonal block, [(b+1) 256, n), and the blocks are
-// packed one after another, so block b starts at sum_{b'<b} (n - (b'+1) 256).
-// Column c of block b is at sym_col_off(n, b) + c - (b+1) 256; one head holds
+// the columns right of its diagonal block, [(b+1) 128, n), and the blocks are
+// packed one after another, so block b starts at sum_{b'<b} (n - (b'+1) 128).
+// Column c of block b is at sym_col_off(n, b) + c - (b+1) 128; one head holds
 // sym_head_floats(n) floats.
 __host__ __device__ inline int64_t sym_col_off(int64_t n, int b) {
   return (int64_t)b * n - (int64_t)(GRAM_ROW_BLOCK / 2) * b * (b + 1);
