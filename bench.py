@@ -1,8 +1,7 @@
-"""Benchmark: one layer-chunk of the head-wise compressed KV cache on one GPU.
+"""Benchmark: the head-wise compressed KV cache hot path on one GPU.
 
-A step is the whole hot path for one layer and one chunk at 480P
-(Wan2.1-1.3B-like layer: 12 heads, head_dim 128, bf16, 1,560 tokens per
-latent frame):
+The headline step is one layer-chunk at 480P (Wan2.1-1.3B-like layer: 12
+heads, head_dim 128, bf16, 1,560 tokens per latent frame):
 
   kvbank_score   Soft-Riesz disturbance of 23,400 candidate keys against the
                  9,360-state bank of every head, mean-normalised, ordered
@@ -12,9 +11,12 @@ latent frame):
                  chunk (up to 24,960 keys per head)
 
 The bank is restored from a device snapshot at the start of every step (the
-same update is replayed), and that copy is inside the timed region.
-Inputs are synthetic (seeded kvsynth generator), resident in HBM before
-timing starts.  Prints one JSON line.
+same update is replayed), and that copy is inside the timed region.  Inputs
+are synthetic (seeded kvsynth generator), resident in HBM before timing
+starts.  The same JSON line also carries the 1080P layer-chunk, the
+Forcing-KV hybrid layer at 480P and the 30-layer streaming rollout, each
+timed with HIP events on the stream the library launches on.  Prints one
+JSON line.
 """
 from __future__ import annotations
 
@@ -32,14 +34,11 @@ if ROOT not in sys.path:
 METRIC = "ms/chunk/layer + attention TFLOP/s (% of bf16 peak) at 480P and 1080P, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
-# fp32 VALU lane-operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
-PEAK_VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
-# VALU issue slots per Soft-Riesz pair at p = 2 (fma, max, reciprocal at half
-# rate = 2 slots, accumulate)
-VALU_SLOTS_PER_PAIR = 5.0
 ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_kernel_480p_hbm_traffic.md")
 ATTN_SOURCES = ("kv_cache_compression_head_amd/csrc/kvb_attention.hip",
                 "kv_cache_compression_head_amd/csrc/kvb_common.hpp")
+DENSITY_SOURCES = ("kv_cache_compression_head_amd/csrc/kvb_gram.hip",
+                   "kv_cache_compression_head_amd/csrc/kvb_common.hpp")
 
 
 def log(msg):
@@ -270,77 +269,279 @@ def cpu_baseline(name: str, seed: int = 0, heads=(0,)):
     return dt, threads, info.kstar
 
 
-def rollout_bench(steps: int, warmup_chunks: int):
-    """Streaming rollout timing: every chunk runs score + update + attention
-    for each of the 30 layers (480P, M = 9,360, 3 departing frames per
-    chunk).  One seeded layer stream supplies the inputs of all layers (each
-    layer keeps its own bank), so the inputs of a chunk are generated once;
-    the banks are first streamed through warmup_chunks chunks to reach the
-    steady state.  Returns (ms per chunk over all layers, details)."""
+def blas_info():
+    """BLAS library and thread count NumPy runs on (for the CPU baseline)."""
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return {"vendor": i.get("internal_api"), "version": i.get("version"),
+                        "threads": i.get("num_threads"), "arch": i.get("architecture")}
+    except Exception:
+        pass
+    return {"vendor": None, "version": None, "threads": None, "arch": None}
+
+
+def cpu_baseline_sampled(name: str, seed: int = 0, head: int = 0, rows: int = 4096):
+    """The fp64 oracle on a bounded, row-sampled piece of one head of the
+    layer-chunk, extrapolated to the layer.  Every stage of the oracle is a
+    sum over independent rows (candidates for the disturbance, bank states
+    for the crossing scan and the new bank's densities, queries for
+    attention), so each stage is timed on its first `rows` rows and scaled by
+    its full row count and by the head count."""
+    import numpy as np
+    from kvsynth import WORKLOADS, LayerGen, frame_tokens
+    from oracle import density as od
+    from oracle.attention import attention
+
+    wl = WORKLOADS[name]
+    gen = LayerGen(wl, seed, 0)
+    prm = od.Params(M=wl.M, tau=wl.tau, sigma=wl.sigma, eps=wl.eps, p=wl.p)
+    (b0, b1), (c0, c1) = wl.bank_updates
+    w0, w1 = wl.window
+    q0, q1 = wl.chunk
+    rw = [f - w0 for f in range(w0, w1)]
+    rc = [f - w0 for f in range(q0, q1)]
+    bK = gen.keys(head, range(b0, b1)).astype(np.float64)
+    cK = gen.keys(head, range(c0, c1)).astype(np.float64)
+    Q = gen.queries(head, range(q0, q1), rc).astype(np.float64)
+    Kall = np.concatenate([gen.keys(head, [0]), bK, gen.keys(head, range(w0, w1), rw), gen.keys(head, range(q0, q1), rc)]
+                          ).astype(np.float64)
+    Vall = np.concatenate([gen.values(head, [0]), gen.values(head, range(b0, b1)), gen.values(head, range(w0, w1)),
+                           gen.values(head, range(q0, q1))]).astype(np.float64)
+    n, N = bK.shape[0], cK.shape[0]
+    kmax = min(N, wl.M)
+    parts = {}
+    t = time.perf_counter()
+    od.phi_rowsum(cK[:rows], bK, prm)                       # disturbance of `rows` candidates
+    parts["disturbance"] = (time.perf_counter() - t) * N / rows
+    r0 = od.phi_rowsum(bK[:rows], bK, prm) - 1.0
+    t = time.perf_counter()
+    od.crossing_times(bK[:rows], r0, r0, cK[:kmax], prm)    # crossing scan of `rows` bank states
+    parts["crossing_scan"] = (time.perf_counter() - t) * n / rows
+    t = time.perf_counter()
+    od.phi_rowsum(bK[:rows], bK, prm)                       # `rows` states' densities in an n-state bank
+    # the update computes them for the bank before and after the update
+    parts["bank_densities"] = 2.0 * (time.perf_counter() - t) * n / rows
+    t = time.perf_counter()
+    attention(Q[:rows], Kall, Vall)
+    parts["attention"] = (time.perf_counter() - t) * wl.Lq / rows
+    total_ms = sum(parts.values()) * wl.H * 1000.0
+    return total_ms, {k: round(v * wl.H * 1000.0, 1) for k, v in parts.items()}
+
+
+def layer_chunk(name: str, steps: int, warmup: int, policy: int = 0, tau=None):
+    """Time `steps` layer-chunk steps after `warmup` untimed ones; returns the
+    step's figures (stage times from events on the library's stream)."""
+    import torch
+    import kv_cache_compression_head_amd as kb
+    wl, lc, snap, inp, lay, Q, O = setup(name, policy=policy, tau=tau)
+    log(f"{name}: setup done")
+    for _ in range(warmup):
+        one_step(lc, snap, inp, lay, Q, O)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one_step(lc, snap, inp, lay, Q, O, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = {"restore": [], "score": [], "update": [], "attention": []}
+    for e in evs:
+        stage["restore"].append(e[0].elapsed_time(e[1]))
+        stage["score"].append(e[1].elapsed_time(e[2]))
+        stage["update"].append(e[2].elapsed_time(e[3]))
+        stage["attention"].append(e[3].elapsed_time(e[4]))
+    avg = {k: sum(v) / len(v) for k, v in stage.items()}
+    kstar = int(lc.out.k_star.cpu()[0])
+    counts = lc.bank.count.cpu().tolist()
+    lkv = [wl.F + c + (wl.window[1] - wl.window[0]) * wl.F + wl.Lq for c in counts]
+    attn_flop = sum(4.0 * wl.Lq * l * wl.d for l in lkv)
+    attn_tflops = attn_flop / (avg["attention"] * 1e-3) / 1e12
+    # algorithmic bytes of the attention launch: Q + O + each head's K and V once
+    attn_bytes = sum(2 * wl.Lq * wl.d * 2 + 2 * l * wl.d * 2 for l in lkv)
+    # the chunk_attention call: attn_bf16_kernel, plus attn_merge_kernel when
+    # the balanced grid splits items (timed together, as one call)
+    bal = kb.chunk_attention_workspace_size(wl.H, wl.d, wl.Lq, kb.KVB_BF16) > 0
+    kname = "attn_bf16_kernel + attn_merge_kernel" if bal else "attn_bf16_kernel"
+    roof = {"kernel": f"{kname} (chunk_attention)", "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": recorded_attention_traffic(name), "algorithmic_flop_per_launch": attn_flop,
+            "algorithmic_bytes_per_launch": attn_bytes}
+    # Soft-Riesz pair counts of the density stages (the algorithmic work; the
+    # crossing scan's figure is its upper bound n * min(N, M))
+    n0 = int(snap.count.min().cpu())
+    N = inp["candK"].shape[1]
+    ev = lc.out.n_evicted.cpu().tolist()
+    score_pairs = wl.H * n0 * N
+    upd_pairs = sum(n0 * min(N, wl.M) + (n0 - e) * e + kstar * min(e, n0 - e) + kstar * (kstar - 1) // 2 for e in ev)
+    valu = recorded_valu_per_pair(name)
+
+    def pair_roof(pairs, ms, stage_name):
+        rate = pairs / (ms * 1e-3)
+        r = {"pairs": pairs, "pairs_per_s": rate, "mfma_equiv_tflops": round(rate * 2 * wl.d / 1e12, 2),
+             "frac_bf16_peak": round(rate * 2 * wl.d / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        v = valu.get(stage_name) if valu else None
+        if v is not None:
+            # counted VALU issue cycles per pair (SIMD cycles, from the
+            # instruction counters) against 1,024 SIMDs at 2.4 GHz
+            r["valu_cycles_per_pair"] = v
+            r["frac_valu_bound"] = round(rate * v / (256 * 4 * 2.4e9), 4)
+        else:
+            r["valu_cycles_per_pair"] = None
+            r["frac_valu_bound"] = None
+        return r
+    density_roof = {"score": pair_roof(score_pairs, avg["score"], "score"),
+                    "update": pair_roof(upd_pairs, avg["update"], "update")}
+    res = {"ms_per_step": wall * 1000.0 / steps, "stages_ms": {k: round(v, 4) for k, v in avg.items()},
+           "attention_tflops": round(attn_tflops, 2),
+           "attention_frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+           "k_star": kstar, "evicted_per_head": ev[:1] + ([] if len(set(ev)) == 1 else ev[1:]),
+           "roofline": roof, "density_stages": density_roof,
+           "workload": f"{name}: one layer-chunk, H={wl.H}, d={wl.d}, F={wl.F}, M={wl.M}, N={N}, Lq={wl.Lq}, "
+                       f"window={wl.window[1] - wl.window[0]} frames, tau={wl.tau}, sigma={wl.sigma}, p={wl.p}"
+                       + (f", policy={policy}" if policy else "")}
+    del lc, snap, inp, lay, Q, O
+    torch.cuda.empty_cache()
+    return wl, res
+
+
+def recorded_valu_per_pair(config: str):
+    """VALU issue cycles per Soft-Riesz pair of the scoring and update stages,
+    from the committed instruction-counter profile (null when that profile
+    was taken on other kernel sources)."""
+    path = os.path.join(ROOT, "profiles", f"density_stages_{config}_valu.md")
+    try:
+        with open(path) as fh:
+            kv = dict(l.split(":", 1) for l in fh.read().splitlines() if l.startswith("record."))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("record.kernel_sources_sha256") != density_source_digest():
+        return None
+    return {"score": float(kv["record.score_valu_cycles_per_pair"]),
+            "update": float(kv["record.update_valu_cycles_per_pair"])}
+
+
+def density_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in DENSITY_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def forcing_bench(steps: int = 10, seed: int = 0):
+    """Forcing-KV hybrid layer at 480P (6 static / 6 dynamic heads, 12
+    history frames of 1,560-token segments, 70 % kept): segment cosine and
+    BottomK (kvbank_score), segment tables (kvbank_update) and the ragged
+    chunk attention (static heads 7,800 keys, dynamic heads 18,720)."""
     import numpy as np
     import torch
     import kv_cache_compression_head_amd as kb
     from kv_cache_compression_head_amd.pipeline import LayerCache
-    from kv_cache_compression_head_amd.rollout import plan
-    from kvsynth import WORKLOADS, LayerGen, frame_tokens
+    from kvsynth import WORKLOADS, LayerGen, frame_tokens, head_labels
+    wl = WORKLOADS["fkv480p"]
+    gen = LayerGen(wl, seed, 0)
+    labels = head_labels(wl, seed)
+    F, H, d = wl.F, wl.H, wl.d
+    h0, h1 = wl.history
+    c0, c1 = wl.chunk
+    hist_f, ch_f = list(range(h0, h1)), list(range(c0, c1))
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(torch.bfloat16).contiguous()
+    hk, hv = dev(gen.keys_all(hist_f, hist_f)), dev(gen.values_all(hist_f))
+    tok = torch.from_numpy(frame_tokens(wl, h0, h1)).to("cuda")
+    lay = kb.KVLayout(sink_k=dev(gen.keys_all([0], [0])), sink_v=dev(gen.values_all([0])),
+                      chunk_k=dev(gen.keys_all(ch_f, ch_f)), chunk_v=dev(gen.values_all(ch_f)))
+    Q = dev(gen.queries_all(ch_f, ch_f))
+    T = len(hist_f)
+    items = T * (F // wl.seg_len)
+    keep = int(math.floor(wl.retention * items))
+    desc = kb.LayerDesc(H=H, d=d, M=0, dtype=kb.KVB_BF16, frame_tokens=F, labels=labels.tolist(),
+                        seg_len=wl.seg_len, retention=wl.retention)
+    lc = LayerCache(desc, seg_cap=min(256, 3 + keep))
+    O = torch.empty(H, wl.Lq, d, dtype=torch.bfloat16, device="cuda")
 
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        D, s, o = lc.score(hk, tok, lay)
+        if ev is not None:
+            ev[1].record()
+        lc.update(hk, hv, tok, D, o, lay)
+        if ev is not None:
+            ev[2].record()
+        lc.attention(Q, O)
+        if ev is not None:
+            ev[3].record()
+    for _ in range(3):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    sc = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    up = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    at = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
+    ndyn = int((labels == 2).sum())
+    cos_bytes = (T + 1) * F * ndyn * d * 2
+    lkv = [F + (F if labels[h] == 1 else keep * wl.seg_len) + wl.Lq for h in range(H)]
+    flop = sum(4.0 * wl.Lq * l * d for l in lkv)
+    return {"workload": f"fkv480p: H={H} (6 static / 6 dynamic), d={d}, F={F}, {T} history frames, "
+                        f"seg_len={wl.seg_len}, r={wl.retention}, Lq={wl.Lq}",
+            "score_ms": round(sc, 4), "update_ms": round(up, 4), "attention_ms": round(at, 4),
+            "step_ms": round(sc + up + at, 4),
+            "segment_cosine": {"call": "kvbank_score (cos_kernel + segmean_kernel + item sort)",
+                               "bytes_read": cos_bytes, "GB/s": round(cos_bytes / sc / 1e6, 1),
+                               "frac_hbm_peak": round(cos_bytes / sc / 1e6 / PEAK_HBM_GBS, 4)},
+            "attention": {"Lkv_static": F + F + wl.Lq, "Lkv_dynamic": F + keep * wl.seg_len + wl.Lq,
+                          "TFLOP/s": round(flop / at / 1e9, 1),
+                          "frac_bf16_peak": round(flop / at / 1e9 / PEAK_BF16_TFLOPS, 4)}}
+
+
+def rollout_bench(chunks: int, layers: int = 0, seed: int = 0):
+    """Streaming rollout: every chunk runs, for each of the 30 layers, the
+    window advance (departing frames re-rotated into bank candidates),
+    kvbank_score, kvbank_update and chunk_attention.  Each layer draws its
+    own seeded frames on the GPU before the chunk's timed region (prepare);
+    the library calls of all layers are timed with events around run()."""
+    import numpy as np
+    import torch
+    from kv_cache_compression_head_amd.rollout import Rollout
+    from kvsynth import WORKLOADS
     wl = WORKLOADS["rollout"]
-    gen = LayerGen(wl, 0, 0)
-    kdt = torch.bfloat16
-    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(kdt).contiguous()
-
-    def chunk_inputs(c):
-        p = plan(c, wl.chunk_frames, wl.window_frames)
-        rt = lambda fr: [f - p.rope_base for f in fr]
-        x = {"N": len(p.departed) * wl.F}
-        if len(p.departed):
-            x["cK"], x["cV"] = dev(gen.keys_all(p.departed)), dev(gen.values_all(p.departed))
-            x["cT"] = torch.from_numpy(frame_tokens(wl, p.departed.start, p.departed.stop).astype(np.int32)).cuda()
-        lay = kb.KVLayout()
-        keep = []
-        if c > 0:
-            sk, sv = dev(gen.keys_all([0])), dev(gen.values_all([0]))
-            keep += [sk, sv]
-            lay.sink_k, lay.sink_v = sk, sv
-        if len(p.window):
-            wk, wv = dev(gen.keys_all(p.window, rt(p.window))), dev(gen.values_all(p.window))
-            keep += [wk, wv]
-            lay.win_k, lay.win_v, lay.win_start, lay.win_len = wk, wv, 0, len(p.window) * wl.F
-        ck, cv = dev(gen.keys_all(p.frames, rt(p.frames))), dev(gen.values_all(p.frames))
-        keep += [ck, cv]
-        lay.chunk_k, lay.chunk_v = ck, cv
-        x["lay"], x["keep"] = lay, keep
-        x["Q"] = dev(gen.queries_all(p.frames, rt(p.frames)))
-        return x
-
-    t = time.time()
-    chunks = [chunk_inputs(c) for c in range(warmup_chunks + steps)]
-    log(f"rollout inputs for {len(chunks)} chunks generated in {time.time() - t:.1f}s")
-    desc = kb.LayerDesc(H=wl.H, d=wl.d, M=wl.M, dtype=kb.KVB_BF16, frame_tokens=wl.F, labels=[0] * wl.H,
-                        tau=wl.tau, sigma=wl.sigma, eps=wl.eps, p=wl.p)
-    caches = [LayerCache(desc, seg_cap=8, max_N=3 * wl.F) for _ in range(wl.layers)]
-    O = torch.empty(wl.H, wl.Lq, wl.d, dtype=kdt, device="cuda")
-
-    def run_chunk(x):
-        for lc in caches:
-            if x["N"]:
-                lc.step(x["cK"], x["cV"], x["cT"], x["lay"])
-            else:
-                lc.update(None, None, None, None, None, x["lay"])
-            lc.attention(x["Q"], O)
-
-    for c in range(warmup_chunks):
-        run_chunk(chunks[c])
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for c in range(warmup_chunks, warmup_chunks + steps):
-        run_chunk(chunks[c])
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1000.0 / steps
-    counts = caches[0].bank.count.cpu().tolist()
-    return ms, {"layers": wl.layers, "chunks_timed": steps, "first_timed_chunk": warmup_chunks,
-                "bank_count_layer0": counts, "k_star_last": int(caches[0].out.k_star.cpu()[0]),
-                "bank_bytes_per_layer": int(caches[0].bank.K.numel() * 2 * 2)}
+    L = layers or wl.layers
+    r = Rollout(wl, L, seed=seed, source="device")
+    ms, ks, counts = [], [], []
+    for c in range(chunks):
+        r.prepare()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _, p = r.run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+        lc0 = r.L[0].cache
+        ks.append(int(lc0.out.k_star.cpu()[0]) if len(p.departed) else None)
+        counts.append(int(lc0.bank.count.max().cpu()))
+    steady = [m for c, m in enumerate(ms) if c >= 4]   # every chunk from the fourth on offers 3 frames
+    a = np.asarray(steady)
+    adm = [k for k in ks if k is not None]
+    return {"workload": f"rollout: {L} layers x {wl.H} heads, 480P (F={wl.F}), M={wl.M}, W={wl.window_frames} frames, "
+                        f"{chunks} chunks of {wl.chunk_frames} frames; per chunk and layer: window advance, score, "
+                        f"update, attention",
+            "chunks": chunks, "layers": L, "total_ms": round(float(sum(ms)), 2),
+            "ms_per_chunk_steady": {"mean": round(float(a.mean()), 3), "p50": round(float(np.percentile(a, 50)), 3),
+                                    "p99": round(float(np.percentile(a, 99)), 3)},
+            "ms_per_layer_chunk_steady": round(float(a.mean()) / L, 4),
+            "layer0_k_star_per_update": adm, "layer0_admitted_total": int(sum(adm)),
+            "layer0_bank_count_per_chunk": counts,
+            "bank_bytes_per_layer": int(r.L[0].cache.bank.K.numel() * 2 * 2)}
 
 
 def main():
@@ -348,8 +549,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="480p", choices=["480p", "1080p", "rollout"])
+    ap.add_argument("--config", default="480p", choices=["480p", "1080p", "fkv480p", "rollout"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="480p/1080p: time that layer-chunk only (no other workloads, side benches)")
+    ap.add_argument("--chunks", type=int, default=80, help="rollout chunks (rollout config and the default line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter yardstick) and exit")
     ap.add_argument("--policy", type=int, default=0,
@@ -367,103 +571,76 @@ def main():
         return
     import kv_cache_compression_head_amd as kb
     kb.load_library()
+    base = {"n_gpus": 1, "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic"}
     if args.config == "rollout":
-        ms, info = rollout_bench(args.steps, max(args.warmup, 6))
-        print(json.dumps({
-            "metric": METRIC, "value": round(ms, 3), "unit": "ms/chunk (30 layers)", "n_gpus": 1,
-            "steps": args.steps, "warmup": max(args.warmup, 6), "ms_per_step": round(ms, 3),
-            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-            "data": "synthetic",
-            "config": {"workload": "rollout: 30 layers x 12 heads, 480P (1,560 tokens/frame), M=9360, 3 departing "
-                                   "frames per chunk, 6-frame window, 3-frame chunk; steady-state chunks"},
-            "ms_per_layer_chunk": round(ms / info["layers"], 4), "rollout": info}), flush=True)
+        ro = rollout_bench(args.chunks)
+        ms = ro["ms_per_chunk_steady"]["mean"]
+        print(json.dumps({"metric": METRIC, "value": ms, "unit": "ms/chunk (30 layers)", "steps": args.chunks,
+                          "warmup": 0, "ms_per_step": ms, **base, "config": {"workload": ro["workload"]},
+                          "rollout": ro}), flush=True)
+        return
+    if args.config == "fkv480p":
+        fk = forcing_bench(args.steps)
+        print(json.dumps({"metric": METRIC, "value": fk["step_ms"], "unit": "ms/chunk/layer", "steps": args.steps,
+                          "warmup": 3, "ms_per_step": fk["step_ms"], **base, "config": {"workload": fk["workload"]},
+                          "fkv480p": fk}), flush=True)
         return
     if (args.policy or args.tau is not None) and not args.no_cpu_baseline:
         print("bench.py: --policy / --tau measure variants; run them with --no-cpu-baseline", file=sys.stderr)
         sys.exit(2)
-    wl, lc, snap, inp, lay, Q, O = setup(args.config, policy=args.policy, tau=args.tau)
-    log("setup done")
-    for _ in range(args.warmup):
-        one_step(lc, snap, inp, lay, Q, O)
-    torch.cuda.synchronize()
-    # timed region: exactly K steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        one_step(lc, snap, inp, lay, Q, O, evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1000.0 / args.steps
-    stage = {"restore": [], "score": [], "update": [], "attention": []}
-    for e in evs:
-        stage["restore"].append(e[0].elapsed_time(e[1]))
-        stage["score"].append(e[1].elapsed_time(e[2]))
-        stage["update"].append(e[2].elapsed_time(e[3]))
-        stage["attention"].append(e[3].elapsed_time(e[4]))
-    avg = {k: sum(v) / len(v) for k, v in stage.items()}
-    kstar = int(lc.out.k_star.cpu()[0])
-    counts = lc.bank.count.cpu().tolist()
-    lkv = [wl.F + c + (wl.window[1] - wl.window[0]) * wl.F + wl.Lq for c in counts]
-    attn_flop = sum(4.0 * wl.Lq * l * wl.d for l in lkv)
-    attn_tflops = attn_flop / (avg["attention"] * 1e-3) / 1e12
-    # algorithmic bytes of the attention launch: Q + O + each head's K and V once
-    attn_bytes = sum(2 * wl.Lq * wl.d * 2 + 2 * l * wl.d * 2 for l in lkv)
-    # the chunk_attention call: attn_bf16_kernel, plus attn_merge_kernel when
-    # the balanced grid splits items (timed together, as one call)
-    import kv_cache_compression_head_amd as kb
-    bal = kb.chunk_attention_workspace_size(wl.H, wl.d, wl.Lq, kb.KVB_BF16) > 0
-    kname = "attn_bf16_kernel + attn_merge_kernel" if bal else "attn_bf16_kernel"
-    roof = {"kernel": f"{kname} (chunk_attention)", "bound": "mfma",
-            "achieved": round(attn_tflops, 2),
-            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": recorded_attention_traffic(args.config), "algorithmic_flop_per_launch": attn_flop,
-            "algorithmic_bytes_per_launch": attn_bytes}
-    # Soft-Riesz pair counts of the density stages (the algorithmic work; the
-    # crossing scan's figure is its upper bound n * min(N, M))
-    n0 = int(snap.count.min().cpu())
-    N = inp["candK"].shape[1]
-    ev = lc.out.n_evicted.cpu().tolist()
-    score_pairs = wl.H * n0 * N
-    upd_pairs = sum(n0 * min(N, wl.M) + (n0 - e) * e + kstar * min(e, n0 - e) + kstar * (kstar - 1) // 2 for e in ev)
-
-    def pair_roof(pairs, ms):
-        rate = pairs / (ms * 1e-3)
-        return {"pairs": pairs, "pairs_per_s": rate, "mfma_equiv_tflops": round(rate * 2 * wl.d / 1e12, 2),
-                "frac_bf16_peak": round(rate * 2 * wl.d / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "frac_valu_bound": round(rate * VALU_SLOTS_PER_PAIR / PEAK_VALU_LANE_OPS, 4)}
-    density_roof = {"score": pair_roof(score_pairs, avg["score"]), "update": pair_roof(upd_pairs, avg["update"])}
-    mem_keys = memory_keys_bench(wl)
-    profile = head_profile_bench(wl)
+    wl, main_res = layer_chunk(args.config, args.steps, args.warmup, args.policy, args.tau)
+    ms_step = main_res.pop("ms_per_step")
+    res = {"metric": METRIC, "value": round(ms_step, 4), "unit": "ms/chunk/layer", "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_step, 4), **base,
+           "config": {"workload": main_res.pop("workload")}, **main_res}
+    if not args.no_extras:
+        res["memory_keys"] = memory_keys_bench(wl)
+        res["head_profile"] = head_profile_bench(wl)
     cpu = None
     if not args.no_cpu_baseline:
-        # a bounded sample of about 10-30 s of CPU work: one head first, then
-        # as many heads as fill about 12 s when one head is quicker than 10 s
-        log("cpu baseline (oracle, 1 head)")
-        nh = 1
-        dt, threads, ks_cpu = cpu_baseline(args.config)
-        if dt < 10.0 and wl.H > 1:
-            nh = min(wl.H, int(math.ceil(12.0 / max(dt, 1e-3))))
-            log(f"cpu baseline (oracle, {nh} heads)")
-            dt, threads, ks_cpu = cpu_baseline(args.config, heads=tuple(range(nh)))
-        cpu = {"value": round(dt / nh * wl.H * 1000.0, 1), "unit": "ms/chunk/layer", "cores": threads, "kind": "oracle",
-               "sample": f"fp64 oracle, {nh} of {wl.H} heads of the same layer-chunk (score + update + attention, "
-                         f"prefix over those heads alone, k*={ks_cpu}), measured {dt:.2f} s, scaled x{wl.H / nh:.2f}",
-               "host_cpus": len(os.sched_getaffinity(0))}
-    res = {
-        "metric": METRIC, "value": round(ms_step, 4), "unit": "ms/chunk/layer", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": False, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{args.config}: one layer-chunk, H={wl.H}, d={wl.d}, F={wl.F}, M={wl.M}, "
-                               f"N={inp['candK'].shape[1]}, Lq={wl.Lq}, window={wl.window[1] - wl.window[0]} frames, "
-                               f"tau={wl.tau}, sigma={wl.sigma}, p={wl.p}"
-                               + (f", policy={args.policy}" if args.policy else "")},
-        "stages_ms": {k: round(v, 4) for k, v in avg.items()},
-        "attention_tflops": round(attn_tflops, 2), "attention_frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-        "k_star": kstar, "roofline": roof, "density_stages": density_roof, "memory_keys": mem_keys,
-        "head_profile": profile,
-        "cpu_baseline": cpu,
-    }
+        blas = blas_info()
+        if args.config == "480p":
+            # a bounded sample of about 10-30 s of CPU work: one head first, then
+            # as many heads as fill about 12 s when one head is quicker than 10 s
+            log("cpu baseline (oracle, 1 head)")
+            nh = 1
+            dt, threads, ks_cpu = cpu_baseline(args.config)
+            if dt < 10.0 and wl.H > 1:
+                nh = min(wl.H, int(math.ceil(12.0 / max(dt, 1e-3))))
+                log(f"cpu baseline (oracle, {nh} heads)")
+                dt, threads, ks_cpu = cpu_baseline(args.config, heads=tuple(range(nh)))
+            cpu = {"value": round(dt / nh * wl.H * 1000.0, 1), "unit": "ms/chunk/layer", "cores": threads,
+                   "kind": "oracle",
+                   "sample": f"fp64 oracle, {nh} of {wl.H} heads of the same layer-chunk (score + update + "
+                             f"attention, prefix over those heads alone, k*={ks_cpu}), measured {dt:.2f} s, "
+                             f"scaled x{wl.H / nh:.2f}",
+                   "blas": blas, "host_cpus": len(os.sched_getaffinity(0))}
+        else:
+            log(f"cpu baseline ({args.config}, row-sampled oracle)")
+            v, parts = cpu_baseline_sampled(args.config)
+            cpu = {"value": round(v, 1), "unit": "ms/chunk/layer", "cores": blas["threads"], "kind": "oracle",
+                   "sample": "fp64 oracle on head 0, each stage timed on its first 4,096 rows and scaled by its "
+                             "row count and by 12 heads (extrapolation)", "stages_ms": parts, "blas": blas,
+                   "host_cpus": len(os.sched_getaffinity(0))}
+    res["cpu_baseline"] = cpu
+    if args.config == "480p" and not args.no_extras and args.policy == 0 and args.tau is None:
+        log("1080p layer-chunk")
+        wl1, r1 = layer_chunk("1080p", max(3, min(args.steps, 5)), 2)
+        r1["value_ms_per_chunk_layer"] = round(r1.pop("ms_per_step"), 3)
+        if not args.no_cpu_baseline:
+            log("cpu baseline (1080p, row-sampled oracle)")
+            v, parts = cpu_baseline_sampled("1080p")
+            r1["cpu_baseline"] = {"value": round(v, 1), "unit": "ms/chunk/layer", "cores": blas["threads"],
+                                  "kind": "oracle",
+                                  "sample": "fp64 oracle on head 0, each stage timed on its first 4,096 rows and "
+                                            "scaled by its row count and by 12 heads (extrapolation)",
+                                  "stages_ms": parts, "blas": blas}
+        res["1080p"] = r1
+        log("fkv480p hybrid layer")
+        res["fkv480p"] = forcing_bench()
+        log(f"rollout ({args.chunks} chunks x 30 layers)")
+        res["rollout"] = rollout_bench(args.chunks)
     print(json.dumps(res), flush=True)
 
 

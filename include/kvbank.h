@@ -66,7 +66,17 @@ typedef struct ihipStream_t* kvb_stream_t;   /* same type as hipStream_t */
 #define KVB_EWORKSPACE (-5)   /* workspace too small */
 #define KVB_EHIP       (-6)   /* HIP runtime error at launch (message in kvb_last_error) */
 
-/* device status bits (kvb_update_out.status) */
+/* device status bits (kvb_update_out.status).  None of these conditions
+ * traps: the kernels read and write only inside each head's slices and go on.
+ * A head's bank never holds more than M pairs (DensityKV paper summary,
+ * appendix B.1, online bank update); a non-finite key has no Soft-Riesz
+ * density (Method, Soft-Riesz density). */
+#define KVB_DEV_NONFINITE 1u  /* a density head's live bank key or candidate key has a non-finite squared
+                                 norm (NaN or Inf element, or overflow); its densities and decisions are
+                                 then meaningless, but every access stays in bounds */
+#define KVB_DEV_COUNT   2u    /* bank count[h] outside [0, M]: the update used min(max(count, 0), M) for
+                                 every read, and the committed count is that clamped value plus k* minus
+                                 the evictions */
 #define KVB_DEV_SEGOVF  4u    /* segment table capacity exceeded (truncated) */
 #define KVB_DEV_EVICT   8u    /* eviction count inconsistent with the crossed set */
 
@@ -190,6 +200,9 @@ int kvbank_workspace_size(const kvb_layer_desc* L, int32_t N, size_t* bytes);
  *                  i covers history rows [i*seg_len, (i+1)*seg_len)), out_order
  *                  = item indices sorted ascending by (score, index)
  *   static heads:  untouched
+ * KVB_ESHAPE when one token's features over the dynamic heads exceed 16 KB
+ * (more than 32 dynamic fp32 heads at d = 128).  The bank's count is read
+ * clamped to [0, M]; kvbank_update reports an out-of-range count.
  * N = 0 is a no-op. */
 int kvbank_score(const kvb_layer_desc* L, const kvb_bank* bank, const void* cand_k, const int32_t* cand_tok,
                  int32_t N, const kvb_kv_layout* lay, float* out_D, float* out_score, int32_t* out_order, void* ws,
@@ -281,6 +294,12 @@ int forcing_head_profile(const kvb_attn_desc* A, const void* Q, const kvb_segmen
 
 /* Message of the last non-OK status on this thread ("" if none). */
 const char* kvb_last_error(void);
+
+/* SHA-256 (64 hex digits) of the sources this library was built from, set
+ * by the package's build script ("unknown" for another build).  A loader can
+ * compare it with the sources beside the library and refuse a stale build.
+ * Static string; no device work. */
+const char* kvb_source_hash(void);
 
 #ifdef __cplusplus
 }

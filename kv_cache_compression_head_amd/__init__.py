@@ -34,7 +34,7 @@ KVB_POL_FRAME_BOTTOMK = 64
 KVB_MAX_SEGMENTS = 256
 HEADER_FUNCTIONS = ("kvbank_workspace_size", "kvbank_score", "kvbank_update", "chunk_attention",
                     "chunk_attention_workspace_size", "kvbank_window_advance", "forcing_head_profile_workspace_size",
-                    "forcing_head_profile", "kvb_last_error")
+                    "forcing_head_profile", "kvb_last_error", "kvb_source_hash")
 
 _c_i32, _c_f32, _c_f64, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 
@@ -112,6 +112,15 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         getattr(lib, f).restype = ctypes.c_int
     lib.kvb_last_error.restype = ctypes.c_char_p
     lib.kvb_last_error.argtypes = []
+    lib.kvb_source_hash.restype = ctypes.c_char_p
+    lib.kvb_source_hash.argtypes = []
+    if os.path.abspath(p) == LIB_PATH:
+        # the in-tree library must have been built from the sources beside it
+        from .build import source_hash
+        built, here = lib.kvb_source_hash().decode(), source_hash()
+        if built != here:
+            raise ImportError(f"{p} is stale (built from sources {built[:12]}, the tree holds {here[:12]}): "
+                              "rebuild it with `python -m kv_cache_compression_head_amd.build`")
     if path is None:
         _lib = lib
     return lib

@@ -114,7 +114,7 @@ constexpr int MAX_SPLITS = 8;
 
 struct Layout {
   size_t normB, normC, augB, augC, k0, k1, v0, v1, t, cp, hist, rhoP, evict, surv, evl, fixl, nsurv, nfix,
-      fmode, accS, accAE, accAA, colAA, cos, split, total;
+      fmode, cnt, accS, accAE, accAA, colAA, cos, split, total;
   int kmax, cps, ncp;
 };
 
@@ -152,6 +152,7 @@ Layout layout_of(const kvb_layer_desc* L, int32_t N) {
   o.nsurv = bump(&off, H * 4);
   o.nfix = bump(&off, H * 4);
   o.fmode = bump(&off, H * 4);
+  o.cnt = bump(&off, H * 4);
   o.accS = bump(&off, H * M * 4);
   o.accAE = bump(&off, H * (int64_t)o.kmax * 4);
   o.accAA = bump(&off, H * (int64_t)o.kmax * 4);
@@ -260,6 +261,11 @@ extern "C" {
 
 const char* kvb_last_error(void) { return g_err; }
 
+#ifndef KVB_SOURCE_HASH
+#define KVB_SOURCE_HASH "unknown"
+#endif
+const char* kvb_source_hash(void) { return KVB_SOURCE_HASH; }
+
 int kvbank_workspace_size(const kvb_layer_desc* L, int32_t N, size_t* bytes) {
   Heads hd;
   int rc = check_layer(L, N, &hd);
@@ -287,6 +293,12 @@ int kvbank_score(const kvb_layer_desc* L, const kvb_bank* bank, const void* cand
     REQ_PTR(out_D, 4, "out_D");
   }
   if (hd.dyn) {
+    // the cosine kernel holds one token's features of every dynamic head in
+    // one wave: at most 1,024 16-byte chunks (64 lanes x 16)
+    const int chunks = hd.ndyn * (L->d * (L->dtype == KVB_BF16 ? 2 : 4) / 16);
+    if (chunks > 1024)
+      return fail(KVB_ESHAPE, "%d dynamic heads of d=%d %s exceed the cosine kernel's 16 KB per token", hd.ndyn,
+                  L->d, L->dtype == KVB_BF16 ? "bf16" : "fp32");
     if (!lay) return fail(KVB_EINVAL, "layout is NULL (needed by dynamic heads)");
     REQ_PTR(lay->chunk_k, 16, "layout.chunk_k");
     if (lay->chunk_len < L->frame_tokens) return fail(KVB_ESHAPE, "chunk_len < frame_tokens");
@@ -422,18 +434,26 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
     int32_t* zp[4] = {out->n_mandatory, out->n_evicted, out->k_star,
                       dens_run ? at<int32_t>(ws, lo.hist) : nullptr};
     const int64_t zn[4] = {H, H, ks_hs ? H : 1, (int64_t)H * (lo.kmax + 2)};
-    HIPCHK(launch_zero_i32(zp, zn, 4, st));
+    if (dens_run) {
+      // the update reads the bank's occupancy only through this clamped copy
+      const CountClamp cc{bank->count, at<int32_t>(ws, lo.cnt), out->status, hd.dens, H, M};
+      HIPCHK(launch_zero_i32_clamp(zp, zn, 4, cc, st));
+    } else {
+      HIPCHK(launch_zero_i32(zp, zn, 4, st));
+    }
   }
   if (hd.dens && N > 0) {
     const int kmax = lo.kmax;
+    const int32_t* cnt = at<int32_t>(ws, lo.cnt);
     float* nB = at<float>(ws, lo.normB);
     float* nC = at<float>(ws, lo.normC);
     void* aB = at<void>(ws, lo.augB);
     void* aC = at<void>(ws, lo.augC);
-    HIPCHK(launch_norms(bank->K, M, nB, aB, cand_k, N, nC, aC, et, H, d, pc.inv_s2, et == ET_BF16 && pc.direct, st));
+    HIPCHK(launch_norms(bank->K, M, nB, aB, cand_k, N, nC, aC, et, H, d, pc.inv_s2, et == ET_BF16 && pc.direct, st,
+                        NormCheck{out->status, cnt, hd.dens, 0, 0}));
     const KeysDesc kd{bank->K, cand_k, nB, nC, aB, aC, M, N, d, H, et};
     ScanLaunch s{};
-    s.k = kd; s.rho = bank->rho; s.rho0 = bank->rho0; s.count = bank->count; s.order = order;
+    s.k = kd; s.rho = bank->rho; s.rho0 = bank->rho0; s.count = cnt; s.order = order;
     s.active = hd.dens; s.kmax = kmax; s.tau = L->params.tau; s.cps = lo.cps; s.ncp = lo.ncp;
     s.cp = at<float>(ws, lo.cp); s.kstar = out->k_star; s.kstar_hs = ks_hs;
     // crossed states survive with densest-only eviction, and below capacity
@@ -444,7 +464,7 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
     s.pc = pc; s.phi_mode = pm;
     HIPCHK(launch_scan(s, false, st));
     SelectLaunch sel{};
-    sel.H = H; sel.M = M; sel.kmax = kmax; sel.active = hd.dens; sel.count = bank->count;
+    sel.H = H; sel.M = M; sel.kmax = kmax; sel.active = hd.dens; sel.count = cnt;
     sel.t = s.t_out; sel.hist = at<int32_t>(ws, lo.hist); sel.kstar = out->k_star; sel.rhoP = s.rhoP;
     sel.kstar_hs = ks_hs;
     sel.fill = (pol & KVB_POL_FILL_BELOW_CAP) ? 1 : 0;

@@ -67,16 +67,16 @@ KVB_DEV s16x4_t lds_tr16(const uint16_t* p) {
 // the builtins costs about a tenth of the attention time here).  The kernel
 // orders them itself: s_waitcnt vmcnt(0) and a barrier before a copied tile
 // is read.  M0 holds the wave's LDS destination (lane l writes 16 bytes at
-// M0 + 16 l); nothing else in the attention kernels uses M0.  No outputs:
-// the data goes to LDS only.
+// M0 + 16 l) and is declared clobbered, so the compiler reloads any value of
+// its own after the statement.  No outputs: the data goes to LDS only.
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 KVB_DEV void lds_copy_buf(i32x4_t rsrc, uint32_t voff, int soff, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc),
                "s"(soff)
-               : "memory");
+               : "memory", "m0");
 }
 KVB_DEV void lds_copy_glb(const void* g, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g) : "memory", "m0");
 }
 // LDS byte address of p (wave-uniform)
 KVB_DEV uint32_t lds_addr(const void* p) {

@@ -129,11 +129,15 @@ struct DmaTile {
 // ---------------------------------------------------------------------------
 // squared norms: one group of CPR lanes per row, 16-byte chunks
 // ---------------------------------------------------------------------------
+// With a status word, a live row of a checked head (bit h of chk) whose
+// squared norm is not finite sets DEV_NONFINITE: every row of the second set
+// is live, and row b of the first set's head h is live when b < the clamped
+// count cntA[h] (rowsA rows per head).
 template <typename E, int CPR>
 __global__ __launch_bounds__(256) void norms_kernel(const E* __restrict__ keysA, int64_t nA, float* __restrict__ outA,
                                                     u32x4_t* __restrict__ augA, const E* __restrict__ keysB,
                                                     int64_t nB, float* __restrict__ outB, u32x4_t* __restrict__ augB,
-                                                    int d, float scale, int direct) {
+                                                    int d, float scale, int direct, NormCheck chk) {
   constexpr int EPC = 16 / sizeof(E);
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int64_t row = gid / CPR;
@@ -158,6 +162,13 @@ __global__ __launch_bounds__(256) void norms_kernel(const E* __restrict__ keysA,
 #pragma unroll
   for (int o = CPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
   if (row < nrows && c == 0) {
+    if (chk.status != nullptr && !isfinite(s)) {
+      const int rph = first ? chk.rowsA : chk.rowsB;
+      const int h = (int)(row / rph), b = (int)(row % rph);
+      bool live = head_on(chk.active, h);
+      if (live && first) live = b < min(max(chk.cntA[h], 0), rph);
+      if (live) atomicOr(chk.status, DEV_NONFINITE);
+    }
     out[row] = s * scale;
     u32x4_t a = {0u, 0u, 0u, 0u};
     if constexpr (sizeof(E) == 2) {
@@ -184,9 +195,13 @@ __global__ __launch_bounds__(256) void norms_kernel(const E* __restrict__ keysA,
 }
 
 hipError_t launch_norms(const void* keysA, int rowsA, float* outA, void* augA, const void* keysB, int rowsB,
-                        float* outB, void* augB, int et, int H, int d, float scale, bool direct, hipStream_t st) {
+                        float* outB, void* augB, int et, int H, int d, float scale, bool direct, hipStream_t st,
+                        NormCheck chk) {
   const int64_t nA = keysA ? (int64_t)H * rowsA : 0, nB = keysB ? (int64_t)H * rowsB : 0;
   if (nA + nB == 0) return hipSuccess;
+  chk.rowsA = rowsA > 0 ? rowsA : 1;
+  chk.rowsB = rowsB > 0 ? rowsB : 1;
+  if (chk.cntA == nullptr) chk.status = nullptr;
   const int esz = et == ET_BF16 ? 2 : 4;
   const int cpr = d * esz / 16;
   const dim3 grid((unsigned)(((nA + nB) * cpr + 255) / 256));
@@ -195,19 +210,19 @@ hipError_t launch_norms(const void* keysA, int rowsA, float* outA, void* augA, c
     const uint16_t* b = (const uint16_t*)keysB;
     if (cpr == 8)
       hipLaunchKernelGGL((norms_kernel<uint16_t, 8>), grid, dim3(256), 0, st, a, nA, outA, (u32x4_t*)augA, b, nB, outB,
-                         (u32x4_t*)augB, d, scale, (int)direct);
+                         (u32x4_t*)augB, d, scale, (int)direct, chk);
     else
       hipLaunchKernelGGL((norms_kernel<uint16_t, 16>), grid, dim3(256), 0, st, a, nA, outA, (u32x4_t*)augA, b, nB, outB,
-                         (u32x4_t*)augB, d, scale, (int)direct);
+                         (u32x4_t*)augB, d, scale, (int)direct, chk);
   } else {
     const float* a = (const float*)keysA;
     const float* b = (const float*)keysB;
     if (cpr == 16)
       hipLaunchKernelGGL((norms_kernel<float, 16>), grid, dim3(256), 0, st, a, nA, outA, (u32x4_t*)augA, b, nB, outB,
-                         (u32x4_t*)augB, d, scale, 0);
+                         (u32x4_t*)augB, d, scale, 0, chk);
     else
       hipLaunchKernelGGL((norms_kernel<float, 32>), grid, dim3(256), 0, st, a, nA, outA, (u32x4_t*)augA, b, nB, outB,
-                         (u32x4_t*)augB, d, scale, 0);
+                         (u32x4_t*)augB, d, scale, 0, chk);
   }
   return hipGetLastError();
 }

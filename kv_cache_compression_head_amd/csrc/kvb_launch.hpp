@@ -8,6 +8,9 @@ namespace kvb {
 
 enum ElemType { ET_BF16 = 0, ET_F32 = 1 };
 
+// device status bits (the C ABI's KVB_DEV_* values)
+enum : uint32_t { DEV_NONFINITE = 1u, DEV_COUNT = 2u, DEV_SEGOVF = 4u, DEV_EVICT = 8u };
+
 struct KeysDesc {            // one layer's keys in two buffers (see KeySpace)
   const void* bankK;
   const void* candK;
@@ -22,8 +25,19 @@ struct KeysDesc {            // one layer's keys in two buffers (see KeySpace)
 // out[r] = |k_r|^2 * scale and aug[r] = the augmentation row of key r (exact
 // split of |k_r|^2, or of |k_r|^2 * scale in the direct form), for two key
 // sets [H][rowsA][d] and [H][rowsB][d] in one launch (a null set is skipped)
+// Optional check of the keys: with status set, a live row of a head in
+// active whose squared norm is not finite ORs DEV_NONFINITE into *status
+// (rows of the first set are live below the clamped count cntA[h]; every row
+// of the second set is live)
+struct NormCheck {
+  uint32_t* status;
+  const int32_t* cntA;
+  uint64_t active;
+  int32_t rowsA, rowsB;   // filled in by launch_norms
+};
 hipError_t launch_norms(const void* keysA, int rowsA, float* outA, void* augA, const void* keysB, int rowsB,
-                        float* outB, void* augB, int et, int H, int d, float scale, bool direct, hipStream_t s);
+                        float* outB, void* augB, int et, int H, int d, float scale, bool direct, hipStream_t s,
+                        NormCheck chk = NormCheck{nullptr, nullptr, 0, 0, 0});
 
 // out[h*out_hstride + split*split_stride + i] = sum_{j in cols} phi(row_i, col_j)
 struct GramLaunch {
@@ -93,6 +107,17 @@ hipError_t launch_scan(const ScanLaunch& a, bool sum_mode, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 // zero count (<= 4) int32 arrays of the given lengths in one launch (null entries skipped)
 hipError_t launch_zero_i32(int32_t* const* ptrs, const int64_t* lens, int count, hipStream_t s);
+// the same clears, and besides cnt[h] = min(max(count[h], 0), M) for the
+// heads in active, with DEV_COUNT ORed into *status when a count was clamped
+struct CountClamp {
+  const int32_t* count;
+  int32_t* cnt;
+  uint32_t* status;
+  uint64_t active;
+  int32_t H, M;
+};
+hipError_t launch_zero_i32_clamp(int32_t* const* ptrs, const int64_t* lens, int count, const CountClamp& cc,
+                                 hipStream_t s);
 
 // keys for sorting: key = float_key(score[h][i]) << 32 | tie[i]; value = i
 hipError_t launch_sort(const float* score, int64_t score_hstride, const int32_t* tie, int64_t tie_hstride,

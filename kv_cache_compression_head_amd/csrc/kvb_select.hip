@@ -15,8 +15,6 @@
 
 namespace kvb {
 
-enum : uint32_t { DEV_NONFINITE = 1u, DEV_COUNT = 2u, DEV_SEGOVF = 4u, DEV_EVICT = 8u };
-
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -52,6 +50,38 @@ hipError_t launch_zero_i32(int32_t* const* ptrs, const int64_t* lens, int count,
   }
   if (tot <= 0) return hipSuccess;
   hipLaunchKernelGGL(zero_i32x4_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, z);
+  return hipGetLastError();
+}
+
+// the clears of zero_i32x4_kernel in every block, and in block 0 the count
+// clamp of the update's prologue
+__global__ void zero_clamp_kernel(ZeroSet z, CountClamp cc) {
+  if (blockIdx.x == 0 && (int)threadIdx.x < cc.H && head_on(cc.active, threadIdx.x)) {
+    const int h = threadIdx.x;
+    const int n = cc.count[h];
+    const int c = min(max(n, 0), cc.M);
+    cc.cnt[h] = c;
+    if (c != n) atomicOr(cc.status, DEV_COUNT);
+  }
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (i < z.n[k]) { z.p[k][i] = 0; return; }
+    i -= z.n[k];
+  }
+}
+
+hipError_t launch_zero_i32_clamp(int32_t* const* ptrs, const int64_t* lens, int count, const CountClamp& cc,
+                                 hipStream_t st) {
+  ZeroSet z{};
+  int64_t tot = 0;
+  for (int k = 0; k < 4; ++k) {
+    z.p[k] = k < count ? ptrs[k] : nullptr;
+    z.n[k] = (k < count && ptrs[k]) ? lens[k] : 0;
+    tot += z.n[k];
+  }
+  const int64_t blocks = (tot + 255) / 256 > 0 ? (tot + 255) / 256 : 1;
+  hipLaunchKernelGGL(zero_clamp_kernel, dim3((unsigned)blocks), dim3(256), 0, st, z, cc);
   return hipGetLastError();
 }
 
@@ -568,7 +598,11 @@ __global__ __launch_bounds__(64) void segments_kernel(SegLaunch a) {
   if (threadIdx.x == 0) {
     push(a.sink_k, a.sink_v, a.sink_len, 0, a.sink_len);
     if (lab == 0) {
-      push(a.bankK, a.bankV, a.M, 0, a.count[h]);
+      // the committed count, clamped (no update ran when N = 0)
+      const int n = a.count[h];
+      const int nc = min(max(n, 0), a.M);
+      if (nc != n) atomicOr(a.status, DEV_COUNT);
+      push(a.bankK, a.bankV, a.M, 0, nc);
       if (a.win_len > 0) {
         const int first = min(a.win_len, a.win_cap - a.win_start);
         push(a.win_k, a.win_v, a.win_cap, a.win_start, first);

@@ -34,7 +34,7 @@ from typing import Dict, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
-    "Workload", "WORKLOADS", "LayerGen", "round_bf16", "bf16_bits",
+    "Workload", "WORKLOADS", "LayerGen", "LayerStream", "round_bf16", "bf16_bits",
     "rope_split", "head_labels", "frame_tokens",
 ]
 
@@ -276,3 +276,45 @@ class LayerGen:
                     heads: Optional[Sequence[int]] = None) -> np.ndarray:
         heads = range(self.wl.H) if heads is None else heads
         return np.stack([self.queries(h, frames, rope_t) for h in heads])
+
+
+class LayerStream:
+    """One layer's frames in time order with bounded memory.
+
+    Holds only the current AR(1) drift state per head, so a rollout of any
+    length costs the same memory.  ``frame(t)`` must be called with
+    t = 0, 1, 2, ... in order and returns post-RoPE keys at temporal
+    coordinate ``rope_t`` (default t), values and queries at the same
+    coordinate, each [H][F][d] float32 rounded to the workload dtype.  The
+    draws and the arithmetic are those of ``LayerGen``, so frame t equals
+    ``LayerGen(wl, seed, layer).keys_all([t], [rope_t])`` bit for bit.
+    """
+
+    def __init__(self, wl: Workload, seed: int = 0, layer: int = 0):
+        self.wl, self.seed, self.layer = wl, seed, layer
+        self._g = LayerGen(wl, seed, layer)
+        self._drift = None   # [H][F][d] float64, drift of frame self.t - 1
+        self.t = 0
+
+    def frame(self, t: int, rope_t: Optional[int] = None):
+        if t != self.t:
+            raise ValueError(f"frames come in order: expected {self.t}, got {t}")
+        wl, g = self.wl, self._g
+        rt = t if rope_t is None else rope_t
+        innov = math.sqrt(1.0 - AR_RHO * AR_RHO)
+        if t == 0:
+            drift = np.zeros((wl.H, wl.F, wl.d))
+        else:
+            z = np.stack([_rng(self.seed, self.layer, h, _S_INNOV, t).standard_normal((wl.F, wl.d))
+                          for h in range(wl.H)])
+            drift = AR_RHO * self._drift + innov * z
+        self._drift = drift
+        self.t += 1
+        keys = np.empty((wl.H, wl.F, wl.d), np.float32)
+        for h in range(wl.H):
+            noise = _rng(self.seed, self.layer, h, _S_NOISE, t).standard_normal((wl.F, wl.d))
+            pre = g._base_of(h) + drift[h] + NOISE_STD * noise
+            keys[h] = g._round(g._rotate(pre[None], [rt]))[0]
+        values = g.values_all([t])
+        queries = g.queries_all([t], [rt])
+        return keys, values, queries

@@ -19,6 +19,8 @@ from typing import Optional
 
 import numpy as np
 
+from .density import _map_blocks
+
 
 def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: Optional[float] = None,
               block: int = 1024) -> np.ndarray:
@@ -32,9 +34,12 @@ def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: Optional[float
     if K.shape[0] == 0:
         out[:] = 0.0
         return out
-    for i in range(0, Q.shape[0], block):
+
+    def rows(i):
         s = (Q[i:i + block] @ K.T) * scale
         s -= s.max(axis=1, keepdims=True)
         np.exp(s, out=s)
         out[i:i + block] = (s @ V) / s.sum(axis=1, keepdims=True)
+    # query blocks are independent (threads with the density module's worker count)
+    _map_blocks(rows, range(0, Q.shape[0], block))
     return out

@@ -59,11 +59,38 @@ blocked prefix-sum tier with a from-scratch brute-force tier.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
 import math
 from typing import List, Optional, Sequence
 
 import numpy as np
+
+# Row blocks of the pairwise sums are independent: with more than one worker
+# they are computed side by side in threads (BLAS then single-threaded per
+# block, and blocks small enough to give every worker a few).  Each row is
+# still the same fp64 sum over the same columns in the same order; only the
+# BLAS rounding order of the dot products may differ (by ~1e-16 relative).
+_WORKERS = 1
+
+
+def set_workers(n: int) -> None:
+    """Threads used for the row blocks of phi_rowsum, density and
+    crossing_times (1: serial)."""
+    global _WORKERS
+    _WORKERS = max(1, int(n))
+
+
+def _map_blocks(fn, starts) -> None:
+    starts = list(starts)
+    if _WORKERS <= 1 or len(starts) <= 1:
+        for i in starts:
+            fn(i)
+        return
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"), cf.ThreadPoolExecutor(max_workers=_WORKERS) as ex:
+        for _ in ex.map(fn, starts):
+            pass
 
 
 @dataclasses.dataclass(frozen=True)
@@ -124,8 +151,11 @@ def phi_matrix(A: np.ndarray, B: np.ndarray, prm: Params) -> np.ndarray:
     return phi(sqdist(A, B), prm)
 
 
-def _row_block(ncols: int) -> int:
-    return max(1, int(16_000_000 // max(1, ncols)))
+def _row_block(ncols: int, nrows: int = 0) -> int:
+    step = max(1, int(16_000_000 // max(1, ncols)))
+    if _WORKERS > 1 and nrows > 0:
+        step = min(step, max(64, -(-nrows // (3 * _WORKERS))))
+    return step
 
 
 def phi_rowsum(A: np.ndarray, B: np.ndarray, prm: Params) -> np.ndarray:
@@ -133,9 +163,11 @@ def phi_rowsum(A: np.ndarray, B: np.ndarray, prm: Params) -> np.ndarray:
     out = np.zeros(A.shape[0], dtype=np.float64)
     if B.shape[0] == 0:
         return out
-    step = _row_block(B.shape[0])
-    for i in range(0, A.shape[0], step):
+    step = _row_block(B.shape[0], A.shape[0])
+
+    def block(i):
         out[i:i + step] = phi_matrix(A[i:i + step], B, prm).sum(axis=1)
+    _map_blocks(block, range(0, A.shape[0], step))
     return out
 
 
@@ -145,12 +177,14 @@ def density(K: np.ndarray, prm: Params) -> np.ndarray:
     out = np.zeros(n, dtype=np.float64)
     if n == 0:
         return out
-    step = _row_block(n)
-    for i in range(0, n, step):
+    step = _row_block(n, n)
+
+    def block(i):
         blk = phi_matrix(K[i:i + step], K, prm)
         rows = np.arange(blk.shape[0])
         blk[rows, i + rows] = 0.0
         out[i:i + step] = blk.sum(axis=1)
+    _map_blocks(block, range(0, n, step))
     return out
 
 
@@ -211,9 +245,10 @@ def crossing_times(bankK, rho, rho0, candK_sorted, prm: Params, at: Sequence[np.
     n, kmax = bankK.shape[0], candK_sorted.shape[0]
     t = np.full(n, kmax + 1, dtype=np.int64)
     vals = [np.empty(n, dtype=np.float64) for _ in at]
-    step = _row_block(kmax + 1)
+    step = _row_block(kmax + 1, n)
     finite = math.isfinite(prm.tau)
-    for i in range(0, n, step):
+
+    def block(i):
         m = min(step, n - i)
         blk = np.empty((m, kmax + 1), dtype=np.float64)
         blk[:, 0] = 0.0
@@ -227,6 +262,7 @@ def crossing_times(bankK, rho, rho0, candK_sorted, prm: Params, at: Sequence[np.
             tt[anyc] = np.argmax(crossed[anyc], axis=1)
         for a, o in zip(at, vals):
             o[i:i + m] = blk[np.arange(m), np.asarray(a)[i:i + m]]
+    _map_blocks(block, range(0, n, step))
     return t, vals
 
 

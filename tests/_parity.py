@@ -11,9 +11,11 @@ only where the oracle's deciding gap is below ``GAP`` (relative):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import math
+import os
 from dataclasses import dataclass, field
-from typing import List
+from typing import Dict, List, Optional
 
 import numpy as np
 
@@ -97,6 +99,7 @@ class Report:
     crossing_near_ties: int = 0
     admitted: List[int] = field(default_factory=list)
     evicted: List[int] = field(default_factory=list)
+    rho_after: Dict[int, np.ndarray] = field(default_factory=dict)   # from-scratch densities of the new bank
 
 
 def check_evictions_oldest(ev_gpu: np.ndarray, mand: np.ndarray, tok: np.ndarray):
@@ -109,12 +112,38 @@ def check_evictions_oldest(ev_gpu: np.ndarray, mand: np.ndarray, tok: np.ndarray
         assert tok[evd].max() < tok[kept].min(), "completion is not the oldest states"
 
 
+def _pool_map(fn, items, workers):
+    """map over items in threads: the oracle's numpy work releases the GIL,
+    so heads are checked side by side on the host's cores."""
+    items = list(items)
+    if workers <= 1 or len(items) <= 1:
+        return [fn(x) for x in items]
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(fn, items))
+
+
+def default_workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def replay_update(before: GpuBank, after: GpuBank, candK, candV, cand_tok, D_gpu, delta_gpu, order_gpu,
                   t_gpu, rhoP_gpu, kstar_gpu, n_mand_gpu, n_ev_gpu, prm: od.Params, heads: List[int],
-                  rtol_D=2e-5, rtol_rho=1e-4) -> Report:
+                  rtol_D=2e-5, rtol_rho=1e-4, workers: int = 0, kstar_heads: Optional[List[int]] = None,
+                  rho_before: Optional[Dict[int, np.ndarray]] = None) -> Report:
     """Stage-replay check of one layer update over the listed density heads,
     under the policy fields of prm.  kstar_gpu: the device's k_star array
-    (entry 0 the shared prefix, or one entry per head)."""
+    (entry 0 the shared prefix, or one entry per head).
+
+    Every value of the listed heads is checked (no sampling).  kstar_heads:
+    the layer's density heads whose GPU crossing times enter the shared
+    prefix check (default: heads); only the listed heads are replayed in
+    fp64.  rho_before: from-scratch densities of the bank before the update
+    per head (a previous replay's rho_after), reused instead of recomputed.
+    The report's rho_after holds the new bank's from-scratch densities."""
     N = cand_tok.shape[0]
     kmax = min(N, prm.M)
     tok = cand_tok.astype(np.int64)
@@ -126,38 +155,47 @@ def replay_update(before: GpuBank, after: GpuBank, candK, candV, cand_tok, D_gpu
     # crossed rows survive (and carry rho') under densest-only eviction and below capacity with fill
     keep_crossed = prm.eviction == "densest" or fill
     rep = Report(kstar=k)
-    tl, ns, cache = [], [], {}
-    for h in heads:
+    workers = workers or default_workers()
+
+    def stage12(h):
         b = before.head(h)
-        rho_def = od.density(b.K, prm)
+        rho_def = rho_before[h] if rho_before is not None and h in rho_before else od.density(b.K, prm)
         # stored density (maintained incrementally on the GPU) vs its definition
         np.testing.assert_allclose(before.rho[h, :b.n], rho_def, rtol=rtol_rho, atol=1e-6)
         # stage 1: disturbance and order
         D, delta = od.disturbance(b.K, candK[h], prm)
         np.testing.assert_allclose(D_gpu[h], D, rtol=rtol_D, atol=1e-6)
         np.testing.assert_allclose(delta_gpu[h], delta, rtol=rtol_D, atol=1e-6)
+        nt = 0
         if prm.order == "source":
             assert order_gpu[h].tolist() == np.argsort(tok, kind="stable").tolist(), "source order"
         else:
-            rep.order_near_ties += check_order(order_gpu[h], delta, tok)
+            nt = check_order(order_gpu[h], delta, tok)
         # stage 2: crossing prefix lengths on the GPU's order
         pi = order_gpu[h].astype(np.int64)
         cs = np.asarray(candK[h], np.float64)[pi[:kmax]]
         tg = t_gpu[h, :b.n].astype(np.int64)
-        rep.crossing_near_ties += check_crossings(tg, b.K, rho_def, b.rho0, cs, prm)
-        tl.append(tg)
-        ns.append(b.n)
-        cache[h] = (b, rho_def, cs, pi, tg)
+        nc = check_crossings(tg, b.K, rho_def, b.rho0, cs, prm)
+        return (b, rho_def, cs, pi, tg, nt, nc)
+
+    res = dict(zip(heads, _pool_map(stage12, heads, workers)))
+    for h in heads:
+        rep.order_near_ties += res[h][5]
+        rep.crossing_near_ties += res[h][6]
     # stage 3: prefix lengths from the GPU's crossing times (integer logic, exact)
+    kh_list = list(heads) if kstar_heads is None else list(kstar_heads)
+    tl = [t_gpu[h, :int(before.count[h])].astype(np.int64) for h in kh_list]
+    ns = [int(before.count[h]) for h in kh_list]
     if per_head:
-        for h, tg_h, n_h in zip(heads, tl, ns):
+        for h, tg_h, n_h in zip(kh_list, tl, ns):
             kh = int(np.nonzero(od.feasible_head(tg_h, n_h, prm.M, kmax, fill))[0].max())
             assert kh == kof(h), f"head {h}: k* {kof(h)} != oracle prefix {kh} on the GPU crossing times"
     else:
         ks_ref, _ = od.feasible_prefix(tl, ns, prm.M, kmax, fill)
         assert ks_ref == k, f"k* {k} != oracle prefix {ks_ref} on the GPU crossing times"
-    for h in heads:
-        b, rho_def, cs, pi, tg = cache[h]
+
+    def stage45(h):
+        b, rho_def, cs, pi, tg = res[h][:5]
         k = kof(h)
         e = max(0, b.n + k - prm.M) if k > 0 else 0
         assert int(n_ev_gpu[h]) == e, f"head {h}: evicted {int(n_ev_gpu[h])} != e {e}"
@@ -166,12 +204,13 @@ def replay_update(before: GpuBank, after: GpuBank, candK, candV, cand_tok, D_gpu
         assert int(n_mand_gpu[h]) == int(crossed.sum()), f"head {h}: n_mandatory"
         mand = crossed if prm.eviction != "densest" else np.zeros(b.n, bool)
         # stage 4: projected densities and eviction set
-        proj = od.projected_density(b.K, rho_def, cs, k, prm)
+        proj = od.projected_density(b.K, rho_def, cs, k, prm) if k > 0 else rho_def
         live = np.ones(b.n, bool) if keep_crossed else ~crossed
         np.testing.assert_allclose(rhoP_gpu[h, :b.n][live], proj[live], rtol=rtol_rho, atol=1e-6)
         new_n = int(after.count[h])
         assert new_n == b.n - e + k, f"head {h}: count {new_n} != {b.n - e + k}"
         new_toks = set(after.tok[h, :new_n].tolist())
+        assert len(new_toks) == new_n, f"head {h}: duplicate token in the bank"
         adm_toks = tok[pi[:k]]
         assert set(adm_toks.tolist()) <= new_toks, f"head {h}: admitted tokens missing"
         ev_gpu = np.array([t not in new_toks for t in b.tok.tolist()], dtype=bool)
@@ -180,10 +219,16 @@ def replay_update(before: GpuBank, after: GpuBank, candK, candV, cand_tok, D_gpu
             check_evictions_oldest(ev_gpu, mand, b.tok)
         else:
             check_evictions(ev_gpu, mand, proj)
-        rep.admitted.append(k)
-        rep.evicted.append(e)
         # stage 5: new bank -- exact pairing, frozen baselines, densities
         hb = after.head(h)
+        if k == 0:
+            # nothing admitted or evicted: the bank and its densities are unchanged
+            assert np.array_equal(after.tok[h, :new_n], before.tok[h, :b.n])
+            assert np.array_equal(after.K[h, :new_n], before.K[h, :b.n])
+            assert np.array_equal(after.V[h, :new_n], before.V[h, :b.n])
+            assert np.array_equal(after.rho0[h, :new_n], before.rho0[h, :b.n])
+            assert np.array_equal(after.rho[h, :new_n], before.rho[h, :b.n])
+            return (k, e, rho_def)
         oldpos = {int(t): i for i, t in enumerate(b.tok.tolist())}
         cpos = {int(t): i for i, t in enumerate(tok.tolist())}
         is_new = np.zeros(hb.n, bool)
@@ -203,6 +248,13 @@ def replay_update(before: GpuBank, after: GpuBank, candK, candV, cand_tok, D_gpu
         np.testing.assert_allclose(hb.rho0[is_new], rho_new[is_new], rtol=rtol_rho, atol=1e-6)
         if prm.baseline == "refresh":
             np.testing.assert_allclose(hb.rho0, rho_new, rtol=rtol_rho, atol=1e-6)
+        return (k, e, rho_new)
+
+    out = _pool_map(stage45, heads, workers)
+    for h, (kk, e, rn) in zip(heads, out):
+        rep.admitted.append(kk)
+        rep.evicted.append(e)
+        rep.rho_after[h] = rn
     return rep
 
 

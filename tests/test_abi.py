@@ -33,6 +33,30 @@ def test_library_exports_every_declared_symbol():
     assert set(_declared()) <= exported
 
 
+def test_library_is_built_from_these_sources():
+    """The loader refuses a library whose embedded source hash differs from
+    the sources beside it; the hash covers every HIP file and the header."""
+    from kv_cache_compression_head_amd import build as kbuild
+    lib = kb.load_library()
+    assert lib.kvb_source_hash().decode() == kbuild.source_hash()
+    names = {os.path.basename(f) for f in kbuild.source_files()}
+    assert "kvbank.h" in names and all(s in names for s in kbuild.SOURCES)
+
+
+def test_dynamic_heads_too_wide_for_the_cosine_kernel():
+    # 33 fp32 dynamic heads of d = 128 need 33 x 32 16-byte chunks per token (> 1,024)
+    import ctypes
+    H = 33
+    desc = kb.LayerDesc(H=H, d=128, M=0, dtype=kb.KVB_F32, frame_tokens=16, labels=[2] * H, seg_len=16,
+                        retention=0.5)
+    lib = kb.load_library()
+    c = desc.c()
+    buf = ctypes.create_string_buffer(4096 + 256)
+    p = (ctypes.addressof(buf) + 255) // 256 * 256
+    rc = lib.kvbank_score(ctypes.byref(c), None, p, p, 16, None, p, p, p, p, 1 << 40, None)
+    assert rc == -2 and b"cosine" in lib.kvb_last_error()
+
+
 def _desc(**kw):
     base = dict(H=2, d=64, M=64, dtype=kb.KVB_F32, frame_tokens=16, labels=[0, 0])
     base.update(kw)

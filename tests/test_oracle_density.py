@@ -294,3 +294,27 @@ def test_bank_bookkeeping_invariants():
                 f, p = divmod(int(b.tok[i]), wl.F)
                 assert np.array_equal(b.V[i], gen.values(h, [f])[p].astype(np.float64))
                 assert np.array_equal(b.K[i], gen.keys(h, [f])[p].astype(np.float64))
+
+
+def test_threaded_row_blocks_match_serial():
+    """The row blocks of the pairwise sums run in threads when workers > 1;
+    each row is the same fp64 sum, so results agree with the serial run to
+    BLAS rounding order."""
+    rng = np.random.default_rng(11)
+    prm = od.Params(M=64)
+    K = rng.normal(size=(700, 16)) * 4
+    C = rng.normal(size=(500, 16)) * 4
+    r1 = od.density(K, prm)
+    D1, _ = od.disturbance(K, C, prm)
+    t1, (v1,) = od.crossing_times(K, r1, r1 * 1.02, C, prm, at=[np.full(700, 37)])
+    try:
+        od.set_workers(4)
+        r2 = od.density(K, prm)
+        D2, _ = od.disturbance(K, C, prm)
+        t2, (v2,) = od.crossing_times(K, r2, r2 * 1.02, C, prm, at=[np.full(700, 37)])
+    finally:
+        od.set_workers(1)
+    np.testing.assert_allclose(r2, r1, rtol=1e-13)
+    np.testing.assert_allclose(D2, D1, rtol=1e-13)
+    np.testing.assert_allclose(v2, v1, rtol=1e-13)
+    assert np.array_equal(t1, t2)
