@@ -544,6 +544,98 @@ def rollout_bench(chunks: int, layers: int = 0, seed: int = 0):
             "bank_bytes_per_layer": int(r.L[0].cache.bank.K.numel() * 2 * 2)}
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (the tables under profiles/ are printed by these)
+# ---------------------------------------------------------------------------
+
+def kernel_role(name: str, seq: dict) -> str:
+    """Short role label of a dispatch from its (demangled, untruncated)
+    kernel name.  gram_kernel<E, D, MODE, SELF, CLIST, DIRECT>: scoring
+    (no lists), the two fix-ups on index lists (survivors x evicted, then
+    admitted x fix-list, in launch order), the symmetric admitted x admitted
+    pass; scan_kernel<E, D, MODE, SUM, DIRECT>: crossing scan or rho' at k*."""
+    import re
+    base = re.sub(r"^void\s+", "", name).split("(")[0]
+    short = base.split("<")[0].split("::")[-1]
+    args = re.findall(r"<(.*)>", base)
+    targs = [a.strip() for a in args[0].split(",")] if args else []
+    if short == "gram_kernel" and len(targs) >= 6:
+        self_, clist = targs[3] == "true", targs[4] == "true"
+        if not clist:
+            return "gram_kernel [scoring: candidates x bank]"
+        if self_:
+            return "gram_kernel [fix-up: admitted x admitted, symmetric]"
+        k = seq.get("fix", 0)
+        seq["fix"] = k + 1
+        return "gram_kernel [fix-up: survivors x evicted]" if k % 2 == 0 else \
+            "gram_kernel [fix-up: admitted x survivors-or-evicted]"
+    if short == "scan_kernel" and len(targs) >= 5:
+        return "scan_kernel [rho' at k*]" if targs[3] == "true" else "scan_kernel [crossing scan]"
+    return short
+
+
+def _csv_rows(d: str, suffix: str):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize_trace(d: str):
+    """Markdown table of kernel durations per role and grid size from a
+    `rocprofv3 --kernel-trace` csv output directory."""
+    rows = sorted(_csv_rows(d, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    seq, agg = {}, {}
+    for r in rows:
+        role = kernel_role(r["Kernel_Name"], seq)
+        grid = int(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0) * int(r.get("Grid_Size_Y", 1) or 1) * \
+            int(r.get("Grid_Size_Z", 1) or 1)
+        wg = int(r.get("Workgroup_Size_X", r.get("Workgroup_Size", 1)) or 1)
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        agg.setdefault((role, grid // max(wg, 1)), []).append(us)
+    tot = sum(sum(v) for v in agg.values())
+    print("| kernel (role) | work-groups | calls | total ms | avg us | min us | max us | share |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (role, wgs), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| {role} | {wgs} | {len(v)} | {sum(v) / 1000:.3f} | {sum(v) / len(v):.1f} | {min(v):.1f} | "
+              f"{max(v):.1f} | {100 * sum(v) / tot:.2f}% |")
+
+
+def summarize_counters(d: str, min_us: float = 0.0):
+    """Markdown table of per-dispatch counter averages per role from a
+    `rocprofv3 --pmc` csv output directory (one row per dispatch and
+    counter), with the dispatch duration."""
+    rows = _csv_rows(d, "counter_collection.csv")
+    disp = {}
+    for r in rows:
+        key = (int(r["Dispatch_Id"]), r.get("Agent_Id", ""))
+        e = disp.setdefault(key, {"name": r["Kernel_Name"], "start": int(r.get("Start_Timestamp", 0) or 0),
+                                  "end": int(r.get("End_Timestamp", 0) or 0), "c": {}})
+        e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    seq, agg = {}, {}
+    for key in sorted(disp, key=lambda k: disp[k]["start"] or k[0]):
+        e = disp[key]
+        role = kernel_role(e["name"], seq)
+        us = (e["end"] - e["start"]) / 1000.0
+        if us < min_us:
+            continue
+        a = agg.setdefault(role, {"n": 0, "us": 0.0, "c": {}})
+        a["n"] += 1
+        a["us"] += us
+        for k, v in e["c"].items():
+            a["c"][k] = a["c"].get(k, 0.0) + v
+    names = sorted({k for a in agg.values() for k in a["c"]})
+    print("| kernel (role) | dispatches | avg us | " + " | ".join(f"{n} / dispatch" for n in names) + " |")
+    print("|---|---|---|" + "---|" * len(names))
+    for role, a in sorted(agg.items(), key=lambda kv: -kv[1]["us"]):
+        vals = " | ".join(f"{a['c'].get(n, 0.0) / a['n']:.6g}" for n in names)
+        print(f"| {role} | {a['n']} | {a['us'] / a['n']:.1f} | {vals} |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -559,7 +651,18 @@ def main():
     ap.add_argument("--policy", type=int, default=0,
                     help="DensityKV policy variant bits (KVB_POL_*; 0 = the method)")
     ap.add_argument("--tau", type=float, default=None, help="override the workload's density growth bound")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print the per-role kernel-time table of a rocprofv3 --kernel-trace csv directory and exit")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print the per-role counter table of a rocprofv3 --pmc csv directory and exit")
+    ap.add_argument("--min-us", type=float, default=0.0, help="with --summarize-counters: skip shorter dispatches")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.min_us)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no "
               "multi-GPU component to run)", file=sys.stderr)

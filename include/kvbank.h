@@ -238,6 +238,22 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
 int chunk_attention(const kvb_attn_desc* A, const void* Q, const kvb_segment* segs, const int32_t* nseg, void* O,
                     void* ws, size_t ws_bytes, kvb_stream_t stream);
 
+/* chunk_attention for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments and result as chunk_attention, without the workspace: when
+ * the balanced grid is taken (chunk_attention_workspace_size > 0) its
+ * partials and flags live in a static device array of the library, 64 MiB
+ * per GPU (enough for every plan on a 256-compute-unit device), kept until
+ * the process ends; its address is looked up once per device, on the first
+ * call made with that device current.  Nothing is allocated or freed, by the
+ * library or by any routine it calls.  Every flag and partial a call reads is
+ * written earlier in the same call, so nothing needs clearing.  Calls on one
+ * GPU share the array: calls that overlap in time on one GPU (two streams,
+ * or two host threads) race and must be serialised by the caller.  A plan
+ * needing more than 64 MiB is KVB_EWORKSPACE (nothing is queued). */
+int chunk_attention_noalloc(const kvb_attn_desc* A, const void* Q, const kvb_segment* segs, const int32_t* nseg,
+                            void* O, kvb_stream_t stream);
+
 /* Workspace bytes for chunk_attention's balanced grid (0: nothing to
  * balance, or the fp32 path).  Depends on the current device's compute-unit
  * count.  Host only; no device work. */

@@ -17,7 +17,8 @@ __all__ = [
     "KVB_POL_REFRESH_BASELINE", "KVB_POL_EVICT_DENSEST", "KVB_POL_EVICT_OLDEST", "KVB_POL_HEAD_PREFIX",
     "KVB_POL_FILL_BELOW_CAP", "KVB_POL_FRAME_BOTTOMK",
     "KvbError", "load_library", "kvbank_workspace_size", "kvbank_score", "kvbank_update",
-    "chunk_attention", "chunk_attention_workspace_size", "kvbank_window_advance", "forcing_head_profile",
+    "chunk_attention", "chunk_attention_noalloc", "chunk_attention_workspace_size", "kvbank_window_advance",
+    "forcing_head_profile",
     "forcing_head_profile_workspace_size", "kvb_last_error", "LayerDesc", "Bank", "KVLayout", "UpdateOut",
     "HEADER_FUNCTIONS",
 ]
@@ -34,7 +35,7 @@ KVB_POL_FRAME_BOTTOMK = 64
 KVB_MAX_SEGMENTS = 256
 HEADER_FUNCTIONS = ("kvbank_workspace_size", "kvbank_score", "kvbank_update", "chunk_attention",
                     "chunk_attention_workspace_size", "kvbank_window_advance", "forcing_head_profile_workspace_size",
-                    "forcing_head_profile", "kvb_last_error", "kvb_source_hash")
+                    "forcing_head_profile", "kvb_last_error", "kvb_source_hash", "chunk_attention_noalloc")
 
 _c_i32, _c_f32, _c_f64, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 
@@ -99,6 +100,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                   _vp, _vp, ctypes.POINTER(kvb_kv_layout), ctypes.POINTER(kvb_update_out), _vp,
                                   ctypes.c_size_t, _vp]
     lib.chunk_attention.argtypes = [ctypes.POINTER(kvb_attn_desc), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.chunk_attention_noalloc.argtypes = [ctypes.POINTER(kvb_attn_desc), _vp, _vp, _vp, _vp, _vp]
     lib.chunk_attention_workspace_size.argtypes = [ctypes.POINTER(kvb_attn_desc), ctypes.POINTER(ctypes.c_size_t)]
     lib.kvbank_window_advance.argtypes = [ctypes.POINTER(kvb_layer_desc), _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                           _c_f32, _vp, _vp, _vp, _vp, _vp]
@@ -106,7 +108,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                                         ctypes.POINTER(ctypes.c_size_t)]
     lib.forcing_head_profile.argtypes = [ctypes.POINTER(kvb_attn_desc), _vp, _vp, _vp, _vp, _c_i32, _c_f32, _vp, _vp,
                                          _vp, _vp, ctypes.c_size_t, _vp]
-    for f in ("kvbank_workspace_size", "kvbank_score", "kvbank_update", "chunk_attention",
+    for f in ("kvbank_workspace_size", "kvbank_score", "kvbank_update", "chunk_attention", "chunk_attention_noalloc",
               "chunk_attention_workspace_size", "kvbank_window_advance", "forcing_head_profile_workspace_size",
               "forcing_head_profile"):
         getattr(lib, f).restype = ctypes.c_int
@@ -348,6 +350,18 @@ def chunk_attention(H: int, d: int, Lq: int, dtype: int, Q, segs, nseg, seg_cap:
         ws = torch.empty(n, dtype=torch.uint8, device=Q.device) if n > 0 else None
     _check(lib.chunk_attention(ctypes.byref(desc), _ptr(Q), _ptr(segs), _ptr(nseg), _ptr(O), _ptr(ws),
                                0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def chunk_attention_noalloc(H: int, d: int, Lq: int, dtype: int, Q, segs, nseg, seg_cap: int, O,
+                            scale: float = 0.0, out_f32: bool = False, stream=None):
+    """chunk_attention without a workspace: the balanced grid's partials live
+    in the library's static per-GPU scratch array (nothing is allocated).
+    Calls that overlap on one GPU race on that array."""
+    lib = load_library()
+    kd = _kv_dtype(dtype)
+    _req(Q, "Q", kd, (H, Lq, d))
+    desc = kvb_attn_desc(int(H), int(d), int(Lq), int(dtype), float(scale), int(seg_cap), int(bool(out_f32)), 0)
+    _check(lib.chunk_attention_noalloc(ctypes.byref(desc), _ptr(Q), _ptr(segs), _ptr(nseg), _ptr(O), _stream(stream)))
 
 
 def kvbank_window_advance(layer: LayerDesc, ring_k, ring_v, start: int, n_rows: int, t_first: int, cand_k, cand_v,

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kvb_launch.hpp"
 #include "../../include/kvbank.h"
 
@@ -253,6 +255,41 @@ hipError_t run_gram(GramLaunch g, int H, int rows_ub, int cols_ub, float* dst, i
   hipError_t e = launch_gram(g, st);
   if (e != hipSuccess || g.splits == 1) return e;
   return launch_sum_splits(split, (int64_t)MAX_SPLITS * split_n, split_n, g.splits, dst, dst_hstride, H, rows_ub, st);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of chunk_attention_noalloc: the balanced grid's partials and flags
+// in a file-scope device array, one copy per GPU, held until the process
+// ends.  Host code never uses the array's name as an address: the device
+// address comes from hipGetSymbolAddress, once per device, and is kept here.
+// ---------------------------------------------------------------------------
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+constexpr int NOALLOC_MAX_DEVICES = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+
+// the current device's address of `scratch` (looked up on the first call on
+// that device, with the device current)
+int scratch_on_current_device(void** out) {
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return fail(KVB_EHIP, "device %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(KVB_EHIP, "hipGetSymbolAddress returned NULL for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVB_OK;
 }
 
 }  // namespace
@@ -547,6 +584,37 @@ int chunk_attention(const kvb_attn_desc* A, const void* Q, const kvb_segment* se
     if (int rc = check_ws(ws, ws_bytes, (size_t)p.bytes)) return rc;
     a.ws = ws;
     a.ws_bytes = ws_bytes;
+  }
+  HIPCHK(launch_attention(a, (hipStream_t)stream));
+  return ok();
+}
+
+int chunk_attention_noalloc(const kvb_attn_desc* A, const void* Q, const kvb_segment* segs, const int32_t* nseg,
+                            void* O, kvb_stream_t stream) {
+  if (!A) return fail(KVB_EINVAL, "attention descriptor is NULL");
+  if (A->H < 1 || A->H > KVB_MAX_HEADS) return fail(KVB_ESHAPE, "H=%d", A->H);
+  if (A->d != 64 && A->d != 128) return fail(KVB_ESHAPE, "d=%d (supported: 64, 128)", A->d);
+  if (A->dtype != KVB_BF16 && A->dtype != KVB_F32) return fail(KVB_EDTYPE, "dtype=%d", A->dtype);
+  if (A->Lq < 0) return fail(KVB_ESHAPE, "Lq=%d", A->Lq);
+  if (A->seg_cap < 1 || A->seg_cap > KVB_MAX_SEGMENTS) return fail(KVB_ESHAPE, "seg_cap=%d", A->seg_cap);
+  if (A->Lq == 0) return ok();
+  REQ_PTR(Q, 16, "Q");
+  REQ_PTR(O, 16, "O");
+  REQ_PTR(segs, 8, "segs");
+  REQ_PTR(nseg, 4, "nseg");
+  AttnLaunch a{};
+  a.H = A->H; a.d = A->d; a.Lq = A->Lq; a.et = A->dtype; a.out_f32 = A->dtype == KVB_F32 ? 1 : (A->out_f32 ? 1 : 0);
+  a.scale = A->scale > 0.0f ? A->scale : 1.0f / sqrtf((float)A->d);
+  a.Q = Q; a.O = O; a.segs = reinterpret_cast<const SegEntry*>(segs); a.nseg = nseg; a.seg_cap = A->seg_cap;
+  const AttnPlan p = attention_plan(A->H, A->d, A->Lq, A->dtype);
+  if (p.use) {
+    if ((size_t)p.bytes > NOALLOC_SCRATCH_BYTES)
+      return fail(KVB_EWORKSPACE, "the balanced grid needs %lld bytes of scratch, more than the %zu of "
+                  "chunk_attention_noalloc's static array", (long long)p.bytes, NOALLOC_SCRATCH_BYTES);
+    void* ptr = nullptr;
+    if (int rc = scratch_on_current_device(&ptr)) return rc;
+    a.ws = ptr;
+    a.ws_bytes = NOALLOC_SCRATCH_BYTES;
   }
   HIPCHK(launch_attention(a, (hipStream_t)stream));
   return ok();

@@ -194,23 +194,33 @@ def density(K: np.ndarray, prm: Params) -> np.ndarray:
 
 @dataclasses.dataclass
 class HeadBank:
-    """One (layer, head) bank: exact K/V rows, token ids and frozen baselines."""
+    """One (layer, head) bank: exact K/V rows, token ids and frozen baselines.
+
+    Xd: density descriptor rows when they are not the keys themselves (the
+    appendix E descriptor ablation: pre-RoPE keys, or [K; V]); X is the
+    descriptor the density uses (Xd, else K)."""
     tok: np.ndarray      # int64 [n]
     K: np.ndarray        # float64 [n, d]
     V: np.ndarray        # float64 [n, d]
     rho0: np.ndarray     # float64 [n]
+    Xd: Optional[np.ndarray] = None   # float64 [n, dx]
 
     @staticmethod
-    def empty(d: int) -> "HeadBank":
-        return HeadBank(np.zeros(0, np.int64), np.zeros((0, d)), np.zeros((0, d)), np.zeros(0))
+    def empty(d: int, dx: Optional[int] = None) -> "HeadBank":
+        return HeadBank(np.zeros(0, np.int64), np.zeros((0, d)), np.zeros((0, d)), np.zeros(0),
+                        None if dx is None else np.zeros((0, dx)))
 
     @property
     def n(self) -> int:
         return int(self.tok.shape[0])
 
+    @property
+    def X(self) -> np.ndarray:
+        return self.K if self.Xd is None else self.Xd
+
     def sorted_by_tok(self) -> "HeadBank":
         o = np.argsort(self.tok, kind="stable")
-        return HeadBank(self.tok[o], self.K[o], self.V[o], self.rho0[o])
+        return HeadBank(self.tok[o], self.K[o], self.V[o], self.rho0[o], None if self.Xd is None else self.Xd[o])
 
 
 # ---------------------------------------------------------------------------
@@ -341,15 +351,18 @@ class UpdateInfo:
 
 def update_layer(banks: List[Optional[HeadBank]], candK: np.ndarray, candV: np.ndarray,
                  cand_tok: np.ndarray, prm: Params, heads: Optional[Sequence[int]] = None,
-                 order: Optional[Sequence[np.ndarray]] = None, kstar: Optional[int] = None):
+                 order: Optional[Sequence[np.ndarray]] = None, kstar: Optional[int] = None, candX=None):
     """Apply one admission/eviction update to the density heads of a layer.
 
     ``banks[h]`` is None for heads that do not keep a density bank; ``heads``
     restricts the update to those heads (default: every head with a bank).
     ``order`` may supply a per-head candidate permutation (stage replay) and
     ``kstar`` a prefix length to apply instead of the computed one.
+    ``candX``: the candidates' density descriptors [H][N][dx] when they are
+    not the keys (the banks then carry theirs in HeadBank.Xd).
     Returns (new_banks, UpdateInfo).  Candidate rows are [H][N][d].
     """
+    Xc_all = candK if candX is None else candX
     H = len(banks)
     heads = [h for h in range(H) if banks[h] is not None] if heads is None else list(heads)
     N = int(cand_tok.shape[0])
@@ -359,10 +372,10 @@ def update_layer(banks: List[Optional[HeadBank]], candK: np.ndarray, candV: np.n
                       [None] * H, [None] * H, [None] * H, [0] * H, None)
     for h in heads:
         b = banks[h]
-        D, delta = disturbance(b.K, candK[h], prm)
+        D, delta = disturbance(b.X, Xc_all[h], prm)
         pi = candidate_order(delta, tok, prm.order) if order is None else np.asarray(order[h], np.int64)
-        rho = density(b.K, prm)
-        t, _ = crossing_times(b.K, rho, b.rho0, np.asarray(candK[h], np.float64)[pi[:kmax]], prm)
+        rho = density(b.X, prm)
+        t, _ = crossing_times(b.X, rho, b.rho0, np.asarray(Xc_all[h], np.float64)[pi[:kmax]], prm)
         info.D[h], info.delta[h], info.order[h], info.t[h], info.rho[h] = D, delta, pi, t, rho
     fill = prm.fill_below_capacity
     if prm.prefix == "head":
@@ -381,7 +394,7 @@ def update_layer(banks: List[Optional[HeadBank]], candK: np.ndarray, candV: np.n
         b = banks[h]
         k = kh[h]
         e = max(0, b.n + k - prm.M)
-        proj_k = projected_density(b.K, info.rho[h], np.asarray(candK[h], np.float64)[info.order[h]], k, prm)
+        proj_k = projected_density(b.X, info.rho[h], np.asarray(Xc_all[h], np.float64)[info.order[h]], k, prm)
         # no density check below capacity in the fill variant: nothing crossed counts
         gated = k > 0 and not (fill and b.n + k <= prm.M)
         crossed = (info.t[h] <= k) if gated else np.zeros(b.n, bool)
@@ -392,25 +405,28 @@ def update_layer(banks: List[Optional[HeadBank]], candK: np.ndarray, candV: np.n
         K2 = np.concatenate([b.K[keep], np.asarray(candK[h], np.float64)[adm]])
         V2 = np.concatenate([b.V[keep], np.asarray(candV[h], np.float64)[adm]])
         tok2 = np.concatenate([b.tok[keep], tok[adm]])
-        rho_new = density(K2, prm)
+        X2 = None if candX is None else np.concatenate([b.X[keep], np.asarray(candX[h], np.float64)[adm]])
+        rho_new = density(K2 if X2 is None else X2, prm)
         if prm.baseline == "refresh":
             rho0 = rho_new
         else:
             rho0 = np.concatenate([b.rho0[keep], rho_new[keep.sum():]])
-        new[h] = HeadBank(tok2, K2, V2, rho0)
+        new[h] = HeadBank(tok2, K2, V2, rho0, X2)
     return new, info
 
 
 def update_layer_brute(banks: List[Optional[HeadBank]], candK, candV, cand_tok, prm: Params,
-                       heads: Optional[Sequence[int]] = None):
+                       heads: Optional[Sequence[int]] = None, candX=None):
     """Same update recomputing every prefix length from scratch (tiny inputs).
 
     For each k the projected density of every bank state is summed directly
     over the first k ordered candidates, with distances from explicit
     differences; no running sums, no Gram form.  Policy variants follow the
     same Params fields, each written out with plain sorts and loops.
-    Returns (new_banks, kstar per head, orders).
+    Returns (new_banks, kstar per head, orders).  candX: candidate
+    descriptors when they are not the keys (banks carry theirs in Xd).
     """
+    Xc_all = candK if candX is None else candX
     H = len(banks)
     heads = [h for h in range(H) if banks[h] is not None] if heads is None else list(heads)
     N = int(cand_tok.shape[0])
@@ -419,7 +435,7 @@ def update_layer_brute(banks: List[Optional[HeadBank]], candK, candV, cand_tok, 
     orders, rhos = {}, {}
     for h in heads:
         b = banks[h]
-        Dmat = phi(sqdist_direct(np.asarray(candK[h], np.float64), b.K), prm)
+        Dmat = phi(sqdist_direct(np.asarray(Xc_all[h], np.float64), b.X), prm)
         D = Dmat.sum(axis=1)
         mean = D.mean() if D.size else 0.0
         delta = D / mean if (b.n > 0 and mean > 0) else np.zeros(N)
@@ -427,7 +443,7 @@ def update_layer_brute(banks: List[Optional[HeadBank]], candK, candV, cand_tok, 
             orders[h] = np.array(sorted(range(N), key=lambda c: tok[c]), dtype=np.int64)
         else:
             orders[h] = np.array(sorted(range(N), key=lambda c: (delta[c], tok[c])), dtype=np.int64)
-        Bm = phi(sqdist_direct(b.K, b.K), prm)
+        Bm = phi(sqdist_direct(b.X, b.X), prm)
         np.fill_diagonal(Bm, 0.0)
         rhos[h] = Bm.sum(axis=1)
 
@@ -435,8 +451,8 @@ def update_layer_brute(banks: List[Optional[HeadBank]], candK, candV, cand_tok, 
         b = banks[h]
         if k == 0:
             return rhos[h].copy()
-        adm = np.asarray(candK[h], np.float64)[orders[h][:k]]
-        return rhos[h] + phi(sqdist_direct(b.K, adm), prm).sum(axis=1)
+        adm = np.asarray(Xc_all[h], np.float64)[orders[h][:k]]
+        return rhos[h] + phi(sqdist_direct(b.X, adm), prm).sum(axis=1)
 
     def crossed_at(h, k):
         b = banks[h]
@@ -477,11 +493,12 @@ def update_layer_brute(banks: List[Optional[HeadBank]], candK, candV, cand_tok, 
         K2 = np.concatenate([b.K[keep], np.asarray(candK[h], np.float64)[adm]])
         V2 = np.concatenate([b.V[keep], np.asarray(candV[h], np.float64)[adm]])
         tok2 = np.concatenate([b.tok[keep], tok[adm]])
-        Bm = phi(sqdist_direct(K2, K2), prm)
+        X2 = None if candX is None else np.concatenate([b.X[keep], np.asarray(candX[h], np.float64)[adm]])
+        Bm = phi(sqdist_direct(K2 if X2 is None else X2, K2 if X2 is None else X2), prm)
         np.fill_diagonal(Bm, 0.0)
         rnew = Bm.sum(axis=1)
         rho0 = rnew if prm.baseline == "refresh" else np.concatenate([b.rho0[keep], rnew[keep.sum():]])
-        new[h] = HeadBank(tok2, K2, V2, rho0)
+        new[h] = HeadBank(tok2, K2, V2, rho0, X2)
     return new, kst, orders
 
 

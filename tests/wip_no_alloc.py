@@ -1,0 +1,71 @@
+"""chunk_attention_noalloc (the entry point for callers that cannot
+allocate) against chunk_attention with a caller workspace, through the C
+ABI: two calls in a row on balanced-grid shapes, the second smaller, each
+bit-identical to the workspace call and within the bf16 attention tolerance
+of the fp64 oracle on sampled rows."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from oracle.attention import attention as oracle_attention
+
+pytestmark = pytest.mark.gpu
+
+
+def _segments(H, parts):
+    """Device segment table [H][len(parts)] over the given [H][n][d] tensors."""
+    import torch
+    import kv_cache_compression_head_amd as kb
+    cap = len(parts)
+    arr = (kb.kvb_segment * (H * cap))()
+    for h in range(H):
+        for i, (K, V) in enumerate(parts):
+            arr[h * cap + i] = kb.kvb_segment(K[h].data_ptr(), V[h].data_ptr(), int(K.shape[1]), 0)
+    segs = torch.from_numpy(np.frombuffer(bytes(arr), dtype=np.uint8).copy()).to("cuda")
+    nseg = torch.full((H,), cap, dtype=torch.int32, device="cuda")
+    return segs, nseg, cap
+
+
+def _case(Lq, lens, seed):
+    import torch
+    import kv_cache_compression_head_amd as kb
+    H, d = 12, 128
+    print(f"[gpu-test] noalloc attention H={H} Lq={Lq} segments={lens} seed={seed}", flush=True)
+    assert kb.chunk_attention_workspace_size(H, d, Lq, kb.KVB_BF16) > 0, "shape must take the balanced grid"
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    mk = lambda n: torch.randn(H, n, d, device="cuda", generator=g).to(torch.bfloat16)
+    Q = mk(Lq)
+    parts = [(mk(n), mk(n)) for n in lens]
+    segs, nseg, cap = _segments(H, parts)
+    O_ws = torch.empty(H, Lq, d, dtype=torch.float32, device="cuda")
+    O_na = torch.full((H, Lq, d), float("nan"), dtype=torch.float32, device="cuda")
+    kb.chunk_attention(H, d, Lq, kb.KVB_BF16, Q, segs, nseg, cap, O_ws, out_f32=True, ws="auto")
+    kb.chunk_attention_noalloc(H, d, Lq, kb.KVB_BF16, Q, segs, nseg, cap, O_na, out_f32=True)
+    torch.cuda.synchronize()
+    assert torch.equal(O_ws, O_na), "noalloc output differs from the workspace call"
+    rows = np.random.default_rng(seed).choice(Lq, 96, replace=False)
+    Qn = Q.float().cpu().numpy().astype(np.float64)
+    On = O_na.cpu().numpy()
+    errs = []
+    for h in (0, H - 1):
+        K = np.concatenate([k[h].float().cpu().numpy() for k, _ in parts]).astype(np.float64)
+        V = np.concatenate([v[h].float().cpu().numpy() for _, v in parts]).astype(np.float64)
+        errs.append(np.abs(On[h][rows] - oracle_attention(Qn[h][rows], K, V)))
+    e = np.concatenate([x.reshape(-1) for x in errs])
+    assert e.max() <= 2e-2 and e.mean() <= 2e-3, (e.max(), e.mean())
+
+
+def test_noalloc_matches_workspace_call_twice():
+    # first call: 1,560 queries (84 items on 256 slots), then a smaller one
+    _case(1560, [1560, 7000, 1560], seed=1)
+    _case(520, [1560, 3001, 520], seed=2)
+
+
+def test_noalloc_rejects_nothing_on_supported_plans():
+    """Every balanced-grid plan on a 256-compute-unit device fits the static
+    scratch (host-side plan sizes)."""
+    import kv_cache_compression_head_amd as kb
+    mx = max(kb.chunk_attention_workspace_size(H, d, Lq, kb.KVB_BF16)
+             for H in (1, 12, 64) for d in (64, 128) for Lq in range(1, 40000, 97))
+    assert 0 < mx <= 64 << 20
