@@ -107,7 +107,23 @@ typedef struct ihipStream_t* kvb_stream_t;   /* same type as hipStream_t */
  * within each frame, floor(r * n) of its n = F / seg_len segments, instead of
  * one BottomK over all (frame, segment) items */
 #define KVB_POL_FRAME_BOTTOMK   64u
-#define KVB_POL_ALL            127u
+/* DensityKV sequential within-block admission (paper summary, appendix E,
+ * within-block competition): instead of the largest shared prefix, kvbank_update
+ * walks the candidates in order and gates each one against the bank as it
+ * stands, earlier admissions included.  Step j offers every density head its
+ * j-th candidate c; with e = max(0, n + 1 - M) the step is feasible when each
+ * head has at most e states x with rho_x + phi(x, c) > tau * rho0_x (decided
+ * by the whole layer; per head with KVB_POL_HEAD_PREFIX; unchecked below
+ * capacity with KVB_POL_FILL_BELOW_CAP).  A feasible step admits c, evicting
+ * the crossed state, else the densest (ties: lower token) or, with
+ * KVB_POL_EVICT_OLDEST, the oldest (KVB_POL_EVICT_DENSEST: the densest);
+ * c's baseline is its density at admission.  Outputs: k_star = admitted
+ * candidates, n_evicted = evictions during the walk (admitted candidates
+ * included), n_mandatory = of them, crossed states; t_cross and rho_proj are
+ * not written.  The workspace holds every head's (M + N)^2 pair interactions
+ * in fp32. */
+#define KVB_POL_SEQUENTIAL     128u
+#define KVB_POL_ALL            255u
 
 typedef struct kvb_params {
   float tau;          /* density growth bound, >= 1 (may be +inf) */
@@ -125,7 +141,10 @@ typedef struct kvb_layer_desc {
   int32_t M;             /* bank capacity per head (>= 0; > 0 when a density head exists) */
   int32_t dtype;         /* KVB_BF16 or KVB_F32 */
   int32_t frame_tokens;  /* F: tokens per latent frame */
-  int32_t reserved;
+  int32_t desc_dim;      /* density descriptor (DensityKV paper summary, appendix E, descriptor ablation):
+                            0 = the post-RoPE keys themselves (the method); 64 or 128 = separate rows of
+                            that dimension in bank->X and layout->cand_x (pre-RoPE keys, or [K; V] when
+                            d = 64).  Density-only layers (no Forcing-KV heads) */
   const uint8_t* label;  /* HOST pointer, H head labels */
   kvb_params params;
 } kvb_layer_desc;
@@ -137,6 +156,7 @@ typedef struct kvb_bank {   /* device pointers, updated in place */
   float* rho0;      /* [H][M] frozen insertion baselines */
   float* rho;       /* [H][M] current densities (maintained incrementally) */
   int32_t* count;   /* [H] occupancy n_h; slots [0, n_h) are live */
+  void* X;          /* [H][M][desc_dim] density descriptors, moved with K and V (desc_dim > 0; else unused) */
 } kvb_bank;
 
 typedef struct kvb_kv_layout {   /* device pointers of the non-bank KV of the layer */
@@ -146,6 +166,7 @@ typedef struct kvb_kv_layout {   /* device pointers of the non-bank KV of the la
   int32_t win_start; int32_t win_len;                         /* live rows: win_len rows from win_start (mod cap) */
   const void* chunk_k; const void* chunk_v; int32_t chunk_len; /* [H][chunk_len][d] current chunk */
   int32_t reserved;
+  const void* cand_x;   /* [H][N][desc_dim] the candidates' density descriptors (desc_dim > 0; else unused) */
 } kvb_kv_layout;
 
 typedef struct kvb_segment {   /* one contiguous run of retained rows of one head */

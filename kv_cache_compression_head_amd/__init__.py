@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 __all__ = [
     "KVB_BF16", "KVB_F32", "KVB_HEAD_DENSITY", "KVB_HEAD_STATIC", "KVB_HEAD_DYNAMIC", "KVB_POL_SOURCE_ORDER",
     "KVB_POL_REFRESH_BASELINE", "KVB_POL_EVICT_DENSEST", "KVB_POL_EVICT_OLDEST", "KVB_POL_HEAD_PREFIX",
-    "KVB_POL_FILL_BELOW_CAP", "KVB_POL_FRAME_BOTTOMK",
+    "KVB_POL_FILL_BELOW_CAP", "KVB_POL_FRAME_BOTTOMK", "KVB_POL_SEQUENTIAL",
     "KvbError", "load_library", "kvbank_workspace_size", "kvbank_score", "kvbank_update",
     "chunk_attention", "chunk_attention_noalloc", "chunk_attention_workspace_size", "kvbank_window_advance",
     "forcing_head_profile",
@@ -32,6 +32,7 @@ KVB_HEAD_DENSITY, KVB_HEAD_STATIC, KVB_HEAD_DYNAMIC = 0, 1, 2
 KVB_POL_SOURCE_ORDER, KVB_POL_REFRESH_BASELINE, KVB_POL_EVICT_DENSEST = 1, 2, 4
 KVB_POL_EVICT_OLDEST, KVB_POL_HEAD_PREFIX, KVB_POL_FILL_BELOW_CAP = 8, 16, 32
 KVB_POL_FRAME_BOTTOMK = 64
+KVB_POL_SEQUENTIAL = 128
 KVB_MAX_SEGMENTS = 256
 HEADER_FUNCTIONS = ("kvbank_workspace_size", "kvbank_score", "kvbank_update", "chunk_attention",
                     "chunk_attention_workspace_size", "kvbank_window_advance", "forcing_head_profile_workspace_size",
@@ -47,17 +48,18 @@ class kvb_params(ctypes.Structure):
 
 class kvb_layer_desc(ctypes.Structure):
     _fields_ = [("H", _c_i32), ("d", _c_i32), ("M", _c_i32), ("dtype", _c_i32), ("frame_tokens", _c_i32),
-                ("reserved", _c_i32), ("label", ctypes.POINTER(ctypes.c_uint8)), ("params", kvb_params)]
+                ("desc_dim", _c_i32), ("label", ctypes.POINTER(ctypes.c_uint8)), ("params", kvb_params)]
 
 
 class kvb_bank(ctypes.Structure):
-    _fields_ = [("K", _vp), ("V", _vp), ("tok", _vp), ("rho0", _vp), ("rho", _vp), ("count", _vp)]
+    _fields_ = [("K", _vp), ("V", _vp), ("tok", _vp), ("rho0", _vp), ("rho", _vp), ("count", _vp), ("X", _vp)]
 
 
 class kvb_kv_layout(ctypes.Structure):
     _fields_ = [("sink_k", _vp), ("sink_v", _vp), ("sink_len", _c_i32), ("win_cap", _c_i32),
                 ("win_k", _vp), ("win_v", _vp), ("win_start", _c_i32), ("win_len", _c_i32),
-                ("chunk_k", _vp), ("chunk_v", _vp), ("chunk_len", _c_i32), ("reserved", _c_i32)]
+                ("chunk_k", _vp), ("chunk_v", _vp), ("chunk_len", _c_i32), ("reserved", _c_i32),
+                ("cand_x", _vp)]
 
 
 class kvb_segment(ctypes.Structure):
@@ -156,13 +158,14 @@ class LayerDesc:
     seg_len: int = 0
     retention: float = 0.0
     policy: int = 0          # OR of KVB_POL_*
+    desc_dim: int = 0        # 0: keys are the density descriptors; 64 / 128: Bank.X and KVLayout.cand_x
 
     def c(self):
         lab = (ctypes.c_uint8 * max(1, len(self.labels)))(*[int(x) for x in self.labels])
         prm = kvb_params(float(self.tau), float(self.sigma), float(self.eps), float(self.p), int(self.seg_len),
                          int(self.policy), float(self.retention))
-        desc = kvb_layer_desc(int(self.H), int(self.d), int(self.M), int(self.dtype), int(self.frame_tokens), 0,
-                              ctypes.cast(lab, ctypes.POINTER(ctypes.c_uint8)), prm)
+        desc = kvb_layer_desc(int(self.H), int(self.d), int(self.M), int(self.dtype), int(self.frame_tokens),
+                              int(self.desc_dim), ctypes.cast(lab, ctypes.POINTER(ctypes.c_uint8)), prm)
         desc._keep = lab   # keep the label array alive with the descriptor
         return desc
 
@@ -206,27 +209,33 @@ class Bank:
     rho0: "object"
     rho: "object"
     count: "object"
+    X: "object" = None       # [H][M][desc_dim] density descriptors (desc_dim > 0)
 
     @staticmethod
-    def empty(H: int, M: int, d: int, dtype):
+    def empty(H: int, M: int, d: int, dtype, desc_dim: int = 0):
         import torch
         dev = torch.device("cuda")
         return Bank(torch.zeros(H, M, d, dtype=dtype, device=dev), torch.zeros(H, M, d, dtype=dtype, device=dev),
                     torch.full((H, M), -1, dtype=torch.int32, device=dev),
                     torch.zeros(H, M, dtype=torch.float32, device=dev),
                     torch.zeros(H, M, dtype=torch.float32, device=dev),
-                    torch.zeros(H, dtype=torch.int32, device=dev))
+                    torch.zeros(H, dtype=torch.int32, device=dev),
+                    torch.zeros(H, M, desc_dim, dtype=dtype, device=dev) if desc_dim else None)
+
+    def _parts(self):
+        return tuple(x for x in (self.K, self.V, self.tok, self.rho0, self.rho, self.count, self.X) if x is not None)
 
     def clone(self) -> "Bank":
-        return Bank(*(x.clone() for x in (self.K, self.V, self.tok, self.rho0, self.rho, self.count)))
+        return Bank(*(x.clone() for x in (self.K, self.V, self.tok, self.rho0, self.rho, self.count)),
+                    None if self.X is None else self.X.clone())
 
     def copy_(self, other: "Bank"):
-        for a, b in zip((self.K, self.V, self.tok, self.rho0, self.rho, self.count),
-                        (other.K, other.V, other.tok, other.rho0, other.rho, other.count)):
+        for a, b in zip(self._parts(), other._parts()):
             a.copy_(b, non_blocking=True)
 
     def c(self):
-        return kvb_bank(_ptr(self.K), _ptr(self.V), _ptr(self.tok), _ptr(self.rho0), _ptr(self.rho), _ptr(self.count))
+        return kvb_bank(_ptr(self.K), _ptr(self.V), _ptr(self.tok), _ptr(self.rho0), _ptr(self.rho), _ptr(self.count),
+                        _ptr(self.X))
 
 
 @dataclasses.dataclass
@@ -240,13 +249,15 @@ class KVLayout:
     win_len: int = 0
     chunk_k: "object" = None
     chunk_v: "object" = None
+    cand_x: "object" = None   # [H][N][desc_dim] candidate density descriptors (desc_dim > 0)
 
     def c(self):
         sl = 0 if self.sink_k is None else int(self.sink_k.shape[1])
         wc = 0 if self.win_k is None else int(self.win_k.shape[1])
         cl = 0 if self.chunk_k is None else int(self.chunk_k.shape[1])
         return kvb_kv_layout(_ptr(self.sink_k), _ptr(self.sink_v), sl, wc, _ptr(self.win_k), _ptr(self.win_v),
-                             int(self.win_start), int(self.win_len), _ptr(self.chunk_k), _ptr(self.chunk_v), cl, 0)
+                             int(self.win_start), int(self.win_len), _ptr(self.chunk_k), _ptr(self.chunk_v), cl, 0,
+                             _ptr(self.cand_x))
 
 
 @dataclasses.dataclass
@@ -293,6 +304,18 @@ def kvbank_workspace_size(layer: LayerDesc, N: int) -> int:
     return int(out.value)
 
 
+def _req_desc(layer: LayerDesc, bank: Optional[Bank], lay: Optional[KVLayout], N: int):
+    """Shapes of the density descriptors when the layer uses its own (desc_dim > 0)."""
+    if not layer.desc_dim:
+        return
+    kd = _kv_dtype(layer.dtype)
+    if bank is not None:
+        _req(bank.X, "bank.X", kd, (layer.H, layer.M, layer.desc_dim))
+    if lay is None or lay.cand_x is None:
+        raise ValueError("desc_dim > 0 needs KVLayout.cand_x")
+    _req(lay.cand_x, "cand_x", kd, (layer.H, N, layer.desc_dim))
+
+
 def kvbank_score(layer: LayerDesc, bank: Optional[Bank], cand_k, cand_tok, N: int, lay: Optional[KVLayout],
                  out_D, out_score, out_order, ws, stream=None):
     import torch
@@ -303,6 +326,7 @@ def kvbank_score(layer: LayerDesc, bank: Optional[Bank], cand_k, cand_tok, N: in
         _req(cand_k, "cand_k", kd, (layer.H, N, layer.d))
         _req(out_score, "out_score", torch.float32, (layer.H, N))
         _req(out_order, "out_order", torch.int32, (layer.H, N))
+        _req_desc(layer, bank, lay, N)
     cb = bank.c() if bank is not None else None
     cl = lay.c() if lay is not None else None
     _check(lib.kvbank_score(ctypes.byref(desc), ctypes.byref(cb) if cb is not None else None, _ptr(cand_k),
@@ -319,6 +343,7 @@ def kvbank_update(layer: LayerDesc, bank: Optional[Bank], cand_k, cand_v, cand_t
     if N > 0:
         _req(cand_k, "cand_k", kd, (layer.H, N, layer.d))
         _req(cand_v, "cand_v", kd, (layer.H, N, layer.d))
+        _req_desc(layer, bank, lay, N)
     cb = bank.c() if bank is not None else None
     cl = lay.c()
     co = out.c()

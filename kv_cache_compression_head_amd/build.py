@@ -19,7 +19,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvbank.so")
 ARCH = "gfx950"
 
-SOURCES = ["kvb_api.hip", "kvb_gram.hip", "kvb_select.hip", "kvb_forcing.hip", "kvb_attention.hip", "kvb_rope.hip"]
+SOURCES = ["kvb_api.hip", "kvb_gram.hip", "kvb_select.hip", "kvb_forcing.hip", "kvb_attention.hip", "kvb_rope.hip",
+           "kvb_sequential.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

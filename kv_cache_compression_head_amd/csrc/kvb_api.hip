@@ -88,6 +88,11 @@ int check_layer(const kvb_layer_desc* L, int32_t N, Heads* hd) {
   }
   if ((hd->dyn || hd->stat) && N % L->frame_tokens != 0)
     return fail(KVB_ESHAPE, "Forcing-KV heads need N (%d) to be a multiple of frame_tokens (%d)", N, L->frame_tokens);
+  if (L->desc_dim != 0) {
+    if (L->desc_dim != 64 && L->desc_dim != 128)
+      return fail(KVB_ESHAPE, "desc_dim=%d (supported: 0 = the keys, 64, 128)", L->desc_dim);
+    if (hd->dyn || hd->stat) return fail(KVB_EPARAM, "density descriptors apply to density-only layers");
+  }
   return KVB_OK;
 }
 
@@ -116,7 +121,8 @@ constexpr int MAX_SPLITS = 8;
 
 struct Layout {
   size_t normB, normC, augB, augC, k0, k1, v0, v1, t, cp, hist, rhoP, evict, surv, evl, fixl, nsurv, nfix,
-      fmode, cnt, accS, accAE, accAA, colAA, cos, split, total;
+      fmode, cnt, accS, accAE, accAA, colAA, cos, split, seqP, seqRR, seqTok, seqLog, seqAdm, seqFree, seqAlive,
+      total;
   int kmax, cps, ncp;
 };
 
@@ -162,6 +168,17 @@ Layout layout_of(const kvb_layer_desc* L, int32_t N) {
   o.colAA = bump(&off, H * sym_head_floats(o.kmax) * 4);
   o.cos = bump(&off, (int64_t)N * 4);
   o.split = bump(&off, H * (int64_t)MAX_SPLITS * (N > L->M ? N : L->M) * 4);
+  if (L->params.policy & KVB_POL_SEQUENTIAL) {
+    // sequential admission: every head's pair interactions over its M + N states
+    const int64_t S = M + N;
+    o.seqP = bump(&off, H * S * S * 4);
+    o.seqRR = bump(&off, H * S * 8);
+    o.seqTok = bump(&off, H * S * 4);
+    o.seqLog = bump(&off, H * (int64_t)N * 4);
+    o.seqAdm = bump(&off, H * 4);
+    o.seqFree = bump(&off, H * M * 4);
+    o.seqAlive = bump(&off, H * (int64_t)N * 4);
+  }
   o.total = off;
   return o;
 }
@@ -176,7 +193,25 @@ int check_bank(const kvb_bank* B, const kvb_layer_desc* L) {
   REQ_PTR(B->rho0, 4, "bank.rho0");
   REQ_PTR(B->rho, 4, "bank.rho");
   REQ_PTR(B->count, 4, "bank.count");
-  (void)L;
+  if (L->desc_dim) REQ_PTR(B->X, 16, "bank.X (desc_dim > 0)");
+  return KVB_OK;
+}
+
+// The density's rows: the keys, or the descriptor arrays when desc_dim > 0
+struct DensRows {
+  const void* bank;
+  const void* cand;
+  int dim;
+};
+int density_rows(const kvb_layer_desc* L, const kvb_bank* B, const void* cand_k, const kvb_kv_layout* lay,
+                 DensRows* r) {
+  if (!L->desc_dim) {
+    *r = DensRows{B->K, cand_k, L->d};
+    return KVB_OK;
+  }
+  if (!lay) return fail(KVB_EINVAL, "layout is NULL (desc_dim > 0 needs layout.cand_x)");
+  REQ_PTR(lay->cand_x, 16, "layout.cand_x (desc_dim > 0)");
+  *r = DensRows{B->X, lay->cand_x, L->desc_dim};
   return KVB_OK;
 }
 
@@ -344,13 +379,16 @@ int kvbank_score(const kvb_layer_desc* L, const kvb_bank* bank, const void* cand
   const int H = L->H, M = L->M, d = L->d, et = L->dtype;
   const PhiConst pc = phi_const(L->params);
   if (hd.dens) {
+    DensRows dr{};
+    if ((rc = density_rows(L, bank, cand_k, lay, &dr))) return rc;
     float* nB = at<float>(ws, lo.normB);
     float* nC = at<float>(ws, lo.normC);
     void* aB = at<void>(ws, lo.augB);
     void* aC = at<void>(ws, lo.augC);
-    HIPCHK(launch_norms(bank->K, M, nB, aB, cand_k, N, nC, aC, et, H, d, pc.inv_s2, et == ET_BF16 && pc.direct, st));
+    HIPCHK(launch_norms(dr.bank, M, nB, aB, dr.cand, N, nC, aC, et, H, dr.dim, pc.inv_s2, et == ET_BF16 && pc.direct,
+                        st));
     GramLaunch g{};
-    g.k = KeysDesc{bank->K, cand_k, nB, nC, aB, aC, M, N, d, H, et};
+    g.k = KeysDesc{dr.bank, dr.cand, nB, nC, aB, aC, M, N, dr.dim, H, et};
     g.rows = VList{nullptr, nullptr, 0, 0, 0, M, N, 0};
     g.cols = VList{nullptr, bank->count, 0, 1, 0, 0, M, 0};
     g.pc = pc;
@@ -479,16 +517,37 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
       HIPCHK(launch_zero_i32(zp, zn, 4, st));
     }
   }
-  if (hd.dens && N > 0) {
+  DensRows dr{};
+  if (hd.dens && N > 0 && (rc = density_rows(L, bank, cand_k, lay, &dr))) return rc;
+  if (hd.dens && N > 0 && (pol & KVB_POL_SEQUENTIAL)) {
+    SeqLaunch q{};
+    q.H = H; q.M = M; q.N = N; q.active = hd.dens; q.P = at<float>(ws, lo.seqP); q.cnt = at<int32_t>(ws, lo.cnt);
+    q.rho = bank->rho; q.rho0 = bank->rho0; q.bank_tok = bank->tok; q.cand_tok = cand_tok; q.order = order;
+    q.tau = L->params.tau; q.fill = (pol & KVB_POL_FILL_BELOW_CAP) ? 1 : 0;
+    q.evict_mode = (pol & KVB_POL_EVICT_DENSEST) ? 1 : (pol & KVB_POL_EVICT_OLDEST) ? 2 : 0;
+    q.per_head = ks_hs;
+    q.st_rr = at<uint64_t>(ws, lo.seqRR); q.st_tok = at<int32_t>(ws, lo.seqTok); q.log = at<int32_t>(ws, lo.seqLog);
+    q.n_adm = at<int32_t>(ws, lo.seqAdm); q.kstar = out->k_star; q.kstar_hs = ks_hs; q.n_ev = out->n_evicted;
+    q.n_mand = out->n_mandatory; q.status = out->status;
+    SeqGather g{};
+    g.H = H; g.M = M; g.N = N; g.d = d; g.dx = d; g.et = et; g.active = hd.dens; g.cnt = q.cnt; g.st_rr = q.st_rr;
+    g.st_tok = q.st_tok; g.log = q.log; g.n_adm = q.n_adm; g.freel = at<int32_t>(ws, lo.seqFree);
+    g.alive = at<int32_t>(ws, lo.seqAlive); g.refresh = (pol & KVB_POL_REFRESH_BASELINE) ? 1 : 0;
+    g.rho = bank->rho; g.rho0 = bank->rho0; g.bank_tok = bank->tok; g.count = bank->count;
+    g.bankK = bank->K; g.bankV = bank->V; g.candK = cand_k; g.candV = cand_v;
+    g.bankX = L->desc_dim ? bank->X : nullptr; g.candX = L->desc_dim ? lay->cand_x : nullptr; g.dx = dr.dim;
+    g.cand_tok = cand_tok; g.status = out->status;
+    HIPCHK(launch_sequential(q, g, dr.bank, dr.cand, dr.dim, pc, pm, st));
+  } else if (hd.dens && N > 0) {
     const int kmax = lo.kmax;
     const int32_t* cnt = at<int32_t>(ws, lo.cnt);
     float* nB = at<float>(ws, lo.normB);
     float* nC = at<float>(ws, lo.normC);
     void* aB = at<void>(ws, lo.augB);
     void* aC = at<void>(ws, lo.augC);
-    HIPCHK(launch_norms(bank->K, M, nB, aB, cand_k, N, nC, aC, et, H, d, pc.inv_s2, et == ET_BF16 && pc.direct, st,
-                        NormCheck{out->status, cnt, hd.dens, 0, 0}));
-    const KeysDesc kd{bank->K, cand_k, nB, nC, aB, aC, M, N, d, H, et};
+    HIPCHK(launch_norms(dr.bank, M, nB, aB, dr.cand, N, nC, aC, et, H, dr.dim, pc.inv_s2, et == ET_BF16 && pc.direct,
+                        st, NormCheck{out->status, cnt, hd.dens, 0, 0}));
+    const KeysDesc kd{dr.bank, dr.cand, nB, nC, aB, aC, M, N, dr.dim, H, et};
     ScanLaunch s{};
     s.k = kd; s.rho = bank->rho; s.rho0 = bank->rho0; s.count = cnt; s.order = order;
     s.active = hd.dens; s.kmax = kmax; s.tau = L->params.tau; s.cps = lo.cps; s.ncp = lo.ncp;
@@ -538,6 +597,7 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
     ap.H = H; ap.M = M; ap.N = N; ap.d = d; ap.et = et; ap.kmax = kmax; ap.active = hd.dens;
     ap.bankK = bank->K; ap.bankV = bank->V; ap.bank_tok = bank->tok; ap.rho0 = bank->rho0; ap.rho = bank->rho;
     ap.count = bank->count; ap.candK = cand_k; ap.candV = cand_v; ap.cand_tok = cand_tok; ap.order = order;
+    ap.bankX = L->desc_dim ? bank->X : nullptr; ap.candX = L->desc_dim ? lay->cand_x : nullptr; ap.dx = L->desc_dim;
     ap.D = D; ap.kstar = out->k_star; ap.kstar_hs = ks_hs;
     ap.refresh = (pol & KVB_POL_REFRESH_BASELINE) ? 1 : 0; ap.surv = sel.surv; ap.n_surv = sel.n_surv; ap.evl = sel.evl;
     ap.n_ev = sel.n_ev; ap.rhoP = s.rhoP; ap.acc_surv = at<float>(ws, lo.accS);

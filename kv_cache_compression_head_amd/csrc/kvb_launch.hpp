@@ -176,8 +176,49 @@ struct ApplyLaunch {
   const float* acc_adm_ev;    // [H][kmax] sum over fixl for admitted
   const int32_t* fmode;       // [H]
   const float* acc_adm_adm;   // [H][kmax] sum over other admitted for admitted
+  void* bankX; const void* candX; int32_t dx;   // density descriptors moved with K and V (null: none)
 };
 hipError_t launch_apply(const ApplyLaunch& a, hipStream_t s);
+
+// ---- sequential within-block admission --------------------------------------
+constexpr int KVB_SEQ_MAX_HEADS = 64;
+struct SeqLaunch {
+  int32_t H, M, N;
+  uint64_t active;            // bit h: density head
+  float* P;                   // [H][M+N][M+N] pair interactions (bank slots, then candidates)
+  const int32_t* cnt;         // [H] clamped occupancy before the block
+  const float* rho; const float* rho0; const int32_t* bank_tok;   // bank [H][M]
+  const int32_t* cand_tok;    // [N]
+  const int32_t* order;       // [H][N]
+  float tau;
+  int32_t fill, evict_mode, per_head;
+  uint64_t* st_rr;            // [H][M+N] (rho, rho0) of each state
+  int32_t* st_tok;            // [H][M+N] token id of live states, -1 otherwise
+  int32_t* log;               // [H][N] admitted candidates in admission order
+  int32_t* n_adm;             // [H]
+  int32_t* kstar;             // out: admissions ([1] shared, [H] per head)
+  int32_t kstar_hs;
+  int32_t* n_ev;              // out [H]: evictions during the walk
+  int32_t* n_mand;            // out [H]: of them, crossed states
+  uint32_t* status;
+};
+struct SeqGather {
+  int32_t H, M, N, d, dx, et;
+  uint64_t active;
+  const int32_t* cnt;
+  const uint64_t* st_rr; const int32_t* st_tok;
+  const int32_t* log; const int32_t* n_adm;
+  int32_t* freel;             // [H][M] scratch
+  int32_t* alive;             // [H][N] scratch
+  int32_t refresh;
+  float* rho; float* rho0; int32_t* bank_tok; int32_t* count;
+  void* bankK; void* bankV; void* bankX;          // bankX may be null (descriptors are the keys)
+  const void* candK; const void* candV; const void* candX;
+  const int32_t* cand_tok;
+  uint32_t* status;
+};
+hipError_t launch_sequential(const SeqLaunch& a, const SeqGather& g, const void* bankX, const void* candX, int dx,
+                             const PhiConst& pc, int phi_mode, hipStream_t s);
 
 // ---- segment tables ---------------------------------------------------------
 struct SegEntry { const void* k; const void* v; int32_t len; int32_t pad; };

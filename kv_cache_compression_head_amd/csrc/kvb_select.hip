@@ -540,6 +540,29 @@ __global__ __launch_bounds__(256) void apply_adm_kernel(ApplyLaunch a) {
   }
 }
 
+// descriptor rows of the admitted candidates, into the slots apply_adm_kernel
+// gives their keys (16-byte chunks)
+__global__ __launch_bounds__(256) void apply_adm_x_kernel(ApplyLaunch a) {
+  const int h = blockIdx.y;
+  if (!head_on(a.active, h)) return;
+  const int ks = a.kstar[h * a.kstar_hs];
+  const int esz = a.et == ET_BF16 ? 2 : 4;
+  const int cpr = a.dx * esz / 16;
+  const int u = blockIdx.x * 256 + threadIdx.x;
+  const int j = u / cpr, c = u % cpr;
+  if (j >= ks) return;
+  const int64_t hb = (int64_t)h * a.M;
+  const int ne = a.n_ev[h];
+  const int nold = a.n_surv[h] + ne;
+  const int slot = j < ne ? a.evl[hb + j] : nold + (j - ne);
+  const int cand = a.order[(int64_t)h * a.N + j];
+  if ((unsigned)slot >= (unsigned)a.M || (unsigned)cand >= (unsigned)a.N) return;
+  const int64_t rowb = (int64_t)a.dx * esz;
+  const char* src = (const char*)a.candX + ((int64_t)h * a.N + cand) * rowb;
+  char* dst = (char*)a.bankX + (hb + slot) * rowb;
+  *reinterpret_cast<u32x4_t*>(dst + c * 16) = *reinterpret_cast<const u32x4_t*>(src + c * 16);
+}
+
 __global__ void commit_count_kernel(ApplyLaunch a) {
   const int h = threadIdx.x;
   if (h >= a.H || !head_on(a.active, h)) return;
@@ -557,6 +580,11 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t st) {
       hipLaunchKernelGGL((apply_adm_kernel<8>), dim3((a.kmax + 15) / 16, a.H), dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL((apply_adm_kernel<32>), dim3((a.kmax + 3) / 4, a.H), dim3(256), 0, st, a);
+  }
+  if (a.bankX && a.candX && a.kmax > 0) {
+    const int cprx = a.dx * (a.et == ET_BF16 ? 2 : 4) / 16;
+    hipLaunchKernelGGL(apply_adm_x_kernel, dim3((unsigned)(((int64_t)a.kmax * cprx + 255) / 256), a.H), dim3(256), 0,
+                       st, a);
   }
   hipLaunchKernelGGL(commit_count_kernel, dim3(1), dim3(64), 0, st, a);
   return hipGetLastError();

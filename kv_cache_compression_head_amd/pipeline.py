@@ -27,7 +27,7 @@ class LayerCache:
         self.desc = desc
         self.H, self.d, self.M = desc.H, desc.d, desc.M
         self.kdt = torch_dtype(desc.dtype)
-        self.bank = Bank.empty(self.H, max(self.M, 1), self.d, self.kdt) if self.M > 0 else None
+        self.bank = Bank.empty(self.H, max(self.M, 1), self.d, self.kdt, desc.desc_dim) if self.M > 0 else None
         self.out = UpdateOut.alloc(self.H, seg_cap, self.M, diagnostics)
         self.ws = None
         self._aws = None

@@ -68,7 +68,7 @@ def _desc(**kw):
     (dict(M=0), -2), (dict(tau=0.5), -4), (dict(tau=math.nan), -4), (dict(sigma=0.0), -4), (dict(p=-1.0), -4),
     (dict(eps=0.0), -4), (dict(labels=[0, 7]), -4), (dict(labels=[2, 2], seg_len=5), -4),
     (dict(labels=[2, 2], seg_len=4, retention=1.5), -4), (dict(frame_tokens=0), -2),
-    (dict(policy=128), -4), (dict(policy=kb.KVB_POL_EVICT_DENSEST | kb.KVB_POL_EVICT_OLDEST), -4),
+    (dict(policy=256), -4), (dict(policy=kb.KVB_POL_EVICT_DENSEST | kb.KVB_POL_EVICT_OLDEST), -4),
 ])
 def test_host_validation(kw, code):
     with pytest.raises(kb.KvbError) as e:
