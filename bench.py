@@ -375,8 +375,12 @@ def layer_chunk(name: str, steps: int, warmup: int, policy: int = 0, tau=None):
     n0 = int(snap.count.min().cpu())
     N = inp["candK"].shape[1]
     ev = lc.out.n_evicted.cpu().tolist()
+    # the crossing scan runs unless the whole bank is replaced (min(N, M) = M:
+    # k* = M without it, reported as n_mandatory = -1)
+    scanned = min(lc.out.n_mandatory.cpu().tolist()) >= 0
     score_pairs = wl.H * n0 * N
-    upd_pairs = sum(n0 * min(N, wl.M) + (n0 - e) * e + kstar * min(e, n0 - e) + kstar * (kstar - 1) // 2 for e in ev)
+    upd_pairs = sum((n0 * min(N, wl.M) if scanned else 0) + (n0 - e) * e + kstar * min(e, n0 - e)
+                    + kstar * (kstar - 1) // 2 for e in ev)
     valu = recorded_valu_per_pair(name)
 
     def pair_roof(pairs, ms, stage_name):
@@ -399,6 +403,7 @@ def layer_chunk(name: str, steps: int, warmup: int, policy: int = 0, tau=None):
            "attention_tflops": round(attn_tflops, 2),
            "attention_frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
            "k_star": kstar, "evicted_per_head": ev[:1] + ([] if len(set(ev)) == 1 else ev[1:]),
+           "crossing_scan": scanned,
            "roofline": roof, "density_stages": density_roof,
            "workload": f"{name}: one layer-chunk, H={wl.H}, d={wl.d}, F={wl.F}, M={wl.M}, N={N}, Lq={wl.Lq}, "
                        f"window={wl.window[1] - wl.window[0]} frames, tau={wl.tau}, sigma={wl.sigma}, p={wl.p}"
@@ -613,8 +618,10 @@ def summarize_counters(d: str, min_us: float = 0.0):
     disp = {}
     for r in rows:
         key = (int(r["Dispatch_Id"]), r.get("Agent_Id", ""))
+        wg = int(r.get("Workgroup_Size", 0) or 0) or 1
         e = disp.setdefault(key, {"name": r["Kernel_Name"], "start": int(r.get("Start_Timestamp", 0) or 0),
-                                  "end": int(r.get("End_Timestamp", 0) or 0), "c": {}})
+                                  "end": int(r.get("End_Timestamp", 0) or 0), "c": {},
+                                  "wgs": int(r.get("Grid_Size", 0) or 0) // wg})
         e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     seq, agg = {}, {}
     for key in sorted(disp, key=lambda k: disp[k]["start"] or k[0]):
@@ -623,17 +630,18 @@ def summarize_counters(d: str, min_us: float = 0.0):
         us = (e["end"] - e["start"]) / 1000.0
         if us < min_us:
             continue
-        a = agg.setdefault(role, {"n": 0, "us": 0.0, "c": {}})
+        a = agg.setdefault((role, e["wgs"]), {"n": 0, "us": 0.0, "c": {}})
         a["n"] += 1
         a["us"] += us
         for k, v in e["c"].items():
             a["c"][k] = a["c"].get(k, 0.0) + v
     names = sorted({k for a in agg.values() for k in a["c"]})
-    print("| kernel (role) | dispatches | avg us | " + " | ".join(f"{n} / dispatch" for n in names) + " |")
-    print("|---|---|---|" + "---|" * len(names))
-    for role, a in sorted(agg.items(), key=lambda kv: -kv[1]["us"]):
+    print("| kernel (role) | work-groups | dispatches | avg us | " + " | ".join(f"{n} / dispatch" for n in names)
+          + " |")
+    print("|---|---|---|---|" + "---|" * len(names))
+    for (role, wgs), a in sorted(agg.items(), key=lambda kv: -kv[1]["us"]):
         vals = " | ".join(f"{a['c'].get(n, 0.0) / a['n']:.6g}" for n in names)
-        print(f"| {role} | {a['n']} | {a['us'] / a['n']:.1f} | {vals} |")
+        print(f"| {role} | {wgs} | {a['n']} | {a['us'] / a['n']:.1f} | {vals} |")
 
 
 def main():

@@ -116,8 +116,10 @@ typedef struct ihipStream_t* kvb_stream_t;   /* same type as hipStream_t */
  * by the whole layer; per head with KVB_POL_HEAD_PREFIX; unchecked below
  * capacity with KVB_POL_FILL_BELOW_CAP).  A feasible step admits c, evicting
  * the crossed state, else the densest (ties: lower token) or, with
- * KVB_POL_EVICT_OLDEST, the oldest (KVB_POL_EVICT_DENSEST: the densest);
- * c's baseline is its density at admission.  Outputs: k_star = admitted
+ * KVB_POL_EVICT_OLDEST, the oldest (KVB_POL_EVICT_DENSEST: the densest).
+ * Only growth from later blocks counts against a baseline: the block's
+ * admitted candidates cannot cross during the walk and take their density in
+ * the bank as baseline when it ends.  Outputs: k_star = admitted
  * candidates, n_evicted = evictions during the walk (admitted candidates
  * included), n_mandatory = of them, crossed states; t_cross and rho_proj are
  * not written.  The workspace holds every head's (M + N)^2 pair interactions
@@ -178,7 +180,10 @@ typedef struct kvb_segment {   /* one contiguous run of retained rows of one hea
 
 typedef struct kvb_update_out {   /* device pointers written by kvbank_update */
   int32_t* k_star;        /* [1] shared admitted prefix length; [H] per head with KVB_POL_HEAD_PREFIX */
-  int32_t* n_mandatory;   /* [H] states that crossed tau * rho0 at k* */
+  int32_t* n_mandatory;   /* [H] states that crossed tau * rho0 at k*; -1 when min(N, M) = M and neither
+                             t_cross nor rho_proj is given: every head can then admit k = M (the e(M) = n
+                             evictions cover any crossed set), the whole bank is replaced whatever crossed,
+                             and the crossing scan is skipped */
   int32_t* n_evicted;     /* [H] */
   uint32_t* status;       /* [1] OR of KVB_DEV_* bits (caller zeroes it) */
   kvb_segment* segs;      /* [H][seg_cap] segment table read by chunk_attention */
@@ -251,9 +256,10 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
  * over every slot of the GPU: items (head, 128-query tile) left over after
  * whole rounds are cut along the keys into a main piece and a tail, whose
  * fp32 partials (o, reference, denominator) a second kernel merges.  This is
- * taken only when one work-group per item would leave the last round at
- * least a fifth empty (the size is then 0 otherwise).  ws = NULL runs one
- * work-group per item.  Both give the same result up to rounding.
+ * taken whenever the items do not fill whole rounds (the size is 0 when they
+ * do); the cut is derived on the device from the segment lengths, so heads
+ * of different lengths are balanced too.  ws = NULL runs one work-group per
+ * item.  Both give the same result up to rounding.
  * A too-small non-NULL workspace is KVB_EWORKSPACE.  Calls that share one
  * workspace must not overlap. */
 int chunk_attention(const kvb_attn_desc* A, const void* Q, const kvb_segment* segs, const int32_t* nseg, void* O,
@@ -263,7 +269,7 @@ int chunk_attention(const kvb_attn_desc* A, const void* Q, const kvb_segment* se
  * HIP graph capture, tight serving loops, harnesses that forbid allocation.
  * Same arguments and result as chunk_attention, without the workspace: when
  * the balanced grid is taken (chunk_attention_workspace_size > 0) its
- * partials and flags live in a static device array of the library, 64 MiB
+ * partials and flags live in a static device array of the library, 72 MiB
  * per GPU (enough for every plan on a 256-compute-unit device), kept until
  * the process ends; its address is looked up once per device, on the first
  * call made with that device current.  Nothing is allocated or freed, by the
@@ -271,7 +277,7 @@ int chunk_attention(const kvb_attn_desc* A, const void* Q, const kvb_segment* se
  * written earlier in the same call, so nothing needs clearing.  Calls on one
  * GPU share the array: calls that overlap in time on one GPU (two streams,
  * or two host threads) race and must be serialised by the caller.  A plan
- * needing more than 64 MiB is KVB_EWORKSPACE (nothing is queued). */
+ * needing more than 72 MiB is KVB_EWORKSPACE (nothing is queued). */
 int chunk_attention_noalloc(const kvb_attn_desc* A, const void* Q, const kvb_segment* segs, const int32_t* nseg,
                             void* O, kvb_stream_t stream);
 

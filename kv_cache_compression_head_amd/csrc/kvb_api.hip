@@ -121,8 +121,8 @@ constexpr int MAX_SPLITS = 8;
 
 struct Layout {
   size_t normB, normC, augB, augC, k0, k1, v0, v1, t, cp, hist, rhoP, evict, surv, evl, fixl, nsurv, nfix,
-      fmode, cnt, accS, accAE, accAA, colAA, cos, split, seqP, seqRR, seqTok, seqLog, seqAdm, seqFree, seqAlive,
-      total;
+      fmode, cnt, evsel, evblk, accS, accAE, accAA, colAA, cos, split, seqP, seqRR, seqTok, seqLog, seqAdm, seqFree,
+      seqAlive, total;
   int kmax, cps, ncp;
 };
 
@@ -161,6 +161,8 @@ Layout layout_of(const kvb_layer_desc* L, int32_t N) {
   o.nfix = bump(&off, H * 4);
   o.fmode = bump(&off, H * 4);
   o.cnt = bump(&off, H * 4);
+  o.evsel = bump(&off, H * 32);
+  o.evblk = bump(&off, H * ((M + 255) / 256) * 4);
   o.accS = bump(&off, H * M * 4);
   o.accAE = bump(&off, H * (int64_t)o.kmax * 4);
   o.accAA = bump(&off, H * (int64_t)o.kmax * 4);
@@ -298,7 +300,7 @@ hipError_t run_gram(GramLaunch g, int H, int rows_ub, int cols_ub, float* dst, i
 // ends.  Host code never uses the array's name as an address: the device
 // address comes from hipGetSymbolAddress, once per device, and is kept here.
 // ---------------------------------------------------------------------------
-constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)72 << 20;
 constexpr int NOALLOC_MAX_DEVICES = 64;
 
 }  // namespace
@@ -558,7 +560,13 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
     s.t_out = out->t_cross ? out->t_cross : at<int32_t>(ws, lo.t);
     s.rhoP = out->rho_proj ? out->rho_proj : at<float>(ws, lo.rhoP);
     s.pc = pc; s.phi_mode = pm;
-    HIPCHK(launch_scan(s, false, st));
+    // With min(N, M) = M every density head can admit k = M: e(M) = n covers
+    // any crossed set, so k* = M and the whole bank leaves whatever crossed.
+    // Unless the per-state diagnostics are asked for, the crossing scan, the
+    // prefix search and the rho' pass decide nothing here and are skipped
+    // (n_mandatory is then -1).
+    const bool replace_all = kmax == M && !out->t_cross && !out->rho_proj;
+    if (!replace_all) HIPCHK(launch_scan(s, false, st));
     SelectLaunch sel{};
     sel.H = H; sel.M = M; sel.kmax = kmax; sel.active = hd.dens; sel.count = cnt;
     sel.t = s.t_out; sel.hist = at<int32_t>(ws, lo.hist); sel.kstar = out->k_star; sel.rhoP = s.rhoP;
@@ -569,8 +577,14 @@ int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, c
     sel.evl = at<int32_t>(ws, lo.evl); sel.n_surv = at<int32_t>(ws, lo.nsurv); sel.n_ev = out->n_evicted;
     sel.n_mand = out->n_mandatory; sel.status = out->status;
     sel.fixl = at<int32_t>(ws, lo.fixl); sel.n_fix = at<int32_t>(ws, lo.nfix); sel.fmode = at<int32_t>(ws, lo.fmode);
-    HIPCHK(launch_kstar(sel, st));
-    HIPCHK(launch_scan(s, true, st));
+    sel.evsel = at<void>(ws, lo.evsel); sel.evblk = at<int32_t>(ws, lo.evblk);
+    sel.skip_cross = replace_all ? 1 : 0;
+    if (replace_all) {
+      HIPCHK(launch_fill_i32(out->k_star, ks_hs ? H : 1, kmax, st));
+    } else {
+      HIPCHK(launch_kstar(sel, st));
+      HIPCHK(launch_scan(s, true, st));
+    }
     HIPCHK(launch_evict(sel, st));
     // density fix-ups: survivors x evicted, admitted x evicted, admitted x admitted
     GramLaunch g{};

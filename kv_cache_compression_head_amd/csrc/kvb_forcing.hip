@@ -12,7 +12,6 @@
 
 namespace kvb {
 
-constexpr int COS_MAXC = 16;   // 16-byte chunks per lane (<= 64 heads x 16 chunks)
 
 struct CosArgs {
   const void* hist; const void* nxt;
@@ -21,50 +20,75 @@ struct CosArgs {
   float* cosbuf;
 };
 
-// one wave per token position p: walks frames 0..T, keeping the previous
-// frame's chunks in registers
-template <typename E>
+// One wave per token position p walks frames 0..T.  The wave's lanes hold
+// the token's features over the dynamic heads as 16-byte chunks (chunk
+// lane + 64 k, k < KC); U frames are loaded at once before any of them is
+// reduced, so every wave keeps U x KC loads in flight (the kernel is bound
+// by HBM, not by the reductions).
+template <typename E, int KC>
 __global__ __launch_bounds__(256) void cos_kernel(CosArgs a) {
   constexpr int EPC = 16 / sizeof(E);
+  constexpr int U = KC >= 8 ? 1 : 8 / KC;   // frames per batch of loads
   const int lane = lane_id();
   const int p = blockIdx.x * 4 + wave_id();
   if (p >= a.F) return;
   const int cpr = a.d / EPC;
   const int nch = a.ndyn * cpr;
-  u32x4_t prev[COS_MAXC];
+  // element offsets of this lane's chunks: frame 0 of the history, and the
+  // first row of the next chunk
+  int64_t hoff[KC], noff[KC];
+  bool ok[KC];
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    const int c = lane + 64 * k;
+    ok[k] = c < nch;
+    const int hd = ok[k] ? a.dyn_heads[c / cpr] : 0;
+    const int cc = ok[k] ? c % cpr : 0;
+    hoff[k] = ((int64_t)hd * a.T * a.F + p) * a.d + cc * EPC;
+    noff[k] = ((int64_t)hd * a.nxt_rows + p) * a.d + cc * EPC;
+  }
+  const int64_t fstride = (int64_t)a.F * a.d;
+  u32x4_t prev[KC];
   float nprev = 0.f;
-  for (int t = 0; t <= a.T; ++t) {
-    float nn = 0.f, dot = 0.f;
+  for (int t0 = 0; t0 <= a.T; t0 += U) {
+    u32x4_t cur[U][KC];
 #pragma unroll
-    for (int k = 0; k < COS_MAXC; ++k) {
-      const int c = lane + 64 * k;
-      if (64 * k >= nch) break;
-      u32x4_t cur = {0u, 0u, 0u, 0u};
-      if (c < nch) {
-        const int hd = a.dyn_heads[c / cpr];
-        const int cc = c % cpr;
-        const E* base;
-        if (t < a.T) base = (const E*)a.hist + (((int64_t)hd * a.T * a.F) + (int64_t)t * a.F + p) * a.d;
-        else base = (const E*)a.nxt + ((int64_t)hd * a.nxt_rows + p) * a.d;
-        cur = *reinterpret_cast<const u32x4_t*>(base + cc * EPC);
-      }
-      const E* e = reinterpret_cast<const E*>(&cur);
-      const E* f = reinterpret_cast<const E*>(&prev[k]);
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u;
 #pragma unroll
-      for (int j = 0; j < EPC; ++j) {
-        const float x = Ops<E>::to_f32(e[j]);
-        nn = __builtin_fmaf(x, x, nn);
-        if (t > 0) dot = __builtin_fmaf(x, Ops<E>::to_f32(f[j]), dot);
+      for (int k = 0; k < KC; ++k) {
+        cur[u][k] = u32x4_t{0u, 0u, 0u, 0u};
+        if (ok[k] && t <= a.T) {
+          const E* src = t < a.T ? (const E*)a.hist + hoff[k] + t * fstride : (const E*)a.nxt + noff[k];
+          cur[u][k] = *reinterpret_cast<const u32x4_t*>(src);
+        }
       }
-      prev[k] = cur;
     }
-    nn = wave_sum(nn);
-    if (t > 0) {
-      dot = wave_sum(dot);
-      const float den = fmaxf(sqrtf(nprev) * sqrtf(nn), 1e-8f);
-      if (lane == 0) a.cosbuf[(int64_t)(t - 1) * a.F + p] = dot / den;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u;
+      if (t > a.T) break;
+      float nn = 0.f, dot = 0.f;
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        const E* e = reinterpret_cast<const E*>(&cur[u][k]);
+        const E* f = reinterpret_cast<const E*>(&prev[k]);
+#pragma unroll
+        for (int j = 0; j < EPC; ++j) {
+          const float x = Ops<E>::to_f32(e[j]);
+          nn = __builtin_fmaf(x, x, nn);
+          if (t > 0) dot = __builtin_fmaf(x, Ops<E>::to_f32(f[j]), dot);
+        }
+        prev[k] = cur[u][k];
+      }
+      nn = wave_sum(nn);
+      if (t > 0) {
+        dot = wave_sum(dot);
+        const float den = fmaxf(sqrtf(nprev) * sqrtf(nn), 1e-8f);
+        if (lane == 0) a.cosbuf[(int64_t)(t - 1) * a.F + p] = dot / den;
+      }
+      nprev = nn;
     }
-    nprev = nn;
   }
 }
 
@@ -95,8 +119,20 @@ hipError_t launch_segment_cosine(const CosLaunch& c, hipStream_t st) {
   for (int i = 0; i < 64; ++i) a.dyn_heads[i] = c.dyn_heads[i];
   a.cosbuf = c.cosbuf;
   const dim3 grid((unsigned)((c.F + 3) / 4));
-  if (c.et == ET_BF16) hipLaunchKernelGGL(cos_kernel<uint16_t>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(cos_kernel<float>, grid, dim3(256), 0, st, a);
+  const int cpr = c.d * (c.et == ET_BF16 ? 2 : 4) / 16;
+  const int kc = (c.ndyn * cpr + 63) / 64;   // <= 16 (checked on the host)
+#define KVB_COS(E)                                                                                 \
+  if (kc <= 1) hipLaunchKernelGGL((cos_kernel<E, 1>), grid, dim3(256), 0, st, a);                  \
+  else if (kc <= 2) hipLaunchKernelGGL((cos_kernel<E, 2>), grid, dim3(256), 0, st, a);             \
+  else if (kc <= 4) hipLaunchKernelGGL((cos_kernel<E, 4>), grid, dim3(256), 0, st, a);             \
+  else if (kc <= 8) hipLaunchKernelGGL((cos_kernel<E, 8>), grid, dim3(256), 0, st, a);             \
+  else hipLaunchKernelGGL((cos_kernel<E, 16>), grid, dim3(256), 0, st, a);
+  if (c.et == ET_BF16) {
+    KVB_COS(uint16_t)
+  } else {
+    KVB_COS(float)
+  }
+#undef KVB_COS
   const int items = c.T * (c.F / c.seg_len);
   hipLaunchKernelGGL(segmean_kernel, dim3(items), dim3(256), 0, st, c.cosbuf, c.F, c.seg_len, c.ndyn, a, c.scores,
                      c.score_hstride);

@@ -155,6 +155,9 @@ struct SelectLaunch {
   int32_t* fixl;             // [H][M] column list of the admitted-state fix-up
   int32_t* n_fix;            // [H]
   int32_t* fmode;            // [H] 1: fixl = survivors (direct sum), 0: fixl = evicted (subtract)
+  int32_t skip_cross;        // 1: no crossing scan ran (k* = M replaces the whole bank); n_mand = -1
+  void* evsel;               // [H] per-head eviction plan (32 bytes each), scratch
+  int32_t* evblk;            // [H][ceil(M / 256)] per-block evicted / surviving counts, scratch
 };
 hipError_t launch_kstar(const SelectLaunch& a, hipStream_t s);
 hipError_t launch_evict(const SelectLaunch& a, hipStream_t s);

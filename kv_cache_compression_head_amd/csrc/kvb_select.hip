@@ -354,7 +354,35 @@ KVB_DEV uint64_t evict_key(float rp, int32_t tok, bool oldest) {
   return oldest ? t : (((uint64_t)float_key(rp) << 32) | t);
 }
 
-__global__ __launch_bounds__(1024) void evict_kernel(SelectLaunch a) {
+// Eviction in three launches, so that the per-state passes run on many
+// work-groups per head:
+//   evict_select_kernel  (one block per head) the counts, and the threshold
+//                        key of the r-th largest key when a partial
+//                        completion is needed (8-bit MSB-first radix select);
+//                        the crossed count at k* is read from the crossing-
+//                        time prefix sums, so the common cases pass over no
+//                        state at all
+//   evict_flags_kernel   (256 states per block) the eviction flag of every
+//                        slot and each block's evicted / surviving counts
+//   evict_write_kernel   (256 states per block) the block's offset from the
+//                        counts before it, then ballot compaction of the
+//                        evicted and surviving slots in ascending slot order
+struct EvSel {        // per head, written by evict_select_kernel
+  uint64_t thr;       // completion threshold: keys >= thr are evicted
+  int32_t n, e, r, nm, nm_crossed, mode;   // mode: 0 no completion, 1 all non-crossed, 2 keys >= thr
+};
+static_assert(sizeof(EvSel) <= 32, "per-head eviction plan slot");
+
+KVB_DEV bool evict_flag(const SelectLaunch& a, const EvSel& q, int64_t hb, int b, int ks) {
+  const bool gated = ks > 0 && !(a.fill && q.n + ks <= a.M) && !a.skip_cross;
+  const bool force = a.evict_mode != 1;
+  if (force && gated && a.t[hb + b] <= ks) return true;
+  if (q.mode == 1) return true;
+  if (q.mode == 2) return evict_key(a.rhoP[hb + b], a.bank_tok[hb + b], a.evict_mode == 2) >= q.thr;
+  return false;
+}
+
+__global__ __launch_bounds__(1024) void evict_select_kernel(SelectLaunch a) {
   const int h = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -369,39 +397,32 @@ __global__ __launch_bounds__(1024) void evict_kernel(SelectLaunch a) {
   const bool gated = ks > 0 && !(a.fill && n + ks <= M);
   const bool oldest = a.evict_mode == 2;
   const bool force = a.evict_mode != 1;
-  __shared__ int hist[256];
-  __shared__ int s_nm;
-  __shared__ uint64_t s_prefix, s_mask;
-  __shared__ int s_rem;
-  __shared__ int wsum[16];
-  __shared__ int s_base_e, s_base_s;
-  if (tid == 0) { s_nm = 0; s_prefix = 0; s_mask = 0; s_base_e = 0; s_base_s = 0; }
-  __syncthreads();
-  int nm_local = 0;
-  for (int b = tid; b < n; b += 1024) nm_local += (gated && a.t[hb + b] <= ks) ? 1 : 0;
-  atomicAdd(&s_nm, nm_local);
-  __syncthreads();
-  const int nm_crossed = s_nm;
-  const int nm = force ? nm_crossed : 0;   // forced evictions
+  // |V_h(k*)| from the prefix sums of the crossing-time histogram (not
+  // computed when the whole bank is replaced without a crossing scan)
+  const int nm_crossed = a.skip_cross ? -1 : (gated ? a.hist[(int64_t)h * (a.kmax + 2) + ks] : 0);
+  const int nm = (force && !a.skip_cross) ? nm_crossed : 0;
   int r = e - nm;
   if (r < 0) {
     if (tid == 0) atomicOr(a.status, DEV_EVICT);
     r = 0;
   }
-  if (tid == 0) s_rem = r;
-  __syncthreads();
-  // radix select of the r-th largest key among non-crossed states; none to
-  // pick (r = 0) or all of them (r = n - nm) need no select
-  if (r > 0 && r < n - nm) {
-    __shared__ int wsc[4];
-    __shared__ int s_sel;
+  // none to pick (r = 0) or all of them (r = n - nm): no select
+  const int mode = r == 0 ? 0 : (r >= n - nm ? 1 : 2);
+  __shared__ int hist[256];
+  __shared__ uint64_t s_prefix, s_mask;
+  __shared__ int s_rem;
+  __shared__ int wsc[4];
+  __shared__ int s_sel;
+  if (mode == 2) {
+    if (tid == 0) { s_prefix = 0; s_mask = 0; s_rem = r; }
+    __syncthreads();
     for (int pass = 0; pass < 8; ++pass) {
       const int shift = 56 - 8 * pass;
       for (int i = tid; i < 256; i += 1024) hist[i] = 0;
       __syncthreads();
       const uint64_t pre = s_prefix, msk = s_mask;
       for (int b = tid; b < n; b += 1024) {
-        if (force && gated && a.t[hb + b] <= ks) continue;
+        if (force && gated && !a.skip_cross && a.t[hb + b] <= ks) continue;
         const uint64_t key = evict_key(a.rhoP[hb + b], a.bank_tok[hb + b], oldest);
         if ((key & msk) == pre) atomicAdd(&hist[(key >> shift) & 0xFF], 1);
       }
@@ -436,59 +457,100 @@ __global__ __launch_bounds__(1024) void evict_kernel(SelectLaunch a) {
       __syncthreads();
     }
   }
-  // keys >= thr are evicted among the non-crossed states (all of them when
-  // r covers every such state)
-  const uint64_t thr = (r >= n - nm) ? 0ull : s_prefix;
-  // admitted states' densities: sum over the survivors directly when they are
-  // fewer than the evicted states, else D(c) minus the evicted interactions
-  const bool direct = (n - e) < e;
-  // compaction in ascending slot order
-  for (int base = 0; base < n; base += 1024) {
-    const int b = base + tid;
-    bool ev = false, live = b < n;
-    if (live) {
-      const bool mand = force && gated && a.t[hb + b] <= ks;
-      ev = mand || (r > 0 && evict_key(a.rhoP[hb + b], a.bank_tok[hb + b], oldest) >= thr);
-      a.evict[hb + b] = ev ? 1 : 0;
-    }
-    const uint64_t be = __ballot(live && ev);
-    const uint64_t bs = __ballot(live && !ev);
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int pe = __popcll(be & lt), ps = __popcll(bs & lt);
-    if (lane == 0) wsum[w] = (__popcll(be) << 16) | __popcll(bs);
-    __syncthreads();
-    int oe = 0, os = 0;
-    for (int j = 0; j < w; ++j) { oe += wsum[j] >> 16; os += wsum[j] & 0xFFFF; }
-    const int be0 = s_base_e, bs0 = s_base_s;
-    if (live && ev) {
-      a.evl[hb + be0 + oe + pe] = b;
-      if (!direct) a.fixl[hb + be0 + oe + pe] = b;
-    }
-    if (live && !ev) {
-      a.surv[hb + bs0 + os + ps] = b;
-      if (direct) a.fixl[hb + bs0 + os + ps] = b;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int te = 0, ts = 0;
-      for (int j = 0; j < 16; ++j) { te += wsum[j] >> 16; ts += wsum[j] & 0xFFFF; }
-      s_base_e += te; s_base_s += ts;
-    }
-    __syncthreads();
-  }
-  for (int b = n + tid; b < M; b += 1024) a.evict[hb + b] = 0;
   if (tid == 0) {
-    a.n_ev[h] = s_base_e;
-    a.n_surv[h] = s_base_s;
-    a.n_mand[h] = nm_crossed;
-    a.n_fix[h] = direct ? s_base_s : s_base_e;
-    a.fmode[h] = direct ? 1 : 0;
-    if (s_base_e != e) atomicOr(a.status, DEV_EVICT);
+    EvSel q;
+    q.thr = mode == 2 ? s_prefix : 0ull;
+    q.n = n; q.e = e; q.r = r; q.nm = nm; q.nm_crossed = nm_crossed; q.mode = mode;
+    reinterpret_cast<EvSel*>(a.evsel)[h] = q;
+  }
+}
+
+__global__ __launch_bounds__(256) void evict_flags_kernel(SelectLaunch a) {
+  const int h = blockIdx.y;
+  if (!head_on(a.active, h)) return;
+  const int64_t hb = (int64_t)h * a.M;
+  const EvSel q = reinterpret_cast<const EvSel*>(a.evsel)[h];
+  const int ks = a.kstar[h * a.kstar_hs];
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  const bool live = b < q.n;
+  const bool ev = live && evict_flag(a, q, hb, b, ks);
+  if (b < a.M) a.evict[hb + b] = ev ? 1 : 0;
+  __shared__ int cnt[2];
+  if (threadIdx.x == 0) { cnt[0] = 0; cnt[1] = 0; }
+  __syncthreads();
+  const uint64_t be = __ballot(ev), bs = __ballot(live && !ev);
+  if (lane_id() == 0) {
+    atomicAdd(&cnt[0], __popcll(be));
+    atomicAdd(&cnt[1], __popcll(bs));
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) a.evblk[(int64_t)h * gridDim.x + blockIdx.x] = (cnt[0] << 16) | cnt[1];
+}
+
+__global__ __launch_bounds__(256) void evict_write_kernel(SelectLaunch a) {
+  const int h = blockIdx.y;
+  if (!head_on(a.active, h)) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t hb = (int64_t)h * a.M;
+  const EvSel q = reinterpret_cast<const EvSel*>(a.evsel)[h];
+  const int nblk = gridDim.x, blk = blockIdx.x;
+  const int32_t* bc = a.evblk + (int64_t)h * nblk;
+  const bool direct = (q.n - q.e) < q.e;
+  // offsets of this block: the counts of the blocks before it; the last
+  // block also writes the totals
+  __shared__ int s_oe, s_os, s_we[4], s_ws[4];
+  if (w == 0) {
+    int oe = 0, os = 0, te = 0, ts = 0;
+    for (int i = lane; i < nblk; i += 64) {
+      const int v = bc[i];
+      if (i < blk) { oe += v >> 16; os += v & 0xFFFF; }
+      te += v >> 16;
+      ts += v & 0xFFFF;
+    }
+    oe = wave_sum_i(oe);
+    os = wave_sum_i(os);
+    te = wave_sum_i(te);
+    ts = wave_sum_i(ts);
+    if (lane == 0) {
+      s_oe = oe;
+      s_os = os;
+      if (blk == nblk - 1) {
+        a.n_ev[h] = te;
+        a.n_surv[h] = ts;
+        a.n_mand[h] = q.nm_crossed;
+        a.n_fix[h] = direct ? ts : te;
+        a.fmode[h] = direct ? 1 : 0;
+        if (te != q.e) atomicOr(a.status, DEV_EVICT);
+      }
+    }
+  }
+  const int b = blk * 256 + tid;
+  const bool live = b < q.n;
+  const bool ev = live && a.evict[hb + b];
+  const uint64_t be = __ballot(ev), bs = __ballot(live && !ev);
+  if (lane == 0) { s_we[w] = __popcll(be); s_ws[w] = __popcll(bs); }
+  __syncthreads();
+  int oe = s_oe, os = s_os;
+  for (int k = 0; k < w; ++k) { oe += s_we[k]; os += s_ws[k]; }
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  if (ev) {
+    const int j = oe + __popcll(be & lt);
+    a.evl[hb + j] = b;
+    if (!direct) a.fixl[hb + j] = b;
+  }
+  if (live && !ev) {
+    const int j = os + __popcll(bs & lt);
+    a.surv[hb + j] = b;
+    if (direct) a.fixl[hb + j] = b;
   }
 }
 
 hipError_t launch_evict(const SelectLaunch& a, hipStream_t st) {
-  hipLaunchKernelGGL(evict_kernel, dim3(a.H), dim3(1024), 0, st, a);
+  hipLaunchKernelGGL(evict_select_kernel, dim3(a.H), dim3(1024), 0, st, a);
+  const unsigned nblk = (unsigned)((a.M + 255) / 256);
+  if (nblk == 0) return hipGetLastError();
+  hipLaunchKernelGGL(evict_flags_kernel, dim3(nblk, a.H), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(evict_write_kernel, dim3(nblk, a.H), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

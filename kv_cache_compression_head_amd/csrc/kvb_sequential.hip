@@ -10,8 +10,11 @@
 // method's prefix is shared by the heads (per head with KVB_POL_HEAD_PREFIX).
 // A feasible step admits c everywhere: the crossed state, else the densest
 // (ties: lower token id) or the oldest, leaves when e = 1; survivors take
-// rho'_x - phi(x, y) for the evicted y; c takes rho0 = rho = its density among
-// the states left.  An infeasible step changes nothing.
+// rho'_x - phi(x, y) for the evicted y; c enters with its density among the
+// states left.  Only growth from later blocks counts against a baseline, so
+// the block's candidates have none until the block ends (they never cross)
+// and then take their density in the bank.  An infeasible step changes
+// nothing.
 //
 // Three kernels:
 //   pair_phi_kernel  every head's pairwise interactions over its M + N states
@@ -212,7 +215,8 @@ __global__ __launch_bounds__(1024) void seq_walk_kernel(SeqLaunch a) {
         const int c = cx[q] - a.M;
         const float rc = y >= 0 ? Sc[q] - Pc[y] : Sc[q];
         if (y >= 0) st_tok(tk + y, -1);
-        st_rr(rr + cx[q], rc, rc);
+        // no baseline until the block ends: +inf never crosses
+        st_rr(rr + cx[q], rc, __builtin_inff());
         st_tok(tk + cx[q], a.cand_tok[c]);
         a.log[(int64_t)h * a.N + n_adm[q]] = c;
       }
@@ -346,9 +350,11 @@ __global__ __launch_bounds__(1024) void seq_gather_kernel(SeqGather g) {
     }
     *reinterpret_cast<u32x4_t*>(dst + chunk * 16) = *reinterpret_cast<const u32x4_t*>(src + chunk * 16);
     if (part == 0) {
+      // the block's candidates take their baselines together: their density
+      // in the bank at the end of the walk
       const uint64_t v = ld_rr(rr + M + c);
       g.rho[hb + slot] = __uint_as_float((uint32_t)v);
-      g.rho0[hb + slot] = g.refresh ? __uint_as_float((uint32_t)v) : __uint_as_float((uint32_t)(v >> 32));
+      g.rho0[hb + slot] = __uint_as_float((uint32_t)v);
       g.bank_tok[hb + slot] = g.cand_tok[c];
     }
   }

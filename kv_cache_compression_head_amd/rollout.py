@@ -100,6 +100,28 @@ class Rollout:
             self.L.append(_Layer(wl, l, seed, lc, source, self.kdt))
         self.c = 0
         self._prepared = None
+        # host streams: the next chunk's frames are drawn in worker threads
+        # (one per layer) while the current chunk runs
+        self._pool = None
+        self._next = None
+        if source == "host":
+            import concurrent.futures as cf
+            self._pool = cf.ThreadPoolExecutor(max_workers=max(1, len(self.L)))
+
+    def _draw(self, x: "_Layer", frames: range):
+        return [x.stream.frame(f) for f in frames]
+
+    def _draw_all(self, c: int):
+        p = plan(c, self.wl.chunk_frames, self.wl.window_frames)
+        if self._next is not None and self._next[0] == c:
+            futs = self._next[1]
+        else:
+            futs = [self._pool.submit(self._draw, x, p.frames) for x in self.L]
+        self._next = None
+        out = [f.result() for f in futs]
+        pn = plan(c + 1, self.wl.chunk_frames, self.wl.window_frames)
+        self._next = (c + 1, [self._pool.submit(self._draw, x, pn.frames) for x in self.L])
+        return out
 
     @property
     def caches(self) -> List[LayerCache]:
@@ -117,11 +139,12 @@ class Rollout:
         queries at temporal coordinate = frame index, [H][3F][d] on the device."""
         p = plan(self.c, self.wl.chunk_frames, self.wl.window_frames)
         keep = self.wl.window_frames + self.wl.chunk_frames
+        drawn = self._draw_all(self.c) if self.source == "host" else None
         out = []
-        for x in self.L:
+        for li, x in enumerate(self.L):
             ks, vs, qs = [], [], []
-            for f in p.frames:
-                k, v, q = x.stream.frame(f)
+            for fi, f in enumerate(p.frames):
+                k, v, q = drawn[li][fi] if drawn is not None else x.stream.frame(f)
                 if self.source == "host":
                     x.recent[f] = (k, v, q)
                     for old in [g for g in x.recent if 0 < g < f - keep + 1]:   # frame 0 is the sink

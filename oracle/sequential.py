@@ -23,15 +23,23 @@ Density-Constrained Bank Update"; appendix B.1, "Online Bank Update"):
   fill-below-capacity variant a step with n + 1 <= M is feasible unchecked
 * a feasible step admits c in every head: the eviction set is the crossed
   states, then the highest rho' (ties: lower token id) up to e (or the
-  densest-only / oldest-first variants); survivors take
-  rho_x = rho'_x - sum over the evicted y of phi(x, y); c takes the baseline
-  rho0_c = rho_c = its density among the states live after the eviction
+  densest-only / oldest-first variants), over every live state; survivors
+  take rho_x = rho'_x - sum over the evicted y of phi(x, y); c enters with
+  its density among the states live after the eviction
+* baselines: the page's update rule lets only growth from later blocks count
+  against a baseline, and co-admitted candidates set theirs together.  So a
+  candidate admitted during the block has no baseline until the block ends
+  (it cannot cross, though it adds density and takes capacity, and can be
+  evicted as the densest); at the end every candidate of the block still in
+  the bank takes rho0 = its density in the bank
 * an infeasible step rejects c in every head and changes nothing
 * after the last step, the refresh-baseline variant sets every live state's
   baseline to its density
 
-A candidate admitted at one step can be evicted at a later one.  With one
-candidate per block the walk is the method's prefix rule for k <= 1.
+A candidate admitted at one step can be evicted at a later one.  From an
+empty bank every candidate of the first block is admitted, as with the
+prefix method.  With one candidate per block the walk is the method's rule
+for k <= 1.
 
 Descriptors: the density is computed on descriptor rows X (post-RoPE keys by
 default; pre-RoPE keys or [K; V] in the appendix E descriptor ablation),
@@ -145,11 +153,12 @@ def update_layer_sequential(banks: List[Optional[HeadBank]], candK, candV, cand_
             live[y] = False
         for y in ev:
             rho[live] -= s["P"][y][live]
-        # the candidate's baseline: its density among the states now live
+        # the candidate's density among the states now live; its baseline is
+        # set when the block ends
         rc = float(s["P"][c][live].sum())
         live[c] = True
         rho[c] = rc
-        s["rho0"][c] = rc
+        s["rho0"][c] = math.inf
         s["n"] += 1 - len(ev)
         info.admitted_h[h].append(j)
         info.evicted_h[h].extend(int(s["tok"][y]) for y in ev)
@@ -176,7 +185,8 @@ def update_layer_sequential(banks: List[Optional[HeadBank]], candK, candV, cand_
         V2 = np.concatenate([b.V[keep], np.asarray(candV[h], np.float64)[idx_c]])
         X2 = np.concatenate([b.X[keep], np.asarray(candX[h], np.float64)[idx_c]])
         tok2 = np.concatenate([b.tok[keep], tok_c[idx_c]])
-        rho0 = np.concatenate([s["rho0"][:n0][keep], s["rho0"][adm]])
+        # the block's candidates take their baselines together, at the end
+        rho0 = np.concatenate([s["rho0"][:n0][keep], s["rho"][adm]])
         if prm.baseline == "refresh":
             rho0 = np.concatenate([s["rho"][:n0][keep], s["rho"][adm]])
         new[h] = HeadBank(tok2, K2, V2, rho0, None if b.Xd is None and candX is candK else X2)
@@ -246,11 +256,9 @@ def update_layer_sequential_brute(banks: List[Optional[HeadBank]], candK, candV,
             rest.sort(key=lambda i: (-proj[i], live[i][0]))
         ev += rest[: e - len(ev)]
         kept = [live[i] for i in range(n) if i not in ev]
-        Xk = np.array([s[3] for s in kept] + [np.asarray(candX[h][c], np.float64)]) if kept else \
-            np.asarray(candX[h][c], np.float64)[None]
-        rc = float(_density_direct(Xk, prm)[-1])
+        # no baseline until the block ends (inf: never crosses)
         kept.append((int(tok_c[c]), np.asarray(candK[h][c], np.float64), np.asarray(candV[h][c], np.float64),
-                     np.asarray(candX[h][c], np.float64), rc))
+                     np.asarray(candX[h][c], np.float64), math.inf))
         cur[h] = kept
 
     for j in range(N):
@@ -274,7 +282,10 @@ def update_layer_sequential_brute(banks: List[Optional[HeadBank]], candK, candV,
         V2 = np.array([s[2] for s in live]).reshape(-1, d)
         X2 = np.array([s[3] for s in live]).reshape(-1, dx)
         rho0 = np.array([s[4] for s in live])
+        dens = _density_direct(X2, prm)
+        # this block's candidates take their densities in the final bank
+        rho0 = np.where(np.isinf(rho0), dens, rho0)
         if prm.baseline == "refresh":
-            rho0 = _density_direct(X2, prm)
+            rho0 = dens
         new[h] = HeadBank(tok2, K2, V2, rho0, X2)
     return new, adm, orders

@@ -209,3 +209,44 @@ def test_tiny_source_order_oldest_is_a_window():
     last = wl.bank_updates[-1][1] * wl.F
     for h in range(wl.H):
         assert sorted(bank.tok[h, :bank.count[h]].tolist()) == list(range(last - 64, last))
+
+
+def _replace_all_pair(wl, prm, seed=0):
+    """The same stream through two layers: one asks for the per-state
+    diagnostics (crossing scan), the other does not, so that its updates with
+    min(N, M) = M take the path without the scan.  Returns both layers."""
+    import torch
+    import kv_cache_compression_head_amd as kb
+    gen = LayerGen(wl, seed, 0)
+    a = gc.layer_for(wl, prm, diagnostics=True)
+    b = gc.layer_for(wl, prm, diagnostics=False)
+    kdt = gc.kv_dtype(wl)
+    for (t0, t1) in wl.bank_updates:
+        cK, cV = gc.dev(gen.keys_all(range(t0, t1)), kdt), gc.dev(gen.values_all(range(t0, t1)), kdt)
+        ct = gc.dev_i32(frame_tokens(wl, t0, t1))
+        for lc in (a, b):
+            lc.out.status.zero_()
+            D, s, o = lc.score(cK, ct, kb.KVLayout())
+            lc.update(cK, cV, ct, D, o, kb.KVLayout())
+        torch.cuda.synchronize()
+        assert int(a.out.status.cpu()[0]) == 0 and int(b.out.status.cpu()[0]) == 0
+        N = cK.shape[1]
+        if N >= prm.M:
+            assert b.out.n_mandatory.cpu().tolist() == [-1] * wl.H
+        for x, y in ((a.bank.K, b.bank.K), (a.bank.V, b.bank.V), (a.bank.tok, b.bank.tok),
+                     (a.bank.rho0, b.bank.rho0), (a.bank.rho, b.bank.rho), (a.bank.count, b.bank.count),
+                     (a.out.k_star, b.out.k_star), (a.out.n_evicted, b.out.n_evicted)):
+            assert torch.equal(x, y), "the path without the crossing scan differs"
+    return a, b
+
+
+@pytest.mark.parametrize("tau", [2.0, 1.05])
+def test_tiny_whole_bank_replaced_without_scan(tau):
+    """Blocks of 48 candidates into a bank of 40: k* = M and every state
+    leaves, whatever crossed; the path without the crossing scan gives the
+    same bank bit for bit, and the diagnostics path replays against the
+    oracle."""
+    wl = WORKLOADS["tiny"]
+    prm = _prm(wl, M=40, tau=tau)
+    _stream(wl, prm, attn=False)
+    _replace_all_pair(wl, prm)

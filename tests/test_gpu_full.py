@@ -87,6 +87,33 @@ def test_480p_layer_chunk():
     assert rep.kstar > 0
 
 
+def test_480p_whole_bank_replaced_without_scan():
+    """The 480P layer-chunk (N = 23,400 > M) without per-state diagnostics
+    takes the path without the crossing scan (every state leaves at k* = M
+    whatever crossed): the same bank, bit for bit, as with the scan."""
+    import torch
+    import kv_cache_compression_head_amd as kb
+    wl = WORKLOADS["480p"]
+    prm = od.Params(M=wl.M, tau=wl.tau, sigma=wl.sigma, eps=wl.eps, p=wl.p)
+    gen = LayerGen(wl, 0, 0)
+    kdt = gc.kv_dtype(wl)
+    a = gc.layer_for(wl, prm, diagnostics=True)
+    b = gc.layer_for(wl, prm, diagnostics=False)
+    for (t0, t1) in wl.bank_updates:
+        gc.banner(f"480p whole-bank replacement: frames {t0}..{t1}")
+        cK, cV = gc.dev(gen.keys_all(range(t0, t1)), kdt), gc.dev(gen.values_all(range(t0, t1)), kdt)
+        ct = gc.dev_i32(frame_tokens(wl, t0, t1))
+        for lc in (a, b):
+            D, s, o = lc.score(cK, ct, kb.KVLayout())
+            lc.update(cK, cV, ct, D, o, kb.KVLayout())
+        torch.cuda.synchronize()
+    assert b.out.n_mandatory.cpu().tolist() == [-1] * wl.H
+    assert int(a.out.k_star.cpu()[0]) == wl.M
+    for x, y in ((a.bank.K, b.bank.K), (a.bank.V, b.bank.V), (a.bank.tok, b.bank.tok), (a.bank.rho0, b.bank.rho0),
+                 (a.bank.rho, b.bank.rho), (a.bank.count, b.bank.count)):
+        assert torch.equal(x, y)
+
+
 @pytest.mark.timeout(600)
 def test_480p_partial_eviction():
     """N = 4,680 candidates (three frames) offered to a full bank of 9,360:

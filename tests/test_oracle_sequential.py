@@ -46,13 +46,17 @@ def test_golden_sequential_example():
     np.testing.assert_allclose(nb.rho0, [float(Fraction(s["final_rho0"][str(t)])) for t in nb.tok], rtol=1e-13)
     np.testing.assert_allclose(od.density(nb.K, prm), [float(Fraction(s["final_density"][str(t)])) for t in nb.tok],
                                rtol=1e-13)
-    # the prefix method on the same block admits all three together
+    # the prefix method on the same block stops before the rejected candidate
     newp, infop = od.update_layer([bank], cK, cK, ctok, prm)
     assert infop.kstar == g["prefix_method"]["kstar"]
-    assert sorted(newp[0].tok.tolist()) == g["prefix_method"]["final_tok"]
+    nbp = newp[0].sorted_by_tok()
+    assert nbp.tok.tolist() == g["prefix_method"]["final_tok"]
+    assert nbp.rho0[-1] == pytest.approx(float(Fraction(g["prefix_method"]["rho0_10"])), rel=1e-13)
     # the brute tier agrees
     newb, adm, _ = oseq.update_layer_sequential_brute([bank], cK, cK, ctok, prm)
-    assert sorted(newb[0].tok.tolist()) == s["final_tok"]
+    nbb = newb[0].sorted_by_tok()
+    assert nbb.tok.tolist() == s["final_tok"]
+    np.testing.assert_allclose(nbb.rho0, [float(Fraction(s["final_rho0"][str(t)])) for t in nbb.tok], rtol=1e-13)
 
 
 def _random_layer(rng, M, heads=2, d=6):
@@ -123,6 +127,26 @@ def test_fifo_window_at_p0_tau_inf():
         seen += sorted(ctok.tolist())
         for h in range(wl.H):
             assert sorted(banks[h].tok.tolist()) == sorted(seen[-prm.M:])
+
+
+def test_empty_bank_admits_the_whole_first_block():
+    """From an empty bank nothing can cross (the block's candidates take their
+    baselines at the end), so the first block is admitted whole, as with the
+    prefix method."""
+    wl = WORKLOADS["tiny"]
+    gen = LayerGen(wl, 2, 0)
+    prm = od.Params(M=64, tau=2.0)
+    t0, t1 = wl.bank_updates[0]
+    ctok = frame_tokens(wl, t0, t1)
+    cK = gen.keys_all(range(t0, t1)).astype(np.float64)
+    empty = [od.HeadBank.empty(wl.d) for _ in range(wl.H)]
+    a, info = oseq.update_layer_sequential(empty, cK, cK, ctok, prm)
+    b, _ = od.update_layer(empty, cK, cK, ctok, prm)
+    for h in range(wl.H):
+        assert len(info.admitted_h[h]) == len(ctok)
+        x, y = a[h].sorted_by_tok(), b[h].sorted_by_tok()
+        assert x.tok.tolist() == y.tok.tolist()
+        np.testing.assert_allclose(x.rho0, y.rho0, rtol=1e-12)
 
 
 def test_growth_invariant_and_capacity_after_every_block():
