@@ -20,18 +20,22 @@ struct CosArgs {
   float* cosbuf;
 };
 
-// One wave per token position p walks frames 0..T.  The wave's lanes hold
-// the token's features over the dynamic heads as 16-byte chunks (chunk
-// lane + 64 k, k < KC); U frames are loaded at once before any of them is
-// reduced, so every wave keeps U x KC loads in flight (the kernel is bound
-// by HBM, not by the reductions).
+// One wave per (token position p, group of U cosines).  The wave's lanes
+// hold the token's features over the dynamic heads as 16-byte chunks (chunk
+// lane + 64 k, k < KC).  Group g computes the cosines of frame pairs
+// (t, t + 1) for t in [g U, g U + U): it loads its U + 1 frames at once
+// (one frame shared with the next group) before reducing any of them, so
+// every wave keeps (U + 1) KC loads in flight and the token's frames are
+// spread over several waves; the kernel is bound by HBM, not by the
+// reductions.
 template <typename E, int KC>
 __global__ __launch_bounds__(256) void cos_kernel(CosArgs a) {
   constexpr int EPC = 16 / sizeof(E);
-  constexpr int U = KC >= 8 ? 1 : 8 / KC;   // frames per batch of loads
+  constexpr int U = KC >= 16 ? 1 : 16 / KC;   // cosines per wave
   const int lane = lane_id();
   const int p = blockIdx.x * 4 + wave_id();
   if (p >= a.F) return;
+  const int t0 = blockIdx.y * U;              // first frame of the group
   const int cpr = a.d / EPC;
   const int nch = a.ndyn * cpr;
   // element offsets of this lane's chunks: frame 0 of the history, and the
@@ -48,47 +52,43 @@ __global__ __launch_bounds__(256) void cos_kernel(CosArgs a) {
     noff[k] = ((int64_t)hd * a.nxt_rows + p) * a.d + cc * EPC;
   }
   const int64_t fstride = (int64_t)a.F * a.d;
-  u32x4_t prev[KC];
+  u32x4_t fr[U + 1][KC];
+#pragma unroll
+  for (int u = 0; u <= U; ++u) {
+    const int t = t0 + u;
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      fr[u][k] = u32x4_t{0u, 0u, 0u, 0u};
+      if (ok[k] && t <= a.T) {
+        const E* src = t < a.T ? (const E*)a.hist + hoff[k] + t * fstride : (const E*)a.nxt + noff[k];
+        fr[u][k] = *reinterpret_cast<const u32x4_t*>(src);
+      }
+    }
+  }
   float nprev = 0.f;
-  for (int t0 = 0; t0 <= a.T; t0 += U) {
-    u32x4_t cur[U][KC];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = t0 + u;
+  for (int u = 0; u <= U; ++u) {
+    const int t = t0 + u;
+    if (t > a.T) break;
+    float nn = 0.f, dot = 0.f;
 #pragma unroll
-      for (int k = 0; k < KC; ++k) {
-        cur[u][k] = u32x4_t{0u, 0u, 0u, 0u};
-        if (ok[k] && t <= a.T) {
-          const E* src = t < a.T ? (const E*)a.hist + hoff[k] + t * fstride : (const E*)a.nxt + noff[k];
-          cur[u][k] = *reinterpret_cast<const u32x4_t*>(src);
-        }
+    for (int k = 0; k < KC; ++k) {
+      const E* e = reinterpret_cast<const E*>(&fr[u][k]);
+      const E* f = reinterpret_cast<const E*>(&fr[u > 0 ? u - 1 : 0][k]);
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) {
+        const float x = Ops<E>::to_f32(e[j]);
+        nn = __builtin_fmaf(x, x, nn);
+        if (u > 0) dot = __builtin_fmaf(x, Ops<E>::to_f32(f[j]), dot);
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = t0 + u;
-      if (t > a.T) break;
-      float nn = 0.f, dot = 0.f;
-#pragma unroll
-      for (int k = 0; k < KC; ++k) {
-        const E* e = reinterpret_cast<const E*>(&cur[u][k]);
-        const E* f = reinterpret_cast<const E*>(&prev[k]);
-#pragma unroll
-        for (int j = 0; j < EPC; ++j) {
-          const float x = Ops<E>::to_f32(e[j]);
-          nn = __builtin_fmaf(x, x, nn);
-          if (t > 0) dot = __builtin_fmaf(x, Ops<E>::to_f32(f[j]), dot);
-        }
-        prev[k] = cur[u][k];
-      }
-      nn = wave_sum(nn);
-      if (t > 0) {
-        dot = wave_sum(dot);
-        const float den = fmaxf(sqrtf(nprev) * sqrtf(nn), 1e-8f);
-        if (lane == 0) a.cosbuf[(int64_t)(t - 1) * a.F + p] = dot / den;
-      }
-      nprev = nn;
+    nn = wave_sum(nn);
+    if (u > 0) {
+      dot = wave_sum(dot);
+      const float den = fmaxf(sqrtf(nprev) * sqrtf(nn), 1e-8f);
+      if (lane == 0) a.cosbuf[(int64_t)(t - 1) * a.F + p] = dot / den;
     }
+    nprev = nn;
   }
 }
 
@@ -118,14 +118,16 @@ hipError_t launch_segment_cosine(const CosLaunch& c, hipStream_t st) {
   a.ndyn = c.ndyn;
   for (int i = 0; i < 64; ++i) a.dyn_heads[i] = c.dyn_heads[i];
   a.cosbuf = c.cosbuf;
-  const dim3 grid((unsigned)((c.F + 3) / 4));
   const int cpr = c.d * (c.et == ET_BF16 ? 2 : 4) / 16;
   const int kc = (c.ndyn * cpr + 63) / 64;   // <= 16 (checked on the host)
+  const int kcp = kc <= 1 ? 1 : kc <= 2 ? 2 : kc <= 4 ? 4 : kc <= 8 ? 8 : 16;
+  const int U = kcp >= 16 ? 1 : 16 / kcp;   // cosines per wave, as in the kernel
+  const dim3 grid((unsigned)((c.F + 3) / 4), (unsigned)((c.T + U - 1) / U));
 #define KVB_COS(E)                                                                                 \
-  if (kc <= 1) hipLaunchKernelGGL((cos_kernel<E, 1>), grid, dim3(256), 0, st, a);                  \
-  else if (kc <= 2) hipLaunchKernelGGL((cos_kernel<E, 2>), grid, dim3(256), 0, st, a);             \
-  else if (kc <= 4) hipLaunchKernelGGL((cos_kernel<E, 4>), grid, dim3(256), 0, st, a);             \
-  else if (kc <= 8) hipLaunchKernelGGL((cos_kernel<E, 8>), grid, dim3(256), 0, st, a);             \
+  if (kcp == 1) hipLaunchKernelGGL((cos_kernel<E, 1>), grid, dim3(256), 0, st, a);                 \
+  else if (kcp == 2) hipLaunchKernelGGL((cos_kernel<E, 2>), grid, dim3(256), 0, st, a);            \
+  else if (kcp == 4) hipLaunchKernelGGL((cos_kernel<E, 4>), grid, dim3(256), 0, st, a);            \
+  else if (kcp == 8) hipLaunchKernelGGL((cos_kernel<E, 8>), grid, dim3(256), 0, st, a);            \
   else hipLaunchKernelGGL((cos_kernel<E, 16>), grid, dim3(256), 0, st, a);
   if (c.et == ET_BF16) {
     KVB_COS(uint16_t)

@@ -208,10 +208,34 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint64_t* __restrict__
   }
 }
 
+// small n (<= 1024): every item's rank is the number of keys before it
+// (smaller, or equal and at a lower index)
+__global__ __launch_bounds__(1024) void rank_sort_kernel(const float* __restrict__ score, int64_t score_hstride,
+                                                        const int32_t* __restrict__ tie, int64_t tie_hstride,
+                                                        uint64_t on, int n, int32_t* __restrict__ out,
+                                                        int64_t out_hstride) {
+  const int h = blockIdx.x;
+  if (!head_on(on, h)) return;
+  __shared__ uint64_t sk[1024];
+  const int i = threadIdx.x;
+  if (i < n) sk[i] = sort_key(score, tie, tie_hstride, h, i, score_hstride);
+  __syncthreads();
+  if (i >= n) return;
+  const uint64_t key = sk[i];
+  int r = 0;
+  for (int j = 0; j < n; ++j) r += (sk[j] < key || (sk[j] == key && j < i)) ? 1 : 0;
+  out[(int64_t)h * out_hstride + r] = i;
+}
+
 hipError_t launch_sort(const float* score, int64_t score_hstride, const int32_t* tie, int64_t tie_hstride,
                        uint64_t on, int H, int n, uint64_t* k0, uint64_t* k1, int32_t* v0, int32_t* v1,
                        int32_t* out, int64_t out_hstride, hipStream_t st) {
   if (n <= 0) return hipSuccess;
+  if (n <= 1024) {
+    hipLaunchKernelGGL(rank_sort_kernel, dim3(H), dim3(1024), 0, st, score, score_hstride, tie, tie_hstride, on, n,
+                       out, out_hstride);
+    return hipGetLastError();
+  }
   const int nb = (n + SORT_BS - 1) / SORT_BS;
   const bool single = nb == 1;
   hipLaunchKernelGGL(block_sort_kernel, dim3(nb, H), dim3(SORT_BS / 2), 0, st, score, score_hstride, tie, tie_hstride, on,
