@@ -135,22 +135,71 @@ __global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __
   const int tid = threadIdx.x;
 
   // ---- work plan ----
-  // Items are (head, 128-query tile), head-major.  Without a partial buffer
+  // Items are (head, 256-query tile), head-major.  Without a partial buffer
   // the grid has one work-group per item.  With one, the grid is one
   // work-group per slot: `rounds` rounds of whole items, then the Ir items
   // left over are balanced over all G work-groups.  Each of those keeps a
   // main piece, key tiles [0, T), in the work-group of its own index (so
   // the work-groups of a head sweep its keys together, as in the plain
-  // grid); the tails [T, n) go to the remaining G - Ir work-groups, each
-  // taking up to k consecutive items of one head (the same tail keys, read
-  // from L2 after the first).  T is the smallest length at or above the
-  // even share for which the tails fit, counting one tile of start-up per
-  // extra piece.  Every work-group derives the same T from the segment
+  // grid).  The tails [T, n) of the longer items fill slots: first the
+  // G - Ir spare work-groups (room T each), then the work-groups whose own
+  // item is shorter than T (room T - n), in head order.  A slot takes
+  // consecutive tails of one head (the same tail keys, read from L2 after
+  // the first), each costing its length plus one tile of start-up.  T is
+  // the smallest length at or above the even share for which every tail
+  // finds a slot; every work-group derives the same plan from the segment
   // lengths.  Split items leave fp32 partials that attn_merge_kernel adds.
   __shared__ int s_nt[ATT_MAX_HEADS];
   __shared__ int s_T;
   const int base = rounds * G;          // first left-over item
   const int h0 = base / nqt;
+  // left-over items of head hh: [first_of(hh), (hh + 1) nqt)
+  auto first_of = [&](int hh) -> int { return max(hh * nqt, base); };
+  // Tail fill for cut tc.  Slot groups in order: g = 0, the spare
+  // work-groups; g = 1 + hh, the left-over items of head hh when it is
+  // shorter than tc.  Returns whether every tail is placed; with a target
+  // slot (tg, tj) also its tails: items [*first, *first + *cnt) of head *th.
+  auto fill = [&](int tc, int tg, int tj, int* th, int* first, int* cnt) -> bool {
+    int gi = 0, used = 0;
+    // (heads before h0 have no left-over item: their groups are empty)
+    auto gcount = [&](int g) -> int {
+      if (g == 0) return G - Ir;
+      const int hh = g - 1;
+      return hh >= h0 && s_nt[hh] < tc ? (hh + 1) * nqt - first_of(hh) : 0;
+    };
+    auto groom = [&](int g) -> int { return g == 0 ? tc : tc - s_nt[g - 1]; };
+    for (int hh = h0; hh < H; ++hh) {
+      const int r = s_nt[hh] - tc;
+      if (r <= 0) continue;
+      int rem = (hh + 1) * nqt - first_of(hh), it = first_of(hh);
+      while (rem > 0) {
+        if (gi > H) return false;
+        const int m = gcount(gi) - used;
+        const int k = groom(gi) / (r + 1);
+        if (m <= 0 || k <= 0) {
+          ++gi;
+          used = 0;
+          continue;
+        }
+        const int take = min((rem + k - 1) / k, m);
+        if (tg == gi && tj >= used && tj < used + take) {
+          *th = hh;
+          *first = it + (tj - used) * k;
+          *cnt = min(k, rem - (tj - used) * k);
+          return true;
+        }
+        const int placed = min(rem, take * k);
+        rem -= placed;
+        it += placed;
+        used += take;
+        if (used >= gcount(gi)) {
+          ++gi;
+          used = 0;
+        }
+      }
+    }
+    return tg < 0;
+  };
   int T = 0;
   if (Ir > 0) {
     if (w == 0) {
@@ -166,26 +215,14 @@ __global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __
       int64_t work = 0;
       int ntmax = 0;
       for (int hh = h0; hh < H; ++hh) {
-        const int cnt = (hh + 1) * nqt - max(hh * nqt, base);
-        work += (int64_t)cnt * s_nt[hh];
+        work += (int64_t)((hh + 1) * nqt - first_of(hh)) * s_nt[hh];
         ntmax = max(ntmax, s_nt[hh]);
       }
       const int tlo = max(1, (int)((work + G - 1) / G));
-      const int tc = tlo + lane;   // candidate lengths, one per lane
-      int need = 0;
-      bool ok = true;
-      for (int hh = h0; hh < H; ++hh) {
-        const int cnt = (hh + 1) * nqt - max(hh * nqt, base);
-        const int r = s_nt[hh] - tc;
-        if (r > 0) {
-          const int k = tc / (r + 1);
-          if (k == 0) ok = false;
-          else need += (cnt + k - 1) / k;
-        }
-      }
-      ok = ok && need <= G - Ir;
-      const uint64_t m = __ballot(ok);
-      if (lane == 0) s_T = m ? tlo + (int)__builtin_ctzll(m) : ntmax;
+      int dh, df, dc;
+      const bool ok = fill(tlo + lane, -1, 0, &dh, &df, &dc);   // candidate cuts, one per lane
+      const uint64_t msk = __ballot(ok);
+      if (lane == 0) s_T = msk ? tlo + (int)__builtin_ctzll(msk) : ntmax;
     }
     __syncthreads();
     T = __builtin_amdgcn_readfirstlane(s_T);
@@ -521,32 +558,32 @@ __global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __
   // this work-group's tail range: items [tl_first, tl_first + tl_cnt) of
   // one head, key tiles [T, tl_nt)
   int tl_first = 0, tl_cnt = 0, tl_nt = 0;
-  if (Ir > 0 && bl >= Ir) {
-    int c = bl - Ir;
-    for (int hh = h0; hh < H; ++hh) {
-      const int cnt = (hh + 1) * nqt - max(hh * nqt, base);
-      const int r = s_nt[hh] - T;
-      if (r <= 0) continue;
-      const int k = T / (r + 1);
-      const int nh = (cnt + k - 1) / k;
-      if (c < nh) {
-        tl_first = max(hh * nqt, base) + c * k;
-        tl_cnt = min(cnt, (c + 1) * k) - c * k;
-        tl_nt = s_nt[hh];
-        break;
+  if (Ir > 0) {
+    int tg = -1, tj = 0;
+    if (bl >= Ir) {
+      tg = 0;
+      tj = bl - Ir;
+    } else {
+      const int hh = (base + bl) / nqt;
+      if (s_nt[hh] < T) {
+        tg = 1 + hh;
+        tj = base + bl - first_of(hh);
       }
-      c -= nh;
     }
+    int th = 0;
+    if (tg >= 0 && fill(T, tg, tj, &th, &tl_first, &tl_cnt)) tl_nt = s_nt[th];
+    else tl_cnt = 0;
   }
   // pieces in order: whole items of each round, then the main piece (or the
-  // whole left-over item) or the tails; one call site keeps one copy of the
-  // tile loop
-  const int npieces = rounds + (Ir > 0 ? (bl < Ir ? 1 : tl_cnt) : 0);
+  // whole left-over item), then the tails; one call site keeps one copy of
+  // the tile loop
+  const int npieces = rounds + (Ir > 0 ? (bl < Ir ? 1 : 0) + tl_cnt : 0);
   for (int pc = 0; pc < npieces; ++pc) {
     int item, t0 = 0, t1 = 1 << 30, slot = -1, ir = -1;
+    const int pt = pc - rounds - (bl < Ir ? 1 : 0);   // tail index (when >= 0)
     if (pc < rounds) {
       item = pc * G + bl;
-    } else if (bl < Ir) {
+    } else if (pt < 0) {
       item = base + bl;
       ir = bl;
       const int nt = s_nt[item / nqt];
@@ -555,7 +592,7 @@ __global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __
         slot = 0;
       }
     } else {
-      item = tl_first + (pc - rounds);
+      item = tl_first + pt;
       ir = item - base;
       t0 = T;
       t1 = tl_nt;

@@ -149,6 +149,20 @@ def test_attention_balanced_multi_tail():
     assert e.max() <= 1e-2 and e.mean() <= 1e-3, (e.max(), e.mean())
 
 
+def test_attention_balanced_short_items_take_tails():
+    """Heads of two lengths, as in the Forcing-KV hybrid layer (6 heads of
+    7,800 keys, 6 of 18,720; 228 items on 256 slots): the work-groups whose
+    own item is short also take tails of the long heads' items, besides the
+    spare work-groups.  Three heads against the oracle; every head against
+    the one-work-group-per-item grid."""
+    lens = [[1560, 1560, 4680]] * 6 + [[1560, 12480, 4680]] * 6
+    _attention_case(128, 4680, lens, "bf16", heads=[0, 6, 11])
+    a = _attention_case(128, 4680, lens, "bf16", ret=True)
+    b = _attention_case(128, 4680, lens, "bf16", ws=None, ret=True)
+    e = np.abs(a - b)
+    assert e.max() <= 1e-2 and e.mean() <= 1e-3, (e.max(), e.mean())
+
+
 def test_attention_balanced_d64():
     """d = 64 on the balanced grid, with a ragged tail tile."""
     _attention_case(64, 1000, [[900, 333], [1500], [64, 64, 7]], "bf16")
