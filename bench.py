@@ -649,7 +649,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="480p", choices=["480p", "1080p", "fkv480p", "rollout"])
+    ap.add_argument("--config", default="480p", choices=["480p", "480p_block", "1080p", "fkv480p", "rollout"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="480p/1080p: time that layer-chunk only (no other workloads, side benches)")
@@ -748,6 +748,10 @@ def main():
                                             "scaled by its row count and by 12 heads (extrapolation)",
                                   "stages_ms": parts, "blas": blas}
         res["1080p"] = r1
+        log("480p_block layer-chunk (one finalized block into a full bank)")
+        wlb, rb = layer_chunk("480p_block", max(5, min(args.steps, 20)), 3)
+        rb["value_ms_per_chunk_layer"] = round(rb.pop("ms_per_step"), 4)
+        res["480p_block"] = rb
         log("fkv480p hybrid layer")
         res["fkv480p"] = forcing_bench()
         log(f"rollout ({args.chunks} chunks x 30 layers)")

@@ -382,7 +382,9 @@ KVB_DEV uint64_t evict_key(float rp, int32_t tok, bool oldest) {
 // work-groups per head:
 //   evict_select_kernel  (one block per head) the counts, and the threshold
 //                        key of the r-th largest key when a partial
-//                        completion is needed (8-bit MSB-first radix select);
+//                        completion is needed (8-bit MSB-first radix select,
+//                        ended once every key of the selected bin is taken:
+//                        the threshold is then that bin's smallest key);
 //                        the crossed count at k* is read from the crossing-
 //                        time prefix sums, so the common cases pass over no
 //                        state at all
@@ -436,7 +438,8 @@ __global__ __launch_bounds__(1024) void evict_select_kernel(SelectLaunch a) {
   __shared__ uint64_t s_prefix, s_mask;
   __shared__ int s_rem;
   __shared__ int wsc[4];
-  __shared__ int s_sel;
+  __shared__ int s_sel, s_cnt;
+  __shared__ unsigned long long s_min;
   if (mode == 2) {
     if (tid == 0) { s_prefix = 0; s_mask = 0; s_rem = r; }
     __syncthreads();
@@ -471,14 +474,36 @@ __global__ __launch_bounds__(1024) void evict_select_kernel(SelectLaunch a) {
         int off = 0;
         for (int k = 0; k < w; ++k) off += wsc[k];
         const int S = off + inc;
-        if (S >= rem && S - c < rem) { s_sel = d; s_rem = rem - (S - c); }
+        if (S >= rem && S - c < rem) { s_sel = d; s_rem = rem - (S - c); s_cnt = c; }
       }
       __syncthreads();
       if (tid == 0) {
         s_prefix = pre | ((uint64_t)s_sel << shift);
         s_mask = msk | (0xFFull << shift);
+        s_min = ~0ull;
       }
       __syncthreads();
+      if (s_cnt == s_rem) {
+        // every key of the selected bin is taken (always so once the bin
+        // holds a single key): the threshold is the bin's smallest key
+        const uint64_t pre2 = s_prefix, msk2 = s_mask;
+        unsigned long long mn = ~0ull;
+        for (int b = tid; b < n; b += 1024) {
+          if (force && gated && !a.skip_cross && a.t[hb + b] <= ks) continue;
+          const uint64_t key = evict_key(a.rhoP[hb + b], a.bank_tok[hb + b], oldest);
+          if ((key & msk2) == pre2) mn = key < mn ? key : mn;
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+          const unsigned long long v = __shfl_xor(mn, o);
+          mn = v < mn ? v : mn;
+        }
+        if (lane == 0 && mn != ~0ull) atomicMin(&s_min, mn);
+        __syncthreads();
+        if (tid == 0) s_prefix = s_min;
+        __syncthreads();
+        break;
+      }
     }
   }
   if (tid == 0) {

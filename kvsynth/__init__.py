@@ -154,6 +154,11 @@ WORKLOADS: Dict[str, Workload] = {
     # update offering frames 7-21 (N = 23,400), window 22-27, chunk 28-30.
     "480p": Workload(name="480p", H=12, d=128, width=52, height=30, dtype="bf16", M=9360, tau=2.0,
                      bank_updates=((1, 7), (7, 22)), window=(22, 28), chunk=(28, 31)),
+    # 480P, one finalized block: the same layer with the pages' per-block pool,
+    # frames 7-9 (N = 4,680) offered to the full bank of frames 1-6; window
+    # 10-15, chunk 16-18.  Part of the bank survives (partial eviction).
+    "480p_block": Workload(name="480p_block", H=12, d=128, width=52, height=30, dtype="bf16", M=9360, tau=2.0,
+                           bank_updates=((1, 7), (7, 10)), window=(10, 16), chunk=(16, 19)),
     # Forcing-KV hybrid heads at 480P: 6 static / 6 dynamic (seeded), history frames
     # 1-12, chunk 13-15, 1,560-token segments, 70% of segments kept.
     "fkv480p": Workload(name="fkv480p", H=12, d=128, width=52, height=30, dtype="bf16", M=0,

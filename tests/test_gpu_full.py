@@ -116,10 +116,11 @@ def test_480p_whole_bank_replaced_without_scan():
 
 @pytest.mark.timeout(600)
 def test_480p_partial_eviction():
-    """N = 4,680 candidates (three frames) offered to a full bank of 9,360:
-    the new bank keeps part of the old one."""
-    wl = WORKLOADS["480p"]
-    rep, cold, after = _layer_chunk("480p", cand_frames=(7, 10))
+    """One finalized block, N = 4,680 candidates (three frames), offered to
+    a full bank of 9,360 (the 480p_block workload that bench.py times): the
+    new bank keeps part of the old one."""
+    wl = WORKLOADS["480p_block"]
+    rep, cold, after = _layer_chunk("480p_block")
     assert 0 < rep.kstar <= 3 * wl.F
     for h in range(wl.H):
         e = rep.evicted[h]
