@@ -397,7 +397,9 @@ __global__ __launch_bounds__((gram_nt<SELF, CLIST>()), ((SELF && CLIST) ? 3 : 4)
       load_issue(tile + 1, nY, nA, nV);
       if (tile + 2 < t1) load_index(tile + 2);
     }
-    // both subtiles' products first (independent chains)
+    // both subtiles' products first: two independent chains, interleaved
+    // so that each fragment read and each product has the other chain's
+    // product to hide behind
     // column fragment k of subtile sub: sub 32 D + at(n, off32(k, lane)),
     // stepped from one start offset (the swizzle repeats every 32 rows);
     // the start is rebuilt per tile so the compiler does not keep a register
@@ -410,15 +412,15 @@ __global__ __launch_bounds__((gram_nt<SELF, CLIST>()), ((SELF && CLIST) ? 3 : 4)
     };
     f32x16_t cc[2];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int rr = 32 * sub + nn;
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int i = 0; i < 16; ++i) cc[sub][i] = 0.0f;
 #pragma unroll
-      for (int k = 0; k < NK; ++k)
-        cc[sub] = O::mma32(xf[k], O::load(cY + yoff(sub, k)), cc[sub]);
-      cc[sub] = O::mma32(xa, A::yfrag(cA[rr], lane), cc[sub]);
-    }
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) cc[sub] = O::mma32(xf[k], O::load(cY + yoff(sub, k)), cc[sub]);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) cc[sub] = O::mma32(xa, A::yfrag(cA[32 * sub + nn], lane), cc[sub]);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int yv = cV[32 * sub + nn];
