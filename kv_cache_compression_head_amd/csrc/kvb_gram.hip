@@ -797,17 +797,20 @@ __global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const floa
         if constexpr (sizeof(E) == 2) return 32 * half * D + T::at_step(c0, O::off32(k, 0));
         else return T::at(32 * half + (lane & 31), O::off32(k, lane));
       };
+      // the two halves' chains interleaved (each fragment read and product
+      // has the other chain's product to hide behind)
       f32x16_t accs[2];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int cr = 32 * half + (lane & 31);
+      for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int i = 0; i < 16; ++i) accs[half][i] = 0.0f;
 #pragma unroll
-        for (int k = 0; k < NK; ++k)
-          accs[half] = O::mma32(O::load(cC + coff(half, k)), bf[k], accs[half]);
-        accs[half] = O::mma32(A::yfrag(cA[cr], lane), ba, accs[half]);
-      }
+      for (int k = 0; k < NK; ++k)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) accs[half] = O::mma32(O::load(cC + coff(half, k)), bf[k], accs[half]);
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        accs[half] = O::mma32(A::yfrag(cA[32 * half + (lane & 31)], lane), ba, accs[half]);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int sub = 2 * stg + half;
