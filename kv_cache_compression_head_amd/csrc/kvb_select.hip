@@ -619,34 +619,52 @@ __global__ void apply_surv_kernel(ApplyLaunch a) {
   if (a.refresh) a.rho0[hb + slot] = r;
 }
 
-// 8 rows per 256-thread block; each row moves K and V (16-byte chunks)
+// Gather of admitted rows.  TPR threads per row, each moving U 16-byte
+// chunks: chunk r + TPR i of the row's K chunks followed by its V chunks, so
+// that each load and store instruction covers whole consecutive 16 TPR-byte
+// pieces of a row and every thread keeps U loads in flight.
 template <int CPR>
 __global__ __launch_bounds__(256) void apply_adm_kernel(ApplyLaunch a) {
+  constexpr int U = 4;
+  constexpr int TPR = 2 * CPR / U;   // threads per row
+  constexpr int RPB = 256 / TPR;     // rows per block
+  static_assert(CPR % U == 0 && 256 % TPR == 0, "gather shape");
   const int h = blockIdx.y;
   if (!head_on(a.active, h)) return;
   const int ks = a.kstar[h * a.kstar_hs];
-  constexpr int RPB = 256 / (2 * CPR);
-  const int j = blockIdx.x * RPB + threadIdx.x / (2 * CPR);
+  const int j = blockIdx.x * RPB + threadIdx.x / TPR;
   if (j >= ks) return;
-  const int part = (threadIdx.x % (2 * CPR)) / CPR;   // 0 = K, 1 = V
-  const int c = threadIdx.x % CPR;
+  const int r = threadIdx.x % TPR;
   const int64_t hb = (int64_t)h * a.M;
   const int ne = a.n_ev[h];
   const int nold = a.n_surv[h] + ne;
   const int slot = j < ne ? a.evl[hb + j] : nold + (j - ne);
   const int cand = a.order[(int64_t)h * a.N + j];
   if ((unsigned)slot >= (unsigned)a.M || (unsigned)cand >= (unsigned)a.N) return;
-  const int esz = a.et == ET_BF16 ? 2 : 4;
-  const int64_t rowb = (int64_t)a.d * esz;
-  const char* src = (const char*)(part ? a.candV : a.candK) + ((int64_t)h * a.N + cand) * rowb;
-  char* dst = (char*)(part ? a.bankV : a.bankK) + (hb + slot) * rowb;
-  *reinterpret_cast<u32x4_t*>(dst + c * 16) = *reinterpret_cast<const u32x4_t*>(src + c * 16);
-  if (threadIdx.x % (2 * CPR) == 0) {
+  const int64_t rowb = (int64_t)CPR * 16;
+  const char* srcK = (const char*)a.candK + ((int64_t)h * a.N + cand) * rowb;
+  const char* srcV = (const char*)a.candV + ((int64_t)h * a.N + cand) * rowb;
+  char* dstK = (char*)a.bankK + (hb + slot) * rowb;
+  char* dstV = (char*)a.bankV + (hb + slot) * rowb;
+  u32x4_t v[U];
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    const int c = r + TPR * i;   // < 2 CPR
+    const char* src = c < CPR ? srcK + c * 16 : srcV + (c - CPR) * 16;
+    v[i] = *reinterpret_cast<const u32x4_t*>(src);
+  }
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    const int c = r + TPR * i;
+    char* dst = c < CPR ? dstK + c * 16 : dstV + (c - CPR) * 16;
+    *reinterpret_cast<u32x4_t*>(dst) = v[i];
+  }
+  if (r == 0) {
     const int64_t hk = (int64_t)h * a.kmax + j;
-    const float r = a.fmode[h] ? a.acc_adm_ev[hk] + a.acc_adm_adm[hk]
-                               : (a.D[(int64_t)h * a.N + cand] - a.acc_adm_ev[hk]) + a.acc_adm_adm[hk];
-    a.rho[hb + slot] = r;
-    a.rho0[hb + slot] = r;
+    const float rr = a.fmode[h] ? a.acc_adm_ev[hk] + a.acc_adm_adm[hk]
+                                : (a.D[(int64_t)h * a.N + cand] - a.acc_adm_ev[hk]) + a.acc_adm_adm[hk];
+    a.rho[hb + slot] = rr;
+    a.rho0[hb + slot] = rr;
     a.bank_tok[hb + slot] = a.cand_tok[cand];
   }
 }
@@ -685,12 +703,13 @@ hipError_t launch_apply(const ApplyLaunch& a, hipStream_t st) {
     hipLaunchKernelGGL(apply_surv_kernel, dim3((a.M + 255) / 256, a.H), dim3(256), 0, st, a);
   const int cpr = a.d * (a.et == ET_BF16 ? 2 : 4) / 16;
   if (a.kmax > 0) {
+    // rows per block: 256 / (2 cpr / 4)
     if (cpr == 16)
-      hipLaunchKernelGGL((apply_adm_kernel<16>), dim3((a.kmax + 7) / 8, a.H), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((apply_adm_kernel<16>), dim3((a.kmax + 31) / 32, a.H), dim3(256), 0, st, a);
     else if (cpr == 8)
-      hipLaunchKernelGGL((apply_adm_kernel<8>), dim3((a.kmax + 15) / 16, a.H), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((apply_adm_kernel<8>), dim3((a.kmax + 63) / 64, a.H), dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((apply_adm_kernel<32>), dim3((a.kmax + 3) / 4, a.H), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((apply_adm_kernel<32>), dim3((a.kmax + 15) / 16, a.H), dim3(256), 0, st, a);
   }
   if (a.bankX && a.candX && a.kmax > 0) {
     const int cprx = a.dx * (a.et == ET_BF16 ? 2 : 4) / 16;
