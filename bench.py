@@ -508,7 +508,7 @@ def forcing_bench(steps: int = 10, seed: int = 0):
                           "frac_bf16_peak": round(flop / at / 1e9 / PEAK_BF16_TFLOPS, 4)}}
 
 
-def rollout_bench(chunks: int, layers: int = 0, seed: int = 0):
+def rollout_bench(chunks: int, layers: int = 0, seed: int = 0, policy: int = 0):
     """Streaming rollout: every chunk runs, for each of the 30 layers, the
     window advance (departing frames re-rotated into bank candidates),
     kvbank_score, kvbank_update and chunk_attention.  Each layer draws its
@@ -520,8 +520,8 @@ def rollout_bench(chunks: int, layers: int = 0, seed: int = 0):
     from kvsynth import WORKLOADS
     wl = WORKLOADS["rollout"]
     L = layers or wl.layers
-    r = Rollout(wl, L, seed=seed, source="device")
-    ms, ks, counts = [], [], []
+    r = Rollout(wl, L, seed=seed, source="device", policy=policy)
+    ms, ks, counts, evs = [], [], [], []
     for c in range(chunks):
         r.prepare()
         torch.cuda.synchronize()
@@ -533,18 +533,20 @@ def rollout_bench(chunks: int, layers: int = 0, seed: int = 0):
         ms.append(e0.elapsed_time(e1))
         lc0 = r.L[0].cache
         ks.append(int(lc0.out.k_star.cpu()[0]) if len(p.departed) else None)
+        evs.append(int(lc0.out.n_evicted.cpu().sum()) if len(p.departed) else None)
         counts.append(int(lc0.bank.count.max().cpu()))
     steady = [m for c, m in enumerate(ms) if c >= 4]   # every chunk from the fourth on offers 3 frames
     a = np.asarray(steady)
     adm = [k for k in ks if k is not None]
     return {"workload": f"rollout: {L} layers x {wl.H} heads, 480P (F={wl.F}), M={wl.M}, W={wl.window_frames} frames, "
                         f"{chunks} chunks of {wl.chunk_frames} frames; per chunk and layer: window advance, score, "
-                        f"update, attention",
+                        f"update, attention" + (f"; policy={policy}" if policy else ""),
             "chunks": chunks, "layers": L, "total_ms": round(float(sum(ms)), 2),
             "ms_per_chunk_steady": {"mean": round(float(a.mean()), 3), "p50": round(float(np.percentile(a, 50)), 3),
                                     "p99": round(float(np.percentile(a, 99)), 3)},
             "ms_per_layer_chunk_steady": round(float(a.mean()) / L, 4),
             "layer0_k_star_per_update": adm, "layer0_admitted_total": int(sum(adm)),
+            "layer0_evicted_per_update_all_heads": [e for e in evs if e is not None],
             "layer0_bank_count_per_chunk": counts,
             "bank_bytes_per_layer": int(r.L[0].cache.bank.K.numel() * 2 * 2)}
 
@@ -685,7 +687,7 @@ def main():
     base = {"n_gpus": 1, "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic"}
     if args.config == "rollout":
-        ro = rollout_bench(args.chunks)
+        ro = rollout_bench(args.chunks, policy=args.policy)
         ms = ro["ms_per_chunk_steady"]["mean"]
         print(json.dumps({"metric": METRIC, "value": ms, "unit": "ms/chunk (30 layers)", "steps": args.chunks,
                           "warmup": 0, "ms_per_step": ms, **base, "config": {"workload": ro["workload"]},
@@ -756,6 +758,13 @@ def main():
         res["fkv480p"] = forcing_bench()
         log(f"rollout ({args.chunks} chunks x 30 layers)")
         res["rollout"] = rollout_bench(args.chunks)
+        # under the method's own rule the banks stop admitting once every
+        # prefix would push a state past tau while the bank is below capacity
+        # (layer0_k_star_per_update above); with the fill-below-capacity
+        # variant the banks reach M and then admit and evict at every update
+        nf = min(args.chunks, 40)
+        log(f"rollout, fill below capacity ({nf} chunks x 30 layers)")
+        res["rollout_fill"] = rollout_bench(nf, policy=kb.KVB_POL_FILL_BELOW_CAP)
     print(json.dumps(res), flush=True)
 
 

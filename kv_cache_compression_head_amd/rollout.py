@@ -84,16 +84,17 @@ class Rollout:
     (each layer's stream is keyed by its index, so running a subset gives
     the same per-layer results as running them all).  source: "host"
     (seeded NumPy frames; the oracle can regenerate them) or "device"
-    (seeded frames drawn on the GPU)."""
+    (seeded frames drawn on the GPU).  policy: KVB_POL_* bits of every
+    layer's bank (0: the method as the pages state it)."""
 
     def __init__(self, wl: Workload, layers: Union[int, Sequence[int]], seed: int = 0, diagnostics: bool = False,
-                 source: str = "host"):
+                 source: str = "host", policy: int = 0):
         self.wl, self.seed, self.source = wl, seed, source
         self.layer_ids = list(range(layers)) if isinstance(layers, int) else list(layers)
         self.kdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
         dt = KVB_BF16 if wl.dtype == "bf16" else KVB_F32
         self.desc = LayerDesc(H=wl.H, d=wl.d, M=wl.M, dtype=dt, frame_tokens=wl.F, labels=[0] * wl.H,
-                              tau=wl.tau, sigma=wl.sigma, eps=wl.eps, p=wl.p)
+                              tau=wl.tau, sigma=wl.sigma, eps=wl.eps, p=wl.p, policy=policy)
         self.L: List[_Layer] = []
         for l in self.layer_ids:
             lc = LayerCache(self.desc, seg_cap=8, max_N=wl.chunk_frames * wl.F, diagnostics=diagnostics)
