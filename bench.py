@@ -37,6 +37,9 @@ PEAK_HBM_GBS = 8000.0
 ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_kernel_480p_hbm_traffic.md")
 ATTN_SOURCES = ("kv_cache_compression_head_amd/csrc/kvb_attention.hip",
                 "kv_cache_compression_head_amd/csrc/kvb_common.hpp")
+HBM_SOURCES = ("kv_cache_compression_head_amd/csrc/kvb_select.hip",
+               "kv_cache_compression_head_amd/csrc/kvb_forcing.hip",
+               "kv_cache_compression_head_amd/csrc/kvb_common.hpp")
 DENSITY_SOURCES = ("kv_cache_compression_head_amd/csrc/kvb_gram.hip",
                    "kv_cache_compression_head_amd/csrc/kvb_common.hpp")
 
@@ -404,7 +407,7 @@ def layer_chunk(name: str, steps: int, warmup: int, policy: int = 0, tau=None):
            "attention_frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
            "k_star": kstar, "evicted_per_head": ev[:1] + ([] if len(set(ev)) == 1 else ev[1:]),
            "crossing_scan": scanned,
-           "roofline": roof, "density_stages": density_roof,
+           "roofline": roof, "density_stages": density_roof, "hbm_kernels": recorded_hbm_kernels(name),
            "workload": f"{name}: one layer-chunk, H={wl.H}, d={wl.d}, F={wl.F}, M={wl.M}, N={N}, Lq={wl.Lq}, "
                        f"window={wl.window[1] - wl.window[0]} frames, tau={wl.tau}, sigma={wl.sigma}, p={wl.p}"
                        + (f", policy={policy}" if policy else "")}
@@ -428,6 +431,40 @@ def recorded_valu_per_pair(config: str):
         return None
     return {"score": float(kv["record.score_valu_cycles_per_pair"]),
             "update": float(kv["record.update_valu_cycles_per_pair"])}
+
+
+def recorded_hbm_kernels(config: str):
+    """HBM-bound kernels of the workload (the gather of admitted rows, the
+    segment cosine) from the committed FETCH_SIZE / WRITE_SIZE profile:
+    counted and algorithmic bytes over the dispatch's duration in that run,
+    against 8 TB/s.  Null when the profile was taken on other kernel
+    sources.  These kernels run inside kvbank_update / kvbank_score, so the
+    bench's events cannot time them alone."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"kernels_{config}_hbm_traffic.md")
+    try:
+        with open(path) as fh:
+            kv = dict(l.split(":", 1) for l in fh.read().splitlines() if l.startswith("record."))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    h = hashlib.sha256()
+    for f in HBM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if kv.get("record.kernel_sources_sha256") != h.hexdigest():
+        return None
+    out = {}
+    for name in ("gather", "segment_cosine"):
+        if f"record.{name}_us" not in kv:
+            continue
+        us = float(kv[f"record.{name}_us"])
+        cb, ab = int(kv[f"record.{name}_counted_bytes"]), int(kv[f"record.{name}_algorithmic_bytes"])
+        out[name] = {"kernel": kv[f"record.{name}_kernel"], "us": us, "algorithmic_bytes": ab, "counted_bytes": cb,
+                     "GB/s_algorithmic": round(ab / us / 1e3, 1), "GB/s_counted": round(cb / us / 1e3, 1),
+                     "frac_hbm_peak": round(ab / us / 1e3 / PEAK_HBM_GBS, 4),
+                     "source": f"profiles/kernels_{config}_hbm_traffic.md"}
+    return out or None
 
 
 def density_source_digest() -> str:
@@ -503,6 +540,7 @@ def forcing_bench(steps: int = 10, seed: int = 0):
             "segment_cosine": {"call": "kvbank_score (cos_kernel + segmean_kernel + item sort)",
                                "bytes_read": cos_bytes, "GB/s": round(cos_bytes / sc / 1e6, 1),
                                "frac_hbm_peak": round(cos_bytes / sc / 1e6 / PEAK_HBM_GBS, 4)},
+            "hbm_kernels": recorded_hbm_kernels("fkv480p"),
             "attention": {"Lkv_static": F + F + wl.Lq, "Lkv_dynamic": F + keep * wl.seg_len + wl.Lq,
                           "TFLOP/s": round(flop / at / 1e9, 1),
                           "frac_bf16_peak": round(flop / at / 1e9 / PEAK_BF16_TFLOPS, 4)}}
