@@ -13,6 +13,13 @@
 namespace kvb {
 
 
+#ifndef COS_ROWS_NF
+#define COS_ROWS_NF 4
+#endif
+#ifndef COS_ROWS_NH
+#define COS_ROWS_NH 8
+#endif
+
 struct CosArgs {
   const void* hist; const void* nxt;
   int32_t H, d, F, T, nxt_rows, ndyn;
@@ -92,6 +99,67 @@ __global__ __launch_bounds__(256) void cos_kernel(CosArgs a) {
   }
 }
 
+// Row-group form for up to NH dynamic heads: CPR lanes hold one token's
+// key row of one head (16 bytes each), so every load instruction of a wave
+// reads 64 / CPR consecutive token rows of one head, one contiguous piece.
+// A work-group takes 4 (64 / CPR) consecutive tokens and NF consecutive
+// frames (NF - 1 frame pairs; the last frame is shared with the next
+// group), and issues all NF x NH loads of a lane before reducing any of
+// them.  Per lane the heads' partial sums are added in head order, then the
+// CPR lanes of the row are added by a butterfly.
+template <typename E, int CPR, int NH, int NF>
+__global__ __launch_bounds__(256) void cos_rows_kernel(CosArgs a) {
+  constexpr int EPC = 16 / sizeof(E);
+  constexpr int TPW = 64 / CPR;   // tokens per wave
+  const int lane = lane_id(), w = wave_id();
+  const int c = lane % CPR;
+  const int p = (blockIdx.x * 4 + w) * TPW + lane / CPR;
+  const bool okp = p < a.F;
+  const int t0 = blockIdx.y * (NF - 1);   // first frame of the group
+  u32x4_t fr[NF][NH];
+#pragma unroll
+  for (int u = 0; u < NF; ++u) {
+    const int t = t0 + u;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      fr[u][h] = u32x4_t{0u, 0u, 0u, 0u};
+      if (h < a.ndyn && okp && t <= a.T) {
+        const int hd = a.dyn_heads[h];
+        const E* src = t < a.T ? (const E*)a.hist + (((int64_t)hd * a.T + t) * a.F + p) * a.d + c * EPC
+                               : (const E*)a.nxt + ((int64_t)hd * a.nxt_rows + p) * a.d + c * EPC;
+        fr[u][h] = *reinterpret_cast<const u32x4_t*>(src);
+      }
+    }
+  }
+  float nprev = 0.f;
+#pragma unroll
+  for (int u = 0; u < NF; ++u) {
+    const int t = t0 + u;
+    float nn = 0.f, dot = 0.f;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const E* e = reinterpret_cast<const E*>(&fr[u][h]);
+      const E* f = reinterpret_cast<const E*>(&fr[u > 0 ? u - 1 : 0][h]);
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) {
+        const float x = Ops<E>::to_f32(e[j]);
+        nn = __builtin_fmaf(x, x, nn);
+        if (u > 0) dot = __builtin_fmaf(x, Ops<E>::to_f32(f[j]), dot);
+      }
+    }
+#pragma unroll
+    for (int o = CPR / 2; o >= 1; o >>= 1) {
+      nn += __shfl_xor(nn, o);
+      if (u > 0) dot += __shfl_xor(dot, o);
+    }
+    if (u > 0 && c == 0 && okp && t <= a.T) {
+      const float den = fmaxf(sqrtf(nprev) * sqrtf(nn), 1e-8f);
+      a.cosbuf[(int64_t)(t - 1) * a.F + p] = dot / den;
+    }
+    nprev = nn;
+  }
+}
+
 // segment means: one work-group per (frame, segment) item, fixed-order sum
 __global__ __launch_bounds__(256) void segmean_kernel(const float* __restrict__ cosbuf, int F, int seg_len, int ndyn,
                                                       CosArgs a, float* __restrict__ scores, int64_t shs) {
@@ -119,6 +187,20 @@ hipError_t launch_segment_cosine(const CosLaunch& c, hipStream_t st) {
   for (int i = 0; i < 64; ++i) a.dyn_heads[i] = c.dyn_heads[i];
   a.cosbuf = c.cosbuf;
   const int cpr = c.d * (c.et == ET_BF16 ? 2 : 4) / 16;
+  if (c.ndyn <= COS_ROWS_NH && (cpr == 8 || cpr == 16 || cpr == 32)) {
+    constexpr int NF = COS_ROWS_NF;
+    const dim3 g((unsigned)((c.F + 4 * (64 / cpr) - 1) / (4 * (64 / cpr))), (unsigned)((c.T + NF - 2) / (NF - 1)));
+#define KVB_COSR(E)                                                                                           \
+  if (cpr == 8) hipLaunchKernelGGL((cos_rows_kernel<E, 8, COS_ROWS_NH, NF>), g, dim3(256), 0, st, a);        \
+  else if (cpr == 16) hipLaunchKernelGGL((cos_rows_kernel<E, 16, COS_ROWS_NH, NF>), g, dim3(256), 0, st, a); \
+  else hipLaunchKernelGGL((cos_rows_kernel<E, 32, COS_ROWS_NH, NF>), g, dim3(256), 0, st, a);
+    if (c.et == ET_BF16) {
+      KVB_COSR(uint16_t)
+    } else {
+      KVB_COSR(float)
+    }
+#undef KVB_COSR
+  } else {
   const int kc = (c.ndyn * cpr + 63) / 64;   // <= 16 (checked on the host)
   const int kcp = kc <= 1 ? 1 : kc <= 2 ? 2 : kc <= 4 ? 4 : kc <= 8 ? 8 : 16;
   const int U = kcp >= 16 ? 1 : 16 / kcp;   // cosines per wave, as in the kernel
@@ -135,6 +217,7 @@ hipError_t launch_segment_cosine(const CosLaunch& c, hipStream_t st) {
     KVB_COS(float)
   }
 #undef KVB_COS
+  }
   const int items = c.T * (c.F / c.seg_len);
   hipLaunchKernelGGL(segmean_kernel, dim3(items), dim3(256), 0, st, c.cosbuf, c.F, c.seg_len, c.ndyn, a, c.scores,
                      c.score_hstride);
