@@ -32,7 +32,7 @@ from typing import Dict, List, Optional, Sequence, Union
 import numpy as np
 import torch
 
-from kvsynth import ROPE_BASE, LayerStream, Workload, frame_tokens
+from kvsynth import ROPE_BASE, LayerStream, Workload
 
 from . import KVB_BF16, KVB_F32, KVLayout, LayerDesc, kvbank_window_advance
 from .pipeline import LayerCache
@@ -197,7 +197,10 @@ class Rollout:
                     ring_before = (x.ring_k.clone(), x.ring_v.clone())
                 kvbank_window_advance(self.desc, x.ring_k, x.ring_v, self._slot(dep[0]), N, dep[0], ck, cv,
                                       new_k, new_v, rope_base=ROPE_BASE)
-                ct = torch.from_numpy(frame_tokens(wl, dep[0], dep[-1] + 1)).to("cuda")
+                # token ids frame * F + p of the departed frames: one contiguous
+                # range, made on the device (a host-to-device copy here would
+                # wait for the stream and stall the launches of every layer)
+                ct = torch.arange(dep[0] * F, (dep[-1] + 1) * F, dtype=torch.int32, device="cuda")
             lay = KVLayout()
             if x.sink_k is not None:
                 lay.sink_k, lay.sink_v = x.sink_k, x.sink_v

@@ -123,6 +123,14 @@ def test_forcing_small_shapes():
     _run(wl)
 
 
+def test_forcing_many_dynamic_heads():
+    """Ten dynamic heads: more than the row-group cosine kernel holds, so
+    the segment similarity takes the per-token kernel."""
+    wl = dataclasses.replace(WORKLOADS["fkv480p"], width=8, height=4, H=12, n_static=2, seg_len=8, retention=0.5,
+                             history=(1, 6), chunk=(6, 9), name="fkv-10dyn")
+    _run(wl)
+
+
 @pytest.mark.parametrize("r", [0.3, 0.33, 0.5])
 def test_forcing_per_frame_bottomk(r):
     """Section 3.4 as printed: six segments per frame, floor(r 6) kept in
