@@ -408,6 +408,8 @@ KVB_DEV bool evict_flag(const SelectLaunch& a, const EvSel& q, int64_t hb, int b
   return false;
 }
 
+constexpr int EV_KPT = 16;   // keys per thread held in registers by the eviction select
+
 __global__ __launch_bounds__(1024) void evict_select_kernel(SelectLaunch a) {
   const int h = blockIdx.x;
   const int tid = threadIdx.x;
@@ -442,16 +444,39 @@ __global__ __launch_bounds__(1024) void evict_select_kernel(SelectLaunch a) {
   __shared__ unsigned long long s_min;
   if (mode == 2) {
     if (tid == 0) { s_prefix = 0; s_mask = 0; s_rem = r; }
+    // Up to EV_KPT keys per thread are read once into registers (all their
+    // loads in flight together); the passes then bin registers.  Larger
+    // banks read the keys from memory at every pass.
+    const bool inreg = n <= EV_KPT * 1024;
+    uint64_t kr[EV_KPT];
+    uint32_t live = 0;
+    if (inreg) {
+#pragma unroll
+      for (int i = 0; i < EV_KPT; ++i) {
+        const int b = tid + 1024 * i;
+        kr[i] = 0;
+        if (b < n && !(force && gated && !a.skip_cross && a.t[hb + b] <= ks)) {
+          kr[i] = evict_key(a.rhoP[hb + b], a.bank_tok[hb + b], oldest);
+          live |= 1u << i;
+        }
+      }
+    }
     __syncthreads();
     for (int pass = 0; pass < 8; ++pass) {
       const int shift = 56 - 8 * pass;
       for (int i = tid; i < 256; i += 1024) hist[i] = 0;
       __syncthreads();
       const uint64_t pre = s_prefix, msk = s_mask;
-      for (int b = tid; b < n; b += 1024) {
-        if (force && gated && !a.skip_cross && a.t[hb + b] <= ks) continue;
-        const uint64_t key = evict_key(a.rhoP[hb + b], a.bank_tok[hb + b], oldest);
-        if ((key & msk) == pre) atomicAdd(&hist[(key >> shift) & 0xFF], 1);
+      if (inreg) {
+#pragma unroll
+        for (int i = 0; i < EV_KPT; ++i)
+          if (((live >> i) & 1u) && (kr[i] & msk) == pre) atomicAdd(&hist[(kr[i] >> shift) & 0xFF], 1);
+      } else {
+        for (int b = tid; b < n; b += 1024) {
+          if (force && gated && !a.skip_cross && a.t[hb + b] <= ks) continue;
+          const uint64_t key = evict_key(a.rhoP[hb + b], a.bank_tok[hb + b], oldest);
+          if ((key & msk) == pre) atomicAdd(&hist[(key >> shift) & 0xFF], 1);
+        }
       }
       __syncthreads();
       // suffix counts S(d) = #keys with digit >= d: thread t < 256 takes digit
@@ -488,10 +513,16 @@ __global__ __launch_bounds__(1024) void evict_select_kernel(SelectLaunch a) {
         // holds a single key): the threshold is the bin's smallest key
         const uint64_t pre2 = s_prefix, msk2 = s_mask;
         unsigned long long mn = ~0ull;
-        for (int b = tid; b < n; b += 1024) {
-          if (force && gated && !a.skip_cross && a.t[hb + b] <= ks) continue;
-          const uint64_t key = evict_key(a.rhoP[hb + b], a.bank_tok[hb + b], oldest);
-          if ((key & msk2) == pre2) mn = key < mn ? key : mn;
+        if (inreg) {
+#pragma unroll
+          for (int i = 0; i < EV_KPT; ++i)
+            if (((live >> i) & 1u) && (kr[i] & msk2) == pre2) mn = kr[i] < mn ? kr[i] : mn;
+        } else {
+          for (int b = tid; b < n; b += 1024) {
+            if (force && gated && !a.skip_cross && a.t[hb + b] <= ks) continue;
+            const uint64_t key = evict_key(a.rhoP[hb + b], a.bank_tok[hb + b], oldest);
+            if ((key & msk2) == pre2) mn = key < mn ? key : mn;
+          }
         }
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) {
