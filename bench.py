@@ -541,9 +541,47 @@ def forcing_bench(steps: int = 10, seed: int = 0):
                                "bytes_read": cos_bytes, "GB/s": round(cos_bytes / sc / 1e6, 1),
                                "frac_hbm_peak": round(cos_bytes / sc / 1e6 / PEAK_HBM_GBS, 4)},
             "hbm_kernels": recorded_hbm_kernels("fkv480p"),
+            "segment_scoring_layers": score_layers_bench(wl, labels, T),
             "attention": {"Lkv_static": F + F + wl.Lq, "Lkv_dynamic": F + keep * wl.seg_len + wl.Lq,
                           "TFLOP/s": round(flop / at / 1e9, 1),
                           "frac_bf16_peak": round(flop / at / 1e9 / PEAK_BF16_TFLOPS, 4)}}
+
+
+def score_layers_bench(wl, labels, T, layers: int = 30, iters: int = 10):
+    """kvbank_score_layers on the hybrid layer's shape for the 30 layers of
+    the model at once (every layer's own history and chunk keys, drawn on the
+    device): one launch each for the cosines, the segment means and the
+    BottomK orders.  Bytes = the dynamic heads' history and first chunk frame
+    of every layer, read once."""
+    import torch
+    import kv_cache_compression_head_amd as kb
+    H, d, F = wl.H, wl.d, wl.F
+    N = T * F
+    desc = kb.LayerDesc(H=H, d=d, M=0, dtype=kb.KVB_BF16, frame_tokens=F, labels=[int(x) for x in labels],
+                        seg_len=wl.seg_len, retention=wl.retention)
+    g = torch.Generator(device="cuda").manual_seed(3)
+    K = torch.randn(layers, H, N, d, device="cuda", generator=g).to(torch.bfloat16)
+    C = torch.randn(layers, H, wl.Lq, d, device="cuda", generator=g).to(torch.bfloat16)
+    sc = torch.empty(layers, H, N, dtype=torch.float32, device="cuda")
+    od = torch.empty(layers, H, N, dtype=torch.int32, device="cuda")
+    ws = torch.empty(kb.kvbank_score_layers_workspace_size(desc, layers, N), dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        kb.kvbank_score_layers(desc, K, C, sc, od, ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(iters):
+        kb.kvbank_score_layers(desc, K, C, sc, od, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    ndyn = int(sum(1 for x in labels if int(x) == 2))
+    nbytes = layers * (T + 1) * F * ndyn * d * 2
+    del K, C, sc, od, ws
+    torch.cuda.empty_cache()
+    return {"call": "kvbank_score_layers (cos_rows_kernel + segmean_kernel + rank_sort_kernel, all layers)",
+            "layers": layers, "ms": round(ms, 4), "bytes_read": nbytes, "GB/s": round(nbytes / ms / 1e6, 1),
+            "frac_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
 
 
 def rollout_bench(chunks: int, layers: int = 0, seed: int = 0, policy: int = 0):

@@ -234,6 +234,31 @@ int kvbank_score(const kvb_layer_desc* L, const kvb_bank* bank, const void* cand
                  int32_t N, const kvb_kv_layout* lay, float* out_D, float* out_score, int32_t* out_order, void* ws,
                  size_t ws_bytes, kvb_stream_t stream);
 
+/* Forcing-KV segment scoring of several layers in one call (Forcing-KV notes,
+ * section 3.4 and the section 3.5 sketch: a layer's dynamic heads score each
+ * history segment by the mean cosine between adjacent frames; the layers of
+ * a model score independently).  For nlayers layers that share the
+ * descriptor L and whose heads are all static or dynamic, this gives the
+ * same outputs, bit for bit, as kvbank_score on each layer l with
+ *   cand_k  + l * cand_layer_stride   [H][N][d] history keys of layer l
+ *   chunk_k + l * chunk_layer_stride  [H][chunk_len][d] the chunk's keys
+ *                                     (its first frame pairs with the last
+ *                                     history frame)
+ *   out_score + l * H * N, out_order + l * H * N   (as kvbank_score's)
+ * (strides in elements, multiples of 16 bytes), with the cosines, the
+ * segment means and the BottomK orders of all layers in one launch each: at
+ * one layer the segment cosine reads too few bytes to reach the memory
+ * bandwidth past a launch.  Static heads' rows are untouched.  Workspace:
+ * kvbank_score_layers_workspace_size bytes (the per-token cosines).
+ * KVB_EPARAM with density heads, with KVB_POL_FRAME_BOTTOMK or with more
+ * than 1,024 items (N / seg_len) per layer; KVB_ESHAPE for strides shorter
+ * than one layer, chunk_len < frame_tokens, or as kvbank_score.  N = 0,
+ * nlayers = 0 or no dynamic head is a no-op. */
+int kvbank_score_layers_workspace_size(const kvb_layer_desc* L, int32_t nlayers, int32_t N, size_t* bytes);
+int kvbank_score_layers(const kvb_layer_desc* L, int32_t nlayers, const void* cand_k, int64_t cand_layer_stride,
+                        const void* chunk_k, int64_t chunk_layer_stride, int32_t chunk_len, int32_t N,
+                        float* out_score, int32_t* out_order, void* ws, size_t ws_bytes, kvb_stream_t stream);
+
 /* Admission / eviction and segment table (DensityKV appendix B.1 "Online
  * Bank Update"; Forcing-KV sections 3.3-3.4).
  *   density heads: shared prefix k*, eviction set, exact K/V/token moves into

@@ -17,6 +17,7 @@ __all__ = [
     "KVB_POL_REFRESH_BASELINE", "KVB_POL_EVICT_DENSEST", "KVB_POL_EVICT_OLDEST", "KVB_POL_HEAD_PREFIX",
     "KVB_POL_FILL_BELOW_CAP", "KVB_POL_FRAME_BOTTOMK", "KVB_POL_SEQUENTIAL",
     "KvbError", "load_library", "kvbank_workspace_size", "kvbank_score", "kvbank_update",
+    "kvbank_score_layers", "kvbank_score_layers_workspace_size",
     "chunk_attention", "chunk_attention_noalloc", "chunk_attention_workspace_size", "kvbank_window_advance",
     "forcing_head_profile",
     "forcing_head_profile_workspace_size", "kvb_last_error", "LayerDesc", "Bank", "KVLayout", "UpdateOut",
@@ -36,7 +37,8 @@ KVB_POL_SEQUENTIAL = 128
 KVB_MAX_SEGMENTS = 256
 HEADER_FUNCTIONS = ("kvbank_workspace_size", "kvbank_score", "kvbank_update", "chunk_attention",
                     "chunk_attention_workspace_size", "kvbank_window_advance", "forcing_head_profile_workspace_size",
-                    "forcing_head_profile", "kvb_last_error", "kvb_source_hash", "chunk_attention_noalloc")
+                    "forcing_head_profile", "kvb_last_error", "kvb_source_hash", "chunk_attention_noalloc",
+                    "kvbank_score_layers_workspace_size", "kvbank_score_layers")
 
 _c_i32, _c_f32, _c_f64, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 
@@ -101,6 +103,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kvbank_update.argtypes = [ctypes.POINTER(kvb_layer_desc), ctypes.POINTER(kvb_bank), _vp, _vp, _vp, _c_i32,
                                   _vp, _vp, ctypes.POINTER(kvb_kv_layout), ctypes.POINTER(kvb_update_out), _vp,
                                   ctypes.c_size_t, _vp]
+    lib.kvbank_score_layers_workspace_size.argtypes = [ctypes.POINTER(kvb_layer_desc), _c_i32, _c_i32,
+                                                      ctypes.POINTER(ctypes.c_size_t)]
+    lib.kvbank_score_layers.argtypes = [ctypes.POINTER(kvb_layer_desc), _c_i32, _vp, ctypes.c_int64, _vp,
+                                        ctypes.c_int64, _c_i32, _c_i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.chunk_attention.argtypes = [ctypes.POINTER(kvb_attn_desc), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.chunk_attention_noalloc.argtypes = [ctypes.POINTER(kvb_attn_desc), _vp, _vp, _vp, _vp, _vp]
     lib.chunk_attention_workspace_size.argtypes = [ctypes.POINTER(kvb_attn_desc), ctypes.POINTER(ctypes.c_size_t)]
@@ -111,6 +117,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.forcing_head_profile.argtypes = [ctypes.POINTER(kvb_attn_desc), _vp, _vp, _vp, _vp, _c_i32, _c_f32, _vp, _vp,
                                          _vp, _vp, ctypes.c_size_t, _vp]
     for f in ("kvbank_workspace_size", "kvbank_score", "kvbank_update", "chunk_attention", "chunk_attention_noalloc",
+              "kvbank_score_layers_workspace_size", "kvbank_score_layers",
               "chunk_attention_workspace_size", "kvbank_window_advance", "forcing_head_profile_workspace_size",
               "forcing_head_profile"):
         getattr(lib, f).restype = ctypes.c_int
@@ -333,6 +340,38 @@ def kvbank_score(layer: LayerDesc, bank: Optional[Bank], cand_k, cand_tok, N: in
                             _ptr(cand_tok), int(N), ctypes.byref(cl) if cl is not None else None, _ptr(out_D),
                             _ptr(out_score), _ptr(out_order), _ptr(ws), 0 if ws is None else ws.numel(),
                             _stream(stream)))
+
+
+def kvbank_score_layers_workspace_size(layer: LayerDesc, nlayers: int, N: int) -> int:
+    lib = load_library()
+    desc = layer.c()
+    n = ctypes.c_size_t(0)
+    _check(lib.kvbank_score_layers_workspace_size(ctypes.byref(desc), int(nlayers), int(N), ctypes.byref(n)))
+    return int(n.value)
+
+
+def kvbank_score_layers(layer: LayerDesc, cand_k, chunk_k, out_score, out_order, ws=None, stream=None):
+    """Forcing-KV segment scoring of several layers that share `layer`:
+    cand_k [L][H][N][d] history keys, chunk_k [L][H][chunk_len][d] the
+    chunk's keys, out_score float32 / out_order int32 [L][H][N].  Allocates
+    the workspace when none is given."""
+    import torch
+    lib = load_library()
+    desc = layer.c()
+    kd = _kv_dtype(layer.dtype)
+    if cand_k.dim() != 4 or chunk_k.dim() != 4:
+        raise ValueError("cand_k and chunk_k must be [L][H][rows][d]")
+    nl, N, cl = int(cand_k.shape[0]), int(cand_k.shape[2]), int(chunk_k.shape[2])
+    _req(cand_k, "cand_k", kd, (nl, layer.H, N, layer.d))
+    _req(chunk_k, "chunk_k", kd, (nl, layer.H, cl, layer.d))
+    _req(out_score, "out_score", torch.float32, (nl, layer.H, N))
+    _req(out_order, "out_order", torch.int32, (nl, layer.H, N))
+    if ws is None:
+        ws = torch.empty(max(1, kvbank_score_layers_workspace_size(layer, nl, N)), dtype=torch.uint8,
+                         device=cand_k.device)
+    _check(lib.kvbank_score_layers(ctypes.byref(desc), nl, _ptr(cand_k), layer.H * N * layer.d, _ptr(chunk_k),
+                                   layer.H * cl * layer.d, cl, N, _ptr(out_score), _ptr(out_order), _ptr(ws),
+                                   ws.numel(), _stream(stream)))
 
 
 def kvbank_update(layer: LayerDesc, bank: Optional[Bank], cand_k, cand_v, cand_tok, N: int, D, order,

@@ -439,6 +439,73 @@ int kvbank_score(const kvb_layer_desc* L, const kvb_bank* bank, const void* cand
   return ok();
 }
 
+// Forcing-KV segment scoring of several layers that share one descriptor:
+// the cosines, the segment means and the BottomK order of every layer in
+// one launch each.
+static int check_score_layers(const kvb_layer_desc* L, int32_t nlayers, int32_t N, Heads* hd) {
+  int rc = check_layer(L, N, hd);
+  if (rc) return rc;
+  if (nlayers < 0 || nlayers > 65535) return fail(KVB_ESHAPE, "nlayers=%d outside [0, 65535]", nlayers);
+  if (hd->dens) return fail(KVB_EPARAM, "kvbank_score_layers takes Forcing-KV layers only (no density heads)");
+  if (L->params.policy & KVB_POL_FRAME_BOTTOMK)
+    return fail(KVB_EPARAM, "kvbank_score_layers orders the items of the whole history (no KVB_POL_FRAME_BOTTOMK)");
+  if (hd->dyn) {
+    const int items = N / L->params.seg_len;
+    if (items > 1024) return fail(KVB_EPARAM, "%d items per layer (at most 1,024)", items);
+    const int chunks = hd->ndyn * (L->d * (L->dtype == KVB_BF16 ? 2 : 4) / 16);
+    if (chunks > 1024)
+      return fail(KVB_ESHAPE, "%d dynamic heads of d=%d %s exceed the cosine kernel's 16 KB per token", hd->ndyn,
+                  L->d, L->dtype == KVB_BF16 ? "bf16" : "fp32");
+  }
+  return KVB_OK;
+}
+
+int kvbank_score_layers_workspace_size(const kvb_layer_desc* L, int32_t nlayers, int32_t N, size_t* bytes) {
+  Heads hd;
+  int rc = check_score_layers(L, nlayers, N, &hd);
+  if (rc) return rc;
+  if (!bytes) return fail(KVB_EINVAL, "bytes is NULL");
+  // the cosine of every token and frame pair of every layer
+  *bytes = hd.dyn ? (((size_t)nlayers * (size_t)N * 4 + 255) & ~(size_t)255) : 0;
+  return ok();
+}
+
+int kvbank_score_layers(const kvb_layer_desc* L, int32_t nlayers, const void* cand_k, int64_t cand_layer_stride,
+                        const void* chunk_k, int64_t chunk_layer_stride, int32_t chunk_len, int32_t N,
+                        float* out_score, int32_t* out_order, void* ws, size_t ws_bytes, kvb_stream_t stream) {
+  Heads hd;
+  int rc = check_score_layers(L, nlayers, N, &hd);
+  if (rc) return rc;
+  if (N == 0 || nlayers == 0 || !hd.dyn) return ok();
+  const int H = L->H, d = L->d, F = L->frame_tokens;
+  REQ_PTR(cand_k, 16, "cand_k");
+  REQ_PTR(chunk_k, 16, "chunk_k");
+  REQ_PTR(out_score, 4, "out_score");
+  REQ_PTR(out_order, 4, "out_order");
+  if (chunk_len < F) return fail(KVB_ESHAPE, "chunk_len=%d < frame_tokens=%d", chunk_len, F);
+  const int64_t esz = L->dtype == KVB_BF16 ? 2 : 4;
+  if (cand_layer_stride < (int64_t)H * N * d || (cand_layer_stride * esz) % 16 != 0)
+    return fail(KVB_ESHAPE, "cand_layer_stride=%lld (at least H N d, 16-byte multiple)", (long long)cand_layer_stride);
+  if (chunk_layer_stride < (int64_t)H * chunk_len * d || (chunk_layer_stride * esz) % 16 != 0)
+    return fail(KVB_ESHAPE, "chunk_layer_stride=%lld (at least H chunk_len d, 16-byte multiple)",
+                (long long)chunk_layer_stride);
+  size_t need = 0;
+  if ((rc = kvbank_score_layers_workspace_size(L, nlayers, N, &need))) return rc;
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int T = N / F, seg = L->params.seg_len, items = N / seg;
+  CosLaunch c{};
+  c.hist = cand_k; c.nxt = chunk_k; c.et = L->dtype; c.H = H; c.d = d; c.F = F; c.T = T; c.seg_len = seg;
+  c.nxt_rows = chunk_len; c.ndyn = hd.ndyn;
+  for (int i = 0; i < hd.ndyn; ++i) c.dyn_heads[i] = hd.dyn_list[i];
+  c.cosbuf = (float*)ws; c.scores = out_score; c.score_hstride = N;
+  c.nlayers = nlayers; c.hist_ls = cand_layer_stride; c.nxt_ls = chunk_layer_stride; c.score_ls = (int64_t)H * N;
+  HIPCHK(launch_segment_cosine(c, st));
+  HIPCHK(launch_rank_sort_layers(out_score, N, (int64_t)H * N, hd.dyn, H, items, nlayers, out_order, N,
+                                 (int64_t)H * N, st));
+  return ok();
+}
+
 int kvbank_update(const kvb_layer_desc* L, kvb_bank* bank, const void* cand_k, const void* cand_v,
                   const int32_t* cand_tok, int32_t N, const float* D, const int32_t* order,
                   const kvb_kv_layout* lay, kvb_update_out* out, void* ws, size_t ws_bytes, kvb_stream_t stream) {

@@ -25,6 +25,7 @@ struct CosArgs {
   int32_t H, d, F, T, nxt_rows, ndyn;
   int32_t dyn_heads[64];
   float* cosbuf;
+  int64_t hist_ls, nxt_ls;   // layer strides (elements); layer = blockIdx.z
 };
 
 // One wave per (token position p, group of U cosines).  The wave's lanes
@@ -43,6 +44,10 @@ __global__ __launch_bounds__(256) void cos_kernel(CosArgs a) {
   const int p = blockIdx.x * 4 + wave_id();
   if (p >= a.F) return;
   const int t0 = blockIdx.y * U;              // first frame of the group
+  const int layer = blockIdx.z;
+  const E* hist = (const E*)a.hist + layer * a.hist_ls;
+  const E* nxt = (const E*)a.nxt + layer * a.nxt_ls;
+  float* cosbuf = a.cosbuf + (int64_t)layer * a.T * a.F;
   const int cpr = a.d / EPC;
   const int nch = a.ndyn * cpr;
   // element offsets of this lane's chunks: frame 0 of the history, and the
@@ -67,7 +72,7 @@ __global__ __launch_bounds__(256) void cos_kernel(CosArgs a) {
     for (int k = 0; k < KC; ++k) {
       fr[u][k] = u32x4_t{0u, 0u, 0u, 0u};
       if (ok[k] && t <= a.T) {
-        const E* src = t < a.T ? (const E*)a.hist + hoff[k] + t * fstride : (const E*)a.nxt + noff[k];
+        const E* src = t < a.T ? hist + hoff[k] + t * fstride : nxt + noff[k];
         fr[u][k] = *reinterpret_cast<const u32x4_t*>(src);
       }
     }
@@ -93,7 +98,7 @@ __global__ __launch_bounds__(256) void cos_kernel(CosArgs a) {
     if (u > 0) {
       dot = wave_sum(dot);
       const float den = fmaxf(sqrtf(nprev) * sqrtf(nn), 1e-8f);
-      if (lane == 0) a.cosbuf[(int64_t)(t - 1) * a.F + p] = dot / den;
+      if (lane == 0) cosbuf[(int64_t)(t - 1) * a.F + p] = dot / den;
     }
     nprev = nn;
   }
@@ -116,6 +121,10 @@ __global__ __launch_bounds__(256) void cos_rows_kernel(CosArgs a) {
   const int p = (blockIdx.x * 4 + w) * TPW + lane / CPR;
   const bool okp = p < a.F;
   const int t0 = blockIdx.y * (NF - 1);   // first frame of the group
+  const int layer = blockIdx.z;
+  const E* hist = (const E*)a.hist + layer * a.hist_ls;
+  const E* nxt = (const E*)a.nxt + layer * a.nxt_ls;
+  float* cosbuf = a.cosbuf + (int64_t)layer * a.T * a.F;
   u32x4_t fr[NF][NH];
 #pragma unroll
   for (int u = 0; u < NF; ++u) {
@@ -125,8 +134,8 @@ __global__ __launch_bounds__(256) void cos_rows_kernel(CosArgs a) {
       fr[u][h] = u32x4_t{0u, 0u, 0u, 0u};
       if (h < a.ndyn && okp && t <= a.T) {
         const int hd = a.dyn_heads[h];
-        const E* src = t < a.T ? (const E*)a.hist + (((int64_t)hd * a.T + t) * a.F + p) * a.d + c * EPC
-                               : (const E*)a.nxt + ((int64_t)hd * a.nxt_rows + p) * a.d + c * EPC;
+        const E* src = t < a.T ? hist + (((int64_t)hd * a.T + t) * a.F + p) * a.d + c * EPC
+                               : nxt + ((int64_t)hd * a.nxt_rows + p) * a.d + c * EPC;
         fr[u][h] = *reinterpret_cast<const u32x4_t*>(src);
       }
     }
@@ -154,7 +163,7 @@ __global__ __launch_bounds__(256) void cos_rows_kernel(CosArgs a) {
     }
     if (u > 0 && c == 0 && okp && t <= a.T) {
       const float den = fmaxf(sqrtf(nprev) * sqrtf(nn), 1e-8f);
-      a.cosbuf[(int64_t)(t - 1) * a.F + p] = dot / den;
+      cosbuf[(int64_t)(t - 1) * a.F + p] = dot / den;
     }
     nprev = nn;
   }
@@ -162,11 +171,14 @@ __global__ __launch_bounds__(256) void cos_rows_kernel(CosArgs a) {
 
 // segment means: one work-group per (frame, segment) item, fixed-order sum
 __global__ __launch_bounds__(256) void segmean_kernel(const float* __restrict__ cosbuf, int F, int seg_len, int ndyn,
-                                                      CosArgs a, float* __restrict__ scores, int64_t shs) {
+                                                      CosArgs a, float* __restrict__ scores, int64_t shs,
+                                                      int64_t score_ls) {
   const int item = blockIdx.x;
+  const int layer = blockIdx.y;
   const int nseg = F / seg_len;
   const int t = item / nseg, j = item % nseg;
-  const float* src = cosbuf + (int64_t)t * F + (int64_t)j * seg_len;
+  const float* src = cosbuf + (int64_t)layer * a.T * F + (int64_t)t * F + (int64_t)j * seg_len;
+  scores += layer * score_ls;
   __shared__ float red[256];
   float s = 0.f;
   for (int i = threadIdx.x; i < seg_len; i += 256) s += src[i];
@@ -186,10 +198,14 @@ hipError_t launch_segment_cosine(const CosLaunch& c, hipStream_t st) {
   a.ndyn = c.ndyn;
   for (int i = 0; i < 64; ++i) a.dyn_heads[i] = c.dyn_heads[i];
   a.cosbuf = c.cosbuf;
+  a.hist_ls = c.nlayers > 1 ? c.hist_ls : 0;
+  a.nxt_ls = c.nlayers > 1 ? c.nxt_ls : 0;
+  const unsigned nl = (unsigned)(c.nlayers > 1 ? c.nlayers : 1);
   const int cpr = c.d * (c.et == ET_BF16 ? 2 : 4) / 16;
   if (c.ndyn <= COS_ROWS_NH && (cpr == 8 || cpr == 16 || cpr == 32)) {
     constexpr int NF = COS_ROWS_NF;
-    const dim3 g((unsigned)((c.F + 4 * (64 / cpr) - 1) / (4 * (64 / cpr))), (unsigned)((c.T + NF - 2) / (NF - 1)));
+    const dim3 g((unsigned)((c.F + 4 * (64 / cpr) - 1) / (4 * (64 / cpr))), (unsigned)((c.T + NF - 2) / (NF - 1)),
+                 nl);
 #define KVB_COSR(E)                                                                                           \
   if (cpr == 8) hipLaunchKernelGGL((cos_rows_kernel<E, 8, COS_ROWS_NH, NF>), g, dim3(256), 0, st, a);        \
   else if (cpr == 16) hipLaunchKernelGGL((cos_rows_kernel<E, 16, COS_ROWS_NH, NF>), g, dim3(256), 0, st, a); \
@@ -204,7 +220,7 @@ hipError_t launch_segment_cosine(const CosLaunch& c, hipStream_t st) {
   const int kc = (c.ndyn * cpr + 63) / 64;   // <= 16 (checked on the host)
   const int kcp = kc <= 1 ? 1 : kc <= 2 ? 2 : kc <= 4 ? 4 : kc <= 8 ? 8 : 16;
   const int U = kcp >= 16 ? 1 : 16 / kcp;   // cosines per wave, as in the kernel
-  const dim3 grid((unsigned)((c.F + 3) / 4), (unsigned)((c.T + U - 1) / U));
+  const dim3 grid((unsigned)((c.F + 3) / 4), (unsigned)((c.T + U - 1) / U), nl);
 #define KVB_COS(E)                                                                                 \
   if (kcp == 1) hipLaunchKernelGGL((cos_kernel<E, 1>), grid, dim3(256), 0, st, a);                 \
   else if (kcp == 2) hipLaunchKernelGGL((cos_kernel<E, 2>), grid, dim3(256), 0, st, a);            \
@@ -219,8 +235,8 @@ hipError_t launch_segment_cosine(const CosLaunch& c, hipStream_t st) {
 #undef KVB_COS
   }
   const int items = c.T * (c.F / c.seg_len);
-  hipLaunchKernelGGL(segmean_kernel, dim3(items), dim3(256), 0, st, c.cosbuf, c.F, c.seg_len, c.ndyn, a, c.scores,
-                     c.score_hstride);
+  hipLaunchKernelGGL(segmean_kernel, dim3(items, nl), dim3(256), 0, st, c.cosbuf, c.F, c.seg_len, c.ndyn, a, c.scores,
+                     c.score_hstride, nl > 1 ? c.score_ls : 0);
   return hipGetLastError();
 }
 

@@ -120,6 +120,9 @@ hipError_t launch_zero_i32_clamp(int32_t* const* ptrs, const int64_t* lens, int 
                                  hipStream_t s);
 
 // keys for sorting: key = float_key(score[h][i]) << 32 | tie[i]; value = i
+hipError_t launch_rank_sort_layers(const float* score, int64_t score_hstride, int64_t score_ls, uint64_t on, int H,
+                                   int n, int nlayers, int32_t* out, int64_t out_hstride, int64_t out_ls,
+                                   hipStream_t st);
 hipError_t launch_sort(const float* score, int64_t score_hstride, const int32_t* tie, int64_t tie_hstride,
                        uint64_t head_on, int H, int n, uint64_t* kbuf0, uint64_t* kbuf1,
                        int32_t* vbuf0, int32_t* vbuf1, int32_t* out_order, int64_t out_hstride,
@@ -251,6 +254,11 @@ struct CosLaunch {
   float* cosbuf;       // [T][F]
   float* scores;       // [H][N] (written for dynamic heads)
   int64_t score_hstride;
+  // several layers in one launch (kvbank_score_layers): layer l reads
+  // hist + l hist_ls, nxt + l nxt_ls (elements) and writes cosbuf + l T F,
+  // scores + l score_ls; nlayers = 1 for one layer
+  int32_t nlayers;
+  int64_t hist_ls, nxt_ls, score_ls;
 };
 hipError_t launch_segment_cosine(const CosLaunch& a, hipStream_t s);
 

@@ -213,9 +213,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint64_t* __restrict__
 __global__ __launch_bounds__(1024) void rank_sort_kernel(const float* __restrict__ score, int64_t score_hstride,
                                                         const int32_t* __restrict__ tie, int64_t tie_hstride,
                                                         uint64_t on, int n, int32_t* __restrict__ out,
-                                                        int64_t out_hstride) {
+                                                        int64_t out_hstride, int64_t score_ls, int64_t out_ls) {
   const int h = blockIdx.x;
   if (!head_on(on, h)) return;
+  // layer blockIdx.y of a batch of layers (strides 0 for one layer)
+  score += blockIdx.y * score_ls;
+  out += blockIdx.y * out_ls;
   __shared__ uint64_t sk[1024];
   const int i = threadIdx.x;
   if (i < n) sk[i] = sort_key(score, tie, tie_hstride, h, i, score_hstride);
@@ -233,7 +236,7 @@ hipError_t launch_sort(const float* score, int64_t score_hstride, const int32_t*
   if (n <= 0) return hipSuccess;
   if (n <= 1024) {
     hipLaunchKernelGGL(rank_sort_kernel, dim3(H), dim3(1024), 0, st, score, score_hstride, tie, tie_hstride, on, n,
-                       out, out_hstride);
+                       out, out_hstride, (int64_t)0, (int64_t)0);
     return hipGetLastError();
   }
   const int nb = (n + SORT_BS - 1) / SORT_BS;
@@ -250,6 +253,17 @@ hipError_t launch_sort(const float* score, int64_t score_hstride, const int32_t*
     uint64_t* tk = ka; ka = kb; kb = tk;
     int32_t* tv = va; va = vb; vb = tv;
   }
+  return hipGetLastError();
+}
+
+// the rank sort of up to 1,024 items for each of nlayers layers (layer l's
+// scores and order at + l score_ls, + l out_ls)
+hipError_t launch_rank_sort_layers(const float* score, int64_t score_hstride, int64_t score_ls, uint64_t on, int H,
+                                   int n, int nlayers, int32_t* out, int64_t out_hstride, int64_t out_ls,
+                                   hipStream_t st) {
+  if (n <= 0 || nlayers <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rank_sort_kernel, dim3(H, nlayers), dim3(1024), 0, st, score, score_hstride, nullptr, (int64_t)0,
+                     on, n, out, out_hstride, score_ls, out_ls);
   return hipGetLastError();
 }
 

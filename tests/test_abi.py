@@ -180,3 +180,39 @@ def test_head_profile_rejects_before_launch():
     b = kb.kvb_attn_desc(2, 96, 40, 1, 0.0, 4, 1, 0)
     assert lib.forcing_head_profile_workspace_size(ctypes.byref(b), 100, ctypes.byref(n)) == -2
     assert lib.forcing_head_profile_workspace_size(ctypes.byref(a), -1, ctypes.byref(n)) == -2
+
+
+def test_score_layers_rejects_before_launch():
+    """kvbank_score_layers takes Forcing-KV layers only, checks the layer
+    strides, the item count and the workspace on the host; nlayers = 0 is a
+    no-op."""
+    lib = kb.load_library()
+    F, N = 16, 64
+    fk = kb.LayerDesc(H=4, d=64, M=0, dtype=kb.KVB_BF16, frame_tokens=F, labels=[1, 2, 2, 1], seg_len=8,
+                      retention=0.5)
+    dn = kb.LayerDesc(H=4, d=64, M=32, dtype=kb.KVB_BF16, frame_tokens=F, labels=[0, 2, 2, 1], seg_len=8,
+                      retention=0.5)
+    n = ctypes.c_size_t(0)
+    c = fk.c()
+    assert lib.kvbank_score_layers_workspace_size(ctypes.byref(c), 3, N, ctypes.byref(n)) == 0
+    assert n.value == (3 * N * 4 + 255) // 256 * 256
+    cd = dn.c()
+    assert lib.kvbank_score_layers_workspace_size(ctypes.byref(cd), 3, N, ctypes.byref(n)) == -4
+    per = dict(fk.__dict__)
+    per["policy"] = kb.KVB_POL_FRAME_BOTTOMK
+    cf = kb.LayerDesc(**per).c()
+    assert lib.kvbank_score_layers_workspace_size(ctypes.byref(cf), 3, N, ctypes.byref(n)) == -4
+    sl = lib.kvbank_score_layers
+    hs, cs = 4 * N * 64, 4 * 2 * F * 64    # one layer of history keys, of chunk keys
+    ws = 1 << 40
+
+    def call(nl=3, hstr=hs, cstr=cs, cl=2 * F, wsb=ws, ck=16, desc=c):
+        return sl(ctypes.byref(desc), nl, ck, hstr, 32, cstr, cl, N, 48, 64, 256, wsb, None)
+    assert call(nl=0, ck=None) == 0
+    assert call(hstr=hs - 8) == -2              # stride shorter than a layer
+    assert call(cstr=cs + 4) == -2              # not a 16-byte multiple
+    assert call(cl=F - 1) == -2                 # chunk shorter than a frame
+    assert call(ck=17) == -1                    # misaligned
+    assert call(wsb=16) == -5                   # workspace too small
+    assert call(desc=cd) == -4                  # density heads
+    assert kb.kvb_last_error()

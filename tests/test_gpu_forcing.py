@@ -197,3 +197,54 @@ def test_forcing_order_shared_across_layers():
     kept1 = of.bottomk(scores[1], wl.retention)
     assert kept1.tolist() != kept0.tolist()
     gc.banner(f"shared order: layer-0 kept {kept0.tolist()} layer-1 own {kept1.tolist()}")
+
+
+@pytest.mark.parametrize("case", ["fkv480p", "fkv-10dyn"])
+def test_score_layers_matches_per_layer(case):
+    """kvbank_score_layers on three layers (each with its own seeded keys)
+    gives, bit for bit, kvbank_score's segment scores and BottomK orders of
+    each layer, leaves static heads' rows untouched, and matches the oracle's
+    segment scores.  fkv-10dyn takes the per-token cosine kernel."""
+    import torch
+    import kv_cache_compression_head_amd as kb
+    if case == "fkv480p":
+        wl = WORKLOADS["fkv480p"]
+    else:
+        wl = dataclasses.replace(WORKLOADS["fkv480p"], width=8, height=4, H=12, n_static=2, seg_len=8,
+                                 retention=0.5, history=(1, 6), chunk=(6, 9), name="fkv-10dyn")
+    labels = head_labels(wl, 0)
+    desc = kb.LayerDesc(H=wl.H, d=wl.d, M=0, dtype=kb.KVB_BF16, frame_tokens=wl.F, labels=labels.tolist(),
+                        seg_len=wl.seg_len, retention=wl.retention)
+    h0, h1 = wl.history
+    c0, c1 = wl.chunk
+    hist_f, ch_f = list(range(h0, h1)), list(range(c0, c1))
+    nl = 3
+    K, C = [], []
+    for layer in range(nl):
+        gen = LayerGen(wl, 0, layer)
+        K.append(gen.keys_all(hist_f, hist_f))
+        C.append(gen.keys_all(ch_f, ch_f))
+    kdt = torch.bfloat16
+    Kd, Cd = gc.dev(np.stack(K), kdt), gc.dev(np.stack(C), kdt)
+    N = Kd.shape[2]
+    items = N // wl.seg_len
+    gc.banner(f"score_layers {case}: {nl} layers, N={N}, items={items}")
+    sc = torch.full((nl, wl.H, N), -7.0, dtype=torch.float32, device="cuda")
+    od = torch.full((nl, wl.H, N), -1, dtype=torch.int32, device="cuda")
+    kb.kvbank_score_layers(desc, Kd, Cd, sc, od)
+    torch.cuda.synchronize()
+    ws = torch.empty(kb.kvbank_workspace_size(desc, N), dtype=torch.uint8, device="cuda")
+    dyn = [h for h in range(wl.H) if labels[h] == 2]
+    stat = [h for h in range(wl.H) if labels[h] == 1]
+    for layer in range(nl):
+        s1 = torch.full((wl.H, N), -7.0, dtype=torch.float32, device="cuda")
+        o1 = torch.full((wl.H, N), -1, dtype=torch.int32, device="cuda")
+        kb.kvbank_score(desc, None, Kd[layer], None, N, kb.KVLayout(chunk_k=Cd[layer]), None, s1, o1, ws)
+        torch.cuda.synchronize()
+        for h in dyn:
+            assert torch.equal(sc[layer, h, :items], s1[h, :items]), (layer, h)
+            assert torch.equal(od[layer, h, :items], o1[h, :items]), (layer, h)
+        for h in stat:
+            assert bool((sc[layer, h] == -7.0).all()) and bool((od[layer, h] == -1).all()), (layer, h)
+        ref = of.segment_scores(K[layer][dyn], C[layer][dyn][:, :wl.F], wl.F, wl.seg_len)
+        np.testing.assert_allclose(sc[layer, dyn[0], :items].cpu().numpy(), ref, rtol=2e-5, atol=2e-6)
