@@ -455,7 +455,7 @@ def recorded_hbm_kernels(config: str):
     if kv.get("record.kernel_sources_sha256") != h.hexdigest():
         return None
     out = {}
-    for name in ("gather", "segment_cosine"):
+    for name in ("gather", "segment_cosine", "segment_cosine_30_layers"):
         if f"record.{name}_us" not in kv:
             continue
         us = float(kv[f"record.{name}_us"])
