@@ -537,7 +537,7 @@ def forcing_bench(steps: int = 10, seed: int = 0):
                         f"seg_len={wl.seg_len}, r={wl.retention}, Lq={wl.Lq}",
             "score_ms": round(sc, 4), "update_ms": round(up, 4), "attention_ms": round(at, 4),
             "step_ms": round(sc + up + at, 4),
-            "segment_cosine": {"call": "kvbank_score (cos_kernel + segmean_kernel + item sort)",
+            "segment_cosine": {"call": "kvbank_score (cos_rows_kernel + segmean_kernel + rank_sort_kernel)",
                                "bytes_read": cos_bytes, "GB/s": round(cos_bytes / sc / 1e6, 1),
                                "frac_hbm_peak": round(cos_bytes / sc / 1e6 / PEAK_HBM_GBS, 4)},
             "hbm_kernels": recorded_hbm_kernels("fkv480p"),
