@@ -352,15 +352,19 @@ __global__ __launch_bounds__((gram_nt<SELF, CLIST>()), ((SELF && CLIST) ? 3 : 4)
     const int vlo = cols.base + tile * TC;   // one key set for the whole tile
     return (vlo + TC <= (int)hk.M || vlo >= (int)hk.M) && vlo + TC <= (int)hk.lim;
   };
+  // (range columns read no list: their positions are computed when a
+  // partial tile is issued, and a full tile needs none)
   auto load_index = [&](int tile) {
-    if (CLIST && full(tile)) {
-      const int rl = (int)(lane_part() / T::CPR);
-      const int32_t* ip = cidx + tile * TC + wu * LD::RPI + rl;
+    if constexpr (CLIST) {
+      if (full(tile)) {
+        const int rl = (int)(lane_part() / T::CPR);
+        const int32_t* ip = cidx + tile * TC + wu * LD::RPI + rl;
 #pragma unroll
-      for (int i = 0; i < LD::PASSW; ++i) ld.vi[i] = ip[i * LD::NW * LD::RPI];
-      ld.va = wu == 0 ? cidx[tile * TC + lane] : 0;
-    } else {
-      ld.index(tile, raw);
+        for (int i = 0; i < LD::PASSW; ++i) ld.vi[i] = ip[i * LD::NW * LD::RPI];
+        ld.va = wu == 0 ? cidx[tile * TC + lane] : 0;
+      } else {
+        ld.index(tile, raw);
+      }
     }
   };
   auto load_issue = [&](int tile, E* nY, u32x4_t* nA, int* nV) {
@@ -385,6 +389,7 @@ __global__ __launch_bounds__((gram_nt<SELF, CLIST>()), ((SELF && CLIST) ? 3 : 4)
         dma16(hk.aug(v), nA);
       }
     } else {
+      if constexpr (!CLIST) ld.index(tile, raw);
       ld.issue(tile, fix, hk, nY, nA, nV, fb);
     }
   };
