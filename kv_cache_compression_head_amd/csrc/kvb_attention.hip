@@ -247,12 +247,6 @@ __global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __
   int ucur = 0, ulo = 0, uhi = -1;
   const void* ubk = nullptr;
   const void* ubv = nullptr;
-  auto slow_row = [&](int j, const void* const* bases) -> const uint16_t* {
-    j = min(j, Lkv - 1);
-    int s = 0;
-    while (s + 1 < nseg && s_pre[s + 1] <= j) ++s;
-    return (const uint16_t*)bases[s] + (int64_t)(j - s_pre[s]) * D;
-  };
   // byte offsets (inside a 64-row tile) of the source chunks this lane copies
   // to LDS slots (row, lane % CPR): the same for K and V, fixed for the kernel
   uint32_t koff[KPASS];
@@ -291,13 +285,18 @@ __global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __
         lds_copy_buf(rvs, koff[i], soff, lds_addr(sVn + (wu * KPASS + i) * 64 * 8));
       }
     } else {
+      // each row finds its segment from the tile's first one (ucur holds
+      // kbase) on, once for its K and V rows
 #pragma unroll
       for (int i = 0; i < KPASS; ++i) {
         const int sl = (wu * KPASS + i) * 64 + lane;
         const int r = sl / CPR, c = sl % CPR;
-        const int e = (c ^ att_swz<CPR>(r)) * 8;
-        lds_copy_glb(slow_row(kbase + r, s_k) + e, lds_addr(sKn + (wu * KPASS + i) * 64 * 8));
-        lds_copy_glb(slow_row(kbase + r, s_v) + e, lds_addr(sVn + (wu * KPASS + i) * 64 * 8));
+        const int j = min(kbase + r, Lkv - 1);
+        int sg = ucur;
+        while (sg + 1 < nseg && s_pre[sg + 1] <= j) ++sg;
+        const int64_t ro = (int64_t)(j - s_pre[sg]) * D + (c ^ att_swz<CPR>(r)) * 8;
+        lds_copy_glb((const uint16_t*)s_k[sg] + ro, lds_addr(sKn + (wu * KPASS + i) * 64 * 8));
+        lds_copy_glb((const uint16_t*)s_v[sg] + ro, lds_addr(sVn + (wu * KPASS + i) * 64 * 8));
       }
     }
   };
