@@ -328,14 +328,21 @@ __global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __
   // whenever they stay finite (fp32 and bf16 reach 2^127), which the pass
   // checks at the end.  SAFE: the reference follows the running maximum,
   // moved only when a tile raises it by more than 2^8 (numerator and
-  // denominator are rescaled together).
-  constexpr int FIRST = 0, FAST = 1, SAFE = 2;
+  // denominator are rescaled together).  IDLE: a wave whose queries all
+  // lie past Lq only copies its share of the next tile and meets the
+  // barrier.
+  constexpr int FIRST = 0, FAST = 1, SAFE = 2, IDLE = 3;
   auto step = [&](auto mode_c, int tile, const uint16_t* sKc, const uint16_t* sVc, uint16_t* sKn,
                   uint16_t* sVn) __attribute__((always_inline)) {
     constexpr int mode = decltype(mode_c)::value;
     const int kbase = tile * ATT_TK;
     const bool more = tile + 1 < t_end;
     if (more) fetch(kbase + ATT_TK, sKn, sVn);
+    if constexpr (mode == IDLE) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      return;
+    }
 
     // ---- S^T = K Q^T ----
     // MFMA issue at raised wave priority: the SIMD's other wave, between its
@@ -505,27 +512,41 @@ __global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): query fragments resident before the tiles
 
-    // fast pass (tile t in buffer set (t - t0) & 1)
-    reset();
-    if (t_beg < t_end) step(std::integral_constant<int, FIRST>{}, t_beg, sK0, sV0, sK1, sV1);
-    for (int tile = t_beg + 1; tile < t_end; tile += 2) {
-      step(std::integral_constant<int, FAST>{}, tile, sK1, sV1, sK0, sV0);
-      if (tile + 1 < t_end) step(std::integral_constant<int, FAST>{}, tile + 1, sK0, sV0, sK1, sV1);
-    }
+    // fast pass (tile t in buffer set (t - t0) & 1).  A wave with no query
+    // below Lq (the padding of a head's last query tile) takes the same
+    // barriers and its share of the copies, in a loop of its own: the chip
+    // holds this kernel at its power limit, and the skipped products leave
+    // that power to the work that counts (480P layer-chunk: 0.608 -> 0.602 ms).
+    auto fast_pass = [&](auto first_c, auto fast_c) __attribute__((always_inline)) {
+      reset();
+      if (t_beg < t_end) step(first_c, t_beg, sK0, sV0, sK1, sV1);
+      for (int tile = t_beg + 1; tile < t_end; tile += 2) {
+        step(fast_c, tile, sK1, sV1, sK0, sV0);
+        if (tile + 1 < t_end) step(fast_c, tile + 1, sK0, sV0, sK1, sV1);
+      }
+    };
+    auto safe_pass = [&](auto safe_c) __attribute__((always_inline)) {
+      reset();
+      for (int tile = t_beg; tile < t_end; tile += 2) {
+        step(safe_c, tile, sK0, sV0, sK1, sV1);
+        if (tile + 1 < t_end) step(safe_c, tile + 1, sK1, sV1, sK0, sV0);
+      }
+    };
+    const bool idle = qt * ATT_QB + wu * ATT_QW >= Lq;   // (wu: the wave index as a uniform value)
+    if (idle) fast_pass(std::integral_constant<int, IDLE>{}, std::integral_constant<int, IDLE>{});
+    else fast_pass(std::integral_constant<int, FIRST>{}, std::integral_constant<int, FAST>{});
     // a non-finite numerator or denominator anywhere in the work-group (a
     // query whose scores rose by about 2^127 past its first tile's): redo the
-    // piece's tiles with the running-maximum pass
+    // piece's tiles with the running-maximum pass (an idle wave's sums are
+    // the zeros of reset)
     float chk = L[0][0] + L[1][0];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) chk += (o[db][qb][0] + o[db][qb][1]) + (o[db][qb][2] + o[db][qb][3]);
     if (__syncthreads_or(!__builtin_isfinite(chk))) {
-      reset();
-      for (int tile = t_beg; tile < t_end; tile += 2) {
-        step(std::integral_constant<int, SAFE>{}, tile, sK0, sV0, sK1, sV1);
-        if (tile + 1 < t_end) step(std::integral_constant<int, SAFE>{}, tile + 1, sK1, sV1, sK0, sV0);
-      }
+      if (idle) safe_pass(std::integral_constant<int, IDLE>{});
+      else safe_pass(std::integral_constant<int, SAFE>{});
     }
 
     if (slot >= 0) {
