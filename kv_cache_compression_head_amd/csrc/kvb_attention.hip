@@ -132,6 +132,7 @@ __global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __
   const int bl = xcd_remap(blockIdx.x, G);   // head-major items, one XCD per range
   const int lane = lane_id(), w = wave_id();
   const int g = lane >> 4;
+  const int wu = __builtin_amdgcn_readfirstlane(w);   // the wave index as a uniform value
   const int tid = threadIdx.x;
 
   // ---- work plan ----
@@ -202,13 +203,15 @@ __global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __
   };
   int T = 0;
   if (Ir > 0) {
-    if (w == 0) {
-      for (int hh = h0 + lane; hh < H; hh += 64) {
-        const int ns = min(nseg_p[hh], min(seg_cap, ATT_MAXSEG));
-        int64_t len = 0;
-        for (int s = 0; s < ns; ++s) len += segs[(int64_t)hh * seg_cap + s].len;
-        s_nt[hh] = (int)((len + ATT_TK - 1) / ATT_TK);
-      }
+    // tiles per head: one wave per head, its lanes reading the segment
+    // lengths in parallel
+    for (int hh = h0 + wu; hh < H; hh += ATT_NW) {
+      const int ns = min(nseg_p[hh], min(seg_cap, ATT_MAXSEG));
+      int len = 0;
+      for (int sg = lane; sg < ns; sg += 64) len += segs[(int64_t)hh * seg_cap + sg].len;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) len += __shfl_xor(len, o);
+      if (lane == 0) s_nt[hh] = (len + ATT_TK - 1) / ATT_TK;
     }
     __syncthreads();
     if (w == 0) {
@@ -263,7 +266,6 @@ __global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __
     const uint32_t vl = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
     return (const void*)(((uint64_t)vh << 32) | (uint64_t)vl);
   };
-  const int wu = __builtin_amdgcn_readfirstlane(w);
   auto fetch = [&](int kbase, uint16_t* sKn, uint16_t* sVn) __attribute__((always_inline)) {
     if (kbase < ulo || kbase + ATT_TK > uhi) {
       if (kbase < ulo) ucur = 0;   // a new pass over the tiles
@@ -474,19 +476,32 @@ __global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __
   auto piece = [&](int item, int t0, int t1, int slot, int ir) __attribute__((always_inline)) {
     const int hn = item / nqt, qt = item % nqt;
     if (hn != h) {
-      // every wave's last table read came before the previous barrier
+      // every wave's last table read came before the previous barrier.
+      // Wave 0 reads the head's table 64 entries at a time (one load
+      // latency, not one per segment) and scans the lengths into offsets.
       h = hn;
       nseg = min(nseg_p[h], min(seg_cap, ATT_MAXSEG));
-      if (tid == 0) {
-        int acc = 0;
-        for (int s = 0; s < nseg; ++s) {
-          const SegEntry e = segs[(int64_t)h * seg_cap + s];
-          s_pre[s] = acc;
-          s_k[s] = e.k;
-          s_v[s] = e.v;
-          acc += e.len;
+      if (w == 0) {
+        int carry = 0;
+        for (int s0 = 0; s0 < nseg; s0 += 64) {
+          const int sg = s0 + lane;
+          int len = 0;
+          if (sg < nseg) {
+            const SegEntry e = segs[(int64_t)h * seg_cap + sg];
+            s_k[sg] = e.k;
+            s_v[sg] = e.v;
+            len = e.len;
+          }
+          int x = len;   // inclusive scan over the wave
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o);
+            if (lane >= o) x += y;
+          }
+          if (sg < nseg) s_pre[sg] = carry + x - len;
+          carry += __shfl(x, 63);
         }
-        s_pre[nseg] = acc;
+        if (lane == 0) s_pre[nseg] = carry;
       }
       __syncthreads();
       Lkv = __builtin_amdgcn_readfirstlane(s_pre[nseg]);
