@@ -117,8 +117,12 @@ hipError_t launch_delta(const float* D, const int32_t* count, uint64_t on, int H
 
 // ---------------------------------------------------------------------------
 // sort: key = float_key(score) << 32 | tie (tie = token id or item index),
-// ascending; value = index.  Blocks of 2048 are sorted in LDS (bitonic), then
-// sorted runs are merged pairwise by rank (binary search in the other run).
+// ascending; value = index.  Blocks of 2048 are sorted by a bitonic network
+// whose steps between elements less than 128 apart run in registers (lane
+// shuffles within a wave, no barrier) and the rest through LDS.  Sorted
+// runs are then merged pairwise by rank: an element's place is its index in
+// its own run plus the number of keys before it in the other run (keys
+// equal to it count from the first run only, so places never collide).
 // ---------------------------------------------------------------------------
 constexpr int SORT_BS = 2048;
 
@@ -127,6 +131,25 @@ KVB_DEV uint64_t sort_key(const float* score, const int32_t* tie, int64_t tie_hs
   // no score: the tie key alone (source order, by token id)
   const uint32_t hi = score ? float_key(score[(int64_t)h * score_hstride + i]) : 0u;
   const uint32_t lo = tie ? (uint32_t)tie[(int64_t)h * tie_hstride + i] : (uint32_t)i;
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// the value of lane (lane ^ m), m a power of two below 64 known at compile
+// time: lane moves within a quad for m < 4, swizzles within 32 lanes below
+// 32, a permute across the halves for 32
+KVB_DEV int lane_xor(int v, int m) {
+  switch (m) {
+    case 1: return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);   // quad_perm (1, 0, 3, 2)
+    case 2: return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);   // quad_perm (2, 3, 0, 1)
+    case 4: return __builtin_amdgcn_ds_swizzle(v, (4 << 10) | 0x1F);
+    case 8: return __builtin_amdgcn_ds_swizzle(v, (8 << 10) | 0x1F);
+    case 16: return __builtin_amdgcn_ds_swizzle(v, (16 << 10) | 0x1F);
+    default: return __shfl_xor(v, m);
+  }
+}
+KVB_DEV uint64_t lane_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)lane_xor((int)(uint32_t)v, m);
+  const uint32_t hi = (uint32_t)lane_xor((int)(uint32_t)(v >> 32), m);
   return ((uint64_t)hi << 32) | lo;
 }
 
@@ -140,42 +163,97 @@ __global__ __launch_bounds__(1024) void block_sort_kernel(const float* __restric
   __shared__ uint64_t sk[SORT_BS];
   __shared__ int32_t sv[SORT_BS];
   const int base = blockIdx.x * SORT_BS;
-  for (int i = threadIdx.x; i < SORT_BS; i += 1024) {
-    const int g = base + i;
-    if (g < n) {
-      sk[i] = sort_key(score, tie, tie_hstride, h, g, score_hstride);
-      sv[i] = g;
-    } else {
-      sk[i] = ~0ull;
-      sv[i] = -1;
-    }
+  // thread t holds elements 2t and 2t + 1
+  const int t = threadIdx.x;
+  uint64_t k[2];
+  int32_t v[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int g = base + 2 * t + b;
+    k[b] = g < n ? sort_key(score, tie, tie_hstride, h, g, score_hstride) : ~0ull;
+    v[b] = g < n ? g : -1;
   }
-  __syncthreads();
-  // bitonic network: one compare-exchange per thread and step
-  const int p = threadIdx.x;
-  for (int k = 2; k <= SORT_BS; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const int i = (p / j) * 2 * j + (p % j);
-      const int l = i + j;
-      const bool up = ((i & k) == 0);
-      const uint64_t a = sk[i], b = sk[l];
-      if ((a > b) == up) {
-        sk[i] = b; sk[l] = a;
-        const int32_t t = sv[i]; sv[i] = sv[l]; sv[l] = t;
-      }
+#pragma unroll
+  for (int kk = 2; kk <= SORT_BS; kk <<= 1) {
+    int j = kk >> 1;
+    if (j >= 128) {
+      // steps across waves: one compare-exchange per thread and step in LDS
+      sk[2 * t] = k[0];
+      sk[2 * t + 1] = k[1];
+      sv[2 * t] = v[0];
+      sv[2 * t + 1] = v[1];
       __syncthreads();
+#pragma unroll
+      for (; j >= 128; j >>= 1) {
+        const int i = (t / j) * 2 * j + (t % j);
+        const int l = i + j;
+        const bool up = ((i & kk) == 0);
+        const uint64_t a = sk[i], c = sk[l];
+        if ((a > c) == up) {
+          sk[i] = c;
+          sk[l] = a;
+          const int32_t tv = sv[i];
+          sv[i] = sv[l];
+          sv[l] = tv;
+        }
+        __syncthreads();
+      }
+      k[0] = sk[2 * t];
+      k[1] = sk[2 * t + 1];
+      v[0] = sv[2 * t];
+      v[1] = sv[2 * t + 1];
+    }
+    // steps within a wave: element 2t + b meets 2(t ^ j/2) + b (j >= 2), or
+    // its neighbour in the same thread (j = 1); the lower index of a pair
+    // keeps the smaller key when its kk bit is clear
+#pragma unroll
+    for (; j >= 2; j >>= 1) {
+      const bool keep_min = (((2 * t) & j) == 0) == (((2 * t) & kk) == 0);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const uint64_t pk = lane_xor_u64(k[b], j >> 1);
+        const int32_t pv = lane_xor(v[b], j >> 1);
+        const bool lt = pk < k[b];
+        const uint64_t mn = lt ? pk : k[b], mx = lt ? k[b] : pk;
+        const uint64_t nk = keep_min ? mn : mx;
+        v[b] = nk != k[b] ? pv : v[b];
+        k[b] = nk;
+      }
+    }
+    {
+      const bool up = ((2 * t) & kk) == 0;
+      const bool sw = (k[0] > k[1]) == up;
+      const uint64_t k0 = sw ? k[1] : k[0], k1 = sw ? k[0] : k[1];
+      const int32_t v0 = sw ? v[1] : v[0], v1 = sw ? v[0] : v[1];
+      k[0] = k0;
+      k[1] = k1;
+      v[0] = v0;
+      v[1] = v1;
     }
   }
-  for (int i = threadIdx.x; i < SORT_BS; i += 1024) {
-    const int g = base + i;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int g = base + 2 * t + b;
     if (g < n) {
-      if (final_out) final_out[(int64_t)h * final_hstride + g] = sv[i];
+      if (final_out) final_out[(int64_t)h * final_hstride + g] = v[b];
       else {
-        kout[(int64_t)h * n + g] = sk[i];
-        vout[(int64_t)h * n + g] = sv[i];
+        kout[(int64_t)h * n + g] = k[b];
+        vout[(int64_t)h * n + g] = v[b];
       }
     }
   }
+}
+
+// number of keys in run[0, len) before key: smaller, or (before_equal) equal
+KVB_DEV int run_rank(const uint64_t* run, int len, uint64_t key, bool before_equal) {
+  int lo = 0, hi = len;
+  while (lo < hi) {
+    const int m = (lo + hi) >> 1;
+    const uint64_t x = run[m];
+    if (x < key || (before_equal && x == key)) lo = m + 1;
+    else hi = m;
+  }
+  return lo;
 }
 
 __global__ __launch_bounds__(256) void merge_kernel(const uint64_t* __restrict__ kin, const int32_t* __restrict__ vin,
@@ -191,16 +269,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint64_t* __restrict__
   const int a0 = pair0, a1 = min(n, pair0 + L);
   const int b0 = a1, b1 = min(n, pair0 + 2 * L);
   const uint64_t key = kin[hb + i];
-  int lo, hi, pos;
-  if (i < a1) {   // element of run A: count B elements < key
-    lo = b0; hi = b1;
-    while (lo < hi) { const int m = (lo + hi) >> 1; if (kin[hb + m] < key) lo = m + 1; else hi = m; }
-    pos = pair0 + (i - a0) + (lo - b0);
-  } else {        // element of run B: count A elements < key
-    lo = a0; hi = a1;
-    while (lo < hi) { const int m = (lo + hi) >> 1; if (kin[hb + m] < key) lo = m + 1; else hi = m; }
-    pos = pair0 + (i - b0) + (lo - a0);
-  }
+  int pos;
+  if (i < a1) pos = pair0 + (i - a0) + run_rank(kin + hb + b0, b1 - b0, key, false);   // run A: B's smaller keys
+  else pos = pair0 + (i - b0) + run_rank(kin + hb + a0, a1 - a0, key, true);           // run B: A's keys up to key
   if (final_out) final_out[(int64_t)h * final_hstride + pos] = vin[hb + i];
   else {
     kout[hb + pos] = key;
@@ -247,7 +318,7 @@ hipError_t launch_sort(const float* score, int64_t score_hstride, const int32_t*
   uint64_t* ka = k0; uint64_t* kb = k1;
   int32_t* va = v0; int32_t* vb = v1;
   for (int L = SORT_BS; L < n; L <<= 1) {
-    const bool last = 2 * L >= n;
+    const bool last = 2 * (int64_t)L >= n;
     hipLaunchKernelGGL(merge_kernel, dim3((n + 255) / 256, H), dim3(256), 0, st, ka, va, on, n, L, kb, vb,
                        last ? out : nullptr, out_hstride);
     uint64_t* tk = ka; ka = kb; kb = tk;
