@@ -144,9 +144,10 @@ typedef struct kvb_layer_desc {
   int32_t dtype;         /* KVB_BF16 or KVB_F32 */
   int32_t frame_tokens;  /* F: tokens per latent frame */
   int32_t desc_dim;      /* density descriptor (DensityKV paper summary, appendix E, descriptor ablation):
-                            0 = the post-RoPE keys themselves (the method); 64 or 128 = separate rows of
-                            that dimension in bank->X and layout->cand_x (pre-RoPE keys, or [K; V] when
-                            d = 64).  Density-only layers (no Forcing-KV heads) */
+                            0 = the post-RoPE keys themselves (the method); 64, 128 or (bf16 only) 256 =
+                            separate rows of that dimension in bank->X and layout->cand_x (pre-RoPE keys,
+                            or [K; V]: 128 wide when d = 64, 256 wide when d = 128).  Other widths are
+                            KVB_ESHAPE.  Density-only layers (no Forcing-KV heads) */
   const uint8_t* label;  /* HOST pointer, H head labels */
   kvb_params params;
 } kvb_layer_desc;

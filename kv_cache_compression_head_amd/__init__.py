@@ -165,7 +165,7 @@ class LayerDesc:
     seg_len: int = 0
     retention: float = 0.0
     policy: int = 0          # OR of KVB_POL_*
-    desc_dim: int = 0        # 0: keys are the density descriptors; 64 / 128: Bank.X and KVLayout.cand_x
+    desc_dim: int = 0        # 0: keys are the density descriptors; 64 / 128 / 256 (bf16): Bank.X and KVLayout.cand_x
 
     def c(self):
         lab = (ctypes.c_uint8 * max(1, len(self.labels)))(*[int(x) for x in self.labels])

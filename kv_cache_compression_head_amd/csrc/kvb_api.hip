@@ -89,8 +89,8 @@ int check_layer(const kvb_layer_desc* L, int32_t N, Heads* hd) {
   if ((hd->dyn || hd->stat) && N % L->frame_tokens != 0)
     return fail(KVB_ESHAPE, "Forcing-KV heads need N (%d) to be a multiple of frame_tokens (%d)", N, L->frame_tokens);
   if (L->desc_dim != 0) {
-    if (L->desc_dim != 64 && L->desc_dim != 128)
-      return fail(KVB_ESHAPE, "desc_dim=%d (supported: 0 = the keys, 64, 128)", L->desc_dim);
+    if (L->desc_dim != 64 && L->desc_dim != 128 && !(L->desc_dim == 256 && L->dtype == KVB_BF16))
+      return fail(KVB_ESHAPE, "desc_dim=%d (supported: 0 = the keys, 64, 128; 256 for bf16)", L->desc_dim);
     if (hd->dyn || hd->stat) return fail(KVB_EPARAM, "density descriptors apply to density-only layers");
   }
   return KVB_OK;

@@ -92,7 +92,7 @@ struct DmaTile {
   static constexpr int RPI = 64 / T::CPR;           // rows per copy
   static constexpr int PASSW = TC / (RPI * NW);     // copies per wave and tile
   static_assert(TC == 64 && PASSW * RPI * NW == TC, "tile shape");
-  static_assert(sizeof(E) != 2 || (NW * RPI) % 16 == 0, "the swizzle must repeat across a lane's copies");
+  static_assert((NW * RPI) % T::SWZ_PERIOD == 0, "the swizzle must repeat across a lane's copies");
   int vi[PASSW];
   int va;
   // Per-lane offsets are recomputed from an opaque lane id at each use: kept
@@ -211,6 +211,9 @@ hipError_t launch_norms(const void* keysA, int rowsA, float* outA, void* augA, c
     if (cpr == 8)
       hipLaunchKernelGGL((norms_kernel<uint16_t, 8>), grid, dim3(256), 0, st, a, nA, outA, (u32x4_t*)augA, b, nB, outB,
                          (u32x4_t*)augB, d, scale, (int)direct, chk);
+    else if (cpr == 32)
+      hipLaunchKernelGGL((norms_kernel<uint16_t, 32>), grid, dim3(256), 0, st, a, nA, outA, (u32x4_t*)augA, b, nB,
+                         outB, (u32x4_t*)augB, d, scale, (int)direct, chk);
     else
       hipLaunchKernelGGL((norms_kernel<uint16_t, 16>), grid, dim3(256), 0, st, a, nA, outA, (u32x4_t*)augA, b, nB, outB,
                          (u32x4_t*)augB, d, scale, (int)direct, chk);
@@ -247,9 +250,12 @@ constexpr int GRAM_ROWS = 256;    // rows per work-group (32 per wave)
 constexpr int SYM_NT = 256;
 static_assert(SYM_NT / 2 == GRAM_ROW_BLOCK, "rows per work-group of the symmetric self-Gram");
 template <bool SELF, bool CLIST> constexpr int gram_nt() { return (SELF && CLIST) ? SYM_NT : GRAM_NT; }
+// waves per SIMD the register budget is sized for: 256-wide rows (bf16
+// descriptors) hold twice the row fragments and run two
+template <int D, bool SELF, bool CLIST> constexpr int gram_wpe() { return D > 128 ? 2 : ((SELF && CLIST) ? 3 : 4); }
 
 template <typename E, int D, int MODE, bool SELF, bool CLIST, bool DIRECT>
-__global__ __launch_bounds__((gram_nt<SELF, CLIST>()), ((SELF && CLIST) ? 3 : 4)) void gram_kernel(KeySpace<E> ks, VList rows, VList cols,
+__global__ __launch_bounds__((gram_nt<SELF, CLIST>()), (gram_wpe<D, SELF, CLIST>())) void gram_kernel(KeySpace<E> ks, VList rows, VList cols,
                                                          float* __restrict__ out, int64_t out_hstride,
                                                          int64_t split_stride, PhiConst pc, uint64_t active,
                                                          float* __restrict__ colsum, int64_t col_ld) {
@@ -644,7 +650,8 @@ hipError_t launch_gram(const GramLaunch& g, hipStream_t st) {
   const dim3 grid((unsigned)((g.rows.n + GRAM_ROWS - 1) / GRAM_ROWS), (unsigned)g.k.H,
                   (unsigned)(g.splits > 0 ? g.splits : 1));
   if (g.k.et == ET_BF16) {
-    if (g.k.d == 128) gram_dispatch_mode<uint16_t, 128>(g, grid, st);
+    if (g.k.d == 256) gram_dispatch_mode<uint16_t, 256>(g, grid, st);
+    else if (g.k.d == 128) gram_dispatch_mode<uint16_t, 128>(g, grid, st);
     else gram_dispatch_mode<uint16_t, 64>(g, grid, st);
   } else {
     if (g.k.d == 128) gram_dispatch_mode<float, 128>(g, grid, st);
@@ -719,7 +726,7 @@ hipError_t launch_sum_splits(const float* src, int64_t src_hstride, int64_t spli
 // sum pass:  rhoP_b = S_b(k*) starting from the nearest checkpoint.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int MODE, bool SUM, bool DIRECT>
-__global__ __launch_bounds__(256, 4) void scan_kernel(KeySpace<E> ks, const float* __restrict__ rho,
+__global__ __launch_bounds__(256, (D > 128 ? 2 : 4)) void scan_kernel(KeySpace<E> ks, const float* __restrict__ rho,
                                                    const float* __restrict__ rho0, const int32_t* __restrict__ count,
                                                    const int32_t* __restrict__ order, uint64_t active,
                                                    int kmax, float tau, int cps, int ncp, float* __restrict__ cp,
@@ -1031,7 +1038,8 @@ hipError_t launch_scan(const ScanLaunch& a, bool sum, hipStream_t st) {
   if (a.k.M <= 0) return hipSuccess;
   const dim3 grid((unsigned)((a.k.M + 127) / 128), (unsigned)a.k.H);
   if (a.k.et == ET_BF16) {
-    if (a.k.d == 128) scan_dispatch_mode<uint16_t, 128>(a, sum, grid, st);
+    if (a.k.d == 256) scan_dispatch_mode<uint16_t, 256>(a, sum, grid, st);
+    else if (a.k.d == 128) scan_dispatch_mode<uint16_t, 128>(a, sum, grid, st);
     else scan_dispatch_mode<uint16_t, 64>(a, sum, grid, st);
   } else {
     if (a.k.d == 128) scan_dispatch_mode<float, 128>(a, sum, grid, st);

@@ -31,6 +31,8 @@ namespace kvb {
 // ---------------------------------------------------------------------------
 // pair interactions: P[h][x][y] = phi(|X_x - X_y|^2), 16 x 16 pairs per block
 // ---------------------------------------------------------------------------
+constexpr int PAIR_MAXD = 256;   // widest row: 256-wide descriptors ([K; V] at d = 128)
+
 template <typename E, int MODE>
 __global__ __launch_bounds__(256) void pair_phi_kernel(const E* __restrict__ bankX, const E* __restrict__ candX,
                                                        int M, int N, int dx, PhiConst pc, uint64_t active,
@@ -39,8 +41,9 @@ __global__ __launch_bounds__(256) void pair_phi_kernel(const E* __restrict__ ban
   if (!head_on(active, h)) return;
   const int S = M + N;
   const int x0 = blockIdx.y * 16, y0 = blockIdx.x * 16;
-  __shared__ float sx[16][129];
-  __shared__ float sy[16][129];
+  // (odd row stride: the 16 rows of one column fall in 16 different banks)
+  __shared__ float sx[16][PAIR_MAXD + 1];
+  __shared__ float sy[16][PAIR_MAXD + 1];
   auto row = [&](int v) -> const E* {
     return v < M ? bankX + ((int64_t)h * M + v) * dx : candX + ((int64_t)h * N + (v - M)) * dx;
   };
@@ -367,6 +370,7 @@ __global__ __launch_bounds__(1024) void seq_gather_kernel(SeqGather g) {
 
 hipError_t launch_sequential(const SeqLaunch& a, const SeqGather& g, const void* bankX, const void* candX, int dx,
                              const PhiConst& pc, int phi_mode, hipStream_t st) {
+  if (dx < 1 || dx > PAIR_MAXD) return hipErrorInvalidValue;
   const int S = a.M + a.N;
   const dim3 pgrid((unsigned)((S + 15) / 16), (unsigned)((S + 15) / 16), (unsigned)a.H);
 #define KVB_PAIR(E, MODE)                                                                                     \

@@ -77,6 +77,20 @@ def test_host_validation(kw, code):
     assert kb.kvb_last_error()
 
 
+def test_descriptor_widths():
+    """Descriptor rows of 64 and 128 in either precision; 256 ([K; V] at
+    d = 128) in bf16 only; any other width is a shape error."""
+    for dt in (kb.KVB_F32, kb.KVB_BF16):
+        for dx in (64, 128):
+            assert kb.kvbank_workspace_size(_desc(dtype=dt, desc_dim=dx), 48) > 0
+    assert kb.kvbank_workspace_size(_desc(d=128, dtype=kb.KVB_BF16, desc_dim=256), 48) > 0
+    for kw in (dict(dtype=kb.KVB_F32, desc_dim=256), dict(dtype=kb.KVB_BF16, desc_dim=96),
+               dict(dtype=kb.KVB_BF16, desc_dim=512)):
+        with pytest.raises(kb.KvbError) as e:
+            kb.kvbank_workspace_size(_desc(**kw), 48)
+        assert e.value.code == -2 and "desc_dim" in kb.kvb_last_error()
+
+
 def test_negative_N_and_forcing_multiple():
     with pytest.raises(kb.KvbError) as e:
         kb.kvbank_workspace_size(_desc(), -1)

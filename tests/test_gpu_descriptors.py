@@ -113,6 +113,14 @@ def test_mid_bf16_kv_d64():
     _stream(MID, od.Params(M=MID.M, tau=1.1), "kv")
 
 
+@pytest.mark.parametrize("sequential", [False, True])
+def test_mid_bf16_kv_d128(sequential):
+    """[K; V] at head dimension 128: 256-wide descriptors (the appendix E
+    ablation at the head width of the pages' backbone)."""
+    wl = dataclasses.replace(MID, d=128, name="mid-d128")
+    _stream(wl, od.Params(M=wl.M, tau=1.1), "kv", sequential)
+
+
 def test_mid_bf16_prerope_d128():
     wl = dataclasses.replace(MID, d=128, name="mid-d128")
     _stream(wl, od.Params(M=wl.M, tau=1.1), "prerope")
