@@ -181,23 +181,18 @@ template <typename E, int D> struct HeadKeys {
 
 // LDS key tiles: rows of D elements with no padding; the 16-byte chunks of
 // row r are XOR-swizzled so that the 16 rows read by one quarter-wave hit 16
-// different 16-byte bank groups (8 for the 512-byte rows of 256-wide bf16
-// descriptors, whose swizzle repeats every 8 rows).
+// different 16-byte bank groups.
 template <typename E, int D> struct Tile {
   static constexpr int EPC = 16 / (int)sizeof(E);   // elements per chunk
   static constexpr int CPR = D / EPC;               // chunks per row
-  static_assert(CPR == 8 || CPR == 16 || CPR == 32, "row width");
   KVB_DEV static int swz(int r) {
     if constexpr (sizeof(E) == 2) {
       if constexpr (CPR == 16) return r & 15;
-      else if constexpr (CPR == 32) return r & 7;
       else return (r >> 1) & 7;
     } else {
       return 0;
     }
   }
-  // rows after which the swizzle repeats
-  static constexpr int SWZ_PERIOD = sizeof(E) != 2 ? 1 : (CPR == 16 ? 16 : (CPR == 32 ? 8 : 16));
   // element offset of element e of row r (e is a fragment start)
   KVB_DEV static int at(int r, int e) { return r * D + (((e / EPC) ^ swz(r)) * EPC) + e % EPC; }
   // at(r, e + f) from a0 = at(r, e), for a fragment step f whose chunk bits

@@ -70,11 +70,29 @@ template <> struct Aug<float> {
 
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 
+// 256-wide bf16 rows (the [K; V] descriptors of d = 128 heads): a 512-byte
+// row spans the 64 LDS banks twice, so the chunk swizzle r & 7 (8 rows on 8
+// distinct 16-byte bank groups) repeats every 8 rows
+template <> struct Tile<uint16_t, 256> {
+  static constexpr int EPC = 8;
+  static constexpr int CPR = 32;
+  KVB_DEV static int swz(int r) { return r & 7; }
+  KVB_DEV static int at(int r, int e) { return r * 256 + (((e / EPC) ^ swz(r)) * EPC) + e % EPC; }
+  // (as in the general tile: the chunk bits of f and e are disjoint)
+  KVB_DEV static int at_step(int a0, int f) { return a0 ^ f; }
+};
+// rows after which Tile<E, D>'s swizzle repeats
+template <typename E, int D> constexpr int swz_period() {
+  if constexpr (sizeof(E) != 2) return 1;
+  else if constexpr (D == 256) return 8;
+  else return 16;
+}
+
 // Stages TC key rows (gathered by virtual index) and their augmentation rows
 // into LDS with direct-to-LDS loads.  NT threads in NW waves; copy i of wave
 // w fills tile rows (i NW + w) RPI .. + RPI - 1 (one contiguous KiB of LDS),
 // lane l taking row + l / CPR and LDS chunk l % CPR.  The rows of one lane
-// differ by multiples of NW RPI >= 16, which the swizzle ignores, so the
+// differ by multiples of NW RPI, a multiple of the swizzle's period, so the
 // lane's source chunk offset is the same for every copy.  Wave 0 copies the
 // augmentation rows and records each row's index (-1 when absent) in sV
 // when given.
@@ -92,7 +110,7 @@ struct DmaTile {
   static constexpr int RPI = 64 / T::CPR;           // rows per copy
   static constexpr int PASSW = TC / (RPI * NW);     // copies per wave and tile
   static_assert(TC == 64 && PASSW * RPI * NW == TC, "tile shape");
-  static_assert((NW * RPI) % T::SWZ_PERIOD == 0, "the swizzle must repeat across a lane's copies");
+  static_assert((NW * RPI) % swz_period<E, D>() == 0, "the swizzle must repeat across a lane's copies");
   int vi[PASSW];
   int va;
   // Per-lane offsets are recomputed from an opaque lane id at each use: kept
