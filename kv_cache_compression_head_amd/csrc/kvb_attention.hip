@@ -151,7 +151,7 @@ __global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __
   // finds a slot; every work-group derives the same plan from the segment
   // lengths.  Split items leave fp32 partials that attn_merge_kernel adds.
   __shared__ int s_nt[ATT_MAX_HEADS];
-  __shared__ int s_T;
+  __shared__ int s_T, s_whole;
   const int base = rounds * G;          // first left-over item
   const int h0 = base / nqt;
   // left-over items of head hh: [first_of(hh), (hh + 1) nqt)
@@ -202,6 +202,7 @@ __global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __
     return tg < 0;
   };
   int T = 0;
+  int bli = bl;   // this work-group's left-over item (when below Ir)
   if (Ir > 0) {
     // tiles per head: one wave per head, its lanes reading the segment
     // lengths in parallel
@@ -216,19 +217,34 @@ __global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __
     __syncthreads();
     if (w == 0) {
       int64_t work = 0;
-      int ntmax = 0;
+      int ntmax = 0, ntmin = 1 << 30;
       for (int hh = h0; hh < H; ++hh) {
         work += (int64_t)((hh + 1) * nqt - first_of(hh)) * s_nt[hh];
         ntmax = max(ntmax, s_nt[hh]);
+        ntmin = min(ntmin, s_nt[hh]);
       }
+      // Left-over items of one length that fill at least four fifths of
+      // the slots run whole (cut T = the longest item): at the chip's power
+      // limit the idle slots cost less than the split's partials, merge and
+      // tail re-reads (480P layer-chunk, 228 items on 256 slots: 0.613 ->
+      // 0.601 ms).  Items of different lengths are always balanced.
+      const bool whole = ntmin == ntmax && 5 * Ir >= 4 * G;
       const int tlo = max(1, (int)((work + G - 1) / G));
       int dh, df, dc;
-      const bool ok = fill(tlo + lane, -1, 0, &dh, &df, &dc);   // candidate cuts, one per lane
+      const bool ok = !whole && fill(tlo + lane, -1, 0, &dh, &df, &dc);   // candidate cuts, one per lane
       const uint64_t msk = __ballot(ok);
-      if (lane == 0) s_T = msk ? tlo + (int)__builtin_ctzll(msk) : ntmax;
+      if (lane == 0) {
+        s_T = msk ? tlo + (int)__builtin_ctzll(msk) : ntmax;
+        s_whole = whole;
+      }
     }
     __syncthreads();
     T = __builtin_amdgcn_readfirstlane(s_T);
+    // whole left-over items sit where a grid of one work-group per item
+    // puts them: the first Ir dispatches, Ir / 8 per XCD (each XCD's L2
+    // then serves as many items as in that grid); the other work-groups
+    // have no piece
+    if (__builtin_amdgcn_readfirstlane(s_whole)) bli = (int)blockIdx.x < Ir ? xcd_remap(blockIdx.x, Ir) : Ir;
   }
 
   // per-piece state (set by `piece` below)
@@ -595,14 +611,14 @@ __global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __
   int tl_first = 0, tl_cnt = 0, tl_nt = 0;
   if (Ir > 0) {
     int tg = -1, tj = 0;
-    if (bl >= Ir) {
+    if (bli >= Ir) {
       tg = 0;
-      tj = bl - Ir;
+      tj = bli - Ir;
     } else {
-      const int hh = (base + bl) / nqt;
+      const int hh = (base + bli) / nqt;
       if (s_nt[hh] < T) {
         tg = 1 + hh;
-        tj = base + bl - first_of(hh);
+        tj = base + bli - first_of(hh);
       }
     }
     int th = 0;
@@ -612,15 +628,15 @@ __global__ __launch_bounds__(ATT_NT, 2) void attn_bf16_kernel(const uint16_t* __
   // pieces in order: whole items of each round, then the main piece (or the
   // whole left-over item), then the tails; one call site keeps one copy of
   // the tile loop
-  const int npieces = rounds + (Ir > 0 ? (bl < Ir ? 1 : 0) + tl_cnt : 0);
+  const int npieces = rounds + (Ir > 0 ? (bli < Ir ? 1 : 0) + tl_cnt : 0);
   for (int pc = 0; pc < npieces; ++pc) {
     int item, t0 = 0, t1 = 1 << 30, slot = -1, ir = -1;
-    const int pt = pc - rounds - (bl < Ir ? 1 : 0);   // tail index (when >= 0)
+    const int pt = pc - rounds - (bli < Ir ? 1 : 0);   // tail index (when >= 0)
     if (pc < rounds) {
       item = pc * G + bl;
     } else if (pt < 0) {
-      item = base + bl;
-      ir = bl;
+      item = base + bli;
+      ir = bli;
       const int nt = s_nt[item / nqt];
       if (nt > T) {
         t1 = T;

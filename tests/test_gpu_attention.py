@@ -163,6 +163,18 @@ def test_attention_balanced_short_items_take_tails():
     assert e.max() <= 1e-2 and e.mean() <= 1e-3, (e.max(), e.mean())
 
 
+def test_attention_whole_items_of_one_length():
+    """12 heads of one length x 19 query tiles (228 items on 256 slots, more
+    than four fifths): the plan keeps every item whole, so the output equals
+    the one-work-group-per-item grid bit for bit; three heads against the
+    oracle."""
+    lens = [[1560, 640]] * 12
+    _attention_case(128, 4680, lens, "bf16", heads=[0, 5, 11])
+    a = _attention_case(128, 4680, lens, "bf16", ret=True)
+    b = _attention_case(128, 4680, lens, "bf16", ws=None, ret=True)
+    assert np.array_equal(a, b)
+
+
 def test_attention_balanced_d64():
     """d = 64 on the balanced grid, with a ragged tail tile."""
     _attention_case(64, 1000, [[900, 333], [1500], [64, 64, 7]], "bf16")
