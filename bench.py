@@ -34,7 +34,13 @@ if ROOT not in sys.path:
 METRIC = "ms/chunk/layer + attention TFLOP/s (% of bf16 peak) at 480P and 1080P, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
-ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_kernel_480p_hbm_traffic.md")
+
+
+def attn_traffic_file(config: str) -> str:
+    """The committed attention HBM-traffic record of a workload."""
+    return os.path.join(ROOT, "profiles", f"attn_bf16_kernel_{config}_hbm_traffic.md")
+
+
 ATTN_SOURCES = ("kv_cache_compression_head_amd/csrc/kvb_attention.hip",
                 "kv_cache_compression_head_amd/csrc/kvb_common.hpp")
 HBM_SOURCES = ("kv_cache_compression_head_amd/csrc/kvb_select.hip",
@@ -121,7 +127,7 @@ def recorded_attention_traffic(config: str):
     WRITE_SIZE profile, or None when that profile was taken on other kernel
     sources (or another workload)."""
     try:
-        with open(ATTN_TRAFFIC_FILE) as fh:
+        with open(attn_traffic_file(config)) as fh:
             kv = dict(l.split(":", 1) for l in fh.read().splitlines() if l.startswith("record."))
     except OSError:
         return None
